@@ -1,0 +1,187 @@
+/*
+ * fp4.h -- block-scaled 4-bit floating point (NVFP4 / MXFP4) on AMD MI355X.
+ *
+ * C ABI of libfp4.so.  Every entry point enqueues its work on `stream` (a
+ * hipStream_t passed as void*; NULL is the default stream) and returns
+ * without synchronizing.  All tensor pointers are DEVICE memory owned by the
+ * caller; the library allocates nothing and keeps no state between calls, so
+ * the calls are reentrant and may be issued from several host threads.
+ *
+ * Error behaviour: every argument is validated on the host before any HIP
+ * call; on a validation error nothing is enqueued and no output is touched.
+ * A failed launch returns FP4_EHIP (the HIP error is read and cleared).
+ * Faults inside a kernel surface at the caller's next synchronization, as for
+ * any kernel.  Nothing falls back to another algorithm: a combination the
+ * library does not implement returns FP4_EUNSUPPORTED.
+ *
+ * Formats (aisyndicate.ch "FP4 auf Blackwell: Was NVFP4 fuer lokale KI
+ * wirklich aendert", section "Was NVFP4 von frueheren 4-Bit-Formaten
+ * unterscheidet"; pimento.cloud "FP8, NVFP4 czy AWQ?", section "Czym roznia
+ * sie FP8, NVFP4, MXFP4 i AWQ?"):
+ *   element  E2M1: sign, 2 exponent bits (bias 1), 1 mantissa bit;
+ *            magnitudes {0, 0.5, 1, 1.5, 2, 3, 4, 6}.
+ *   NVFP4    blocks of 16 elements, one E4M3 scale byte per block (bias 7,
+ *            max 448) and one FP32 scale per tensor.
+ *   MXFP4    blocks of 32 elements, one E8M0 scale byte per block (2^(c-127)).
+ *
+ * Layouts (canonical at this boundary):
+ *   values   row-major [rows, k], contiguous; blocks run along k, so k must be
+ *            a multiple of the block size (16 or 32).
+ *   codes    uint8 [rows, k/2]: byte j of a row holds element 2j in its low
+ *            nibble and element 2j+1 in its high nibble.
+ *   scales   uint8 [rows, k/block], row-major, one byte per block.
+ *   tensor scale (NVFP4 only): one float in device memory.
+ *
+ * Rounding (the pages state none; these are the library's definitions):
+ *   NVFP4 tensor scale s_t = fp32(max|x| / 2688) (2688 = 6 * 448), or 1 when
+ *   that is 0.  Block scale = E4M3 nearest-even of fp32(a_b / fp32(6 s_t)),
+ *   saturating at 448.  S_b = fp32(E4M3(sb) * s_t); elements are scaled by one
+ *   multiply with r_b = fp32(1 / S_b) (a block with S_b == 0 or an infinite
+ *   r_b keeps only sign bits) and rounded to E2M1 nearest-even with ties to
+ *   the even code, saturating at 6; the sign of zero is kept.
+ *   MXFP4 block scale = smallest 2^k with a_b <= 6 * 2^k ("rounded to the
+ *   next power of two"), clamped to [2^-127, 2^127]; an all-zero block gets
+ *   code 0.  Elements are x * 2^-k (exact) rounded as above.
+ * Non-finite inputs are outside the contract (no fault, unspecified codes).
+ */
+#ifndef FP4_H
+#define FP4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FP4_NVFP4 = 0, /* 16-element blocks, E4M3 block scale + FP32 tensor scale */
+  FP4_MXFP4 = 1  /* 32-element blocks, E8M0 block scale */
+} fp4_format;
+
+typedef enum {
+  FP4_F32 = 0,  /* IEEE binary32 */
+  FP4_BF16 = 1, /* bfloat16 */
+  FP4_F16 = 2,  /* IEEE binary16 */
+  FP4_E4M3 = 3  /* FP8 E4M3 (bias 7, max 448, no infinity) */
+} fp4_dtype;
+
+typedef enum {
+  FP4_OK = 0,
+  FP4_EINVAL = 1,       /* bad argument: null/misaligned pointer, bad size or enum */
+  FP4_EUNSUPPORTED = 2, /* valid but not implemented combination */
+  FP4_EHIP = 3          /* a HIP launch failed */
+} fp4_status;
+
+typedef enum {
+  FP4_TSCALE_COMPUTE = 0, /* NVFP4: compute s_t from the data, write it to *tensor_scale */
+  FP4_TSCALE_GIVEN = 1    /* NVFP4: read s_t from *tensor_scale (positive, finite) */
+} fp4_tscale_mode;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* fp4_status_string(fp4_status s);
+
+/* Bytes of device workspace fp4_quantize / fp4_hadamard_quantize need for
+ * these arguments: nonzero only for NVFP4 in FP4_TSCALE_COMPUTE mode (the
+ * per-workgroup partial maxima of the tensor amax pass). */
+size_t fp4_quantize_workspace_size(fp4_format fmt, fp4_tscale_mode mode,
+                                   int64_t rows, int64_t k);
+
+/*
+ * fp4_quantize -- block-scaled FP4 quantization of x [rows, k].
+ * Defines: the NVFP4 / MXFP4 formats of the two pages cited above; the
+ * "dynamic scaling" of the FP32 tensor scale (aisyndicate.ch, same section)
+ * is FP4_TSCALE_COMPUTE.
+ *   fmt           FP4_NVFP4 or FP4_MXFP4.
+ *   x, x_dtype    input values, FP4_F32 / FP4_BF16 / FP4_F16; 16-byte aligned.
+ *   rows, k       rows >= 0 (0 enqueues nothing), k > 0, k % block == 0,
+ *                 rows * k < 2^40.
+ *   codes         out, uint8 [rows, k/2]; 16-byte aligned.
+ *   scales        out, uint8 [rows, k/block]; 4-byte aligned.
+ *   tensor_scale  NVFP4: one device float, written (COMPUTE) or read (GIVEN);
+ *                 MXFP4: must be NULL.
+ *   mode          FP4_TSCALE_COMPUTE or FP4_TSCALE_GIVEN (ignored for MXFP4).
+ *   workspace     device scratch of at least fp4_quantize_workspace_size()
+ *                 bytes (may be NULL when that size is 0); 16-byte aligned.
+ * Returns FP4_OK, FP4_EINVAL or FP4_EHIP.
+ */
+fp4_status fp4_quantize(fp4_format fmt, const void* x, fp4_dtype x_dtype,
+                        int64_t rows, int64_t k, uint8_t* codes,
+                        uint8_t* scales, float* tensor_scale,
+                        fp4_tscale_mode mode, void* workspace,
+                        size_t workspace_bytes, void* stream);
+
+/*
+ * fp4_hadamard_quantize -- rotate each block of x by H_b / sqrt(b), then
+ * quantize exactly as fp4_quantize does (the tensor amax of COMPUTE mode is
+ * taken over the rotated values).
+ * Defines: the blockwise Hadamard transform of MR-GPTQ, applied online to
+ * activations and offline to weights (hyper.ai, paper 2509.23202, Abstract).
+ *   b = block size (16 for NVFP4, 32 for MXFP4); H_b is the Sylvester
+ *   Hadamard matrix, computed in fp32 as the butterfly stages h = 1, 2, ...,
+ *   b/2, each pair (j, j+h) -> (y_j + y_{j+h}, y_j - y_{j+h}), then one
+ *   multiply by fp32(1/sqrt(b)).  Because H_b H_b^T = b I, a rotated X times a
+ *   rotated W^T equals X W^T.
+ *   Arguments, alignment and errors as fp4_quantize.
+ */
+fp4_status fp4_hadamard_quantize(fp4_format fmt, const void* x,
+                                 fp4_dtype x_dtype, int64_t rows, int64_t k,
+                                 uint8_t* codes, uint8_t* scales,
+                                 float* tensor_scale, fp4_tscale_mode mode,
+                                 void* workspace, size_t workspace_bytes,
+                                 void* stream);
+
+/*
+ * fp4_dequantize -- codes + scales -> values.
+ * Defines: the inverse of the formats above; FP4_E4M3 output is the FP8 form
+ * an NVFP4 KV cache is dequantized to before attention (hyper.ai story on the
+ * NVFP4 KV cache).
+ *   NVFP4: y = fp32(fp32(v * E4M3(sb)) * s_t) -- the exact product rounded
+ *   once; MXFP4: y = v * 2^(c-127) (exact).  Then converted to out_dtype:
+ *   FP4_F32 as is; FP4_BF16 / FP4_F16 round to nearest even; FP4_E4M3 round
+ *   to nearest even, saturating to +-448 (never NaN).
+ *   codes, scales   inputs, layouts above; 16- and 4-byte aligned.
+ *   tensor_scale    NVFP4: one device float; MXFP4: must be NULL.
+ *   rows, k         as fp4_quantize.
+ *   out             [rows, k] of out_dtype; 16-byte aligned.
+ * Returns FP4_OK, FP4_EINVAL or FP4_EHIP.
+ */
+fp4_status fp4_dequantize(fp4_format fmt, const uint8_t* codes,
+                          const uint8_t* scales, const float* tensor_scale,
+                          int64_t rows, int64_t k, void* out,
+                          fp4_dtype out_dtype, void* stream);
+
+/* Bytes of device workspace fp4_gemm needs for these sizes (0 today). */
+size_t fp4_gemm_workspace_size(fp4_format fmt, int64_t m, int64_t n, int64_t k);
+
+/*
+ * fp4_gemm -- W4A4 matrix multiply C = A B^T on quantized operands.
+ * Defines: W4A4, both weights and activations 4-bit so the products run on
+ * low-precision matrix units (pimento.cloud, section "Dlaczego W8A8 i W4A16
+ * to nie to samo?").
+ *   A = activations [m, k] (codes [m, k/2], scales [m, k/block], a_tscale);
+ *   B = weights     [n, k] (codes [n, k/2], scales [n, k/block], b_tscale);
+ *   both in the same format, blocks along k.  C[i, j] = sum over k of
+ *   deq(A)[i, kk] * deq(B)[j, kk], accumulated in fp32: MXFP4 on the gfx950
+ *   block-scaled MFMA (E8M0 scale per 32 values); NVFP4 by exact in-register
+ *   products v * E4M3(sb) in bf16 on bf16 MFMA, times a_tscale * b_tscale at
+ *   the end.
+ *   c, c_dtype      out, row-major [m, n], FP4_F32 or FP4_BF16 (nearest even).
+ *   a_tscale, b_tscale  NVFP4: device floats; MXFP4: must be NULL.
+ *   workspace       may be NULL when fp4_gemm_workspace_size() is 0.
+ *   m, n >= 0 (0 enqueues nothing), k > 0 with k % 32 == 0 (NVFP4 too).
+ * Pointer alignment: codes 16 bytes, scales 4 bytes, c 16 bytes.
+ * Returns FP4_OK, FP4_EINVAL, FP4_EUNSUPPORTED or FP4_EHIP.
+ */
+fp4_status fp4_gemm(fp4_format fmt, int64_t m, int64_t n, int64_t k,
+                    const uint8_t* a_codes, const uint8_t* a_scales,
+                    const float* a_tscale, const uint8_t* b_codes,
+                    const uint8_t* b_scales, const float* b_tscale, void* c,
+                    fp4_dtype c_dtype, void* workspace, size_t workspace_bytes,
+                    void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP4_H */

@@ -1,1 +1,10 @@
-"""Block-scaled FP4 (NVFP4 / MXFP4) quantization and W4A4 GEMM for MI355X."""
+"""Block-scaled FP4 (NVFP4 / MXFP4) quantization and W4A4 GEMM for MI355X.
+
+The compute lives in libfp4.so (HIP kernels for gfx950 behind the C ABI in
+include/fp4.h); `fp4` is its Python binding.
+"""
+
+from . import fp4
+from .fp4 import quantize, hadamard_quantize, dequantize, gemm, lib
+
+__all__ = ["fp4", "quantize", "hadamard_quantize", "dequantize", "gemm", "lib"]

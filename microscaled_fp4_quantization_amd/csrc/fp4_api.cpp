@@ -1,0 +1,165 @@
+// C ABI of libfp4.so (declared in include/fp4.h): host-side argument checks
+// and dispatch to the HIP launchers.  Every check runs before any HIP call,
+// so a rejected call enqueues nothing and touches no output.
+#include "fp4.h"
+
+#include <hip/hip_runtime.h>
+
+#include "launch.hpp"
+
+namespace {
+
+constexpr int64_t kMaxElements = int64_t(1) << 40;
+
+bool aligned(const void* p, uintptr_t a) {
+  return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0;
+}
+
+int block_of(fp4_format f) { return f == FP4_NVFP4 ? 16 : 32; }
+
+bool valid_format(fp4_format f) { return f == FP4_NVFP4 || f == FP4_MXFP4; }
+
+fp4_status from_hip(hipError_t e) {
+  if (e == hipSuccess) return FP4_OK;
+  (void)hipGetLastError();   // clear the sticky launch error
+  return FP4_EHIP;
+}
+
+// Shared checks of fp4_quantize / fp4_hadamard_quantize.
+fp4_status check_quantize(fp4_format fmt, const void* x, fp4_dtype x_dtype,
+                          int64_t rows, int64_t k, const uint8_t* codes,
+                          const uint8_t* scales, const float* tensor_scale,
+                          fp4_tscale_mode mode, const void* workspace,
+                          size_t workspace_bytes) {
+  if (!valid_format(fmt)) return FP4_EINVAL;
+  if (x_dtype != FP4_F32 && x_dtype != FP4_BF16 && x_dtype != FP4_F16) return FP4_EINVAL;
+  if (fmt == FP4_NVFP4 && mode != FP4_TSCALE_COMPUTE && mode != FP4_TSCALE_GIVEN) return FP4_EINVAL;
+  if (rows < 0 || k <= 0 || k % block_of(fmt) != 0) return FP4_EINVAL;
+  if (rows > 0 && k > kMaxElements / rows) return FP4_EINVAL;
+  if (rows == 0) return FP4_OK;
+  if (!x || !codes || !scales) return FP4_EINVAL;
+  if (!aligned(x, 16) || !aligned(codes, 16) || !aligned(scales, 4)) return FP4_EINVAL;
+  if (fmt == FP4_NVFP4) {
+    if (!tensor_scale || !aligned(tensor_scale, 4)) return FP4_EINVAL;
+    const size_t need = fp4_quantize_workspace_size(fmt, mode, rows, k);
+    if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 16))) return FP4_EINVAL;
+  } else if (tensor_scale) {
+    return FP4_EINVAL;
+  }
+  return FP4_OK;
+}
+
+fp4_status quantize_common(bool hadamard, fp4_format fmt, const void* x,
+                           fp4_dtype x_dtype, int64_t rows, int64_t k,
+                           uint8_t* codes, uint8_t* scales, float* tensor_scale,
+                           fp4_tscale_mode mode, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  fp4_status s = check_quantize(fmt, x, x_dtype, rows, k, codes, scales,
+                                tensor_scale, mode, workspace, workspace_bytes);
+  if (s != FP4_OK || rows == 0) return s;
+  const bool compute = fmt == FP4_NVFP4 && mode == FP4_TSCALE_COMPUTE;
+  return from_hip(launch_quantize((int)fmt, hadamard, x, (int)x_dtype, rows * k,
+                                  codes, scales, tensor_scale, compute,
+                                  workspace, static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* fp4_status_string(fp4_status s) {
+  switch (s) {
+    case FP4_OK: return "FP4_OK";
+    case FP4_EINVAL: return "FP4_EINVAL: invalid argument";
+    case FP4_EUNSUPPORTED: return "FP4_EUNSUPPORTED: combination not implemented";
+    case FP4_EHIP: return "FP4_EHIP: HIP launch failed";
+  }
+  return "unknown fp4_status";
+}
+
+size_t fp4_quantize_workspace_size(fp4_format fmt, fp4_tscale_mode mode,
+                                   int64_t rows, int64_t k) {
+  (void)rows;
+  (void)k;
+  if (!valid_format(fmt)) return 0;
+  return quantize_workspace_bytes((int)fmt, fmt == FP4_NVFP4 && mode == FP4_TSCALE_COMPUTE);
+}
+
+fp4_status fp4_quantize(fp4_format fmt, const void* x, fp4_dtype x_dtype,
+                        int64_t rows, int64_t k, uint8_t* codes,
+                        uint8_t* scales, float* tensor_scale,
+                        fp4_tscale_mode mode, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  return quantize_common(false, fmt, x, x_dtype, rows, k, codes, scales,
+                         tensor_scale, mode, workspace, workspace_bytes, stream);
+}
+
+fp4_status fp4_hadamard_quantize(fp4_format fmt, const void* x,
+                                 fp4_dtype x_dtype, int64_t rows, int64_t k,
+                                 uint8_t* codes, uint8_t* scales,
+                                 float* tensor_scale, fp4_tscale_mode mode,
+                                 void* workspace, size_t workspace_bytes,
+                                 void* stream) {
+  return quantize_common(true, fmt, x, x_dtype, rows, k, codes, scales,
+                         tensor_scale, mode, workspace, workspace_bytes, stream);
+}
+
+fp4_status fp4_dequantize(fp4_format fmt, const uint8_t* codes,
+                          const uint8_t* scales, const float* tensor_scale,
+                          int64_t rows, int64_t k, void* out,
+                          fp4_dtype out_dtype, void* stream) {
+  if (!valid_format(fmt)) return FP4_EINVAL;
+  if (out_dtype != FP4_F32 && out_dtype != FP4_BF16 && out_dtype != FP4_F16 &&
+      out_dtype != FP4_E4M3)
+    return FP4_EINVAL;
+  if (rows < 0 || k <= 0 || k % block_of(fmt) != 0) return FP4_EINVAL;
+  if (rows > 0 && k > kMaxElements / rows) return FP4_EINVAL;
+  if (rows == 0) return FP4_OK;
+  if (!codes || !scales || !out) return FP4_EINVAL;
+  if (!aligned(codes, 16) || !aligned(scales, 4) || !aligned(out, 16)) return FP4_EINVAL;
+  if (fmt == FP4_NVFP4) {
+    if (!tensor_scale || !aligned(tensor_scale, 4)) return FP4_EINVAL;
+  } else if (tensor_scale) {
+    return FP4_EINVAL;
+  }
+  return from_hip(launch_dequantize((int)fmt, codes, scales, tensor_scale, rows * k,
+                                    out, (int)out_dtype,
+                                    static_cast<hipStream_t>(stream)));
+}
+
+size_t fp4_gemm_workspace_size(fp4_format fmt, int64_t m, int64_t n, int64_t k) {
+  if (!valid_format(fmt)) return 0;
+  return gemm_workspace_bytes((int)fmt, m, n, k);
+}
+
+fp4_status fp4_gemm(fp4_format fmt, int64_t m, int64_t n, int64_t k,
+                    const uint8_t* a_codes, const uint8_t* a_scales,
+                    const float* a_tscale, const uint8_t* b_codes,
+                    const uint8_t* b_scales, const float* b_tscale, void* c,
+                    fp4_dtype c_dtype, void* workspace, size_t workspace_bytes,
+                    void* stream) {
+  if (!valid_format(fmt)) return FP4_EINVAL;
+  if (c_dtype != FP4_F32 && c_dtype != FP4_BF16) {
+    return (c_dtype == FP4_F16 || c_dtype == FP4_E4M3) ? FP4_EUNSUPPORTED : FP4_EINVAL;
+  }
+  if (m < 0 || n < 0 || k <= 0 || k % 32 != 0) return FP4_EINVAL;
+  if ((m > 0 && k > kMaxElements / m) || (n > 0 && k > kMaxElements / n)) return FP4_EINVAL;
+  if (m > 0 && n > kMaxElements / m) return FP4_EINVAL;
+  if (m == 0 || n == 0) return FP4_OK;
+  if (!a_codes || !a_scales || !b_codes || !b_scales || !c) return FP4_EINVAL;
+  if (!aligned(a_codes, 16) || !aligned(b_codes, 16) || !aligned(a_scales, 4) ||
+      !aligned(b_scales, 4) || !aligned(c, 16))
+    return FP4_EINVAL;
+  if (fmt == FP4_NVFP4) {
+    if (!a_tscale || !b_tscale || !aligned(a_tscale, 4) || !aligned(b_tscale, 4)) return FP4_EINVAL;
+  } else if (a_tscale || b_tscale) {
+    return FP4_EINVAL;
+  }
+  const size_t need = gemm_workspace_bytes((int)fmt, m, n, k);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return FP4_EINVAL;
+  return from_hip(launch_gemm((int)fmt, m, n, k, a_codes, a_scales, a_tscale,
+                              b_codes, b_scales, b_tscale, c, (int)c_dtype,
+                              workspace, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,36 @@
+// Internal host-side launchers (not part of the C ABI).  Each validates
+// nothing: fp4_api.cpp checks every argument before calling them.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+// Same values as fp4_format / fp4_dtype in include/fp4.h.
+constexpr int kFmtNV = 0;
+constexpr int kFmtMX = 1;
+constexpr int kInF32 = 0;
+constexpr int kInBF16 = 1;
+constexpr int kInF16 = 2;
+constexpr int kOutE4M3 = 3;
+
+size_t quantize_workspace_bytes(int fmt, bool compute);
+
+// n = rows * k elements (a multiple of 16 for NVFP4, 32 for MXFP4).
+hipError_t launch_quantize(int fmt, bool hadamard, const void* x, int dtype,
+                           int64_t n, uint8_t* codes, uint8_t* scales,
+                           float* tscale, bool compute, void* workspace,
+                           hipStream_t stream);
+
+hipError_t launch_dequantize(int fmt, const uint8_t* codes,
+                             const uint8_t* scales, const float* tscale,
+                             int64_t n, void* out, int out_dtype,
+                             hipStream_t stream);
+
+size_t gemm_workspace_bytes(int fmt, int64_t m, int64_t n, int64_t k);
+
+hipError_t launch_gemm(int fmt, int64_t m, int64_t n, int64_t k,
+                       const uint8_t* a_codes, const uint8_t* a_scales,
+                       const float* a_tscale, const uint8_t* b_codes,
+                       const uint8_t* b_scales, const float* b_tscale, void* c,
+                       int c_dtype, void* workspace, hipStream_t stream);

@@ -1,0 +1,275 @@
+// Block-scaled FP4 quantization kernels for gfx950: NVFP4 (16-element blocks,
+// E4M3 scale, FP32 tensor scale) and MXFP4 (32-element blocks, E8M0 scale),
+// optionally preceded by the blockwise Hadamard rotation of MR-GPTQ.
+//
+// Formats: aisyndicate.ch "FP4 auf Blackwell", section "Was NVFP4 von
+// frueheren 4-Bit-Formaten unterscheidet"; pimento.cloud "FP8, NVFP4 czy
+// AWQ?", section "Czym roznia sie FP8, NVFP4, MXFP4 i AWQ?".  Rotation:
+// hyper.ai, paper 2509.23202, Abstract (blockwise Hadamard transforms,
+// computed online for activations).
+//
+// Work decomposition.  A [rows, k] tensor with k a multiple of the block size
+// is a flat run of blocks, so the kernels see it as n = rows*k elements cut
+// into chunks of 8.  Lane t of a wave owns chunk base + t: one 16-byte load
+// for bf16/fp16 input (two for fp32), so every load instruction of a wave
+// reads 1 KiB (bf16) of contiguous memory.  An NVFP4 block is a lane pair
+// (t, t^1), an MXFP4 block a lane quad; block max and the cross-lane
+// butterfly stages use DPP quad permutes.  Each lane writes its 8 codes as
+// one dword (contiguous across the wave) and the first lane of a block writes
+// the scale byte.
+#include "device_common.hpp"
+#include "launch.hpp"
+
+using namespace fp4dev;
+
+namespace {
+
+constexpr int kThreads = 256;        // 4 waves of 64
+constexpr int kUnroll = 4;           // chunks per thread per loop trip
+constexpr int kChunksPerTrip = kThreads * kUnroll;
+constexpr int kMaxPartials = 1024;   // amax partials (workspace floats)
+constexpr int kMaxGrid = 4096;       // grid-stride cap (16 workgroups per CU)
+
+// 8 elements of chunk c widened to fp32 (exact); zeros when !valid.
+template <int DT>
+__device__ __forceinline__ void load_chunk(const void* __restrict__ x, int64_t c,
+                                           bool valid, float v[8]) {
+  if (DT == kInF32) {
+    const float4* p = reinterpret_cast<const float4*>(x) + 2 * c;
+    float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = a;
+    if (valid) { a = p[0]; b = p[1]; }
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  } else {
+    const uint4* p = reinterpret_cast<const uint4*>(x) + c;
+    uint4 w = make_uint4(0u, 0u, 0u, 0u);
+    if (valid) w = *p;
+    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (DT == kInBF16) {
+        v[2 * i] = bf16_lo(ws[i]);
+        v[2 * i + 1] = bf16_hi(ws[i]);
+      } else {
+        v2h h = __builtin_bit_cast(v2h, ws[i]);
+        v[2 * i] = (float)h.x;
+        v[2 * i + 1] = (float)h.y;
+      }
+    }
+  }
+}
+
+// In-place blockwise Hadamard of the 8 values a lane holds, for blocks of B
+// (16: lane pair, 32: lane quad).  Butterfly stages h = 1, 2, 4 inside the
+// lane, h = 8 with lane ^ 1, h = 16 with lane ^ 2; each stage turns the pair
+// (lower, upper) into (lower + upper, lower - upper) in fp32.  Then one
+// multiply by fp32(1/sqrt(B)).
+template <int B>
+__device__ __forceinline__ void fwht_chunk(float v[8], int lane) {
+#pragma unroll
+  for (int h = 1; h < 8; h *= 2) {
+#pragma unroll
+    for (int s = 0; s < 8; s += 2 * h) {
+#pragma unroll
+      for (int j = s; j < s + h; ++j) {
+        float u = v[j], w = v[j + h];
+        v[j] = u + w;
+        v[j + h] = u - w;
+      }
+    }
+  }
+  const bool up1 = (lane & 1) != 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    float p = dpp_f<kDppXor1>(v[j]);
+    v[j] = up1 ? (p - v[j]) : (v[j] + p);
+  }
+  if (B == 32) {
+    const bool up2 = (lane & 2) != 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      float p = dpp_f<kDppXor2>(v[j]);
+      v[j] = up2 ? (p - v[j]) : (v[j] + p);
+    }
+  }
+  const float cb = (B == 16) ? 0.25f : __uint_as_float(0x3E3504F3u);  // fp32(1/sqrt(32))
+#pragma unroll
+  for (int j = 0; j < 8; ++j) v[j] = v[j] * cb;
+}
+
+__device__ __forceinline__ float amax8(const float v[8]) {
+  float a = fmaxf(fabsf(v[0]), fabsf(v[1]));
+  a = fmaxf(a, fmaxf(fabsf(v[2]), fabsf(v[3])));
+  a = fmaxf(a, fmaxf(fabsf(v[4]), fabsf(v[5])));
+  return fmaxf(a, fmaxf(fabsf(v[6]), fabsf(v[7])));
+}
+
+__device__ __forceinline__ float wave_max(float m) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  return m;
+}
+
+// Max over the workgroup; every thread gets the result.
+__device__ __forceinline__ float block_max(float m) {
+  __shared__ float red[kThreads / 64];
+  m = wave_max(m);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  float r = red[0];
+#pragma unroll
+  for (int i = 1; i < kThreads / 64; ++i) r = fmaxf(r, red[i]);
+  __syncthreads();
+  return r;
+}
+
+// Pass 1 of dynamic NVFP4 scaling: per-workgroup max |x| (of the rotated
+// values when HAD > 0) into partials[blockIdx.x].
+template <int DT, int HAD>
+__global__ __launch_bounds__(kThreads) void amax_partial_kernel(
+    const void* __restrict__ x, int64_t nchunks, float* __restrict__ partials) {
+  const int lane = threadIdx.x & 63;
+  float m = 0.0f;
+  for (int64_t base = (int64_t)blockIdx.x * kChunksPerTrip; base < nchunks;
+       base += (int64_t)gridDim.x * kChunksPerTrip) {
+#pragma unroll
+    for (int j = 0; j < kUnroll; ++j) {
+      const int64_t c = base + j * kThreads + threadIdx.x;
+      float v[8];
+      load_chunk<DT>(x, c, c < nchunks, v);
+      if (HAD) fwht_chunk<HAD>(v, lane);
+      m = fmaxf(m, amax8(v));
+    }
+  }
+  m = block_max(m);
+  if (threadIdx.x == 0) partials[blockIdx.x] = m;
+}
+
+// Quantize.  FMT: kFmtNV / kFmtMX.  HAD: 0, 16 or 32.  COMPUTE (NVFP4):
+// reduce the amax partials to s_t here (every workgroup, redundantly: at
+// most 4 KiB from L2) and let workgroup 0 publish it; otherwise read s_t.
+template <int FMT, int DT, int HAD, bool COMPUTE>
+__global__ __launch_bounds__(kThreads) void quantize_kernel(
+    const void* __restrict__ x, int64_t nchunks, uint32_t* __restrict__ codes,
+    uint8_t* __restrict__ scales, float* __restrict__ tscale,
+    const float* __restrict__ partials, int npartials) {
+  const int lane = threadIdx.x & 63;
+  float s_t = 1.0f, d = 6.0f;
+  if (FMT == kFmtNV) {
+    if (COMPUTE) {
+      float m = 0.0f;
+      for (int i = threadIdx.x; i < npartials; i += kThreads) m = fmaxf(m, partials[i]);
+      const float A = block_max(m);
+      s_t = A / 2688.0f;                       // 6 * 448
+      if (s_t == 0.0f) s_t = 1.0f;
+      if (blockIdx.x == 0 && threadIdx.x == 0) *tscale = s_t;
+    } else {
+      s_t = *tscale;
+    }
+    d = 6.0f * s_t;
+  }
+
+  for (int64_t base = (int64_t)blockIdx.x * kChunksPerTrip; base < nchunks;
+       base += (int64_t)gridDim.x * kChunksPerTrip) {
+    float v[kUnroll][8];
+#pragma unroll
+    for (int j = 0; j < kUnroll; ++j) {
+      const int64_t c = base + j * kThreads + threadIdx.x;
+      load_chunk<DT>(x, c, c < nchunks, v[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < kUnroll; ++j) {
+      const int64_t c = base + j * kThreads + threadIdx.x;
+      const bool valid = c < nchunks;
+      if (HAD) fwht_chunk<HAD>(v[j], lane);
+      float a = amax8(v[j]);
+      a = fmaxf(a, dpp_f<kDppXor1>(a));
+      float r;
+      uint32_t sbyte;
+      if (FMT == kFmtNV) {
+        const float u = a / d;
+        sbyte = e4m3_encode_pos(u);
+        const float S = e4m3_decode_pos(sbyte) * s_t;
+        r = 1.0f / S;
+        // S == 0 (zero block) or an overflowing reciprocal: sign bits only.
+        if (!(S != 0.0f && r < __builtin_inff())) r = 0.0f;
+      } else {
+        a = fmaxf(a, dpp_f<kDppXor2>(a));
+        const int kx = mx_block_exponent(a);
+        sbyte = (uint32_t)(kx + 127);
+        r = as_f((uint32_t)(127 - kx) << 23);  // 2^-k, a normal float for k in [-127, 126]
+      }
+      float q[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) q[i] = v[j][i] * r;
+      uint32_t w = e2m1_pack2<0>(0u, q[0], q[1]);
+      w = e2m1_pack2<1>(w, q[2], q[3]);
+      w = e2m1_pack2<2>(w, q[4], q[5]);
+      w = e2m1_pack2<3>(w, q[6], q[7]);
+      if (valid) {
+        __builtin_nontemporal_store(w, codes + c);
+        if (FMT == kFmtNV) {
+          if ((lane & 1) == 0) scales[c >> 1] = (uint8_t)sbyte;
+        } else {
+          if ((lane & 3) == 0) scales[c >> 2] = (uint8_t)sbyte;
+        }
+      }
+    }
+  }
+}
+
+template <int FMT, int DT, int HAD>
+hipError_t launch_typed(const void* x, int64_t nchunks, uint8_t* codes,
+                        uint8_t* scales, float* tscale, bool compute,
+                        void* workspace, hipStream_t stream) {
+  int64_t trips = (nchunks + kChunksPerTrip - 1) / kChunksPerTrip;
+  const int grid = (int)(trips < kMaxGrid ? trips : kMaxGrid);
+  uint32_t* codes32 = reinterpret_cast<uint32_t*>(codes);
+  if (FMT == kFmtNV && compute) {
+    float* partials = reinterpret_cast<float*>(workspace);
+    const int g = (int)(trips < kMaxPartials ? trips : kMaxPartials);
+    hipLaunchKernelGGL((amax_partial_kernel<DT, HAD>), dim3(g), dim3(kThreads), 0,
+                       stream, x, nchunks, partials);
+    hipLaunchKernelGGL((quantize_kernel<FMT, DT, HAD, true>), dim3(grid), dim3(kThreads),
+                       0, stream, x, nchunks, codes32, scales, tscale,
+                       (const float*)partials, g);
+  } else {
+    hipLaunchKernelGGL((quantize_kernel<FMT, DT, HAD, false>), dim3(grid),
+                       dim3(kThreads), 0, stream, x, nchunks, codes32, scales,
+                       tscale, (const float*)nullptr, 0);
+  }
+  return hipGetLastError();
+}
+
+template <int FMT, int HAD>
+hipError_t launch_dtype(int dtype, const void* x, int64_t nchunks, uint8_t* codes,
+                        uint8_t* scales, float* tscale, bool compute,
+                        void* workspace, hipStream_t stream) {
+  switch (dtype) {
+    case kInF32:
+      return launch_typed<FMT, kInF32, HAD>(x, nchunks, codes, scales, tscale, compute, workspace, stream);
+    case kInBF16:
+      return launch_typed<FMT, kInBF16, HAD>(x, nchunks, codes, scales, tscale, compute, workspace, stream);
+    default:
+      return launch_typed<FMT, kInF16, HAD>(x, nchunks, codes, scales, tscale, compute, workspace, stream);
+  }
+}
+
+}  // namespace
+
+size_t quantize_workspace_bytes(int fmt, bool compute) {
+  return (fmt == kFmtNV && compute) ? kMaxPartials * sizeof(float) : 0;
+}
+
+hipError_t launch_quantize(int fmt, bool hadamard, const void* x, int dtype,
+                           int64_t n, uint8_t* codes, uint8_t* scales,
+                           float* tscale, bool compute, void* workspace,
+                           hipStream_t stream) {
+  const int64_t nchunks = n / 8;
+  if (fmt == kFmtNV) {
+    return hadamard ? launch_dtype<kFmtNV, 16>(dtype, x, nchunks, codes, scales, tscale, compute, workspace, stream)
+                    : launch_dtype<kFmtNV, 0>(dtype, x, nchunks, codes, scales, tscale, compute, workspace, stream);
+  }
+  return hadamard ? launch_dtype<kFmtMX, 32>(dtype, x, nchunks, codes, scales, tscale, false, workspace, stream)
+                  : launch_dtype<kFmtMX, 0>(dtype, x, nchunks, codes, scales, tscale, false, workspace, stream);
+}

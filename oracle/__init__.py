@@ -50,6 +50,7 @@ from .quant import (
     MX_BLOCK,
     NV_TSCALE_DIVISOR,
     nvfp4_tensor_scale,
+    nvfp4_tensor_scale_from_amax,
     nvfp4_quantize,
     mxfp4_quantize,
     dequantize,
@@ -64,7 +65,7 @@ __all__ = [
     "E2M1_MAGNITUDES", "e2m1_decode", "e2m1_encode", "e4m3_decode",
     "e4m3_encode", "e4m3_encode_signed", "e8m0_decode", "e8m0_encode_exponent",
     "bf16_round", "NV_BLOCK", "MX_BLOCK", "NV_TSCALE_DIVISOR",
-    "nvfp4_tensor_scale", "nvfp4_quantize", "mxfp4_quantize", "dequantize",
+    "nvfp4_tensor_scale", "nvfp4_tensor_scale_from_amax", "nvfp4_quantize", "mxfp4_quantize", "dequantize",
     "dequantize_exact_f64", "pack_nibbles", "unpack_nibbles",
     "hadamard_blocks", "HADAMARD_NORM", "gemm_ref", "gemm_ref_entries",
 ]

@@ -71,14 +71,19 @@ def unpack_nibbles(packed):
     return out
 
 
-def nvfp4_tensor_scale(x):
-    """FP32 second-level scale of a tensor: fp32(max|x| / 2688), or 1.0 when
-    that is zero."""
-    a = np.float32(np.max(np.abs(np.asarray(x, dtype=np.float32)))) if np.size(x) else np.float32(0)
-    s_t = np.float32(a / NV_TSCALE_DIVISOR)
+def nvfp4_tensor_scale_from_amax(a):
+    """FP32 second-level scale for a tensor whose max |x| is a:
+    fp32(a / 2688), or 1.0 when that is zero."""
+    s_t = np.float32(np.float32(a) / NV_TSCALE_DIVISOR)
     if s_t == 0:
         s_t = np.float32(1.0)
     return s_t
+
+
+def nvfp4_tensor_scale(x):
+    """FP32 second-level scale of a tensor x."""
+    a = np.float32(np.max(np.abs(np.asarray(x, dtype=np.float32)))) if np.size(x) else np.float32(0)
+    return nvfp4_tensor_scale_from_amax(a)
 
 
 def nvfp4_quantize(x, tensor_scale=None):

@@ -1,0 +1,124 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry
+point include/fp4.h declares, and rejects bad arguments on the host before
+any HIP call (every case below fails validation, so nothing is launched)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from microscaled_fp4_quantization_amd import fp4
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+NV, MX = fp4.NVFP4, fp4.MXFP4
+FAKE = ctypes.c_void_p(0x10000)        # aligned, never dereferenced
+FAKE_ODD = ctypes.c_void_p(0x10001)    # misaligned
+
+
+def header_functions():
+    src = open(os.path.join(ROOT, "include", "fp4.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(fp4_[a-z_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_function():
+    L = fp4.lib()
+    names = header_functions()
+    assert set(names) == set(fp4.EXPORTS)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings():
+    L = fp4.lib()
+    for s in range(4):
+        assert L.fp4_status_string(s).decode().startswith("FP4_")
+    assert L.fp4_status_string(99) == b"unknown fp4_status"
+
+
+def test_workspace_sizes():
+    L = fp4.lib()
+    assert L.fp4_quantize_workspace_size(NV, fp4.TSCALE_COMPUTE, 4096, 4096) == 4096
+    assert L.fp4_quantize_workspace_size(NV, fp4.TSCALE_GIVEN, 4096, 4096) == 0
+    assert L.fp4_quantize_workspace_size(MX, fp4.TSCALE_COMPUTE, 4096, 4096) == 0
+    assert L.fp4_gemm_workspace_size(NV, 16, 16, 256) >= 0
+
+
+def _q(fn, fmt=NV, x=FAKE, dt=fp4.BF16, rows=4, k=64, codes=FAKE, scales=FAKE,
+       ts=FAKE, mode=fp4.TSCALE_GIVEN, ws=None, wsb=0):
+    return fn(fmt, x, dt, rows, k, codes, scales, ts, mode, ws, wsb, None)
+
+
+@pytest.mark.parametrize("name", ["fp4_quantize", "fp4_hadamard_quantize"])
+def test_quantize_rejects_bad_arguments(name):
+    f = getattr(fp4.lib(), name)
+    E = fp4.EINVAL
+    assert _q(f, fmt=7) == E
+    assert _q(f, dt=fp4.E4M3) == E                       # not an input dtype
+    assert _q(f, k=40) == E                              # k % 16
+    assert _q(f, fmt=MX, ts=None, k=48) == E             # k % 32
+    assert _q(f, k=0) == E
+    assert _q(f, rows=-1) == E
+    assert _q(f, rows=1 << 30, k=1 << 20) == E           # over 2^40 elements
+    assert _q(f, x=None) == E
+    assert _q(f, codes=None) == E
+    assert _q(f, scales=None) == E
+    assert _q(f, ts=None) == E                           # NVFP4 needs the tensor scale
+    assert _q(f, fmt=MX) == E                            # MXFP4 takes none
+    assert _q(f, x=FAKE_ODD) == E
+    assert _q(f, codes=FAKE_ODD) == E
+    assert _q(f, mode=5) == E
+    # COMPUTE mode without enough workspace
+    assert _q(f, mode=fp4.TSCALE_COMPUTE) == E
+    assert _q(f, mode=fp4.TSCALE_COMPUTE, ws=FAKE, wsb=16) == E
+    # zero rows is a valid no-op (nothing launched)
+    assert _q(f, rows=0, x=None, codes=None, scales=None) == fp4.OK
+
+
+def test_dequantize_rejects_bad_arguments():
+    f = fp4.lib().fp4_dequantize
+    E = fp4.EINVAL
+
+    def d(fmt=NV, codes=FAKE, scales=FAKE, ts=FAKE, rows=4, k=64, out=FAKE, dt=fp4.E4M3):
+        return f(fmt, codes, scales, ts, rows, k, out, dt, None)
+
+    assert d(fmt=3) == E
+    assert d(dt=9) == E
+    assert d(k=24) == E
+    assert d(codes=None) == E
+    assert d(out=None) == E
+    assert d(ts=None) == E
+    assert d(fmt=MX) == E
+    assert d(out=FAKE_ODD) == E
+    assert d(rows=0, codes=None, out=None) == fp4.OK
+
+
+def test_gemm_rejects_bad_arguments():
+    f = fp4.lib().fp4_gemm
+
+    def g(fmt=NV, m=8, n=8, k=64, a=FAKE, asc=FAKE, at=FAKE, b=FAKE, bsc=FAKE, bt=FAKE,
+          c=FAKE, dt=fp4.BF16):
+        return f(fmt, m, n, k, a, asc, at, b, bsc, bt, c, dt, None, 0, None)
+
+    E = fp4.EINVAL
+    assert g(fmt=2) == E
+    assert g(k=48) == E                       # k % 32
+    assert g(m=-1) == E
+    assert g(a=None) == E
+    assert g(bsc=None) == E
+    assert g(c=FAKE_ODD) == E
+    assert g(at=None) == E
+    assert g(fmt=MX) == E                     # MXFP4 takes no tensor scales
+    assert g(dt=fp4.F16) == fp4.EUNSUPPORTED
+    assert g(dt=fp4.E4M3) == fp4.EUNSUPPORTED
+    assert g(dt=11) == E
+    assert g(m=0, a=None, c=None) == fp4.OK
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(fp4, "_lib", None)
+    monkeypatch.setattr(fp4, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        fp4.lib()

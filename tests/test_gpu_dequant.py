@@ -1,0 +1,120 @@
+"""GPU parity: fp4_dequantize bit-exact against the CPU oracle for every
+output type, plus the KV-cache stream (quantize with a given tensor scale,
+dequantize to FP8 E4M3) at full size on sampled slices."""
+
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import microscaled_fp4_quantization_amd as fq
+from microscaled_fp4_quantization_amd import workloads
+from gpu_helpers import DEV, host_f32, note, np_u8, require_gpu
+
+pytestmark = pytest.mark.gpu
+
+_VIEW = {"f32": torch.int32, "bf16": torch.int16, "f16": torch.int16, "e4m3": torch.uint8}
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    require_gpu()
+
+
+def gpu_bits(t, out_dtype):
+    b = t.view(_VIEW[out_dtype]).cpu().numpy()
+    return b.view({"f32": np.uint32, "bf16": np.uint16, "f16": np.uint16, "e4m3": np.uint8}[out_dtype])
+
+
+def oracle_bits(fmt, packed, scales, ts, out_dtype):
+    y = oracle.dequantize(fmt, packed, scales, ts, out_dtype)
+    return y.view(np.uint32) if out_dtype == "f32" else y
+
+
+def check(fmt, codes, scales, ts, out_dtype):
+    note("dequantize %s %s -> %s" % (fmt, tuple(codes.shape), out_dtype))
+    y = fq.dequantize(codes, scales, ts, fmt, out_dtype)
+    torch.cuda.synchronize()
+    got = gpu_bits(y, out_dtype)
+    exp = oracle_bits(fmt, np_u8(codes), np_u8(scales),
+                      None if ts is None else np.float32(ts.item()), out_dtype)
+    bad = np.argwhere(got != exp)
+    assert bad.size == 0, "differs at %s: gpu %s oracle %s" % (bad[:5], got[tuple(bad[:5].T)], exp[tuple(bad[:5].T)])
+
+
+@pytest.mark.parametrize("fmt", ["nvfp4", "mxfp4"])
+@pytest.mark.parametrize("out_dtype", ["f32", "bf16", "f16", "e4m3"])
+def test_random_codes_and_scales(fmt, out_dtype):
+    bs = 16 if fmt == "nvfp4" else 32
+    g = torch.Generator().manual_seed(1)
+    for rows, k in [(1, 64), (5, 96 if fmt == "mxfp4" else 48), (300, 2048), (1031, 1024)]:
+        codes = torch.randint(0, 256, (rows, k // 2), generator=g, dtype=torch.uint8)
+        if fmt == "nvfp4":
+            scales = torch.randint(0, 127, (rows, k // bs), generator=g, dtype=torch.uint8)
+            for ts in (0.5, 1.0 / 3, 3e-3, 7.0):
+                check(fmt, codes.to(DEV), scales.to(DEV), torch.tensor([ts], device=DEV), out_dtype)
+        else:
+            lo, hi = (0, 255) if out_dtype == "f32" else (100, 150)   # stay in range of the narrow types
+            scales = torch.randint(lo, hi, (rows, k // bs), generator=g, dtype=torch.uint8)
+            check(fmt, codes.to(DEV), scales.to(DEV), None, out_dtype)
+
+
+def test_worked_examples(golden_dir):
+    g = json.load(open(os.path.join(golden_dir, "dequant_worked.json")))
+    nv = g["nvfp4"]
+    c = np.array(nv["codes_rows"], dtype=np.uint8)
+    packed = torch.from_numpy((c[:, 0::2] | (c[:, 1::2] << 4)).astype(np.uint8)).to(DEV)
+    sc = torch.tensor([[int(b, 16) for b in r] for r in nv["scales"]], dtype=torch.uint8, device=DEV)
+    ts = torch.tensor([nv["tensor_scale"]], dtype=torch.float32, device=DEV)
+    y8 = fq.dequantize(packed, sc, ts, "nvfp4", "e4m3").view(torch.uint8).cpu().numpy()
+    exp8 = np.zeros_like(y8)
+    for r, row in enumerate(nv["expected_e4m3_nonzero"]):
+        for i, v in row.items():
+            exp8[r, int(i)] = int(v, 16)
+    assert np.array_equal(y8, exp8)
+    for out_dtype in ("f32", "bf16", "f16", "e4m3"):
+        check("nvfp4", packed, sc, ts, out_dtype)
+
+
+def test_quantize_dequantize_round_trip_error():
+    x = torch.randn((256, 1024), generator=torch.Generator().manual_seed(2)).to(torch.bfloat16).to(DEV)
+    for fmt in ("nvfp4", "mxfp4"):
+        codes, scales, ts = fq.quantize(x, fmt)
+        y = fq.dequantize(codes, scales, ts, fmt, "f32")
+        torch.cuda.synchronize()
+        err = (torch.linalg.norm(y - x.float()) / torch.linalg.norm(x.float())).item()
+        assert err < (0.11 if fmt == "nvfp4" else 0.13)
+
+
+def test_kv_stream_full_size_sampled():
+    # K, V [32, 8, 32768, 128] bf16; NVFP4 along head_dim with a given tensor
+    # scale (the cache keeps one fixed scale per tensor), dequantized to FP8.
+    d = workloads.kv(device=DEV)
+    rng = np.random.default_rng(0)
+    for name in ("k", "v"):
+        t = d[name]
+        x2 = t.view(-1, 128)
+        rows = x2.shape[0]
+        amax = np.float32(torch.max(torch.abs(x2)).float().item())    # input preparation
+        s_t = oracle.nvfp4_tensor_scale_from_amax(amax)
+        ts = torch.tensor([float(s_t)], dtype=torch.float32, device=DEV)
+        note("kv quantize %s" % name)
+        codes, scales, _ = fq.quantize(x2, "nvfp4", tensor_scale=ts)
+        note("kv dequantize %s" % name)
+        y8 = fq.dequantize(codes, scales, ts, "nvfp4", "e4m3")
+        torch.cuda.synchronize()
+        for r0 in rng.integers(0, rows - 4096, size=6):
+            sl = slice(int(r0), int(r0) + 4096)
+            p, s, _ = oracle.nvfp4_quantize(host_f32(x2[sl]), s_t)
+            assert np.array_equal(np_u8(scales[sl]), s)
+            assert np.array_equal(np_u8(codes[sl]), p)
+            e8 = oracle.dequantize("nvfp4", p, s, s_t, "e4m3")
+            assert np.array_equal(y8[sl].view(torch.uint8).cpu().numpy(), e8)
+        # last rows (tail of the flat range)
+        sl = slice(rows - 64, rows)
+        p, s, _ = oracle.nvfp4_quantize(host_f32(x2[sl]), s_t)
+        assert np.array_equal(np_u8(codes[sl]), p)
+        del codes, scales, y8

@@ -1,0 +1,173 @@
+"""GPU parity: fp4_gemm against the float64 oracle of the same dequantized
+operands.  Tolerance: relative Frobenius error <= 1e-3 against the oracle
+rounded to the output type (fp32 output: the raw float64 result).  The
+MXFP4 integer special case must be bit-exact."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import microscaled_fp4_quantization_amd as fq
+from microscaled_fp4_quantization_amd import workloads
+from gpu_helpers import DEV, bf16_round_f64, host_f32, note, np_u8, rel_fro, require_gpu
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-3
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    require_gpu()
+
+
+def quant_pair(fmt, x, w, hadamard=False):
+    qx = fq.quantize(x.to(DEV), fmt, hadamard=hadamard)
+    qw = fq.quantize(w.to(DEV), fmt, hadamard=hadamard)
+    return qx, qw
+
+
+def host_q(q):
+    c, s, t = q
+    return np_u8(c), np_u8(s), (None if t is None else np.float32(t.item()))
+
+
+def ref_full(fmt, qx, qw):
+    pa, sa, ta = host_q(qx)
+    pb, sb, tb = host_q(qw)
+    return oracle.gemm_ref(fmt, pa, sa, ta, pb, sb, tb)
+
+
+def check_full(fmt, qx, qw, out_dtype, tol=TOL):
+    note("gemm %s m=%d n=%d k=%d -> %s" % (fmt, qx[0].shape[0], qw[0].shape[0], qx[0].shape[1] * 2, out_dtype))
+    c = fq.gemm(qx, qw, fmt, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    ref = ref_full(fmt, qx, qw)
+    got = c.double().cpu().numpy()
+    target = ref if out_dtype == "f32" else bf16_round_f64(ref)
+    err = rel_fro(got, target)
+    assert err <= tol, err
+    return err
+
+
+def test_mx_integer_special_case_bit_exact():
+    # all scale codes 127 (scale 1): 2v are integers in [-12, 12] and every
+    # partial sum of 4C is an integer below 2^24, so fp32 accumulation in any
+    # order is exact and C must equal int64(2vA) @ int64(2vB)^T / 4 exactly.
+    g = torch.Generator().manual_seed(0)
+    m = n = 256
+    k = 4096
+    ca = torch.randint(0, 256, (m, k // 2), generator=g, dtype=torch.uint8)
+    cb = torch.randint(0, 256, (n, k // 2), generator=g, dtype=torch.uint8)
+    sa = torch.full((m, k // 32), 127, dtype=torch.uint8)
+    sb = torch.full((n, k // 32), 127, dtype=torch.uint8)
+    note("gemm mx integer special case")
+    c = fq.gemm((ca.to(DEV), sa.to(DEV), None), (cb.to(DEV), sb.to(DEV), None), "mxfp4", out_dtype="f32")
+    torch.cuda.synchronize()
+    ia = (2 * oracle.e2m1_decode(oracle.unpack_nibbles(ca.numpy()))).astype(np.int64)
+    ib = (2 * oracle.e2m1_decode(oracle.unpack_nibbles(cb.numpy()))).astype(np.int64)
+    exact = (ia @ ib.T).astype(np.float64) / 4
+    assert np.array_equal(c.cpu().double().numpy(), exact)
+
+
+def test_nv_integer_special_case_bit_exact():
+    # NVFP4 with scale byte 0x38 (1.0) and tensor scales 1: same integer
+    # argument through the fp16 path.
+    g = torch.Generator().manual_seed(1)
+    m, n, k = 128, 192, 2048
+    ca = torch.randint(0, 256, (m, k // 2), generator=g, dtype=torch.uint8)
+    cb = torch.randint(0, 256, (n, k // 2), generator=g, dtype=torch.uint8)
+    sa = torch.full((m, k // 16), 0x38, dtype=torch.uint8)
+    sb = torch.full((n, k // 16), 0x38, dtype=torch.uint8)
+    one = torch.ones(1, dtype=torch.float32, device=DEV)
+    note("gemm nv integer special case")
+    c = fq.gemm((ca.to(DEV), sa.to(DEV), one), (cb.to(DEV), sb.to(DEV), one), "nvfp4", out_dtype="f32")
+    torch.cuda.synchronize()
+    ia = (2 * oracle.e2m1_decode(oracle.unpack_nibbles(ca.numpy()))).astype(np.int64)
+    ib = (2 * oracle.e2m1_decode(oracle.unpack_nibbles(cb.numpy()))).astype(np.int64)
+    assert np.array_equal(c.cpu().double().numpy(), (ia @ ib.T).astype(np.float64) / 4)
+
+
+@pytest.mark.parametrize("fmt", ["nvfp4", "mxfp4"])
+@pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
+def test_random_shapes(fmt, out_dtype):
+    g = torch.Generator().manual_seed(2)
+    for m, n, k in [(1, 1, 32), (7, 9, 64), (37, 50, 96), (64, 64, 128), (130, 257, 544), (256, 512, 2048)]:
+        x = torch.randn((m, k), generator=g).to(torch.bfloat16)
+        w = (torch.randn((n, k), generator=g) * 0.02).to(torch.bfloat16)
+        qx, qw = quant_pair(fmt, x, w)
+        check_full(fmt, qx, qw, out_dtype)
+
+
+def test_tiny_workload():
+    d = workloads.tiny()
+    qx, qw = quant_pair("nvfp4", d["x"], d["w"])
+    check_full("nvfp4", qx, qw, "f32")
+    qx, qw = quant_pair("mxfp4", d["x"], d["w"])
+    check_full("mxfp4", qx, qw, "f32")
+
+
+def test_block_scales_vary_per_block():
+    # each block of A and B on its own scale, including E4M3 subnormal scales
+    g = torch.Generator().manual_seed(3)
+    m, n, k = 96, 80, 512
+    for fmt, bs in (("nvfp4", 16), ("mxfp4", 32)):
+        ca = torch.randint(0, 256, (m, k // 2), generator=g, dtype=torch.uint8)
+        cb = torch.randint(0, 256, (n, k // 2), generator=g, dtype=torch.uint8)
+        if fmt == "nvfp4":
+            sa = torch.randint(1, 127, (m, k // bs), generator=g, dtype=torch.uint8)
+            sb = torch.randint(1, 127, (n, k // bs), generator=g, dtype=torch.uint8)
+            ta = torch.tensor([0.37], device=DEV)
+            tb = torch.tensor([1.9e-3], device=DEV)
+        else:
+            sa = torch.randint(110, 140, (m, k // bs), generator=g, dtype=torch.uint8)
+            sb = torch.randint(110, 140, (n, k // bs), generator=g, dtype=torch.uint8)
+            ta = tb = None
+        qx = (ca.to(DEV), sa.to(DEV), ta)
+        qw = (cb.to(DEV), sb.to(DEV), tb)
+        check_full(fmt, qx, qw, "f32")
+
+
+def _sampled(fmt, qx, qw, c, count=3000, seed=0):
+    pa, sa, ta = host_q(qx)
+    pb, sb, tb = host_q(qw)
+    m, n = c.shape
+    rng = np.random.default_rng(seed)
+    rows = rng.integers(0, m, count)
+    cols = rng.integers(0, n, count)
+    # always include the corners and the last tile edges
+    rows = np.concatenate([rows, [0, m - 1, 0, m - 1]])
+    cols = np.concatenate([cols, [0, n - 1, n - 1, 0]])
+    ref = oracle.gemm_ref_entries(fmt, pa, sa, ta, pb, sb, tb, rows, cols)
+    got = c[torch.from_numpy(rows).to(DEV), torch.from_numpy(cols).to(DEV)].double().cpu().numpy()
+    return got, ref
+
+
+def full_size_case(fmt, x, w, hadamard, out_dtype="bf16"):
+    note("full-size gemm %s m=%d n=%d k=%d" % (fmt, x.shape[0], w.shape[0], x.shape[1]))
+    qx = fq.quantize(x, fmt, hadamard=hadamard)
+    qw = fq.quantize(w, fmt, hadamard=hadamard)
+    c = fq.gemm(qx, qw, fmt, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    got, ref = _sampled(fmt, qx, qw, c)
+    target = ref if out_dtype == "f32" else bf16_round_f64(ref)
+    assert rel_fro(got, target) <= TOL
+    assert torch.isfinite(c).all()
+
+
+def test_decode_full_size():
+    d = workloads.decode(device=DEV)
+    full_size_case("nvfp4", d["x"], d["w"], False)
+    full_size_case("mxfp4", d["x"], d["w"], False)
+
+
+def test_prefill_full_size():
+    d = workloads.prefill(device=DEV)
+    full_size_case("nvfp4", d["x"], d["w"], False)
+
+
+def test_rotated_full_size():
+    d = workloads.rotated(device=DEV)
+    full_size_case("nvfp4", d["x"], d["w"], True)
+    full_size_case("mxfp4", d["x"], d["w"], True)
