@@ -1,0 +1,332 @@
+"""Benchmark of the FP4 hot path on one MI355X.
+
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one pass of the hot path over one batch of synthetic input with
+every input already resident in HBM:
+  decode   (default) online NVFP4 quantize of X bf16 [8, 4096] (tensor scale
+           computed from the data) + NVFP4 W4A4 GEMM against a pre-quantized
+           W [14336, 4096], bf16 out.  Steps cycle over 16 distinct weight
+           copies (about 2x the 256 MB last-level cache) so the weights
+           stream from HBM as they do layer after layer.
+  prefill  NVFP4 quantize of X [4096, 4096] + GEMM vs W [14336, 4096].
+  rotated_nv / rotated_mx  fused Hadamard+quantize of X [2048, 8192] +
+           GEMM vs the offline-rotated W [28672, 8192].
+  kv       NVFP4 quantize of K and V [32*8*32768, 128] bf16 with their given
+           tensor scales + dequantize of both to FP8 E4M3.
+Prints one JSON line.  The dominant kernel of the step is timed with HIP
+events around each of its launches inside the timed region; its algorithmic
+bytes (or flops) per launch give the roofline figure.  The CPU oracle is
+timed on a bounded sample of the same workload on the host.
+"""
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "W4A4 NVFP4 GEMM TFLOPS + quantize GB/s, % of MI355X roofline"
+HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = {"fp4": 10100.0, "f16": 2500.0}
+MALL_BYTES = 256 << 20
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--workload", default="decode",
+                   choices=["decode", "prefill", "rotated_nv", "rotated_mx", "kv"])
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=10.0)
+    return p.parse_args()
+
+
+class Lib:
+    """Direct ctypes calls with pre-built arguments (low host overhead)."""
+
+    def __init__(self, torch, fq):
+        self.torch = torch
+        self.L = fq.lib()
+        self.stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    @staticmethod
+    def p(t):
+        return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+    def check(self, st, what):
+        if st != 0:
+            raise RuntimeError("%s failed: %s" % (what, self.L.fp4_status_string(st).decode()))
+
+    def quantize_call(self, fmt, x, codes, scales, ts, mode, ws, hadamard=False):
+        from microscaled_fp4_quantization_amd import fp4
+        fn = self.L.fp4_hadamard_quantize if hadamard else self.L.fp4_quantize
+        dt = {self.torch.bfloat16: fp4.BF16, self.torch.float32: fp4.F32, self.torch.float16: fp4.F16}[x.dtype]
+        need = self.L.fp4_quantize_workspace_size(fmt, mode, x.shape[0], x.shape[1])
+        args = (fmt, self.p(x), dt, x.shape[0], x.shape[1], self.p(codes), self.p(scales),
+                self.p(ts), mode, self.p(ws) if need else None, need, self.stream)
+        return lambda: self.check(fn(*args), "quantize")
+
+    def gemm_call(self, fmt, a, b, c, c_dtype):
+        (ac, asc, at), (bc, bsc, bt) = a, b
+        m, n, k = ac.shape[0], bc.shape[0], ac.shape[1] * 2
+        args = (fmt, m, n, k, self.p(ac), self.p(asc), self.p(at), self.p(bc), self.p(bsc),
+                self.p(bt), self.p(c), c_dtype, None, 0, self.stream)
+        fn = self.L.fp4_gemm
+        return lambda: self.check(fn(*args), "gemm")
+
+    def dequant_call(self, fmt, codes, scales, ts, out, out_dtype):
+        rows, k = codes.shape[0], codes.shape[1] * 2
+        args = (fmt, self.p(codes), self.p(scales), self.p(ts), rows, k, self.p(out), out_dtype, self.stream)
+        fn = self.L.fp4_dequantize
+        return lambda: self.check(fn(*args), "dequantize")
+
+
+def gemm_bytes(m, n, k, fmt, out_bytes):
+    bs = 16 if fmt == "nvfp4" else 32
+    return (m + n) * (k // 2 + k // bs) + m * n * out_bytes + (8 if fmt == "nvfp4" else 0)
+
+
+def quant_bytes(rows, k, fmt, in_bytes):
+    bs = 16 if fmt == "nvfp4" else 32
+    return rows * k * in_bytes + rows * k // 2 + rows * k // bs + (4 if fmt == "nvfp4" else 0)
+
+
+def setup(workload, torch, fq, lib):
+    """Returns dict with: steps (list of per-step callables split into
+    pre/dominant/post), flops, bytes, dominant info, oracle sample fn."""
+    from microscaled_fp4_quantization_amd import fp4, workloads
+    dev = torch.device("cuda:0")
+    NV, MX = fp4.NVFP4, fp4.MXFP4
+    W = {}
+    if workload in ("decode", "prefill"):
+        m = 8 if workload == "decode" else 4096
+        d = workloads.decode(device=dev) if workload == "decode" else workloads.prefill(device=dev)
+        x, w = d["x"], d["w"]
+        n, k = w.shape
+        wq = fq.quantize(w, "nvfp4")
+        per = gemm_bytes(m, n, k, "nvfp4", 2)
+        copies = 1 if workload == "prefill" else max(1, -(-2 * MALL_BYTES // (n * k // 2 + n * k // 16)))
+        wqs = [wq] + [tuple(t.clone() for t in wq) for _ in range(copies - 1)]
+        xc = torch.empty((m, k // 2), dtype=torch.uint8, device=dev)
+        xs = torch.empty((m, k // 16), dtype=torch.uint8, device=dev)
+        xt = torch.empty(1, dtype=torch.float32, device=dev)
+        ws = torch.empty(4096, dtype=torch.uint8, device=dev)
+        c = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+        q = lib.quantize_call(NV, x, xc, xs, xt, fp4.TSCALE_COMPUTE, ws)
+        gs = [lib.gemm_call(NV, (xc, xs, xt), wqi, c, fp4.BF16) for wqi in wqs]
+        W.update(pre=[q], dominant=gs, post=[], flops=2 * m * n * k,
+                 dom_name="fp4_gemm (NVFP4, m=%d)" % m,
+                 dom_units=per if workload == "decode" else 2 * m * n * k,
+                 dom_bound="hbm" if workload == "decode" else "mfma",
+                 dom_peak=HBM_PEAK_GBS if workload == "decode" else MFMA_PEAK_TFLOPS["f16"],
+                 quant_bytes=quant_bytes(m, k, "nvfp4", 2),
+                 config={"workload": workload, "m": m, "n": n, "k": k, "format": "nvfp4",
+                         "x_dtype": "bf16", "out_dtype": "bf16", "weight_copies": copies},
+                 dtype="e2m1 x e4m3 -> f16 mfma, f32 acc",
+                 host=dict(x=x.float().cpu().numpy(), w=w.float().cpu().numpy(), fmt="nvfp4",
+                           hadamard=False))
+    elif workload in ("rotated_nv", "rotated_mx"):
+        fmt = "nvfp4" if workload == "rotated_nv" else "mxfp4"
+        f = NV if fmt == "nvfp4" else MX
+        d = workloads.rotated(device=dev)
+        x, w = d["x"], d["w"]
+        m, k = x.shape
+        n = w.shape[0]
+        bs = 16 if fmt == "nvfp4" else 32
+        wq = fq.hadamard_quantize(w, fmt)
+        xc = torch.empty((m, k // 2), dtype=torch.uint8, device=dev)
+        xs = torch.empty((m, k // bs), dtype=torch.uint8, device=dev)
+        xt = torch.empty(1, dtype=torch.float32, device=dev) if fmt == "nvfp4" else None
+        ws = torch.empty(4096, dtype=torch.uint8, device=dev)
+        c = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+        q = lib.quantize_call(f, x, xc, xs, xt, fp4.TSCALE_COMPUTE, ws, hadamard=True)
+        g = lib.gemm_call(f, (xc, xs, xt), wq, c, fp4.BF16)
+        W.update(pre=[q], dominant=[g], post=[], flops=2 * m * n * k,
+                 dom_name="fp4_gemm (%s, m=%d)" % (fmt.upper(), m), dom_units=2 * m * n * k,
+                 dom_bound="mfma",
+                 dom_peak=MFMA_PEAK_TFLOPS["fp4" if fmt == "mxfp4" else "f16"],
+                 quant_bytes=quant_bytes(m, k, fmt, 2),
+                 config={"workload": workload, "m": m, "n": n, "k": k, "format": fmt,
+                         "hadamard": bs, "x_dtype": "bf16", "out_dtype": "bf16"},
+                 dtype="e2m1 x e2m1 fp4 mfma (e8m0 scales), f32 acc" if fmt == "mxfp4"
+                 else "e2m1 x e4m3 -> f16 mfma, f32 acc",
+                 host=dict(x=x.float().cpu().numpy(), w=w.float().cpu().numpy(), fmt=fmt,
+                           hadamard=True))
+    else:  # kv
+        d = workloads.kv(device=dev)
+        calls_q, calls_d, outs = [], [], []
+        ts_list = []
+        for name in ("k", "v"):
+            x2 = d[name].view(-1, 128)
+            rows = x2.shape[0]
+            amax = torch.max(torch.abs(x2)).float()
+            ts = (amax / 2688.0).reshape(1).contiguous()
+            codes = torch.empty((rows, 64), dtype=torch.uint8, device=dev)
+            scales = torch.empty((rows, 8), dtype=torch.uint8, device=dev)
+            out = torch.empty((rows, 128), dtype=torch.uint8, device=dev)
+            calls_q.append(lib.quantize_call(NV, x2, codes, scales, ts, fp4.TSCALE_GIVEN, None))
+            calls_d.append(lib.dequant_call(NV, codes, scales, ts, out, fp4.E4M3))
+            outs.append((codes, scales, out))
+            ts_list.append(ts)
+        rows = d["k"].numel() // 128
+        W.update(pre=[], dominant=calls_q, post=calls_d, flops=0,
+                 dom_name="fp4_quantize (NVFP4 given scale, bf16 [2^23,128])",
+                 dom_units=quant_bytes(rows, 128, "nvfp4", 2), dom_bound="hbm", dom_peak=HBM_PEAK_GBS,
+                 quant_bytes=quant_bytes(rows, 128, "nvfp4", 2),
+                 dequant_bytes=rows * 128 * 1.5625,
+                 config={"workload": "kv", "shape": [32, 8, 32768, 128], "format": "nvfp4",
+                         "x_dtype": "bf16", "out_dtype": "e4m3"},
+                 dtype="f32 (quantize arithmetic), e4m3 out",
+                 host=dict(kv=d, ts=ts_list))
+    return W
+
+
+def cpu_baseline(workload, W, seconds):
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        cores = 1
+    h = W["host"]
+    if workload == "kv":
+        # bounded sample: the first rows of K, quantized and dequantized
+        rows = 1 << 16
+        x = h["kv"]["k"].view(-1, 128)[:rows].float().cpu().numpy()
+        st = np.float32(h["ts"][0].item())
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            p, s, _ = oracle.nvfp4_quantize(x, st)
+            oracle.dequantize("nvfp4", p, s, st, "e4m3")
+            reps += 1
+            if time.perf_counter() - t0 >= seconds:
+                break
+        dt = (time.perf_counter() - t0) / reps
+        gbs = (rows * 128 * 2.5625 + rows * 128 * 1.5625) / dt / 1e9
+        return {"value": gbs, "unit": "GB/s", "cores": 1, "kind": "oracle",
+                "sample": "quantize + FP8 dequantize of %d of the 2^23 K rows, %d reps" % (rows, reps)}
+    fmt = h["fmt"]
+    x, w = h["x"], h["w"]
+    if workload in ("prefill", "rotated_nv", "rotated_mx"):
+        x = x[:64]                        # bounded sample: 64 activation rows
+    b = 16 if fmt == "nvfp4" else 32
+    wr = oracle.hadamard_blocks(w, b) if h["hadamard"] else w
+    if fmt == "nvfp4":
+        pw, sw, tw = oracle.nvfp4_quantize(wr)
+    else:
+        (pw, sw), tw = oracle.mxfp4_quantize(wr), None
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        xr = oracle.hadamard_blocks(x, b) if h["hadamard"] else x
+        if fmt == "nvfp4":
+            pa, sa, ta = oracle.nvfp4_quantize(xr)
+        else:
+            (pa, sa), ta = oracle.mxfp4_quantize(xr), None
+        oracle.gemm_ref(fmt, pa, sa, ta, pw, sw, tw)
+        reps += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    dt = (time.perf_counter() - t0) / reps
+    flops = 2.0 * x.shape[0] * w.shape[0] * w.shape[1]
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": "%s step on X rows %d of %d (full W %dx%d), %d reps" % (
+                workload, x.shape[0], h["x"].shape[0], w.shape[0], w.shape[1], reps)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py: this build runs on one GPU only; --gpus %d is not supported "
+              "(the sharded path is described in DESIGN.md, not built)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import microscaled_fp4_quantization_amd as fq
+    torch.cuda.set_device(0)
+    lib = Lib(torch, fq)
+    W = setup(args.workload, torch, fq, lib)
+    pre, dom, post = W["pre"], W["dominant"], W["post"]
+    ndom = len(dom)
+
+    def step(i, ev=None):
+        for f in pre:
+            f()
+        if args.workload == "kv":
+            for j, f in enumerate(dom):
+                if ev is not None:
+                    ev[2 * j].record()
+                f()
+                if ev is not None:
+                    ev[2 * j + 1].record()
+        else:
+            if ev is not None:
+                ev[0].record()
+            dom[i % ndom]()
+            if ev is not None:
+                ev[1].record()
+        for f in post:
+            f()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    nev = 4 if args.workload == "kv" else 2
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, evs[i])
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_total = start.elapsed_time(end)
+    ms_step = ms_total / args.steps
+    dom_ms = []
+    for e in evs:
+        for j in range(nev // 2):
+            dom_ms.append(e[2 * j].elapsed_time(e[2 * j + 1]))
+    dom_avg = sum(dom_ms) / len(dom_ms)
+
+    if W["dom_bound"] == "hbm":
+        achieved = W["dom_units"] / (dom_avg * 1e-3) / 1e9
+        unit = "GB/s"
+    else:
+        achieved = W["dom_units"] / (dom_avg * 1e-3) / 1e12
+        unit = "TFLOP/s"
+    if args.workload == "kv":
+        value = 2 * (W["quant_bytes"] + W["dequant_bytes"]) / (ms_step * 1e-3) / 1e9
+        vunit = "GB/s"
+    else:
+        value = W["flops"] / (ms_step * 1e-3) / 1e12
+        vunit = "TFLOP/s"
+    out = {
+        "metric": METRIC, "value": round(value, 3), "unit": vunit, "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": W["dtype"], "data": "synthetic (seeded, see workloads.py)",
+        "config": W["config"],
+        "roofline": {"bound": W["dom_bound"], "achieved": round(achieved, 2),
+                     "peak": W["dom_peak"], "unit": unit,
+                     "frac": round(achieved / W["dom_peak"], 4), "traffic": None,
+                     "kernel": W["dom_name"], "avg_ms": round(dom_avg, 5),
+                     "units_per_launch": W["dom_units"]},
+        "host_wall_s": round(wall, 4),
+    }
+    if args.workload != "kv":
+        out["quantize_bytes_per_step"] = W["quant_bytes"]
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(args.workload, W, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
