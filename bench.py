@@ -277,19 +277,38 @@ def main():
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
+    # Host cost of enqueuing one step (the GPU may be faster than the host).
+    t0 = time.perf_counter()
+    for i in range(min(args.warmup, 20)):
+        step(i)
+    host_step = (time.perf_counter() - t0) / max(1, min(args.warmup, 20))
+    torch.cuda.synchronize()
+    # Calibrate a GPU spin that outlasts enqueuing all K steps, so the timed
+    # steps run back to back on the GPU and the events measure GPU time only.
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record()
+    torch.cuda._sleep(1 << 20)
+    c1.record()
+    torch.cuda.synchronize()
+    ms_per_cycle = c0.elapsed_time(c1) / float(1 << 20)
+    spin_ms = 2.0 * host_step * 1e3 * (args.steps + 4) + 2.0
+    spin_cycles = int(spin_ms / ms_per_cycle)
     nev = 4 if args.workload == "kv" else 2
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(args.steps)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
+    torch.cuda._sleep(spin_cycles)
     start.record()
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(i, evs[i])
     end.record()
+    enqueue_s = time.perf_counter() - t0
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_total = start.elapsed_time(end)
     ms_step = ms_total / args.steps
+    gpu_fed = enqueue_s * 1e3 < spin_ms     # host stayed ahead of the GPU
     dom_ms = []
     for e in evs:
         for j in range(nev // 2):
@@ -320,6 +339,8 @@ def main():
                      "kernel": W["dom_name"], "avg_ms": round(dom_avg, 5),
                      "units_per_launch": W["dom_units"]},
         "host_wall_s": round(wall, 4),
+        "host_enqueue_ms_per_step": round(enqueue_s * 1e3 / args.steps, 4),
+        "gpu_fed_by_host": bool(gpu_fed),
     }
     if args.workload != "kv":
         out["quantize_bytes_per_step"] = W["quant_bytes"]

@@ -19,6 +19,7 @@ SOURCES = [
     "quantize.hip",
     "dequantize.hip",
     "gemm_simple.hip",
+    "gemm_skinny.hip",
     "gemm.hip",
 ]
 

@@ -1,0 +1,357 @@
+// W4A4 GEMM for few activation rows (m <= 16, the decode shape): a weight
+// stream.  C[m, n] = sum_k deq(X)[m, k] deq(W)[n, k].
+//
+// pimento.cloud "FP8, NVFP4 czy AWQ?", section "Dlaczego W8A8 i W4A16 to nie
+// to samo?": token-by-token generation is bound by reading the weights, so
+// this kernel is built to stream W once at full HBM rate.
+//
+// One workgroup owns 16 weight rows; its 4 waves split k into quarters and
+// add their partial tiles through LDS at the end.  Lane l works on weight
+// row n0 + l % 16 and activation row l % 16 (zero when >= m); per trip it
+// loads 16 bytes (32 values) of its weight row and the same 32 positions of
+// its activation row.  Because a dot product may visit k in any order, the
+// MFMA k-slots are filled with whatever 8 consecutive values a lane holds,
+// identically for both operands.
+//   NVFP4: v_mfma_f32_16x16x32_f16 on exact fp16 products v * E4M3(sb)
+//          (at most 6 significant bits, range [2^-10, 2688]); tensor scales
+//          in the epilogue.
+//   MXFP4: v_mfma_scale_f32_16x16x128_f8f6f4 with both operands E2M1 and
+//          the E8M0 block scale of each lane's 32 values.
+#include "device_common.hpp"
+#include "launch.hpp"
+
+using namespace fp4dev;
+
+namespace {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWaves = 4;
+constexpr int kRows = 16;
+
+__device__ __forceinline__ _Float16 e4m3_to_f16(uint32_t c) {
+  return (_Float16)e4m3_decode_pos(c & 0x7Fu);
+}
+
+__device__ __forceinline__ v8h dequant8(uint32_t w, _Float16 s) {
+  const v2h sv = {s, s};
+  const v2h p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * sv;
+  const v2h p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * sv;
+  const v2h p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * sv;
+  const v2h p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * sv;
+  return (v8h){p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
+}
+
+__device__ __forceinline__ void store_out(void* c, int c_dtype, int64_t idx, float v) {
+  if (c_dtype == kInF32) {
+    reinterpret_cast<float*>(c)[idx] = v;
+  } else {
+    reinterpret_cast<__bf16*>(c)[idx] = (__bf16)v;
+  }
+}
+
+// Adds the 4 waves' 16x16 partial tiles; wave 0 stores C[m, n0 + ...].
+__device__ __forceinline__ void reduce_store(v4f acc, float scale, int64_t m, int64_t n,
+                                             int64_t n0, void* c, int c_dtype) {
+  __shared__ v4f part[kWaves][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  part[wave][lane] = acc;
+  __syncthreads();
+  if (wave == 0) {
+    v4f s = part[0][lane];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) s += part[w][lane];
+    // D layout: lane holds rows 4*(lane/16) + e (weight rows), column lane % 16 (activation row)
+    const int64_t mi = lane & 15;
+    if (mi < m) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int64_t ni = n0 + 4 * (lane >> 4) + e;
+        if (ni < n) store_out(c, c_dtype, mi * n + ni, s[e] * scale);
+      }
+    }
+  }
+}
+
+template <int UNROLL>
+__global__ __launch_bounds__(256) void gemm_nv_skinny(
+    int64_t m, int64_t n, int64_t k, const uint8_t* __restrict__ a,
+    const uint8_t* __restrict__ as, const float* __restrict__ at,
+    const uint8_t* __restrict__ b, const uint8_t* __restrict__ bs,
+    const float* __restrict__ bt, void* __restrict__ c, int c_dtype) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r = lane & 15, g = lane >> 4;
+  const int64_t n0 = (int64_t)blockIdx.x * kRows;
+  const int64_t wrow = (n0 + r < n) ? n0 + r : n - 1;
+  const bool arow_ok = r < m;
+  const int64_t arow = arow_ok ? r : 0;
+  const int64_t kbytes = k / 2, kblocks = k / 16, k32 = k / 32;
+  // a trip covers 128 values; lane group g owns the 32 values at 128*ch + 32*g
+  const int64_t nchunks = (k + 127) / 128;
+  const int64_t per_wave = (nchunks + kWaves - 1) / kWaves;
+  const int64_t c0 = wave * per_wave;
+  const int64_t c1 = (c0 + per_wave < nchunks) ? c0 + per_wave : nchunks;
+  const uint8_t* wp = b + wrow * kbytes + 16 * g;
+  const uint8_t* ap = a + arow * kbytes + 16 * g;
+  const uint8_t* wsp = bs + wrow * kblocks + 2 * g;
+  const uint8_t* asp = as + arow * kblocks + 2 * g;
+  v4f acc = {0.f, 0.f, 0.f, 0.f};
+  for (int64_t ch = c0; ch < c1; ch += UNROLL) {
+    u32x4 wv[UNROLL], av[UNROLL];
+    uint32_t wsv[UNROLL], asv[UNROLL];
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) {
+      const bool ok = (ch + u < c1) && ((ch + u) * 4 + g < k32);
+      const int64_t cc = ok ? ch + u : 0;
+      wv[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wp + cc * 64));
+      wsv[u] = *reinterpret_cast<const uint16_t*>(wsp + cc * 8);
+      av[u] = *reinterpret_cast<const u32x4*>(ap + cc * 64);
+      asv[u] = *reinterpret_cast<const uint16_t*>(asp + cc * 8);
+      if (!ok || !arow_ok) av[u] = (u32x4){0u, 0u, 0u, 0u};
+      if (!ok) wv[u] = (u32x4){0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) {
+      const _Float16 ws0 = e4m3_to_f16(wsv[u] & 0xFFu), ws1 = e4m3_to_f16((wsv[u] >> 8) & 0xFFu);
+      const _Float16 as0 = e4m3_to_f16(asv[u] & 0xFFu), as1 = e4m3_to_f16((asv[u] >> 8) & 0xFFu);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const v8h fw = dequant8(wv[u][j], j < 2 ? ws0 : ws1);
+        const v8h fa = dequant8(av[u][j], j < 2 ? as0 : as1);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(fw, fa, acc, 0, 0, 0);
+      }
+    }
+  }
+  reduce_store(acc, (*at) * (*bt), m, n, n0, c, c_dtype);
+}
+
+template <int UNROLL>
+__global__ __launch_bounds__(256) void gemm_mx_skinny(
+    int64_t m, int64_t n, int64_t k, const uint8_t* __restrict__ a,
+    const uint8_t* __restrict__ as, const uint8_t* __restrict__ b,
+    const uint8_t* __restrict__ bs, void* __restrict__ c, int c_dtype) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r = lane & 15, g = lane >> 4;
+  const int64_t n0 = (int64_t)blockIdx.x * kRows;
+  const int64_t wrow = (n0 + r < n) ? n0 + r : n - 1;
+  const bool arow_ok = r < m;
+  const int64_t arow = arow_ok ? r : 0;
+  const int64_t kbytes = k / 2, kblocks = k / 32;
+  // a trip covers 128 values = 4 blocks of 32; lane group g owns block g
+  const int64_t nchunks = (k + 127) / 128;
+  const int64_t per_wave = (nchunks + kWaves - 1) / kWaves;
+  const int64_t c0 = wave * per_wave;
+  const int64_t c1 = (c0 + per_wave < nchunks) ? c0 + per_wave : nchunks;
+  v4f acc = {0.f, 0.f, 0.f, 0.f};
+  for (int64_t ch = c0; ch < c1; ch += UNROLL) {
+    u32x4 wv[UNROLL], av[UNROLL];
+    int wsv[UNROLL], asv[UNROLL];
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) {
+      const int64_t blk = (ch + u) * 4 + g;
+      const bool ok = (ch + u < c1) && blk < kblocks;
+      const int64_t bb = ok ? blk : 0;
+      wv[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(b + wrow * kbytes + bb * 16));
+      av[u] = *reinterpret_cast<const u32x4*>(a + arow * kbytes + bb * 16);
+      wsv[u] = bs[wrow * kblocks + bb];
+      asv[u] = as[arow * kblocks + bb];
+      if (!ok || !arow_ok) av[u] = (u32x4){0u, 0u, 0u, 0u};
+      if (!ok) wv[u] = (u32x4){0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) {
+      const v8i fw = {(int)wv[u][0], (int)wv[u][1], (int)wv[u][2], (int)wv[u][3], 0, 0, 0, 0};
+      const v8i fa = {(int)av[u][0], (int)av[u][1], (int)av[u][2], (int)av[u][3], 0, 0, 0, 0};
+      acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fw, fa, acc, 4, 4, 0, wsv[u], 0, asv[u]);
+    }
+  }
+  reduce_store(acc, 1.0f, m, n, n0, c, c_dtype);
+}
+
+
+// ---- NVFP4 decode fast path (m <= 8, k % KC == 0) --------------------------
+// One workgroup = 32 weight rows = 2 row tiles x 2 k-halves (one wave each),
+// k processed in chunks of KC values with a two-stage LDS ring:
+//  * weight codes and scales of a chunk are read with fully coalesced
+//    16-byte loads (a wave instruction covers whole 128-byte lines) and
+//    written to LDS, where 16-byte chunk c of row r sits at c ^ (r & 15) so
+//    the 16-row MFMA fragment reads do not collide in a bank;
+//  * the chunk's activations are dequantized once per workgroup to exact fp16
+//    in LDS (same swizzle);
+//  * loads of chunk c+1 are in flight while chunk c is multiplied.
+constexpr int kDecRows = 32;
+constexpr int kDecKC = 1024;
+
+__device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ (row & 15); }
+
+// Activation layout: 16-byte chunk c of row r sits at c ^ ((r & 3) << 2 | (c >> 4) & 3).
+// Both the dequantizing writes (2 rows x 32 items per wave instruction) and
+// the fragment reads (8 rows x 4 lane groups) then spread evenly over the
+// 16 bank groups.
+__device__ __forceinline__ int xswz(int row, int chunk) {
+  return chunk ^ (((row & 3) << 2) | ((chunk >> 4) & 3));
+}
+
+template <int KC>
+struct DecodeStage {
+  uint8_t w[kDecRows][KC / 2];        // weight codes
+  uint8_t s[kDecRows][KC / 16 + 16];  // weight scale bytes (row padded against bank conflicts)
+  _Float16 x[8][KC];                  // dequantized activations
+};
+
+template <int KC, int NCH>
+__global__ __launch_bounds__(256) void gemm_nv_decode(
+    int m, int64_t n, int k, const uint8_t* __restrict__ a,
+    const uint8_t* __restrict__ as, const float* __restrict__ at,
+    const uint8_t* __restrict__ b, const uint8_t* __restrict__ bs,
+    const float* __restrict__ bt, void* __restrict__ c, int c_dtype) {
+  constexpr int WCH = KC / 32;                          // 16-byte code chunks per row
+  constexpr int WLD = kDecRows * WCH / 256;             // code loads per thread
+  constexpr int SLD = kDecRows * KC / 16 / 16;          // 16-byte scale loads (threads)
+  constexpr int XLD = 8 * KC / 32;                      // 32-value activation items
+  static_assert(WLD >= 1 && SLD <= 256 && XLD <= 256, "chunk shape");
+  __shared__ DecodeStage<KC> st[2];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t nbase = (int64_t)blockIdx.x * kDecRows;
+
+  // per-thread global sources, NCH chunks in flight at once
+  u32x4 wreg[NCH][WLD], sreg[NCH], xreg[NCH];
+  uint32_t xsreg[NCH];
+  auto load_chunk = [&](int ch, int slot) {
+    const int64_t kb = (int64_t)ch * KC;
+#pragma unroll
+    for (int i = 0; i < WLD; ++i) {
+      const int idx = tid + 256 * i, row = idx / WCH, cc = idx % WCH;
+      const int64_t gr = (nbase + row < n) ? nbase + row : n - 1;
+      wreg[slot][i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(b + gr * (k / 2) + kb / 2) + cc);
+    }
+    if (tid < SLD) {
+      const int row = tid / (KC / 256), cc = tid % (KC / 256);
+      const int64_t gr = (nbase + row < n) ? nbase + row : n - 1;
+      sreg[slot] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(bs + gr * (k / 16) + kb / 16) + cc);
+    }
+    if (tid < XLD) {
+      const int row = tid / (KC / 32), item = tid % (KC / 32);
+      if (row < m) {
+        xreg[slot] = *reinterpret_cast<const u32x4*>(a + (int64_t)row * (k / 2) + kb / 2 + item * 16);
+        xsreg[slot] = *reinterpret_cast<const uint16_t*>(as + (int64_t)row * (k / 16) + kb / 16 + item * 2);
+      } else {
+        xreg[slot] = (u32x4){0u, 0u, 0u, 0u};
+        xsreg[slot] = 0;
+      }
+    }
+  };
+  auto store_chunk = [&](DecodeStage<KC>& S, int slot) {
+#pragma unroll
+    for (int i = 0; i < WLD; ++i) {
+      const int idx = tid + 256 * i, row = idx / WCH, cc = idx % WCH;
+      *reinterpret_cast<u32x4*>(&S.w[row][swz(row, cc) * 16]) = wreg[slot][i];
+    }
+    if (tid < SLD) {
+      const int row = tid / (KC / 256), cc = tid % (KC / 256);
+      *reinterpret_cast<u32x4*>(&S.s[row][cc * 16]) = sreg[slot];
+    }
+    if (tid < XLD) {
+      const int row = tid / (KC / 32), item = tid % (KC / 32);
+      const v2h s2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(xsreg[slot], 1.0f, false);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const v8h f = dequant8(xreg[slot][j], j < 2 ? s2.x : s2.y);
+        *reinterpret_cast<v8h*>(&S.x[row][xswz(row, item * 4 + j) * 8]) = f;
+      }
+    }
+  };
+
+  const int r = lane & 15, g = lane >> 4;
+  const int rt = wave & 1, kh = wave >> 1;
+  const int wr = rt * 16 + r;                           // weight row in the tile
+  const bool xrow = r < m;
+  const int nchunks = k / KC;
+  v4f acc = {0.f, 0.f, 0.f, 0.f}, acc1 = acc;
+
+  // Chunks go in groups of NCH: all loads of a group are issued before the
+  // first of its chunks is stored to LDS and multiplied.
+  for (int g0 = 0; g0 < nchunks; g0 += NCH) {
+#pragma unroll
+    for (int u = 0; u < NCH; ++u)
+      if (g0 + u < nchunks) load_chunk(g0 + u, u);
+#pragma unroll
+    for (int u = 0; u < NCH; ++u) {
+      const int ch = g0 + u;
+      if (ch >= nchunks) break;
+      DecodeStage<KC>& S = st[u & 1];
+      store_chunk(S, u);
+      __syncthreads();
+      // this wave: k-half kh of the chunk, lane group g owns KC/8 contiguous values
+      constexpr int PER = KC / 8;
+      static_assert(PER == 128, "one 8-byte scale read per chunk");
+      const int v0 = kh * (KC / 2) + g * PER;
+      const uint2 scb = *reinterpret_cast<const uint2*>(&S.s[wr][v0 / 16]);   // 8 blocks
+#pragma unroll
+      for (int q = 0; q < PER / 32; ++q) {              // 32 values = 16 code bytes = 2 blocks
+        const int vq = v0 + q * 32;
+        const u32x4 wc = *reinterpret_cast<const u32x4*>(&S.w[wr][swz(wr, vq / 32) * 16]);
+        const uint32_t sw = (q < 2) ? scb.x : scb.y;
+        const v2h s2 = (q & 1) ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sw, 1.0f, true)
+                               : __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sw, 1.0f, false);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const v8h fw = dequant8(wc[j], j < 2 ? s2.x : s2.y);
+          v8h fx = {0, 0, 0, 0, 0, 0, 0, 0};
+          if (xrow) fx = *reinterpret_cast<const v8h*>(&S.x[r][xswz(r, vq / 8 + j) * 8]);
+          if (j & 1) acc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(fw, fx, acc1, 0, 0, 0);
+          else acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(fw, fx, acc, 0, 0, 0);
+        }
+      }
+    }
+    __syncthreads();
+  }
+
+  // add the two k-halves and store
+  acc += acc1;
+  v4f* part = reinterpret_cast<v4f*>(&st[0]);
+  if (kh == 1) part[rt * 64 + lane] = acc;
+  __syncthreads();
+  if (kh == 0) {
+    acc += part[rt * 64 + lane];
+    const float scale = (*at) * (*bt);
+    if (r < m) {
+      const int64_t n0 = nbase + rt * 16;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int64_t ni = n0 + 4 * g + e;
+        if (ni < n) store_out(c, c_dtype, (int64_t)r * n + ni, acc[e] * scale);
+      }
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_gemm_skinny(int fmt, int64_t m, int64_t n, int64_t k,
+                              const uint8_t* a_codes, const uint8_t* a_scales,
+                              const float* a_tscale, const uint8_t* b_codes,
+                              const uint8_t* b_scales, const float* b_tscale,
+                              void* c, int c_dtype, hipStream_t stream) {
+  const bool aligned16 = ((reinterpret_cast<uintptr_t>(b_scales) | reinterpret_cast<uintptr_t>(b_codes) |
+                           reinterpret_cast<uintptr_t>(a_codes)) & 15) == 0 &&
+                         (reinterpret_cast<uintptr_t>(a_scales) & 1) == 0;
+  if (fmt == kFmtNV && m <= 8 && k % kDecKC == 0 && aligned16) {
+    hipLaunchKernelGGL((gemm_nv_decode<kDecKC, 4>), dim3((unsigned)((n + kDecRows - 1) / kDecRows)),
+                       dim3(256), 0, stream, (int)m, n, (int)k, a_codes, a_scales, a_tscale, b_codes,
+                       b_scales, b_tscale, c, c_dtype);
+    return hipGetLastError();
+  }
+  const dim3 grid((unsigned)((n + kRows - 1) / kRows));
+  if (fmt == kFmtNV) {
+    hipLaunchKernelGGL((gemm_nv_skinny<8>), grid, dim3(256), 0, stream, m, n, k, a_codes,
+                       a_scales, a_tscale, b_codes, b_scales, b_tscale, c, c_dtype);
+  } else {
+    hipLaunchKernelGGL((gemm_mx_skinny<8>), grid, dim3(256), 0, stream, m, n, k, a_codes,
+                       a_scales, b_codes, b_scales, c, c_dtype);
+  }
+  return hipGetLastError();
+}
