@@ -28,6 +28,7 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWaves = 4;
 constexpr int kRows = 16;
@@ -210,38 +211,38 @@ __global__ __launch_bounds__(256) void gemm_nv_decode(
     const float* __restrict__ bt, void* __restrict__ c, int c_dtype) {
   constexpr int WCH = KC / 32;                          // 16-byte code chunks per row
   constexpr int WLD = kDecRows * WCH / 256;             // code loads per thread
-  constexpr int SLD = kDecRows * KC / 16 / 16;          // 16-byte scale loads (threads)
-  constexpr int XLD = 8 * KC / 32;                      // 32-value activation items
-  static_assert(WLD >= 1 && SLD <= 256 && XLD <= 256, "chunk shape");
+  constexpr int SB = kDecRows * (KC / 16) / 256;        // scale bytes per thread
+  static_assert(WLD >= 1 && SB == 8 && 8 * KC / 32 == 256, "chunk shape");
   __shared__ DecodeStage<KC> st[2];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t nbase = (int64_t)blockIdx.x * kDecRows;
+  const int nchunks = k / KC;
 
-  // per-thread global sources, NCH chunks in flight at once
-  u32x4 wreg[NCH][WLD], sreg[NCH], xreg[NCH];
+  // Per-thread global sources, NCH chunks in flight at once.  Every load is
+  // unconditional (indices are clamped instead), so the compiler can wait for
+  // one chunk's loads while the later chunks are still arriving.
+  u32x4 wreg[NCH][WLD], xreg[NCH];
+  u32x2 sreg[NCH];
   uint32_t xsreg[NCH];
+  const int xrow_ld = tid / (KC / 32);                  // activation row this thread dequantizes
+  const int64_t xr_src = xrow_ld < m ? xrow_ld : 0;
   auto load_chunk = [&](int ch, int slot) {
-    const int64_t kb = (int64_t)ch * KC;
+    const int64_t kb = (int64_t)(ch < nchunks ? ch : nchunks - 1) * KC;
 #pragma unroll
     for (int i = 0; i < WLD; ++i) {
       const int idx = tid + 256 * i, row = idx / WCH, cc = idx % WCH;
       const int64_t gr = (nbase + row < n) ? nbase + row : n - 1;
       wreg[slot][i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(b + gr * (k / 2) + kb / 2) + cc);
     }
-    if (tid < SLD) {
-      const int row = tid / (KC / 256), cc = tid % (KC / 256);
+    {
+      const int row = tid / (KC / 16 / SB), cc = tid % (KC / 16 / SB);
       const int64_t gr = (nbase + row < n) ? nbase + row : n - 1;
-      sreg[slot] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(bs + gr * (k / 16) + kb / 16) + cc);
+      sreg[slot] = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(bs + gr * (k / 16) + kb / 16) + cc);
     }
-    if (tid < XLD) {
-      const int row = tid / (KC / 32), item = tid % (KC / 32);
-      if (row < m) {
-        xreg[slot] = *reinterpret_cast<const u32x4*>(a + (int64_t)row * (k / 2) + kb / 2 + item * 16);
-        xsreg[slot] = *reinterpret_cast<const uint16_t*>(as + (int64_t)row * (k / 16) + kb / 16 + item * 2);
-      } else {
-        xreg[slot] = (u32x4){0u, 0u, 0u, 0u};
-        xsreg[slot] = 0;
-      }
+    {
+      const int item = tid % (KC / 32);
+      xreg[slot] = *reinterpret_cast<const u32x4*>(a + xr_src * (k / 2) + kb / 2 + item * 16);
+      xsreg[slot] = *reinterpret_cast<const uint16_t*>(as + xr_src * (k / 16) + kb / 16 + item * 2);
     }
   };
   auto store_chunk = [&](DecodeStage<KC>& S, int slot) {
@@ -250,17 +251,18 @@ __global__ __launch_bounds__(256) void gemm_nv_decode(
       const int idx = tid + 256 * i, row = idx / WCH, cc = idx % WCH;
       *reinterpret_cast<u32x4*>(&S.w[row][swz(row, cc) * 16]) = wreg[slot][i];
     }
-    if (tid < SLD) {
-      const int row = tid / (KC / 256), cc = tid % (KC / 256);
-      *reinterpret_cast<u32x4*>(&S.s[row][cc * 16]) = sreg[slot];
+    {
+      const int row = tid / (KC / 16 / SB), cc = tid % (KC / 16 / SB);
+      *reinterpret_cast<u32x2*>(&S.s[row][cc * SB]) = sreg[slot];
     }
-    if (tid < XLD) {
-      const int row = tid / (KC / 32), item = tid % (KC / 32);
-      const v2h s2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(xsreg[slot], 1.0f, false);
+    {
+      const int item = tid % (KC / 32);
+      const bool live = xrow_ld < m;
+      const v2h s2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(live ? xsreg[slot] : 0u, 1.0f, false);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const v8h f = dequant8(xreg[slot][j], j < 2 ? s2.x : s2.y);
-        *reinterpret_cast<v8h*>(&S.x[row][xswz(row, item * 4 + j) * 8]) = f;
+        const v8h f = dequant8(live ? xreg[slot][j] : 0u, j < 2 ? s2.x : s2.y);
+        *reinterpret_cast<v8h*>(&S.x[xrow_ld][xswz(xrow_ld, item * 4 + j) * 8]) = f;
       }
     }
   };
@@ -269,15 +271,13 @@ __global__ __launch_bounds__(256) void gemm_nv_decode(
   const int rt = wave & 1, kh = wave >> 1;
   const int wr = rt * 16 + r;                           // weight row in the tile
   const bool xrow = r < m;
-  const int nchunks = k / KC;
   v4f acc = {0.f, 0.f, 0.f, 0.f}, acc1 = acc;
 
   // Chunks go in groups of NCH: all loads of a group are issued before the
   // first of its chunks is stored to LDS and multiplied.
   for (int g0 = 0; g0 < nchunks; g0 += NCH) {
 #pragma unroll
-    for (int u = 0; u < NCH; ++u)
-      if (g0 + u < nchunks) load_chunk(g0 + u, u);
+    for (int u = 0; u < NCH; ++u) load_chunk(g0 + u, u);
 #pragma unroll
     for (int u = 0; u < NCH; ++u) {
       const int ch = g0 + u;
