@@ -20,6 +20,7 @@ SOURCES = [
     "dequantize.hip",
     "gemm_simple.hip",
     "gemm_skinny.hip",
+    "gemm_large.hip",
     "gemm.hip",
 ]
 

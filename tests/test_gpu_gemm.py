@@ -95,7 +95,8 @@ def test_random_shapes(fmt, out_dtype):
     g = torch.Generator().manual_seed(2)
     for m, n, k in [(1, 1, 32), (7, 9, 64), (16, 100, 4128), (3, 1000, 800), (16, 17, 160), (17, 33, 96),
                     (8, 100, 4096), (1, 33, 2048), (5, 64, 6144), (4, 47, 8192),
-                    (37, 50, 96), (64, 64, 128), (130, 257, 544), (256, 512, 2048)]:
+                    (37, 50, 96), (64, 64, 128), (130, 257, 544), (256, 512, 2048),
+                    (300, 600, 1024), (1000, 129, 512), (128, 2048, 256), (513, 700, 2304)]:
         x = torch.randn((m, k), generator=g).to(torch.bfloat16)
         w = (torch.randn((n, k), generator=g) * 0.02).to(torch.bfloat16)
         qx, qw = quant_pair(fmt, x, w)
