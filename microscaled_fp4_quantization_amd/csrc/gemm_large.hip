@@ -5,23 +5,25 @@
 // AWQ?", section "Dlaczego W8A8 i W4A16 to nie to samo?": W4A4 runs the
 // products on low-precision matrix units).
 //
-// Tiling: one 256-thread workgroup computes a 256 x 256 tile of C; its four
-// waves own 128 x 128 quadrants.  k advances in stages of 256 values; the
-// packed codes (128 bytes per row per stage) and the scale bytes of A and B
-// for a stage sit in LDS, double buffered, written from registers that were
-// loaded one stage ahead with coalesced 16-byte loads.  In LDS the 16-byte
-// chunk c of a row r is stored at c ^ (r & 7), which spreads the 32-row MFMA
-// fragment reads over all banks.
+// Tiling: a workgroup computes a 256 x 256 tile of C with WMW x WNW waves.
+// k advances in stages of 128 values (64 code bytes per row).  Stages live
+// in a 4-deep LDS ring filled by direct global->LDS buffer loads, so three
+// stages are in flight while one is multiplied and no registers are spent on
+// staging.  A direct load writes lane i's 16 bytes at base + 16 i, so the LDS
+// layout is chosen through the global addresses: in a row r, 16-byte chunk c
+// is stored at position c ^ ((r >> 2) & 3), which keeps the 32-row MFMA
+// fragment reads at the minimum number of bank cycles.  Scale bytes are
+// stored per row as 32-bit words (word w of every row contiguous).
 //
-// MXFP4 (E8M0 scale per 32 values): v_mfma_scale_f32_32x32x64_f8f6f4 with
-// both operands E2M1.  Lane (row r, half h) of an MFMA holds 32 values; in
-// step s (0..3) of a stage it holds block 4h + s, so the four scale bytes it
-// needs in a stage form one dword and the instruction's op_sel picks byte s.
-// NVFP4 (E4M3 scale per 16 values): each 8-value fragment is decoded to
-// fp16 and multiplied by its block scale in fp16 (exact: at most 6
-// significant bits, range [2^-10, 2688]); v_mfma_f32_32x32x16_f16
-// accumulates in fp32 and the epilogue applies the two FP32 tensor scales.
-// Lane half h owns values [128h, 128h + 128) of a stage, 8 per step.
+// MXFP4 (E8M0 scale per 32 values): v_mfma_scale_f32_32x32x64_f8f6f4, both
+// operands E2M1.  In k-step ks (0, 1) of a stage, lane (row r, half h)
+// holds block 2h + ks; its two scale bytes are shifted into the low half of
+// the scale register so the instruction's op_sel is the constant ks.
+// NVFP4 (E4M3 scale per 16 values): fragments are decoded to fp16 and
+// multiplied by their block scale in fp16 (exact: at most 6 significant
+// bits, range [2^-10, 2688]); v_mfma_f32_32x32x16_f16 accumulates in fp32;
+// the two FP32 tensor scales are applied in the epilogue.  Lane half h owns
+// values [64h, 64h + 64) of a stage (blocks 4h .. 4h+3), 8 per k-step.
 //
 // Workgroup -> tile mapping is XCD-aware: consecutive workgroup ids land on
 // different XCDs (each with its own L2), so the ids are regrouped to give
@@ -38,32 +40,32 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void lds_void;
 
-constexpr int BM = 256, BN = 256, BK = 256;
+constexpr int BM = 256, BN = 256, BK = 128;
 constexpr int ROWB = BK / 2;          // code bytes per row per stage
+constexpr int NSTAGE = 4;             // LDS ring depth
 constexpr int NXCD = 8;
+// waves per workgroup along m and n
+constexpr int kMXWM = 2, kMXWN = 4;
+constexpr int kNVWM = 2, kNVWN = 4;
 
 template <int FMT>
 struct LargeStage {
-  static constexpr int SPR = (FMT == kFmtNV) ? BK / 16 : BK / 32;   // scale bytes per row
+  static constexpr int SW = (FMT == kFmtNV) ? 2 : 1;   // scale words per row per stage
   uint8_t a[BM * ROWB];
   uint8_t b[BN * ROWB];
-  uint8_t as[BM * SPR];
-  uint8_t bs[BN * SPR];
+  uint32_t sa[SW][BM];
+  uint32_t sb[SW][BN];
 };
 
-__device__ __forceinline__ int swz8(int row, int chunk) { return chunk ^ (row & 7); }
+__device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ ((row >> 2) & 3); }
 
-// Scaled fp4 MFMA whose scale byte (op_sel) is step ks of the lane's dword;
-// ks is an unrolled loop index, so the switch folds to one instruction.
+// Scaled fp4 MFMA whose scale byte (op_sel) is the k-step ks; ks is an
+// unrolled loop index, so the branch folds to one instruction.
 __device__ __forceinline__ v16f mfma_mx(int ks, v8i a, v8i b, v16f c, int sa, int sb) {
-  switch (ks) {
-    case 0: return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 4, 4, 0, sa, 0, sb);
-    case 1: return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 4, 4, 1, sa, 1, sb);
-    case 2: return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 4, 4, 2, sa, 2, sb);
-    default: return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 4, 4, 3, sa, 3, sb);
-  }
+  if (ks == 0) return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 4, 4, 0, sa, 0, sb);
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 4, 4, 1, sa, 1, sb);
 }
 
 __device__ __forceinline__ v8h dequant8(uint32_t w, _Float16 s) {
@@ -75,16 +77,49 @@ __device__ __forceinline__ v8h dequant8(uint32_t w, _Float16 s) {
   return (v8h){p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
 }
 
-template <int FMT>
-__global__ __launch_bounds__(256, 1) void gemm_large(
-    int64_t m, int64_t n, int64_t k, const uint8_t* __restrict__ a,
+// Direct buffer -> LDS load of SIZE bytes per lane (lane i writes lds + SIZE i).
+// Kept out of the host compilation pass: there the builtin makes clang drop
+// the kernel template's host stub.
+__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t rs, void* lds, int voff, int soff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)lds, 16, voff, soff, 0, 0);
+#endif
+}
+__device__ __forceinline__ void load_lds16_nt(__amdgpu_buffer_rsrc_t rs, void* lds, int voff, int soff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)lds, 16, voff, soff, 0, 2);
+#endif
+}
+__device__ __forceinline__ void load_lds4(__amdgpu_buffer_rsrc_t rs, void* lds, int voff, int soff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)lds, 4, voff, soff, 0, 0);
+#endif
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  // vmcnt N (N < 64); expcnt and lgkmcnt at their maximum (no wait)
+  static_assert(N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+template <int FMT, int WMW, int WNW>
+__global__ __launch_bounds__(64 * WMW * WNW, 1) void gemm_large(
+    int m, int n, int k, const uint8_t* __restrict__ a,
     const uint8_t* __restrict__ as, const float* __restrict__ at,
     const uint8_t* __restrict__ b, const uint8_t* __restrict__ bs,
     const float* __restrict__ bt, void* __restrict__ c, int c_dtype,
     int tiles_m, int tiles_n) {
   using Stage = LargeStage<FMT>;
-  constexpr int SPR = Stage::SPR;
-  __shared__ __attribute__((aligned(16))) Stage st[2];
+  constexpr int SW = Stage::SW;
+  constexpr int NW = WMW * WNW;                // waves
+  constexpr int NL = BM * ROWB / 1024 / NW;    // 1 KiB code blocks per operand per wave
+  constexpr int NSL = 8 * SW / NW;             // scale-word loads (A and B) per wave
+  constexpr int TM = BM / WMW, TN = BN / WNW;  // wave tile
+  constexpr int TI = TM / 32, TJ = TN / 32;    // 32x32 MFMA tiles per wave
+  constexpr int LPS = 2 * NL + NSL;            // loads per thread per stage
+  static_assert(NL * NW * 1024 == BM * ROWB && NSL * NW == 8 * SW && 2 * LPS < 64, "tile shape");
+  __shared__ __attribute__((aligned(16))) Stage st[NSTAGE];
 
   // ---- tile from workgroup id (XCD-aware) --------------------------------
   const int ntiles = tiles_m * tiles_n;
@@ -92,176 +127,202 @@ __global__ __launch_bounds__(256, 1) void gemm_large(
   int tile = wg;
   if (ntiles % NXCD == 0) tile = (wg % NXCD) * (ntiles / NXCD) + wg / NXCD;
   const int tm = tile % tiles_m, tn = tile / tiles_m;
-  const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+  const int m0 = tm * BM, n0 = tn * BN;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t kbytes = k / 2, srow = (FMT == kFmtNV) ? k / 16 : k / 32;
-  const int nstages = (int)(k / BK);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
+  const int kbytes = k / 2, srow = (FMT == kFmtNV) ? k / 16 : k / 32;
+  const int nstages = k / BK;
 
-  // ---- global -> register staging for one stage --------------------------
-  // codes: 2048 16-byte chunks per operand, 8 per thread; chunk q = tid + 256 i
-  // is row q / 8, column chunk q % 8 (a wave covers 8 full 128-byte rows).
-  u32x4 ra[8], rb[8];
-  uint32_t rsa[SPR / 4], rsb[SPR / 4];      // this thread's row of scale bytes
-  // Buffer resources: one scalar descriptor per operand and a 32-bit row
-  // offset per load (the operands are below 2 GiB); the stage offset goes in
-  // the scalar soffset.
-  const __amdgpu_buffer_rsrc_t rs_a = __builtin_amdgcn_make_buffer_rsrc((void*)a, (short)0, (int)(m * kbytes), 0x00020000);
-  const __amdgpu_buffer_rsrc_t rs_b = __builtin_amdgcn_make_buffer_rsrc((void*)b, (short)0, (int)(n * kbytes), 0x00020000);
-  const __amdgpu_buffer_rsrc_t rs_as = __builtin_amdgcn_make_buffer_rsrc((void*)as, (short)0, (int)(m * srow), 0x00020000);
-  const __amdgpu_buffer_rsrc_t rs_bs = __builtin_amdgcn_make_buffer_rsrc((void*)bs, (short)0, (int)(n * srow), 0x00020000);
-  const int64_t arow_s = (m0 + tid < m) ? m0 + tid : m - 1;   // scale row (one per thread)
-  const int64_t brow_s = (n0 + tid < n) ? n0 + tid : n - 1;
-  const int sa_off = (int)(arow_s * srow), sb_off = (int)(brow_s * srow);
-  auto load_stage = [&](int sidx) {
-    const int kb = sidx * ROWB;                                // byte offset in a row
+  // ---- direct global -> LDS loads of one stage ----------------------------
+  // Code block q (1 KiB = 16 rows x 64 bytes) of an operand: lane p fills
+  // position p, i.e. row 16 q + p / 4, stored chunk p % 4, which holds the
+  // logical chunk (p % 4) ^ ((row >> 2) & 3).  All offsets are 32-bit: the
+  // operands are below 2 GiB.  Rows past m or n re-read the last row.
+  const __amdgpu_buffer_rsrc_t rs_a = __builtin_amdgcn_make_buffer_rsrc((void*)a, (short)0, m * kbytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rs_b = __builtin_amdgcn_make_buffer_rsrc((void*)b, (short)0, n * kbytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rs_as = __builtin_amdgcn_make_buffer_rsrc((void*)as, (short)0, m * srow, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rs_bs = __builtin_amdgcn_make_buffer_rsrc((void*)bs, (short)0, n * srow, 0x00020000);
+  int voff_a[NL], voff_b[NL];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int q = tid + 256 * i, row = q >> 3, cc = q & 7;
-      const int64_t ar = (m0 + row < m) ? m0 + row : m - 1;
-      const int64_t br = (n0 + row < n) ? n0 + row : n - 1;
-      ra[i] = __builtin_amdgcn_raw_buffer_load_b128(rs_a, (int)(ar * kbytes) + cc * 16, kb, 0);
-      rb[i] = __builtin_amdgcn_raw_buffer_load_b128(rs_b, (int)(br * kbytes) + cc * 16, kb, 2);
+  for (int i = 0; i < NL; ++i) {
+    const int q = i * NW + wave;
+    const int row = 16 * q + (lane >> 2);
+    const int chunk = (lane & 3) ^ ((row >> 2) & 3);
+    const int ar = (m0 + row < m) ? m0 + row : m - 1;
+    const int br = (n0 + row < n) ? n0 + row : n - 1;
+    voff_a[i] = ar * kbytes + chunk * 16;
+    voff_b[i] = br * kbytes + chunk * 16;
+  }
+  // Scale-word load j of this wave: g = j * NW + wave selects the operand
+  // (g / (4 SW)), the word (g % (4 SW)) / 4 and rows 64 (g % 4) .. + 63.
+  int voff_s[NSL];
+#pragma unroll
+  for (int j = 0; j < NSL; ++j) {
+    const int g = j * NW + wave;
+    const bool isb = g >= 4 * SW;
+    const int word = (g % (4 * SW)) / 4, row = 64 * (g % 4) + lane;
+    const int lim = isb ? n : m, base = isb ? n0 : m0;
+    const int rr = (base + row < lim) ? base + row : lim - 1;
+    voff_s[j] = rr * srow + 4 * word;
+  }
+  // Stage sidx into ring slot `slot`.
+  auto issue_stage = [&](int slot, int sidx) {
+    Stage& S = st[slot];
+    const int kb = sidx * ROWB;
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      const int q = i * NW + wave;
+      load_lds16(rs_a, &S.a[q * 1024], voff_a[i], kb);
+      load_lds16_nt(rs_b, &S.b[q * 1024], voff_b[i], kb);
     }
-    const int sbo = sidx * SPR;
-    if (SPR == 16) {
-      const u32x4 va = __builtin_amdgcn_raw_buffer_load_b128(rs_as, sa_off, sbo, 0);
-      const u32x4 vb = __builtin_amdgcn_raw_buffer_load_b128(rs_bs, sb_off, sbo, 0);
+    const int sbo = sidx * (4 * SW);
 #pragma unroll
-      for (int j = 0; j < SPR / 4; ++j) { rsa[j] = va[j]; rsb[j] = vb[j]; }
-    } else {
-      const u32x2 va = __builtin_amdgcn_raw_buffer_load_b64(rs_as, sa_off, sbo, 0);
-      const u32x2 vb = __builtin_amdgcn_raw_buffer_load_b64(rs_bs, sb_off, sbo, 0);
-#pragma unroll
-      for (int j = 0; j < SPR / 4; ++j) { rsa[j] = va[j]; rsb[j] = vb[j]; }
+    for (int j = 0; j < NSL; ++j) {
+      const int g = j * NW + wave;
+      const bool isb = g >= 4 * SW;
+      const int word = (g % (4 * SW)) / 4, rb = g % 4;
+      uint32_t* dst = isb ? &S.sb[word][64 * rb] : &S.sa[word][64 * rb];
+      load_lds4(isb ? rs_bs : rs_as, dst, voff_s[j], sbo);
     }
   };
-  auto store_stage = [&](Stage& S) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int q = tid + 256 * i, row = q >> 3, cc = q & 7;
-      *reinterpret_cast<u32x4*>(&S.a[row * ROWB + swz8(row, cc) * 16]) = ra[i];
-      *reinterpret_cast<u32x4*>(&S.b[row * ROWB + swz8(row, cc) * 16]) = rb[i];
-    }
-#pragma unroll
-    for (int j = 0; j < SPR / 4; ++j) {
-      reinterpret_cast<uint32_t*>(&S.as[tid * SPR])[j] = rsa[j];
-      reinterpret_cast<uint32_t*>(&S.bs[tid * SPR])[j] = rsb[j];
-    }
-  };
 
-  // ---- accumulators: 4 x 4 tiles of 32 x 32 per wave ---------------------
-  const int wm = wave >> 1, wn = wave & 1;
+  // ---- accumulators: TI x TJ tiles of 32 x 32 per wave -------------------
+  const int wm = wave / WNW, wn = wave % WNW;
   const int r = lane & 31, h = lane >> 5;
-  v16f acc[4][4];
+  v16f acc[TI][TJ];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < TI; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < TJ; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-  load_stage(0);
-  store_stage(st[0]);
-  if (nstages > 1) load_stage(1);
-  __syncthreads();
+  // Prologue: stages 0, 1, 2 (clamped; a repeated stage is never read).
+#pragma unroll
+  for (int p = 0; p < NSTAGE - 1; ++p) issue_stage(p, p < nstages ? p : nstages - 1);
 
+  // Every iteration waits for the oldest stage and issues exactly one more
+  // (near the end a repeat of the last stage into the free slot), so the loop
+  // body has no data-dependent branch and the accumulators stay in place.
   for (int s = 0; s < nstages; ++s) {
-    Stage& S = st[s & 1];
+    wait_vm<2 * LPS>();         // this thread's loads of stage s have landed
+    // Every wave's part of stage s has landed and stage s-1 is consumed.  A
+    // bare s_barrier: __syncthreads() would also drain the loads of the later
+    // stages still in flight.  The memory clobber keeps the compiler from
+    // moving LDS reads across it.
+    __asm__ volatile("s_barrier" ::: "memory");
+    const int nxt = s + NSTAGE - 1;
+    issue_stage(nxt % NSTAGE, nxt < nstages ? nxt : nstages - 1);
+    const Stage& S = st[s % NSTAGE];
+
     if (FMT == kFmtMX) {
-      int sa[4], sb[4];
+      int sa[TI], sb[TJ];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        sa[i] = *reinterpret_cast<const int*>(&S.as[(wm * 128 + 32 * i + r) * SPR + 4 * h]);
-        sb[i] = *reinterpret_cast<const int*>(&S.bs[(wn * 128 + 32 * i + r) * SPR + 4 * h]);
-      }
+      for (int i = 0; i < TI; ++i) sa[i] = (int)(S.sa[0][wm * TM + 32 * i + r] >> (16 * h));
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        u32x4 fb[4];
+      for (int j = 0; j < TJ; ++j) sb[j] = (int)(S.sb[0][wn * TN + 32 * j + r] >> (16 * h));
+      // all fragments of the stage first: one LDS wait instead of one per tile
+      u32x4 fa[2][TI], fb[2][TJ];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int rb_ = wn * 128 + 32 * j + r;
-          fb[j] = *reinterpret_cast<const u32x4*>(&S.b[rb_ * ROWB + swz8(rb_, 4 * h + ks) * 16]);
+      for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+        for (int j = 0; j < TJ; ++j) {
+          const int rb = wn * TN + 32 * j + r;
+          fb[ks][j] = *reinterpret_cast<const u32x4*>(&S.b[rb * ROWB + swz(rb, 2 * h + ks) * 16]);
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int ra_ = wm * 128 + 32 * i + r;
-          const u32x4 va = *reinterpret_cast<const u32x4*>(&S.a[ra_ * ROWB + swz8(ra_, 4 * h + ks) * 16]);
-          const v8i fa = {(int)va[0], (int)va[1], (int)va[2], (int)va[3], 0, 0, 0, 0};
+        for (int i = 0; i < TI; ++i) {
+          const int ra = wm * TM + 32 * i + r;
+          fa[ks][i] = *reinterpret_cast<const u32x4*>(&S.a[ra * ROWB + swz(ra, 2 * h + ks) * 16]);
+        }
+      }
+      // Keep the reads ahead of the MFMAs as one block: interleaving them in
+      // small groups leaves the matrix pipe idle on every LDS wait, while a
+      // read block overlaps the MFMA block of the other wave on the SIMD.
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const v8i fbj = {(int)fb[j][0], (int)fb[j][1], (int)fb[j][2], (int)fb[j][3], 0, 0, 0, 0};
-            acc[i][j] = mfma_mx(ks, fa, fbj, acc[i][j], sa[i], sb[j]);
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int i = 0; i < TI; ++i) {
+          const v8i a8 = {(int)fa[ks][i][0], (int)fa[ks][i][1], (int)fa[ks][i][2], (int)fa[ks][i][3], 0, 0, 0, 0};
+#pragma unroll
+          for (int j = 0; j < TJ; ++j) {
+            const v8i b8 = {(int)fb[ks][j][0], (int)fb[ks][j][1], (int)fb[ks][j][2], (int)fb[ks][j][3], 0, 0, 0, 0};
+            acc[i][j] = mfma_mx(ks, a8, b8, acc[i][j], sa[i], sb[j]);
           }
         }
-      }
     } else {
-      // scales: blocks 8h .. 8h+7 of this stage for each of the 4 row tiles
-      u32x2 sa2[4], sb2[4];
+      // this lane's 4 block scales (word h of its row), decoded in pairs
+      v2h sa01[TI], sa23[TI], sb01[TJ], sb23[TJ];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        sa2[i] = *reinterpret_cast<const u32x2*>(&S.as[(wm * 128 + 32 * i + r) * SPR + 8 * h]);
-        sb2[i] = *reinterpret_cast<const u32x2*>(&S.bs[(wn * 128 + 32 * i + r) * SPR + 8 * h]);
+      for (int i = 0; i < TI; ++i) {
+        const uint32_t w = S.sa[h][wm * TM + 32 * i + r];
+        sa01[i] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false);
+        sa23[i] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true);
       }
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {              // 16-byte code chunk 4h + q: 4 steps
-        u32x4 ca[4], cb[4];
+      for (int j = 0; j < TJ; ++j) {
+        const uint32_t w = S.sb[h][wn * TN + 32 * j + r];
+        sb01[j] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false);
+        sb23[j] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true);
+      }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int ra_ = wm * 128 + 32 * i + r, rb_ = wn * 128 + 32 * i + r;
-          ca[i] = *reinterpret_cast<const u32x4*>(&S.a[ra_ * ROWB + swz8(ra_, 4 * h + q) * 16]);
-          cb[i] = *reinterpret_cast<const u32x4*>(&S.b[rb_ * ROWB + swz8(rb_, 4 * h + q) * 16]);
-        }
-        // blocks 2q and 2q+1 of this lane's 8: bytes 2q, 2q+1 of the scale pair
-        v2h sca[4], scb[4];
+      for (int q = 0; q < 2; ++q) {              // code chunk 2h + q: blocks 4h + 2q, +1
+        u32x4 ca[TI], cb[TJ];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const uint32_t wa = sa2[i][q >> 1], wb = sb2[i][q >> 1];
-          sca[i] = (q & 1) ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(wa, 1.0f, true)
-                           : __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(wa, 1.0f, false);
-          scb[i] = (q & 1) ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(wb, 1.0f, true)
-                           : __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(wb, 1.0f, false);
+        for (int i = 0; i < TI; ++i) {
+          const int ra = wm * TM + 32 * i + r;
+          ca[i] = *reinterpret_cast<const u32x4*>(&S.a[ra * ROWB + swz(ra, 2 * h + q) * 16]);
         }
 #pragma unroll
-        for (int d = 0; d < 4; ++d) {            // 8 values per dword = half a block
-          v8h fa[4], fb[4];
+        for (int j = 0; j < TJ; ++j) {
+          const int rb = wn * TN + 32 * j + r;
+          cb[j] = *reinterpret_cast<const u32x4*>(&S.b[rb * ROWB + swz(rb, 2 * h + q) * 16]);
+        }
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            fa[i] = dequant8(ca[i][d], d < 2 ? sca[i].x : sca[i].y);
-            fb[i] = dequant8(cb[i][d], d < 2 ? scb[i].x : scb[i].y);
+        for (int d = 0; d < 4; ++d) {            // 8 values per dword
+          v8h fa[TI], fb[TJ];
+#pragma unroll
+          for (int i = 0; i < TI; ++i) {
+            const v2h sp = q ? sa23[i] : sa01[i];
+            fa[i] = dequant8(ca[i][d], d < 2 ? sp.x : sp.y);
           }
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
+          for (int j = 0; j < TJ; ++j) {
+            const v2h sp = q ? sb23[j] : sb01[j];
+            fb[j] = dequant8(cb[j][d], d < 2 ? sp.x : sp.y);
+          }
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+          for (int i = 0; i < TI; ++i)
+#pragma unroll
+            for (int j = 0; j < TJ; ++j)
               acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[i], fb[j], acc[i][j], 0, 0, 0);
         }
       }
     }
-    if (s + 1 < nstages) {
-      store_stage(st[(s + 1) & 1]);
-      if (s + 2 < nstages) load_stage(s + 2);
-    }
-    __syncthreads();
   }
+
+  wait_vm<0>();                 // no load may land in LDS after the workgroup ends
 
   // ---- epilogue -----------------------------------------------------------
   // 32x32 D layout: lane holds column lane % 32, register e holds row
   // 8 * (e / 4) + 4 * (lane / 32) + e % 4.
   const float ts = (FMT == kFmtNV) ? (*at) * (*bt) : 1.0f;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < TI; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t col = n0 + wn * 128 + 32 * j + r;
+    for (int j = 0; j < TJ; ++j) {
+      const int col = n0 + wn * TN + 32 * j + r;
       if (col >= n) continue;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int64_t row = m0 + wm * 128 + 32 * i + 8 * (e >> 2) + 4 * h + (e & 3);
+        const int row = m0 + wm * TM + 32 * i + 8 * (e >> 2) + 4 * h + (e & 3);
         if (row < m) {
           const float v = acc[i][j][e] * ts;
-          if (c_dtype == kInF32) reinterpret_cast<float*>(c)[row * n + col] = v;
-          else reinterpret_cast<__bf16*>(c)[row * n + col] = (__bf16)v;
+          const int64_t idx = (int64_t)row * n + col;
+          if (c_dtype == kInF32) reinterpret_cast<float*>(c)[idx] = v;
+          else reinterpret_cast<__bf16*>(c)[idx] = (__bf16)v;
         }
       }
     }
@@ -283,11 +344,13 @@ hipError_t launch_gemm_large(int fmt, int64_t m, int64_t n, int64_t k,
   const int tiles_m = (int)((m + BM - 1) / BM), tiles_n = (int)((n + BN - 1) / BN);
   const dim3 grid((unsigned)(tiles_m * tiles_n));
   if (fmt == kFmtMX) {
-    hipLaunchKernelGGL((gemm_large<kFmtMX>), grid, dim3(256), 0, stream, m, n, k, a_codes,
-                       a_scales, a_tscale, b_codes, b_scales, b_tscale, c, c_dtype, tiles_m, tiles_n);
+    hipLaunchKernelGGL((gemm_large<kFmtMX, kMXWM, kMXWN>), grid, dim3(64 * kMXWM * kMXWN), 0, stream,
+                       (int)m, (int)n, (int)k, a_codes, a_scales, a_tscale, b_codes, b_scales,
+                       b_tscale, c, c_dtype, tiles_m, tiles_n);
   } else {
-    hipLaunchKernelGGL((gemm_large<kFmtNV>), grid, dim3(256), 0, stream, m, n, k, a_codes,
-                       a_scales, a_tscale, b_codes, b_scales, b_tscale, c, c_dtype, tiles_m, tiles_n);
+    hipLaunchKernelGGL((gemm_large<kFmtNV, kNVWM, kNVWN>), grid, dim3(64 * kNVWM * kNVWN), 0, stream,
+                       (int)m, (int)n, (int)k, a_codes, a_scales, a_tscale, b_codes, b_scales,
+                       b_tscale, c, c_dtype, tiles_m, tiles_n);
   }
   return hipGetLastError();
 }
