@@ -12,8 +12,14 @@
 // staging.  A direct load writes lane i's 16 bytes at base + 16 i, so the LDS
 // layout is chosen through the global addresses: in a row r, 16-byte chunk c
 // is stored at position c ^ ((r >> 2) & 3), which keeps the 32-row MFMA
-// fragment reads at the minimum number of bank cycles.  Scale bytes are
-// stored per row as 32-bit words (word w of every row contiguous).
+// fragment reads at the minimum number of bank cycles.
+//
+// Scales travel in groups of 16 bytes per row (4 stages of MXFP4, 2 of
+// NVFP4), one 16-byte load per lane, into a 3-slot LDS ring of their own:
+// fetching a stage's 4 or 8 scale bytes per row on its own would cost one
+// memory request per row for a few bytes, and the request rate, not the
+// byte rate, bounds the operand stream.  Group g + 2 is fetched once the
+// stages of group g - 1 are consumed.
 //
 // MXFP4 (E8M0 scale per 32 values): v_mfma_scale_f32_32x32x64_f8f6f4, both
 // operands E2M1.  In k-step ks (0, 1) of a stage, lane (row r, half h)
@@ -50,14 +56,31 @@ constexpr int NXCD = 8;
 constexpr int kMXWM = 2, kMXWN = 4;
 constexpr int kNVWM = 2, kNVWN = 4;
 
-template <int FMT>
+constexpr int NSGRP = 3;              // scale-group ring depth
+
 struct LargeStage {
-  static constexpr int SW = (FMT == kFmtNV) ? 2 : 1;   // scale words per row per stage
   uint8_t a[BM * ROWB];
   uint8_t b[BN * ROWB];
-  uint32_t sa[SW][BM];
-  uint32_t sb[SW][BN];
 };
+
+// One scale group: 4 words (16 bytes) per row, rows contiguous, A then B.
+struct ScaleGroup {
+  uint32_t w[2][BM * 4];
+};
+
+// All of a workgroup's LDS in one object: the loop's explicit vmcnt waits and
+// barriers order the direct loads against the reads, and with a single
+// object the compiler adds no waits of its own (with several, it drains
+// every load in flight before the first read of the object a load targets).
+struct LargeSmem {
+  LargeStage st[NSTAGE];
+  ScaleGroup sg[NSGRP];
+};
+
+// stages per scale group: 16 bytes per row hold 4 MXFP4 stages (one E8M0
+// byte per 32 values) or 2 NVFP4 stages (one E4M3 byte per 16 values)
+template <int FMT>
+constexpr int stages_per_group() { return FMT == kFmtNV ? 2 : 4; }
 
 __device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ ((row >> 2) & 3); }
 
@@ -90,11 +113,6 @@ __device__ __forceinline__ void load_lds16_nt(__amdgpu_buffer_rsrc_t rs, void* l
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)lds, 16, voff, soff, 0, 2);
 #endif
 }
-__device__ __forceinline__ void load_lds4(__amdgpu_buffer_rsrc_t rs, void* lds, int voff, int soff) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)lds, 4, voff, soff, 0, 0);
-#endif
-}
 
 template <int N>
 __device__ __forceinline__ void wait_vm() {
@@ -110,16 +128,17 @@ __global__ __launch_bounds__(64 * WMW * WNW, 1) void gemm_large(
     const uint8_t* __restrict__ b, const uint8_t* __restrict__ bs,
     const float* __restrict__ bt, void* __restrict__ c, int c_dtype,
     int tiles_m, int tiles_n) {
-  using Stage = LargeStage<FMT>;
-  constexpr int SW = Stage::SW;
+  using Stage = LargeStage;
+  constexpr int G = stages_per_group<FMT>();
   constexpr int NW = WMW * WNW;                // waves
   constexpr int NL = BM * ROWB / 1024 / NW;    // 1 KiB code blocks per operand per wave
-  constexpr int NSL = 8 * SW / NW;             // scale-word loads (A and B) per wave
+  constexpr int NSG = 8 / NW;                  // 1 KiB scale-group blocks (A and B) per wave
   constexpr int TM = BM / WMW, TN = BN / WNW;  // wave tile
   constexpr int TI = TM / 32, TJ = TN / 32;    // 32x32 MFMA tiles per wave
-  constexpr int LPS = 2 * NL + NSL;            // loads per thread per stage
-  static_assert(NL * NW * 1024 == BM * ROWB && NSL * NW == 8 * SW && 2 * LPS < 64, "tile shape");
-  __shared__ __attribute__((aligned(16))) Stage st[NSTAGE];
+  static_assert(BM == BN && NL * NW * 1024 == BM * ROWB && NSG * NW == 8 && 4 * NL + 2 * NSG < 64, "tile shape");
+  __shared__ __attribute__((aligned(16))) LargeSmem smem;
+  Stage* st = smem.st;
+  ScaleGroup* sgr = smem.sg;
 
   // ---- tile from workgroup id (XCD-aware) --------------------------------
   const int ntiles = tiles_m * tiles_n;
@@ -133,6 +152,7 @@ __global__ __launch_bounds__(64 * WMW * WNW, 1) void gemm_large(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
   const int kbytes = k / 2, srow = (FMT == kFmtNV) ? k / 16 : k / 32;
   const int nstages = k / BK;
+  const int ngroups = (nstages + G - 1) / G;
 
   // ---- direct global -> LDS loads of one stage ----------------------------
   // Code block q (1 KiB = 16 rows x 64 bytes) of an operand: lane p fills
@@ -154,17 +174,17 @@ __global__ __launch_bounds__(64 * WMW * WNW, 1) void gemm_large(
     voff_a[i] = ar * kbytes + chunk * 16;
     voff_b[i] = br * kbytes + chunk * 16;
   }
-  // Scale-word load j of this wave: g = j * NW + wave selects the operand
-  // (g / (4 SW)), the word (g % (4 SW)) / 4 and rows 64 (g % 4) .. + 63.
-  int voff_s[NSL];
+  // Scale-group block j of this wave: g = j * NW + wave selects the operand
+  // (g / 4) and rows 64 (g % 4) .. + 63; lane p loads row 64 (g % 4) + p.
+  int voff_s[NSG];
 #pragma unroll
-  for (int j = 0; j < NSL; ++j) {
+  for (int j = 0; j < NSG; ++j) {
     const int g = j * NW + wave;
-    const bool isb = g >= 4 * SW;
-    const int word = (g % (4 * SW)) / 4, row = 64 * (g % 4) + lane;
+    const bool isb = g >= 4;
+    const int row = 64 * (g % 4) + lane;
     const int lim = isb ? n : m, base = isb ? n0 : m0;
     const int rr = (base + row < lim) ? base + row : lim - 1;
-    voff_s[j] = rr * srow + 4 * word;
+    voff_s[j] = rr * srow;
   }
   // Stage sidx into ring slot `slot`.
   auto issue_stage = [&](int slot, int sidx) {
@@ -176,14 +196,15 @@ __global__ __launch_bounds__(64 * WMW * WNW, 1) void gemm_large(
       load_lds16(rs_a, &S.a[q * 1024], voff_a[i], kb);
       load_lds16_nt(rs_b, &S.b[q * 1024], voff_b[i], kb);
     }
-    const int sbo = sidx * (4 * SW);
+  };
+  // Scale group gidx into scale slot `slot` (16-byte aligned: the row pitch
+  // is a multiple of 16 bytes and nstages a multiple of G).
+  auto issue_group = [&](int slot, int gidx) {
 #pragma unroll
-    for (int j = 0; j < NSL; ++j) {
+    for (int j = 0; j < NSG; ++j) {
       const int g = j * NW + wave;
-      const bool isb = g >= 4 * SW;
-      const int word = (g % (4 * SW)) / 4, rb = g % 4;
-      uint32_t* dst = isb ? &S.sb[word][64 * rb] : &S.sa[word][64 * rb];
-      load_lds4(isb ? rs_bs : rs_as, dst, voff_s[j], sbo);
+      const bool isb = g >= 4;
+      load_lds16(isb ? rs_bs : rs_as, &sgr[slot].w[isb][256 * (g % 4)], voff_s[j], 16 * gidx);
     }
   };
 
@@ -198,15 +219,37 @@ __global__ __launch_bounds__(64 * WMW * WNW, 1) void gemm_large(
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-  // Prologue: stages 0, 1, 2 (clamped; a repeated stage is never read).
+  // Prologue, in the order the steady state would have issued it: iteration
+  // i issues code stage i + 3 and, when i % G == 0, scale group i / G + 2, so
+  // the virtual iterations -2G, -G, -3, -2, -1 give groups 0 and 1 and
+  // stages 0, 1, 2 (indexes clamped; a repeated stage or group is never
+  // read).
+  issue_group(0, 0);
+  if (G == 2) {
+    issue_stage(0, 0);
+    issue_stage(1, nstages > 1 ? 1 : 0);
+    issue_group(1, ngroups > 1 ? 1 : 0);
+    issue_stage(2, nstages > 2 ? 2 : nstages - 1);
+  } else {
+    issue_group(1, ngroups > 1 ? 1 : 0);
 #pragma unroll
-  for (int p = 0; p < NSTAGE - 1; ++p) issue_stage(p, p < nstages ? p : nstages - 1);
+    for (int p = 0; p < NSTAGE - 1; ++p) issue_stage(p, p < nstages ? p : nstages - 1);
+  }
 
   // Every iteration waits for the oldest stage and issues exactly one more
   // (near the end a repeat of the last stage into the free slot), so the loop
   // body has no data-dependent branch and the accumulators stay in place.
   for (int s = 0; s < nstages; ++s) {
-    wait_vm<2 * LPS>();         // this thread's loads of stage s have landed
+    // This thread's loads of stage s (and of its scale group, issued earlier)
+    // have landed.  Issued after them: stages s + 1 and s + 2 and the groups
+    // issued in iterations s - 3 .. s - 1, one for each multiple of G there.
+    if (G == 4) {
+      if ((s & 3) == 0) wait_vm<4 * NL>();
+      else wait_vm<4 * NL + NSG>();
+    } else {
+      if ((s & 1) == 0) wait_vm<4 * NL + NSG>();
+      else wait_vm<4 * NL + 2 * NSG>();
+    }
     // Every wave's part of stage s has landed and stage s-1 is consumed.  A
     // bare s_barrier: __syncthreads() would also drain the loads of the later
     // stages still in flight.  The memory clobber keeps the compiler from
@@ -214,14 +257,22 @@ __global__ __launch_bounds__(64 * WMW * WNW, 1) void gemm_large(
     __asm__ volatile("s_barrier" ::: "memory");
     const int nxt = s + NSTAGE - 1;
     issue_stage(nxt % NSTAGE, nxt < nstages ? nxt : nstages - 1);
+    const int grp = s / G;
+    if (s % G == 0) {
+      // group grp - 1 is consumed: its slot takes group grp + 2
+      const int gn = grp + 2;
+      issue_group(gn % NSGRP, gn < ngroups ? gn : ngroups - 1);
+    }
     const Stage& S = st[s % NSTAGE];
+    const ScaleGroup& SG = sgr[grp % NSGRP];
+    const int sw = (s % G) * (4 / G);            // first scale word of stage s
 
     if (FMT == kFmtMX) {
       int sa[TI], sb[TJ];
 #pragma unroll
-      for (int i = 0; i < TI; ++i) sa[i] = (int)(S.sa[0][wm * TM + 32 * i + r] >> (16 * h));
+      for (int i = 0; i < TI; ++i) sa[i] = (int)(SG.w[0][4 * (wm * TM + 32 * i + r) + sw] >> (16 * h));
 #pragma unroll
-      for (int j = 0; j < TJ; ++j) sb[j] = (int)(S.sb[0][wn * TN + 32 * j + r] >> (16 * h));
+      for (int j = 0; j < TJ; ++j) sb[j] = (int)(SG.w[1][4 * (wn * TN + 32 * j + r) + sw] >> (16 * h));
       // all fragments of the stage first: one LDS wait instead of one per tile
       u32x4 fa[2][TI], fb[2][TJ];
 #pragma unroll
@@ -257,13 +308,13 @@ __global__ __launch_bounds__(64 * WMW * WNW, 1) void gemm_large(
       v2h sa01[TI], sa23[TI], sb01[TJ], sb23[TJ];
 #pragma unroll
       for (int i = 0; i < TI; ++i) {
-        const uint32_t w = S.sa[h][wm * TM + 32 * i + r];
+        const uint32_t w = SG.w[0][4 * (wm * TM + 32 * i + r) + sw + h];
         sa01[i] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false);
         sa23[i] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true);
       }
 #pragma unroll
       for (int j = 0; j < TJ; ++j) {
-        const uint32_t w = S.sb[h][wn * TN + 32 * j + r];
+        const uint32_t w = SG.w[1][4 * (wn * TN + 32 * j + r) + sw + h];
         sb01[j] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false);
         sb23[j] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true);
       }
@@ -331,9 +382,10 @@ __global__ __launch_bounds__(64 * WMW * WNW, 1) void gemm_large(
 }  // namespace
 
 bool gemm_large_supported(int fmt, int64_t m, int64_t n, int64_t k) {
-  (void)fmt;
   const int64_t lim = int64_t(1) << 31;     // 32-bit buffer offsets
-  return m >= 128 && n >= 128 && k % BK == 0 && m * (k / 2) < lim && n * (k / 2) < lim;
+  // 16-byte scale rows: k a multiple of 512 (MXFP4) or 256 (NVFP4)
+  const int64_t kq = (fmt == kFmtNV) ? 256 : 512;
+  return m >= 128 && n >= 128 && k % kq == 0 && m * (k / 2) < lim && n * (k / 2) < lim;
 }
 
 hipError_t launch_gemm_large(int fmt, int64_t m, int64_t n, int64_t k,
