@@ -35,6 +35,8 @@
 // different XCDs (each with its own L2), so the ids are regrouped to give
 // every XCD a contiguous run of tiles, ordered m-fastest, so that the tiles
 // sharing a weight slab run on the same L2.
+#include <type_traits>
+
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -53,8 +55,8 @@ constexpr int ROWB = BK / 2;          // code bytes per row per stage
 constexpr int NSTAGE = 4;             // LDS ring depth
 constexpr int NXCD = 8;
 // waves per workgroup along m and n
-constexpr int kMXWM = 2, kMXWN = 4;
-constexpr int kNVWM = 2, kNVWN = 4;
+constexpr int kMXWM = 2, kMXWN = 2;
+constexpr int kNVWM = 2, kNVWN = 2;
 
 constexpr int NSGRP = 3;              // scale-group ring depth
 
@@ -108,10 +110,10 @@ __device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t rs, void* lds,
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)lds, 16, voff, soff, 0, 0);
 #endif
 }
-__device__ __forceinline__ void load_lds16_nt(__amdgpu_buffer_rsrc_t rs, void* lds, int voff, int soff) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)lds, 16, voff, soff, 0, 2);
-#endif
+
+__device__ __forceinline__ void wait_lgkm0() {
+  // lgkmcnt 0; vmcnt and expcnt at their maximum (no wait)
+  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));
 }
 
 template <int N>
@@ -120,6 +122,19 @@ __device__ __forceinline__ void wait_vm() {
   static_assert(N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
+
+// Fragments of one stage for one wave: code chunks x = 0, 1 of its A rows
+// and B columns (MXFP4: k-step x; NVFP4: chunk 2h + x), and the lane's scale
+// word per row (MXFP4: the stage's word, bytes 2h and 2h + 1 are this lane's;
+// NVFP4: word h of the stage).  Nothing here consumes the loaded values, so
+// the reads stay in flight while the previous stage is multiplied.
+template <int TI, int TJ>
+struct Frags {
+  u32x4 a[2][TI];
+  u32x4 b[2][TJ];
+  uint32_t sa[TI];
+  uint32_t sb[TJ];
+};
 
 template <int FMT, int WMW, int WNW>
 __global__ __launch_bounds__(64 * WMW * WNW, 1) void gemm_large(
@@ -135,7 +150,7 @@ __global__ __launch_bounds__(64 * WMW * WNW, 1) void gemm_large(
   constexpr int NSG = 8 / NW;                  // 1 KiB scale-group blocks (A and B) per wave
   constexpr int TM = BM / WMW, TN = BN / WNW;  // wave tile
   constexpr int TI = TM / 32, TJ = TN / 32;    // 32x32 MFMA tiles per wave
-  static_assert(BM == BN && NL * NW * 1024 == BM * ROWB && NSG * NW == 8 && 4 * NL + 2 * NSG < 64, "tile shape");
+  static_assert(BM == BN && NL * NW * 1024 == BM * ROWB && NSG * NW == 8 && 6 * NL + 2 * NSG < 64, "tile shape");
   __shared__ __attribute__((aligned(16))) LargeSmem smem;
   Stage* st = smem.st;
   ScaleGroup* sgr = smem.sg;
@@ -152,9 +167,9 @@ __global__ __launch_bounds__(64 * WMW * WNW, 1) void gemm_large(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
   const int kbytes = k / 2, srow = (FMT == kFmtNV) ? k / 16 : k / 32;
   const int nstages = k / BK;
-  const int ngroups = (nstages + G - 1) / G;
+  const int ngroups = nstages / G;
 
-  // ---- direct global -> LDS loads of one stage ----------------------------
+  // ---- direct global -> LDS loads -----------------------------------------
   // Code block q (1 KiB = 16 rows x 64 bytes) of an operand: lane p fills
   // position p, i.e. row 16 q + p / 4, stored chunk p % 4, which holds the
   // logical chunk (p % 4) ^ ((row >> 2) & 3).  All offsets are 32-bit: the
@@ -186,31 +201,62 @@ __global__ __launch_bounds__(64 * WMW * WNW, 1) void gemm_large(
     const int rr = (base + row < lim) ? base + row : lim - 1;
     voff_s[j] = rr * srow;
   }
-  // Stage sidx into ring slot `slot`.
-  auto issue_stage = [&](int slot, int sidx) {
-    Stage& S = st[slot];
-    const int kb = sidx * ROWB;
+  // Code stage t (clamped to the last; a repeat is never read) into slot t % NSTAGE.
+  auto issue_stage = [&](int t) {
+    Stage& S = st[t % NSTAGE];
+    const int kb = (t < nstages ? t : nstages - 1) * ROWB;
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
       const int q = i * NW + wave;
       load_lds16(rs_a, &S.a[q * 1024], voff_a[i], kb);
-      load_lds16_nt(rs_b, &S.b[q * 1024], voff_b[i], kb);
+      load_lds16(rs_b, &S.b[q * 1024], voff_b[i], kb);
     }
   };
-  // Scale group gidx into scale slot `slot` (16-byte aligned: the row pitch
-  // is a multiple of 16 bytes and nstages a multiple of G).
-  auto issue_group = [&](int slot, int gidx) {
+  // Scale group g (clamped to the last) into scale slot g % NSGRP; 16-byte
+  // aligned: the row pitch is a multiple of 16 bytes and nstages of G.
+  auto issue_group = [&](int g) {
+    ScaleGroup& SG = sgr[g % NSGRP];
+    const int gb = 16 * (g < ngroups ? g : ngroups - 1);
 #pragma unroll
     for (int j = 0; j < NSG; ++j) {
-      const int g = j * NW + wave;
-      const bool isb = g >= 4;
-      load_lds16(isb ? rs_bs : rs_as, &sgr[slot].w[isb][256 * (g % 4)], voff_s[j], 16 * gidx);
+      const int gw = j * NW + wave;
+      const bool isb = gw >= 4;
+      load_lds16(isb ? rs_bs : rs_as, &SG.w[isb][256 * (gw % 4)], voff_s[j], gb);
     }
   };
 
-  // ---- accumulators: TI x TJ tiles of 32 x 32 per wave -------------------
+  // ---- per-wave fragments ------------------------------------------------
   const int wm = wave / WNW, wn = wave % WNW;
   const int r = lane & 31, h = lane >> 5;
+  auto read_frags = [&](int t, Frags<TI, TJ>& F) {
+    const Stage& S = st[t % NSTAGE];
+    const ScaleGroup& SG = sgr[(t / G) % NSGRP];
+    const int sw = (t % G) * (4 / G);            // first scale word of stage t
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+#pragma unroll
+      for (int i = 0; i < TI; ++i) {
+        const int ra = wm * TM + 32 * i + r;
+        F.a[x][i] = *reinterpret_cast<const u32x4*>(&S.a[ra * ROWB + swz(ra, 2 * h + x) * 16]);
+      }
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) {
+        const int rb = wn * TN + 32 * j + r;
+        F.b[x][j] = *reinterpret_cast<const u32x4*>(&S.b[rb * ROWB + swz(rb, 2 * h + x) * 16]);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < TI; ++i) {
+      const uint32_t* w = &SG.w[0][4 * (wm * TM + 32 * i + r) + sw];
+      F.sa[i] = (FMT == kFmtMX) ? w[0] : w[h];
+    }
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) {
+      const uint32_t* w = &SG.w[1][4 * (wn * TN + 32 * j + r) + sw];
+      F.sb[j] = (FMT == kFmtMX) ? w[0] : w[h];
+    }
+  };
+
   v16f acc[TI][TJ];
 #pragma unroll
   for (int i = 0; i < TI; ++i)
@@ -219,88 +265,23 @@ __global__ __launch_bounds__(64 * WMW * WNW, 1) void gemm_large(
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-  // Prologue, in the order the steady state would have issued it: iteration
-  // i issues code stage i + 3 and, when i % G == 0, scale group i / G + 2, so
-  // the virtual iterations -2G, -G, -3, -2, -1 give groups 0 and 1 and
-  // stages 0, 1, 2 (indexes clamped; a repeated stage or group is never
-  // read).
-  issue_group(0, 0);
-  if (G == 2) {
-    issue_stage(0, 0);
-    issue_stage(1, nstages > 1 ? 1 : 0);
-    issue_group(1, ngroups > 1 ? 1 : 0);
-    issue_stage(2, nstages > 2 ? 2 : nstages - 1);
-  } else {
-    issue_group(1, ngroups > 1 ? 1 : 0);
-#pragma unroll
-    for (int p = 0; p < NSTAGE - 1; ++p) issue_stage(p, p < nstages ? p : nstages - 1);
-  }
-
-  // Every iteration waits for the oldest stage and issues exactly one more
-  // (near the end a repeat of the last stage into the free slot), so the loop
-  // body has no data-dependent branch and the accumulators stay in place.
-  for (int s = 0; s < nstages; ++s) {
-    // This thread's loads of stage s (and of its scale group, issued earlier)
-    // have landed.  Issued after them: stages s + 1 and s + 2 and the groups
-    // issued in iterations s - 3 .. s - 1, one for each multiple of G there.
-    if (G == 4) {
-      if ((s & 3) == 0) wait_vm<4 * NL>();
-      else wait_vm<4 * NL + NSG>();
-    } else {
-      if ((s & 1) == 0) wait_vm<4 * NL + NSG>();
-      else wait_vm<4 * NL + 2 * NSG>();
-    }
-    // Every wave's part of stage s has landed and stage s-1 is consumed.  A
-    // bare s_barrier: __syncthreads() would also drain the loads of the later
-    // stages still in flight.  The memory clobber keeps the compiler from
-    // moving LDS reads across it.
-    __asm__ volatile("s_barrier" ::: "memory");
-    const int nxt = s + NSTAGE - 1;
-    issue_stage(nxt % NSTAGE, nxt < nstages ? nxt : nstages - 1);
-    const int grp = s / G;
-    if (s % G == 0) {
-      // group grp - 1 is consumed: its slot takes group grp + 2
-      const int gn = grp + 2;
-      issue_group(gn % NSGRP, gn < ngroups ? gn : ngroups - 1);
-    }
-    const Stage& S = st[s % NSTAGE];
-    const ScaleGroup& SG = sgr[grp % NSGRP];
-    const int sw = (s % G) * (4 / G);            // first scale word of stage s
-
+  auto compute = [&](const Frags<TI, TJ>& F) {
     if (FMT == kFmtMX) {
+      // this lane's two scale bytes into the low half: op_sel is then ks
       int sa[TI], sb[TJ];
 #pragma unroll
-      for (int i = 0; i < TI; ++i) sa[i] = (int)(SG.w[0][4 * (wm * TM + 32 * i + r) + sw] >> (16 * h));
+      for (int i = 0; i < TI; ++i) sa[i] = (int)(F.sa[i] >> (16 * h));
 #pragma unroll
-      for (int j = 0; j < TJ; ++j) sb[j] = (int)(SG.w[1][4 * (wn * TN + 32 * j + r) + sw] >> (16 * h));
-      // all fragments of the stage first: one LDS wait instead of one per tile
-      u32x4 fa[2][TI], fb[2][TJ];
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-#pragma unroll
-        for (int j = 0; j < TJ; ++j) {
-          const int rb = wn * TN + 32 * j + r;
-          fb[ks][j] = *reinterpret_cast<const u32x4*>(&S.b[rb * ROWB + swz(rb, 2 * h + ks) * 16]);
-        }
-#pragma unroll
-        for (int i = 0; i < TI; ++i) {
-          const int ra = wm * TM + 32 * i + r;
-          fa[ks][i] = *reinterpret_cast<const u32x4*>(&S.a[ra * ROWB + swz(ra, 2 * h + ks) * 16]);
-        }
-      }
-      // Keep the reads ahead of the MFMAs as one block: interleaving them in
-      // small groups leaves the matrix pipe idle on every LDS wait, while a
-      // read block overlaps the MFMA block of the other wave on the SIMD.
-      __builtin_amdgcn_sched_barrier(0);
+      for (int j = 0; j < TJ; ++j) sb[j] = (int)(F.sb[j] >> (16 * h));
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
         for (int i = 0; i < TI; ++i) {
-          const v8i a8 = {(int)fa[ks][i][0], (int)fa[ks][i][1], (int)fa[ks][i][2], (int)fa[ks][i][3], 0, 0, 0, 0};
+          const v8i a8 = {(int)F.a[ks][i][0], (int)F.a[ks][i][1], (int)F.a[ks][i][2], (int)F.a[ks][i][3], 0, 0, 0, 0};
 #pragma unroll
           for (int j = 0; j < TJ; ++j) {
-            const v8i b8 = {(int)fb[ks][j][0], (int)fb[ks][j][1], (int)fb[ks][j][2], (int)fb[ks][j][3], 0, 0, 0, 0};
-            acc[i][j] = mfma_mx(ks, a8, b8, acc[i][j], sa[i], sb[j]);
+            const v8i b8 = {(int)F.b[ks][j][0], (int)F.b[ks][j][1], (int)F.b[ks][j][2], (int)F.b[ks][j][3], 0, 0, 0, 0};
+            acc[i][j] = mfma_mx(ks, b8, a8, acc[i][j], sb[j], sa[i]);
           }
         }
     } else {
@@ -308,75 +289,192 @@ __global__ __launch_bounds__(64 * WMW * WNW, 1) void gemm_large(
       v2h sa01[TI], sa23[TI], sb01[TJ], sb23[TJ];
 #pragma unroll
       for (int i = 0; i < TI; ++i) {
-        const uint32_t w = SG.w[0][4 * (wm * TM + 32 * i + r) + sw + h];
-        sa01[i] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false);
-        sa23[i] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true);
+        sa01[i] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(F.sa[i], 1.0f, false);
+        sa23[i] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(F.sa[i], 1.0f, true);
       }
 #pragma unroll
       for (int j = 0; j < TJ; ++j) {
-        const uint32_t w = SG.w[1][4 * (wn * TN + 32 * j + r) + sw + h];
-        sb01[j] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false);
-        sb23[j] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true);
+        sb01[j] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(F.sb[j], 1.0f, false);
+        sb23[j] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(F.sb[j], 1.0f, true);
       }
 #pragma unroll
       for (int q = 0; q < 2; ++q) {              // code chunk 2h + q: blocks 4h + 2q, +1
-        u32x4 ca[TI], cb[TJ];
-#pragma unroll
-        for (int i = 0; i < TI; ++i) {
-          const int ra = wm * TM + 32 * i + r;
-          ca[i] = *reinterpret_cast<const u32x4*>(&S.a[ra * ROWB + swz(ra, 2 * h + q) * 16]);
-        }
-#pragma unroll
-        for (int j = 0; j < TJ; ++j) {
-          const int rb = wn * TN + 32 * j + r;
-          cb[j] = *reinterpret_cast<const u32x4*>(&S.b[rb * ROWB + swz(rb, 2 * h + q) * 16]);
-        }
 #pragma unroll
         for (int d = 0; d < 4; ++d) {            // 8 values per dword
           v8h fa[TI], fb[TJ];
 #pragma unroll
           for (int i = 0; i < TI; ++i) {
             const v2h sp = q ? sa23[i] : sa01[i];
-            fa[i] = dequant8(ca[i][d], d < 2 ? sp.x : sp.y);
+            fa[i] = dequant8(F.a[q][i][d], d < 2 ? sp.x : sp.y);
           }
 #pragma unroll
           for (int j = 0; j < TJ; ++j) {
             const v2h sp = q ? sb23[j] : sb01[j];
-            fb[j] = dequant8(cb[j][d], d < 2 ? sp.x : sp.y);
+            fb[j] = dequant8(F.b[q][j][d], d < 2 ? sp.x : sp.y);
           }
 #pragma unroll
           for (int i = 0; i < TI; ++i)
 #pragma unroll
             for (int j = 0; j < TJ; ++j)
-              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fb[j], fa[i], acc[i][j], 0, 0, 0);
         }
       }
+    }
+  };
+
+  // ---- software pipeline ----------------------------------------------------
+  // Iteration s: wait for stage s + 1 (this wave's loads, then everyone's at
+  // the barrier, which also closes every wave's LDS reads of stage s), load
+  // stage s + 4 into the slot stage s vacated, at the end of a scale group
+  // load group (s + 1) / G + 2 into the slot of the group just finished,
+  // read the fragments of stage s + 1, and multiply stage s from registers
+  // while those reads are in flight.
+  //
+  // In-order completion of this wave's loads gives the wait counts.  The
+  // issue order is that of the steady state from virtual iterations on:
+  // iteration i loads stage i + 4 and, when (i + 1) % G == 0, group
+  // (i + 1) / G + 2.  Issued after stage s + 1: stages s + 2, s + 3 and the
+  // groups of iterations s - 3 .. s - 1.  A group is issued 2G + 1 > 4
+  // iterations before its first stage is read, ahead of that stage's codes.
+  if (G == 4) {
+    issue_group(0);                              // virtual iteration -9
+    issue_group(1);                              // -5
+#pragma unroll
+    for (int t = 0; t < 4; ++t) issue_stage(t);  // -4 .. -1
+    issue_group(2);                              // -1
+    wait_vm<6 * NL + NSG>();                     // stage 0, group 0
+  } else {
+    issue_group(0);                              // -5
+    issue_stage(0);                              // -4
+    issue_stage(1);                              // -3
+    issue_group(1);                              // -3
+    issue_stage(2);                              // -2
+    issue_stage(3);                              // -1
+    issue_group(2);                              // -1
+    wait_vm<6 * NL + 2 * NSG>();                 // stage 0, group 0
+  }
+  __asm__ volatile("s_barrier" ::: "memory");
+  Frags<TI, TJ> F0, F1;
+  read_frags(0, F0);
+
+  // Step J (0 .. G-1) of a trip of G stages: a compile-time position, so the
+  // wait counts and the group load need no branch and the loop body stays
+  // one block the compiler cannot reshuffle across the barriers.
+  auto step = [&](auto J, int s, const Frags<TI, TJ>& Fc, Frags<TI, TJ>& Fn) {
+    constexpr int j = decltype(J)::value;
+    if constexpr (G == 4) {
+      if constexpr (j == 3) wait_vm<4 * NL>();
+      else wait_vm<4 * NL + NSG>();
+    } else {
+      if constexpr (j == 0) wait_vm<4 * NL + 2 * NSG>();
+      else wait_vm<4 * NL + NSG>();
+    }
+    // LDS reads of stage s done in this wave (a builtin wait, which the
+    // compiler's own wait insertion takes into account), then in every wave;
+    // the memory clobber keeps the compiler from moving LDS accesses across.
+    wait_lgkm0();
+    __asm__ volatile("s_barrier" ::: "memory");
+    issue_stage(s + NSTAGE);
+    if constexpr (j == G - 1) issue_group((s + 1) / G + 2);
+    // at s = nstages - 1 this reads the repeated last stage: valid, unused
+    read_frags(s + 1, Fn);
+    compute(Fc);
+    // Spread the loads and LDS reads over the multiplies: a direct load can
+    // stall issue while the memory pipeline drains, and in one block it
+    // would idle the matrix core that long.
+    if constexpr (FMT == kFmtMX) {
+#pragma unroll
+      for (int g = 0; g < 8; ++g) {
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // global load
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);   // LDS reads
+        __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);   // MFMA
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // nstages is a multiple of G (k is a multiple of 512 or 256)
+  for (int s = 0; s < nstages; s += G) {
+    step(std::integral_constant<int, 0>{}, s, F0, F1);
+    step(std::integral_constant<int, 1>{}, s + 1, F1, F0);
+    if constexpr (G == 4) {
+      step(std::integral_constant<int, 2>{}, s + 2, F0, F1);
+      step(std::integral_constant<int, 3>{}, s + 3, F1, F0);
     }
   }
 
   wait_vm<0>();                 // no load may land in LDS after the workgroup ends
 
   // ---- epilogue -----------------------------------------------------------
-  // 32x32 D layout: lane holds column lane % 32, register e holds row
-  // 8 * (e / 4) + 4 * (lane / 32) + e % 4.
+  // The MFMAs take B as the first operand, so in each 32x32 block a lane holds
+  // output row r = lane % 32 and, in registers 4g .. 4g + 3, the four
+  // consecutive columns 8g + 4h .. + 3.  The tile goes through LDS (the ring
+  // is free now) in row-major order and leaves as 16-byte row chunks: direct
+  // stores of the fragments would scatter 2- or 4-byte pieces over 32 rows.
+  wait_lgkm0();
+  __asm__ volatile("s_barrier" ::: "memory");
   const float ts = (FMT == kFmtNV) ? (*at) * (*bt) : 1.0f;
+  uint8_t* ep = reinterpret_cast<uint8_t*>(&smem);
+  const bool f32 = (c_dtype == kInF32);
+  // bf16: the whole 256 x 256 tile, rows of 528 bytes (512 + 16: 16-byte
+  // aligned, writes of the 32 rows of a block spread over the banks);
+  // f32: one 128-row band (the rows of the waves with wm = band) at a time,
+  // rows of 1040 bytes.
+  const int pitch = f32 ? 1040 : 528;
+  const int nband = f32 ? 2 : 1;
+  const int band_rows = BM / nband;
+  const bool vec_ok = f32 ? (n % 4 == 0) : (n % 8 == 0);
+  for (int band = 0; band < nband; ++band) {
+    if (!f32 || wm == band) {
 #pragma unroll
-  for (int i = 0; i < TI; ++i)
+      for (int i = 0; i < TI; ++i)
 #pragma unroll
-    for (int j = 0; j < TJ; ++j) {
-      const int col = n0 + wn * TN + 32 * j + r;
-      if (col >= n) continue;
+        for (int j = 0; j < TJ; ++j) {
+          const int row = (f32 ? 0 : wm * TM) + 32 * i + r;   // row within the band
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int row = m0 + wm * TM + 32 * i + 8 * (e >> 2) + 4 * h + (e & 3);
-        if (row < m) {
-          const float v = acc[i][j][e] * ts;
-          const int64_t idx = (int64_t)row * n + col;
-          if (c_dtype == kInF32) reinterpret_cast<float*>(c)[idx] = v;
-          else reinterpret_cast<__bf16*>(c)[idx] = (__bf16)v;
+          for (int g = 0; g < 4; ++g) {
+            const int col = wn * TN + 32 * j + 8 * g + 4 * h;
+            const float v0 = acc[i][j][4 * g] * ts, v1 = acc[i][j][4 * g + 1] * ts;
+            const float v2 = acc[i][j][4 * g + 2] * ts, v3 = acc[i][j][4 * g + 3] * ts;
+            if (f32) {
+              *reinterpret_cast<float4*>(ep + row * pitch + col * 4) = make_float4(v0, v1, v2, v3);
+            } else {
+              const __bf16 b0 = (__bf16)v0, b1 = (__bf16)v1, b2 = (__bf16)v2, b3 = (__bf16)v3;
+              uint2 u;
+              u.x = (uint32_t)__builtin_bit_cast(uint16_t, b0) | ((uint32_t)__builtin_bit_cast(uint16_t, b1) << 16);
+              u.y = (uint32_t)__builtin_bit_cast(uint16_t, b2) | ((uint32_t)__builtin_bit_cast(uint16_t, b3) << 16);
+              *reinterpret_cast<uint2*>(ep + row * pitch + col * 2) = u;
+            }
+          }
+        }
+    }
+    __syncthreads();
+    // 16-byte chunks: 32 (bf16) or 64 (f32) per row
+    const int cpr = f32 ? 64 : 32, epc = f32 ? 4 : 8;
+    const int row0 = m0 + band * band_rows;
+    for (int idx = tid; idx < band_rows * cpr; idx += 64 * NW) {
+      const int lr = idx / cpr, ch = idx % cpr;
+      const int grow = row0 + lr, gcol = n0 + ch * epc;
+      if (grow >= m || gcol >= n) continue;
+      const uint4 v = *reinterpret_cast<const uint4*>(ep + lr * pitch + ch * 16);
+      const int64_t off = (int64_t)grow * n + gcol;
+      if (vec_ok && gcol + epc <= n) {
+        if (f32) *reinterpret_cast<uint4*>(reinterpret_cast<float*>(c) + off) = v;
+        else *reinterpret_cast<uint4*>(reinterpret_cast<__bf16*>(c) + off) = v;
+      } else if (f32) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (gcol + e < n) reinterpret_cast<uint32_t*>(c)[off + e] = e == 0 ? v.x : e == 1 ? v.y : e == 2 ? v.z : v.w;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t w = (e >> 1) == 0 ? v.x : (e >> 1) == 1 ? v.y : (e >> 1) == 2 ? v.z : v.w;
+          if (gcol + e < n) reinterpret_cast<uint16_t*>(c)[off + e] = (uint16_t)(w >> (16 * (e & 1)));
         }
       }
     }
+    if (band + 1 < nband) __syncthreads();
+  }
 }
 
 }  // namespace
