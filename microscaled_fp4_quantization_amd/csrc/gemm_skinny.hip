@@ -17,6 +17,8 @@
 //          in the epilogue.
 //   MXFP4: v_mfma_scale_f32_16x16x128_f8f6f4 with both operands E2M1 and
 //          the E8M0 block scale of each lane's 32 values.
+#include <cstddef>
+
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -232,12 +234,12 @@ __global__ __launch_bounds__(256) void gemm_nv_decode(
     for (int i = 0; i < WLD; ++i) {
       const int idx = tid + 256 * i, row = idx / WCH, cc = idx % WCH;
       const int64_t gr = (nbase + row < n) ? nbase + row : n - 1;
-      wreg[slot][i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(b + gr * (k / 2) + kb / 2) + cc);
+      wreg[slot][i] = *(reinterpret_cast<const u32x4*>(b + gr * (k / 2) + kb / 2) + cc);
     }
     {
       const int row = tid / (KC / 16 / SB), cc = tid % (KC / 16 / SB);
       const int64_t gr = (nbase + row < n) ? nbase + row : n - 1;
-      sreg[slot] = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(bs + gr * (k / 16) + kb / 16) + cc);
+      sreg[slot] = *(reinterpret_cast<const u32x2*>(bs + gr * (k / 16) + kb / 16) + cc);
     }
     {
       const int item = tid % (KC / 32);
@@ -329,6 +331,150 @@ __global__ __launch_bounds__(256) void gemm_nv_decode(
   }
 }
 
+
+// ---- NVFP4 weight-stream kernel (m <= 8, k = 2048 or 4096, n <= 16384) -------
+// The weight rows are dealt out evenly: one workgroup per CU-share of R rows
+// (R = 8 ceil(n / 2048), at most 64, i.e. up to four 16-row MFMA tiles, the
+// last possibly partial), so every CU streams the same number of bytes.  A
+// workgroup's 16 waves split k: wave w takes the slice [w k / 16,
+// (w + 1) k / 16), one or two 128-value steps, for all its tiles, and issues
+// all its loads at once.  Requests are not served in issue order (a wave's
+// data tends to arrive in one burst at any time during the stream), so each
+// wave depends only on its own loads: it dequantizes its activation slice
+// and stores its scale slices in LDS regions of its own, and the 16 partial
+// tiles meet only at the end.  Lane (r, g) = (lane % 16, lane / 16) reads,
+// per step t, the 16 bytes at 64 t + 16 g of weight row r of each tile: a
+// load instruction covers 64 contiguous bytes of 16 rows.  Rows past the
+// workgroup's share re-read its last row, in the same instruction, so they
+// cost no extra traffic.
+constexpr int kStrWaves = 16;
+constexpr int kStrTiles = 4;                          // 64 rows at most per workgroup
+constexpr int kStrSeg = 4096 / kStrWaves / 16;        // scale bytes per row and slice, at most (16)
+constexpr int kStrPitch = kStrSeg + 4;                // padded: the 16 rows of a read hit distinct banks
+constexpr int kStrXSlice = 4096 / kStrWaves + 8;      // fp16 per activation row and slice (padded)
+
+struct StreamLds {
+  _Float16 x[kStrWaves][8][kStrXSlice];               // dequantized activation slices
+  uint8_t w[kStrWaves][16 * kStrTiles][kStrPitch];    // weight scale slices
+};
+
+template <int NSTEP>
+__global__ __launch_bounds__(64 * kStrWaves) void gemm_nv_stream(
+    int m, int64_t n, int k, int rows_per_wg, const uint8_t* __restrict__ a,
+    const uint8_t* __restrict__ as, const float* __restrict__ at,
+    const uint8_t* __restrict__ b, const uint8_t* __restrict__ bs,
+    const float* __restrict__ bt, void* __restrict__ c, int c_dtype) {
+  __shared__ StreamLds L;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r = lane & 15, g = lane >> 4;
+  const int64_t nbase = (int64_t)blockIdx.x * rows_per_wg;
+  int64_t nlast = nbase + rows_per_wg - 1;              // last row of this share
+  if (nlast > n - 1) nlast = n - 1;
+  const int ks0 = wave * (128 * NSTEP);                 // first value of this wave's slice
+  const int64_t kbytes = k / 2, kblocks = k / 16;
+
+  // ---- all loads of the wave -------------------------------------------------
+  // weight scale slices: lane p loads row p's 8 NSTEP bytes
+  const int64_t swr = (nbase + lane <= nlast) ? nbase + lane : nlast;
+  u32x4 sv;
+  if (NSTEP == 2) {
+    sv = *reinterpret_cast<const u32x4*>(bs + swr * kblocks + ks0 / 16);
+  } else {
+    const u32x2 h = *reinterpret_cast<const u32x2*>(bs + swr * kblocks + ks0 / 16);
+    sv = (u32x4){h.x, h.y, 0u, 0u};
+  }
+  // activation slice: lane -> row lane / 8, 32 NSTEP / 2 values at
+  // (lane % 8) 16 NSTEP of the slice
+  const int xrow = lane >> 3, xc = lane & 7;
+  const int64_t xsrc = xrow < m ? xrow : m - 1;
+  u32x4 xq;
+  uint32_t xs2;
+  if (NSTEP == 2) {
+    xq = *reinterpret_cast<const u32x4*>(a + xsrc * kbytes + ks0 / 2 + 16 * xc);
+    xs2 = *reinterpret_cast<const uint16_t*>(as + xsrc * kblocks + ks0 / 16 + 2 * xc);
+  } else {
+    const u32x2 h = *reinterpret_cast<const u32x2*>(a + xsrc * kbytes + ks0 / 2 + 8 * xc);
+    xq = (u32x4){h.x, h.y, 0u, 0u};
+    xs2 = as[xsrc * kblocks + ks0 / 16 + xc];
+  }
+  // weight codes
+  u32x4 w[kStrTiles][NSTEP];
+#pragma unroll
+  for (int tl = 0; tl < kStrTiles; ++tl) {
+    const int64_t wr = (nbase + 16 * tl + r <= nlast) ? nbase + 16 * tl + r : nlast;
+#pragma unroll
+    for (int t = 0; t < NSTEP; ++t)
+      w[tl][t] = *reinterpret_cast<const u32x4*>(b + wr * kbytes + ks0 / 2 + 64 * t + 16 * g);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  // ---- this wave's LDS regions (loads complete in issue order) ---------------
+  {
+    uint32_t* dd = reinterpret_cast<uint32_t*>(&L.w[wave][lane][0]);
+    dd[0] = sv[0]; dd[1] = sv[1];
+    if (NSTEP == 2) { dd[2] = sv[2]; dd[3] = sv[3]; }
+  }
+  {
+    const bool live = xrow < m;
+    const v2h sc = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(xs2, 1.0f, false);
+#pragma unroll
+    for (int d = 0; d < 2 * NSTEP; ++d) {             // 8 values per dword, 2 dwords per block
+      v8h f = dequant8(xq[d], (NSTEP == 2 && d >= 2) ? sc.y : sc.x);
+      if (!live) f = (v8h){0, 0, 0, 0, 0, 0, 0, 0};
+      *reinterpret_cast<v8h*>(&L.x[wave][xrow][16 * NSTEP * xc + 8 * d]) = f;
+    }
+  }
+  // Only this wave reads these regions: LDS accesses of one wave complete in
+  // order, so no barrier is needed.
+  const _Float16* xf = &L.x[wave][r & 7][32 * g];    // rows >= m are zero; r >= 8 repeats r - 8
+
+  v4f acc[kStrTiles];
+#pragma unroll
+  for (int tl = 0; tl < kStrTiles; ++tl) acc[tl] = (v4f){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int t = 0; t < NSTEP; ++t) {
+    v2h s[kStrTiles];
+#pragma unroll
+    for (int tl = 0; tl < kStrTiles; ++tl) {
+      const uint32_t p = *reinterpret_cast<const uint16_t*>(&L.w[wave][16 * tl + r][8 * t + 2 * g]);
+      s[tl] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(p, 1.0f, false);
+    }
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {                     // 8 values per dword; blocks 2g, 2g+1
+      const v8h fx = *reinterpret_cast<const v8h*>(xf + 128 * t + 8 * d);
+#pragma unroll
+      for (int tl = 0; tl < kStrTiles; ++tl) {
+        const v8h fw = dequant8(w[tl][t][d], d < 2 ? s[tl].x : s[tl].y);
+        acc[tl] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fw, fx, acc[tl], 0, 0, 0);
+      }
+    }
+  }
+
+  // ---- add the 16 slices, store ------------------------------------------------
+  __syncthreads();                                    // LDS becomes the partial area
+  v4f* part = reinterpret_cast<v4f*>(&L);             // [16 waves][tiles][64 lanes]
+#pragma unroll
+  for (int tl = 0; tl < kStrTiles; ++tl) part[(wave * kStrTiles + tl) * 64 + lane] = acc[tl];
+  __syncthreads();
+  if (tid < 64 * kStrTiles) {                         // thread -> (tile, lane)
+    const int tl = tid >> 6, l = tid & 63;
+    v4f sum = part[tl * 64 + l];
+#pragma unroll
+    for (int wv = 1; wv < kStrWaves; ++wv) sum += part[(wv * kStrTiles + tl) * 64 + l];
+    const float scale = (*at) * (*bt);
+    // D layout: lane l holds weight rows 4 (l / 16) + e of the tile, activation row l % 16
+    const int xr = l & 15;
+    if (xr < m) {
+      const int64_t ni = nbase + 16 * tl + 4 * (l >> 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (ni + e <= nlast && 16 * tl + 4 * (l >> 4) + e < rows_per_wg)
+          store_out(c, c_dtype, (int64_t)xr * n + ni + e, sum[e] * scale);
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_gemm_skinny(int fmt, int64_t m, int64_t n, int64_t k,
@@ -339,6 +485,18 @@ hipError_t launch_gemm_skinny(int fmt, int64_t m, int64_t n, int64_t k,
   const bool aligned16 = ((reinterpret_cast<uintptr_t>(b_scales) | reinterpret_cast<uintptr_t>(b_codes) |
                            reinterpret_cast<uintptr_t>(a_codes)) & 15) == 0 &&
                          (reinterpret_cast<uintptr_t>(a_scales) & 1) == 0;
+  if (fmt == kFmtNV && m <= 8 && (k == 2048 || k == 4096) && n <= 16 * kStrTiles * 256 && aligned16) {
+    // an equal share of rows per workgroup, one workgroup per CU (256 CUs)
+    const int rows = (int)(8 * ((n + 2047) / 2048));
+    const dim3 grid((unsigned)((n + rows - 1) / rows));
+    if (k == 4096)
+      hipLaunchKernelGGL(gemm_nv_stream<2>, grid, dim3(64 * kStrWaves), 0, stream, (int)m, n, (int)k,
+                         rows, a_codes, a_scales, a_tscale, b_codes, b_scales, b_tscale, c, c_dtype);
+    else
+      hipLaunchKernelGGL(gemm_nv_stream<1>, grid, dim3(64 * kStrWaves), 0, stream, (int)m, n, (int)k,
+                         rows, a_codes, a_scales, a_tscale, b_codes, b_scales, b_tscale, c, c_dtype);
+    return hipGetLastError();
+  }
   if (fmt == kFmtNV && m <= 8 && k % kDecKC == 0 && aligned16) {
     hipLaunchKernelGGL((gemm_nv_decode<kDecKC, 4>), dim3((unsigned)((n + kDecRows - 1) / kDecRows)),
                        dim3(256), 0, stream, (int)m, n, (int)k, a_codes, a_scales, a_tscale, b_codes,

@@ -110,17 +110,59 @@ __device__ __forceinline__ float wave_max(float m) {
   return m;
 }
 
-// Max over the workgroup; every thread gets the result.
+// Max over a workgroup of NT threads; every thread gets the result.
+template <int NT = kThreads>
 __device__ __forceinline__ float block_max(float m) {
-  __shared__ float red[kThreads / 64];
+  __shared__ float red[NT / 64];
   m = wave_max(m);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
   __syncthreads();
   float r = red[0];
 #pragma unroll
-  for (int i = 1; i < kThreads / 64; ++i) r = fmaxf(r, red[i]);
+  for (int i = 1; i < NT / 64; ++i) r = fmaxf(r, red[i]);
   __syncthreads();
   return r;
+}
+
+// One chunk (8 values, already rotated when the rotation applies) of lane
+// `lane` to codes and, from the first lane of its block, the scale byte.
+// NVFP4: s_t is the tensor scale and d = 6 s_t.
+template <int FMT>
+__device__ __forceinline__ void quantize_chunk(const float v[8], int lane, float s_t, float d,
+                                               int64_t c, bool valid, uint32_t* __restrict__ codes,
+                                               uint8_t* __restrict__ scales) {
+  float a = amax8(v);
+  a = fmaxf(a, dpp_f<kDppXor1>(a));
+  float r;
+  uint32_t sbyte;
+  if (FMT == kFmtNV) {
+    const float u = a / d;
+    sbyte = e4m3_encode_pos(u);
+    const float S = e4m3_decode_pos(sbyte) * s_t;
+    r = 1.0f / S;
+    // S == 0 (zero block) or an overflowing reciprocal: sign bits only.
+    if (!(S != 0.0f && r < __builtin_inff())) r = 0.0f;
+  } else {
+    a = fmaxf(a, dpp_f<kDppXor2>(a));
+    const int kx = mx_block_exponent(a);
+    sbyte = (uint32_t)(kx + 127);
+    r = as_f((uint32_t)(127 - kx) << 23);  // 2^-k, a normal float for k in [-127, 126]
+  }
+  float q[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) q[i] = v[i] * r;
+  uint32_t w = e2m1_pack2<0>(0u, q[0], q[1]);
+  w = e2m1_pack2<1>(w, q[2], q[3]);
+  w = e2m1_pack2<2>(w, q[4], q[5]);
+  w = e2m1_pack2<3>(w, q[6], q[7]);
+  if (valid) {
+    __builtin_nontemporal_store(w, codes + c);
+    if (FMT == kFmtNV) {
+      if ((lane & 1) == 0) scales[c >> 1] = (uint8_t)sbyte;
+    } else {
+      if ((lane & 3) == 0) scales[c >> 2] = (uint8_t)sbyte;
+    }
+  }
 }
 
 // Pass 1 of dynamic NVFP4 scaling: per-workgroup max |x| (of the rotated
@@ -180,41 +222,43 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
 #pragma unroll
     for (int j = 0; j < kUnroll; ++j) {
       const int64_t c = base + j * kThreads + threadIdx.x;
-      const bool valid = c < nchunks;
       if (HAD) fwht_chunk<HAD>(v[j], lane);
-      float a = amax8(v[j]);
-      a = fmaxf(a, dpp_f<kDppXor1>(a));
-      float r;
-      uint32_t sbyte;
-      if (FMT == kFmtNV) {
-        const float u = a / d;
-        sbyte = e4m3_encode_pos(u);
-        const float S = e4m3_decode_pos(sbyte) * s_t;
-        r = 1.0f / S;
-        // S == 0 (zero block) or an overflowing reciprocal: sign bits only.
-        if (!(S != 0.0f && r < __builtin_inff())) r = 0.0f;
-      } else {
-        a = fmaxf(a, dpp_f<kDppXor2>(a));
-        const int kx = mx_block_exponent(a);
-        sbyte = (uint32_t)(kx + 127);
-        r = as_f((uint32_t)(127 - kx) << 23);  // 2^-k, a normal float for k in [-127, 126]
-      }
-      float q[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) q[i] = v[j][i] * r;
-      uint32_t w = e2m1_pack2<0>(0u, q[0], q[1]);
-      w = e2m1_pack2<1>(w, q[2], q[3]);
-      w = e2m1_pack2<2>(w, q[4], q[5]);
-      w = e2m1_pack2<3>(w, q[6], q[7]);
-      if (valid) {
-        __builtin_nontemporal_store(w, codes + c);
-        if (FMT == kFmtNV) {
-          if ((lane & 1) == 0) scales[c >> 1] = (uint8_t)sbyte;
-        } else {
-          if ((lane & 3) == 0) scales[c >> 2] = (uint8_t)sbyte;
-        }
-      }
+      quantize_chunk<FMT>(v[j], lane, s_t, d, c, c < nchunks, codes, scales);
     }
+  }
+}
+
+// NVFP4 with the tensor scale computed from the data, for small tensors
+// (decode activations): one workgroup holds the whole tensor in registers,
+// reduces its max |x| and quantizes, in a single launch instead of two.
+constexpr int kSmallThreads = 1024;
+constexpr int kSmallPer = 4;                                  // chunks per thread
+constexpr int64_t kSmallChunks = (int64_t)kSmallThreads * kSmallPer;   // 32 Ki values
+
+template <int DT, int HAD>
+__global__ __launch_bounds__(kSmallThreads) void quantize_small_kernel(
+    const void* __restrict__ x, int64_t nchunks, uint32_t* __restrict__ codes,
+    uint8_t* __restrict__ scales, float* __restrict__ tscale) {
+  const int lane = threadIdx.x & 63;
+  float v[kSmallPer][8];
+  float m = 0.0f;
+#pragma unroll
+  for (int j = 0; j < kSmallPer; ++j) {
+    // chunk j * 1024 + tid: lane t of a wave still owns chunk = t (mod 64)
+    const int64_t c = (int64_t)j * kSmallThreads + threadIdx.x;
+    load_chunk<DT>(x, c, c < nchunks, v[j]);
+    if (HAD) fwht_chunk<HAD>(v[j], lane);
+    m = fmaxf(m, amax8(v[j]));
+  }
+  const float A = block_max<kSmallThreads>(m);
+  float s_t = A / 2688.0f;                     // 6 * 448
+  if (s_t == 0.0f) s_t = 1.0f;
+  if (threadIdx.x == 0) *tscale = s_t;
+  const float d = 6.0f * s_t;
+#pragma unroll
+  for (int j = 0; j < kSmallPer; ++j) {
+    const int64_t c = (int64_t)j * kSmallThreads + threadIdx.x;
+    quantize_chunk<kFmtNV>(v[j], lane, s_t, d, c, c < nchunks, codes, scales);
   }
 }
 
@@ -225,7 +269,10 @@ hipError_t launch_typed(const void* x, int64_t nchunks, uint8_t* codes,
   int64_t trips = (nchunks + kChunksPerTrip - 1) / kChunksPerTrip;
   const int grid = (int)(trips < kMaxGrid ? trips : kMaxGrid);
   uint32_t* codes32 = reinterpret_cast<uint32_t*>(codes);
-  if (FMT == kFmtNV && compute) {
+  if (FMT == kFmtNV && compute && nchunks <= kSmallChunks) {
+    hipLaunchKernelGGL((quantize_small_kernel<DT, HAD>), dim3(1), dim3(kSmallThreads), 0, stream,
+                       x, nchunks, codes32, scales, tscale);
+  } else if (FMT == kFmtNV && compute) {
     float* partials = reinterpret_cast<float*>(workspace);
     const int g = (int)(trips < kMaxPartials ? trips : kMaxPartials);
     hipLaunchKernelGGL((amax_partial_kernel<DT, HAD>), dim3(g), dim3(kThreads), 0,
