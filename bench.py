@@ -6,18 +6,21 @@ A step is one pass of the hot path over one batch of synthetic input with
 every input already resident in HBM:
   decode   (default) online NVFP4 quantize of X bf16 [8, 4096] (tensor scale
            computed from the data) + NVFP4 W4A4 GEMM against a pre-quantized
-           W [14336, 4096], bf16 out.  Steps cycle over 16 distinct weight
-           copies (about 2x the 256 MB last-level cache) so the weights
+           W [14336, 4096], bf16 out, as one fp4_quantize_gemm call (a single
+           launch; it also writes X's codes, scales and tensor scale).
+           Steps cycle over 17 distinct weight
+           copies (over 2x the 256 MB last-level cache) so the weights
            stream from HBM as they do layer after layer.
   prefill  NVFP4 quantize of X [4096, 4096] + GEMM vs W [14336, 4096].
   rotated_nv / rotated_mx  fused Hadamard+quantize of X [2048, 8192] +
            GEMM vs the offline-rotated W [28672, 8192].
   kv       NVFP4 quantize of K and V [32*8*32768, 128] bf16 with their given
            tensor scales + dequantize of both to FP8 E4M3.
-Prints one JSON line.  The dominant kernel of the step is timed with HIP
-events around each of its launches inside the timed region; its algorithmic
-bytes (or flops) per launch give the roofline figure.  The CPU oracle is
-timed on a bounded sample of the same workload on the host.
+Prints one JSON line.  The timed region is K steps back to back between one
+pair of HIP events (value, ms_per_step).  The dominant kernel is then timed
+the same way over the K steps' launches of it alone; its algorithmic bytes
+(or flops) per launch over that duration give the roofline figure.  The CPU
+oracle is timed on a bounded sample of the same workload on the host.
 """
 
 import argparse
@@ -155,6 +158,18 @@ class Lib:
         fn = self.L.fp4_gemm
         return lambda: self.check(fn(*args), "gemm")
 
+    def quantize_gemm_call(self, fmt, x, a, b, c, c_dtype, ws):
+        from microscaled_fp4_quantization_amd import fp4
+        (ac, asc, at), (bc, bsc, bt) = a, b
+        m, k, n = x.shape[0], x.shape[1], bc.shape[0]
+        dt = {self.torch.bfloat16: fp4.BF16, self.torch.float32: fp4.F32, self.torch.float16: fp4.F16}[x.dtype]
+        need = self.L.fp4_quantize_gemm_workspace_size(fmt, m, n, k)
+        args = (fmt, self.p(x), dt, m, n, k, self.p(ac), self.p(asc), self.p(at), self.p(bc),
+                self.p(bsc), self.p(bt), self.p(c), c_dtype, self.p(ws) if need else None, need,
+                self.stream)
+        fn = self.L.fp4_quantize_gemm
+        return lambda: self.check(fn(*args), "quantize_gemm")
+
     def dequant_call(self, fmt, codes, scales, ts, out, out_dtype):
         rows, k = codes.shape[0], codes.shape[1] * 2
         args = (fmt, self.p(codes), self.p(scales), self.p(ts), rows, k, self.p(out), out_dtype, self.stream)
@@ -193,10 +208,17 @@ def setup(workload, torch, fq, lib):
         xt = torch.empty(1, dtype=torch.float32, device=dev)
         ws = torch.empty(4096, dtype=torch.uint8, device=dev)
         c = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
-        q = lib.quantize_call(NV, x, xc, xs, xt, fp4.TSCALE_COMPUTE, ws)
-        gs = [lib.gemm_call(NV, (xc, xs, xt), wqi, c, fp4.BF16) for wqi in wqs]
-        W.update(pre=[q], dominant=gs, post=[], flops=2 * m * n * k,
-                 dom_name="fp4_gemm (NVFP4, m=%d)" % m,
+        if workload == "decode":
+            # one call: the activations are quantized inside the GEMM launch
+            gs = [lib.quantize_gemm_call(NV, x, (xc, xs, xt), wqi, c, fp4.BF16, ws) for wqi in wqs]
+            pre, name = [], "fp4_quantize_gemm (NVFP4, m=%d)" % m
+            per += 2 * m * k                  # the bf16 activations read
+        else:
+            pre = [lib.quantize_call(NV, x, xc, xs, xt, fp4.TSCALE_COMPUTE, ws)]
+            gs = [lib.gemm_call(NV, (xc, xs, xt), wqi, c, fp4.BF16) for wqi in wqs]
+            name = "fp4_gemm (NVFP4, m=%d)" % m
+        W.update(pre=pre, dominant=gs, post=[], flops=2 * m * n * k,
+                 dom_name=name,
                  dom_units=per if workload == "decode" else 2 * m * n * k,
                  dom_bound="hbm" if workload == "decode" else "mfma",
                  dom_peak=HBM_PEAK_GBS if workload == "decode" else MFMA_PEAK_TFLOPS["f16"],
@@ -333,24 +355,25 @@ def main():
     pre, dom, post = W["pre"], W["dominant"], W["post"]
     ndom = len(dom)
 
-    def step(i, ev=None):
+    def step(i):
         for f in pre:
             f()
         if args.workload == "kv":
-            for j, f in enumerate(dom):
-                if ev is not None:
-                    ev[2 * j].record()
+            for f in dom:
                 f()
-                if ev is not None:
-                    ev[2 * j + 1].record()
         else:
-            if ev is not None:
-                ev[0].record()
             dom[i % ndom]()
-            if ev is not None:
-                ev[1].record()
         for f in post:
             f()
+
+    def dominant(i):
+        # the dominant kernel's launches of step i, alone
+        if args.workload == "kv":
+            for f in dom:
+                f()
+        else:
+            dom[i % ndom]()
+    launches_per_step = len(dom) if args.workload == "kv" else 1
 
     for i in range(args.warmup):
         step(i)
@@ -371,19 +394,31 @@ def main():
     ms_per_cycle = c0.elapsed_time(c1) / float(1 << 20)
     spin_ms = 2.0 * host_step * 1e3 * (args.steps + 4) + 2.0
     spin_cycles = int(spin_ms / ms_per_cycle)
-    nev = 4 if args.workload == "kv" else 2
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(args.steps)]
+    # Timed region: K whole steps back to back, one event pair around them.
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     torch.cuda._sleep(spin_cycles)
     start.record()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(i, evs[i])
+        step(i)
     end.record()
     enqueue_s = time.perf_counter() - t0
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    # The dominant kernel's launch duration: the same K steps' launches of it
+    # back to back between one event pair on the bench stream (an event pair
+    # around each single launch would add its own dispatch and timestamp
+    # cost, several microseconds, to a kernel this short).
+    d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    torch.cuda._sleep(spin_cycles)
+    d0.record()
+    for i in range(args.steps):
+        dominant(i)
+    d1.record()
+    torch.cuda.synchronize()
+    dom_avg = d0.elapsed_time(d1) / (args.steps * launches_per_step)
     if args.copy_bytes:
         # the plain copy of known size that calibrates the HBM byte counters
         src = torch.empty(args.copy_bytes, dtype=torch.uint8, device="cuda:0")
@@ -395,11 +430,6 @@ def main():
     ms_total = start.elapsed_time(end)
     ms_step = ms_total / args.steps
     gpu_fed = enqueue_s * 1e3 < spin_ms     # host stayed ahead of the GPU
-    dom_ms = []
-    for e in evs:
-        for j in range(nev // 2):
-            dom_ms.append(e[2 * j].elapsed_time(e[2 * j + 1]))
-    dom_avg = sum(dom_ms) / len(dom_ms)
 
     if W["dom_bound"] == "hbm":
         achieved = W["dom_units"] / (dom_avg * 1e-3) / 1e9
@@ -424,6 +454,9 @@ def main():
                      "frac": round(achieved / W["dom_peak"], 4),
                      "traffic": recorded_traffic(args.workload),
                      "kernel": W["dom_name"], "avg_ms": round(dom_avg, 5),
+                     "timing": "HIP events around the %d back-to-back launches of it "
+                               "that the %d timed steps make" % (args.steps * launches_per_step,
+                                                                  args.steps),
                      "units_per_launch": W["dom_units"]},
         "host_wall_s": round(wall, 4),
         "host_enqueue_ms_per_step": round(enqueue_s * 1e3 / args.steps, 4),

@@ -164,7 +164,7 @@ size_t fp4_gemm_workspace_size(fp4_format fmt, int64_t m, int64_t n, int64_t k);
  *   both in the same format, blocks along k.  C[i, j] = sum over k of
  *   deq(A)[i, kk] * deq(B)[j, kk], accumulated in fp32: MXFP4 on the gfx950
  *   block-scaled MFMA (E8M0 scale per 32 values); NVFP4 by exact in-register
- *   products v * E4M3(sb) in bf16 on bf16 MFMA, times a_tscale * b_tscale at
+ *   products v * E4M3(sb) in fp16 on fp16 MFMA, times a_tscale * b_tscale at
  *   the end.
  *   c, c_dtype      out, row-major [m, n], FP4_F32 or FP4_BF16 (nearest even).
  *   a_tscale, b_tscale  NVFP4: device floats; MXFP4: must be NULL.
@@ -179,6 +179,40 @@ fp4_status fp4_gemm(fp4_format fmt, int64_t m, int64_t n, int64_t k,
                     const uint8_t* b_scales, const float* b_tscale, void* c,
                     fp4_dtype c_dtype, void* workspace, size_t workspace_bytes,
                     void* stream);
+
+/* Bytes of device workspace fp4_quantize_gemm needs for these sizes. */
+size_t fp4_quantize_gemm_workspace_size(fp4_format fmt, int64_t m, int64_t n,
+                                        int64_t k);
+
+/*
+ * fp4_quantize_gemm -- quantize the activations and multiply: the result is
+ * that of fp4_quantize(fmt, x, x_dtype, m, k, a_codes, a_scales, a_tscale,
+ * FP4_TSCALE_COMPUTE, ...) followed by fp4_gemm(fmt, m, n, k, a_codes,
+ * a_scales, a_tscale, b_codes, b_scales, b_tscale, c, c_dtype, ...), codes,
+ * scales, tensor scale and C alike.
+ * Defines: the decode step of a W4A4 layer -- activations quantized online
+ * per call, the weights streamed once (cloudmagazin.com "FP8, FP4 und vLLM",
+ * section "Rechnung": token-by-token decoding is bound by reading the
+ * weights; hyper.ai, paper 2509.23202, Abstract: activations quantized
+ * online).  For NVFP4 with bf16 x, 1 <= m <= 8, k = 2048 or 4096 and
+ * n <= 16384 it runs as one launch (the activation quantization happens
+ * inside the GEMM's workgroups, each reducing max |x| over the whole tensor
+ * itself); otherwise as the two calls.
+ *   x            in, [m, k] of x_dtype, 16-byte aligned.
+ *   a_codes, a_scales, a_tscale   out, as fp4_quantize (COMPUTE mode).
+ *   b_*, c, c_dtype               as fp4_gemm.
+ *   workspace    at least fp4_quantize_gemm_workspace_size() bytes, 16-byte
+ *                aligned (may be NULL when that size is 0).
+ * Every check of both calls runs before anything is enqueued.
+ * Returns FP4_OK, FP4_EINVAL, FP4_EUNSUPPORTED or FP4_EHIP.
+ */
+fp4_status fp4_quantize_gemm(fp4_format fmt, const void* x, fp4_dtype x_dtype,
+                             int64_t m, int64_t n, int64_t k, uint8_t* a_codes,
+                             uint8_t* a_scales, float* a_tscale,
+                             const uint8_t* b_codes, const uint8_t* b_scales,
+                             const float* b_tscale, void* c, fp4_dtype c_dtype,
+                             void* workspace, size_t workspace_bytes,
+                             void* stream);
 
 #ifdef __cplusplus
 }

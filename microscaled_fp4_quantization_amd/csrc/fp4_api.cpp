@@ -162,4 +162,53 @@ fp4_status fp4_gemm(fp4_format fmt, int64_t m, int64_t n, int64_t k,
                               workspace, static_cast<hipStream_t>(stream)));
 }
 
+size_t fp4_quantize_gemm_workspace_size(fp4_format fmt, int64_t m, int64_t n, int64_t k) {
+  if (!valid_format(fmt)) return 0;
+  const size_t q = fp4_quantize_workspace_size(fmt, FP4_TSCALE_COMPUTE, m, k);
+  const size_t g = gemm_workspace_bytes((int)fmt, m, n, k);
+  return q > g ? q : g;
+}
+
+fp4_status fp4_quantize_gemm(fp4_format fmt, const void* x, fp4_dtype x_dtype,
+                             int64_t m, int64_t n, int64_t k, uint8_t* a_codes,
+                             uint8_t* a_scales, float* a_tscale,
+                             const uint8_t* b_codes, const uint8_t* b_scales,
+                             const float* b_tscale, void* c, fp4_dtype c_dtype,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  // Both calls' checks first, so a rejected call enqueues nothing.
+  fp4_status s = check_quantize(fmt, x, x_dtype, m, k, a_codes, a_scales, a_tscale,
+                                FP4_TSCALE_COMPUTE, workspace, workspace_bytes);
+  if (s != FP4_OK) return s;
+  if (!valid_format(fmt)) return FP4_EINVAL;
+  if (c_dtype != FP4_F32 && c_dtype != FP4_BF16) {
+    return (c_dtype == FP4_F16 || c_dtype == FP4_E4M3) ? FP4_EUNSUPPORTED : FP4_EINVAL;
+  }
+  if (n < 0 || k % 32 != 0) return FP4_EINVAL;
+  if ((n > 0 && k > kMaxElements / n) || (m > 0 && n > kMaxElements / m)) return FP4_EINVAL;
+  if (m == 0) return FP4_OK;
+  if (n > 0) {
+    if (!b_codes || !b_scales || !c) return FP4_EINVAL;
+    if (!aligned(b_codes, 16) || !aligned(b_scales, 4) || !aligned(c, 16)) return FP4_EINVAL;
+    if (fmt == FP4_NVFP4) {
+      if (!b_tscale || !aligned(b_tscale, 4)) return FP4_EINVAL;
+    } else if (b_tscale) {
+      return FP4_EINVAL;
+    }
+    const size_t need = gemm_workspace_bytes((int)fmt, m, n, k);
+    if (need > 0 && (!workspace || workspace_bytes < need)) return FP4_EINVAL;
+  }
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (fmt == FP4_NVFP4 && x_dtype == FP4_BF16 && n > 0) {
+    hipError_t e = hipSuccess;
+    if (launch_quantize_gemm_decode(m, n, k, x, a_codes, a_scales, a_tscale, b_codes, b_scales,
+                                    b_tscale, c, (int)c_dtype, st, &e))
+      return from_hip(e);
+  }
+  s = quantize_common(false, fmt, x, x_dtype, m, k, a_codes, a_scales, a_tscale,
+                      FP4_TSCALE_COMPUTE, workspace, workspace_bytes, stream);
+  if (s != FP4_OK || n == 0) return s;
+  return from_hip(launch_gemm((int)fmt, m, n, k, a_codes, a_scales, a_tscale, b_codes,
+                              b_scales, b_tscale, c, (int)c_dtype, workspace, st));
+}
+
 }  // extern "C"

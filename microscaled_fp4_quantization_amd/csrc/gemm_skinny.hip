@@ -358,13 +358,21 @@ struct StreamLds {
   uint8_t w[kStrWaves][16 * kStrTiles][kStrPitch];    // weight scale slices
 };
 
-template <int NSTEP>
+// QX: the activations come in as bf16 X [m, k] (`a`) and are quantized here,
+// NVFP4 with the tensor scale computed from the data, exactly as
+// quantize_chunk does it: every workgroup reduces max |X| over the whole
+// tensor (16 slices, one per wave) and quantizes its own slices; workgroup 0
+// also writes the codes, scales and tensor scale out (qcodes, qscales,
+// qtscale).  `as` and `at` are unused then.
+template <int NSTEP, bool QX>
 __global__ __launch_bounds__(64 * kStrWaves) void gemm_nv_stream(
     int m, int64_t n, int k, int rows_per_wg, const uint8_t* __restrict__ a,
     const uint8_t* __restrict__ as, const float* __restrict__ at,
     const uint8_t* __restrict__ b, const uint8_t* __restrict__ bs,
-    const float* __restrict__ bt, void* __restrict__ c, int c_dtype) {
+    const float* __restrict__ bt, void* __restrict__ c, int c_dtype,
+    uint8_t* __restrict__ qcodes, uint8_t* __restrict__ qscales, float* __restrict__ qtscale) {
   __shared__ StreamLds L;
+  __shared__ float red[kStrWaves];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = lane & 15, g = lane >> 4;
@@ -375,22 +383,36 @@ __global__ __launch_bounds__(64 * kStrWaves) void gemm_nv_stream(
   const int64_t kbytes = k / 2, kblocks = k / 16;
 
   // ---- all loads of the wave -------------------------------------------------
-  // weight scale slices: lane p loads row p's 8 NSTEP bytes
-  const int64_t swr = (nbase + lane <= nlast) ? nbase + lane : nlast;
-  u32x4 sv;
-  if (NSTEP == 2) {
-    sv = *reinterpret_cast<const u32x4*>(bs + swr * kblocks + ks0 / 16);
-  } else {
-    const u32x2 h = *reinterpret_cast<const u32x2*>(bs + swr * kblocks + ks0 / 16);
-    sv = (u32x4){h.x, h.y, 0u, 0u};
-  }
-  // activation slice: lane -> row lane / 8, 32 NSTEP / 2 values at
-  // (lane % 8) 16 NSTEP of the slice
+  // QX: this wave's slice of X first, lane -> row lane / 8, the 16 NSTEP
+  // values at ks0 + 16 NSTEP (lane % 8) (one or two whole blocks)
   const int xrow = lane >> 3, xc = lane & 7;
   const int64_t xsrc = xrow < m ? xrow : m - 1;
-  u32x4 xq;
-  uint32_t xs2;
-  if (NSTEP == 2) {
+  const int xv0 = ks0 + 16 * NSTEP * xc;
+  u32x4 xb[2 * NSTEP];
+  if (QX) {
+#pragma unroll
+    for (int i = 0; i < 2 * NSTEP; ++i)
+      xb[i] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(a) + xsrc * k + xv0 + 8 * i);
+  }
+  // weight scale slices: lane p loads row p's 8 NSTEP bytes (QX: later,
+  // with the weight codes)
+  const int64_t swr = (nbase + lane <= nlast) ? nbase + lane : nlast;
+  u32x4 sv;
+  auto load_ws = [&]() {
+    if (NSTEP == 2) {
+      sv = *reinterpret_cast<const u32x4*>(bs + swr * kblocks + ks0 / 16);
+    } else {
+      const u32x2 h = *reinterpret_cast<const u32x2*>(bs + swr * kblocks + ks0 / 16);
+      sv = (u32x4){h.x, h.y, 0u, 0u};
+    }
+  };
+  if (!QX) load_ws();
+  // activation slice (quantized input): lane -> row lane / 8, 16 NSTEP
+  // values at (lane % 8) 16 NSTEP of the slice
+  u32x4 xq = {0u, 0u, 0u, 0u};
+  uint32_t xs2 = 0;
+  if (QX) {
+  } else if (NSTEP == 2) {
     xq = *reinterpret_cast<const u32x4*>(a + xsrc * kbytes + ks0 / 2 + 16 * xc);
     xs2 = *reinterpret_cast<const uint16_t*>(as + xsrc * kblocks + ks0 / 16 + 2 * xc);
   } else {
@@ -398,24 +420,98 @@ __global__ __launch_bounds__(64 * kStrWaves) void gemm_nv_stream(
     xq = (u32x4){h.x, h.y, 0u, 0u};
     xs2 = as[xsrc * kblocks + ks0 / 16 + xc];
   }
-  // weight codes
-  u32x4 w[kStrTiles][NSTEP];
+  // QX: this wave's part of max |X|; the workgroup reduces the 16 parts at a
+  // barrier and only then sends its weight loads (queued behind them, the
+  // activation loads of slower waves would wait for the whole stream).
+  float xv[16 * NSTEP], am[NSTEP];
+  if (QX) {
+    const bool live = xrow < m;
 #pragma unroll
-  for (int tl = 0; tl < kStrTiles; ++tl) {
-    const int64_t wr = (nbase + 16 * tl + r <= nlast) ? nbase + 16 * tl + r : nlast;
+    for (int i = 0; i < 2 * NSTEP; ++i)
 #pragma unroll
-    for (int t = 0; t < NSTEP; ++t)
-      w[tl][t] = *reinterpret_cast<const u32x4*>(b + wr * kbytes + ks0 / 2 + 64 * t + 16 * g);
+      for (int j = 0; j < 4; ++j) {
+        xv[8 * i + 2 * j] = live ? bf16_lo(xb[i][j]) : 0.0f;
+        xv[8 * i + 2 * j + 1] = live ? bf16_hi(xb[i][j]) : 0.0f;
+      }
+#pragma unroll
+    for (int bl = 0; bl < NSTEP; ++bl) {
+      float mx = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) mx = fmaxf(mx, fabsf(xv[16 * bl + j]));
+      am[bl] = mx;
+    }
+    float wm = NSTEP == 2 ? fmaxf(am[0], am[1]) : am[0];
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) wm = fmaxf(wm, __shfl_xor(wm, off));
+    if (lane == 0) red[wave] = wm;
+    __builtin_amdgcn_sched_barrier(0);
   }
+  // weight codes (QX: only once every wave's part of max |X| is in, so the
+  // activation loads of the workgroup do not queue behind its weight stream)
+  u32x4 w[kStrTiles][NSTEP];
+  auto load_w = [&]() {
+#pragma unroll
+    for (int tl = 0; tl < kStrTiles; ++tl) {
+      const int64_t wr = (nbase + 16 * tl + r <= nlast) ? nbase + 16 * tl + r : nlast;
+#pragma unroll
+      for (int t = 0; t < NSTEP; ++t)
+        w[tl][t] = *reinterpret_cast<const u32x4*>(b + wr * kbytes + ks0 / 2 + 64 * t + 16 * g);
+    }
+  };
+  if (!QX) load_w();
   __builtin_amdgcn_sched_barrier(0);
 
   // ---- this wave's LDS regions (loads complete in issue order) ---------------
-  {
+  auto store_ws = [&]() {
     uint32_t* dd = reinterpret_cast<uint32_t*>(&L.w[wave][lane][0]);
     dd[0] = sv[0]; dd[1] = sv[1];
     if (NSTEP == 2) { dd[2] = sv[2]; dd[3] = sv[3]; }
-  }
-  {
+  };
+  if (!QX) store_ws();
+  float xscale = 1.0f;                                // the activations' tensor scale
+  if (QX) {
+    // max |x| over the whole tensor: every wave's part is in `red`
+    const bool live = xrow < m;
+    __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));   // lgkmcnt(0), loads stay in flight
+    __asm__ volatile("s_barrier" ::: "memory");
+    load_ws();
+    load_w();
+    __builtin_amdgcn_sched_barrier(0);
+    float A = red[0];
+#pragma unroll
+    for (int i = 1; i < kStrWaves; ++i) A = fmaxf(A, red[i]);
+    float s_t = A / 2688.0f;                          // 6 * 448
+    if (s_t == 0.0f) s_t = 1.0f;
+    const float dd = 6.0f * s_t;
+    xscale = s_t;
+    const bool out = blockIdx.x == 0 && live;
+#pragma unroll
+    for (int bl = 0; bl < NSTEP; ++bl) {
+      const uint32_t sbyte = e4m3_encode_pos(am[bl] / dd);
+      const float S = e4m3_decode_pos(sbyte) * s_t;
+      float r = 1.0f / S;
+      if (!(S != 0.0f && r < __builtin_inff())) r = 0.0f;   // zero block or overflowing reciprocal
+      uint32_t wd[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const float* q = &xv[16 * bl + 8 * h];
+        uint32_t w = e2m1_pack2<0>(0u, q[0] * r, q[1] * r);
+        w = e2m1_pack2<1>(w, q[2] * r, q[3] * r);
+        w = e2m1_pack2<2>(w, q[4] * r, q[5] * r);
+        w = e2m1_pack2<3>(w, q[6] * r, q[7] * r);
+        wd[h] = w;
+        v8h f = dequant8(w, (_Float16)e4m3_decode_pos(sbyte));
+        if (!live) f = (v8h){0, 0, 0, 0, 0, 0, 0, 0};
+        *reinterpret_cast<v8h*>(&L.x[wave][xrow][16 * NSTEP * xc + 16 * bl + 8 * h]) = f;
+      }
+      if (out) {
+        *reinterpret_cast<u32x2*>(qcodes + xsrc * kbytes + (xv0 + 16 * bl) / 2) = (u32x2){wd[0], wd[1]};
+        qscales[xsrc * kblocks + (xv0 + 16 * bl) / 16] = (uint8_t)sbyte;
+      }
+    }
+    if (blockIdx.x == 0 && tid == 0) *qtscale = s_t;
+    store_ws();
+  } else {
     const bool live = xrow < m;
     const v2h sc = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(xs2, 1.0f, false);
 #pragma unroll
@@ -462,7 +558,7 @@ __global__ __launch_bounds__(64 * kStrWaves) void gemm_nv_stream(
     v4f sum = part[tl * 64 + l];
 #pragma unroll
     for (int wv = 1; wv < kStrWaves; ++wv) sum += part[(wv * kStrTiles + tl) * 64 + l];
-    const float scale = (*at) * (*bt);
+    const float scale = (QX ? xscale : *at) * (*bt);
     // D layout: lane l holds weight rows 4 (l / 16) + e of the tile, activation row l % 16
     const int xr = l & 15;
     if (xr < m) {
@@ -490,11 +586,13 @@ hipError_t launch_gemm_skinny(int fmt, int64_t m, int64_t n, int64_t k,
     const int rows = (int)(8 * ((n + 2047) / 2048));
     const dim3 grid((unsigned)((n + rows - 1) / rows));
     if (k == 4096)
-      hipLaunchKernelGGL(gemm_nv_stream<2>, grid, dim3(64 * kStrWaves), 0, stream, (int)m, n, (int)k,
-                         rows, a_codes, a_scales, a_tscale, b_codes, b_scales, b_tscale, c, c_dtype);
+      hipLaunchKernelGGL((gemm_nv_stream<2, false>), grid, dim3(64 * kStrWaves), 0, stream, (int)m, n,
+                         (int)k, rows, a_codes, a_scales, a_tscale, b_codes, b_scales, b_tscale, c,
+                         c_dtype, nullptr, nullptr, nullptr);
     else
-      hipLaunchKernelGGL(gemm_nv_stream<1>, grid, dim3(64 * kStrWaves), 0, stream, (int)m, n, (int)k,
-                         rows, a_codes, a_scales, a_tscale, b_codes, b_scales, b_tscale, c, c_dtype);
+      hipLaunchKernelGGL((gemm_nv_stream<1, false>), grid, dim3(64 * kStrWaves), 0, stream, (int)m, n,
+                         (int)k, rows, a_codes, a_scales, a_tscale, b_codes, b_scales, b_tscale, c,
+                         c_dtype, nullptr, nullptr, nullptr);
     return hipGetLastError();
   }
   if (fmt == kFmtNV && m <= 8 && k % kDecKC == 0 && aligned16) {
@@ -512,4 +610,31 @@ hipError_t launch_gemm_skinny(int fmt, int64_t m, int64_t n, int64_t k,
                        a_scales, b_codes, b_scales, c, c_dtype);
   }
   return hipGetLastError();
+}
+
+// Quantize bf16 activations (NVFP4, tensor scale from the data) and multiply,
+// in one launch, for the decode shapes of the stream kernel; returns false
+// (nothing launched) for any other shape.
+bool launch_quantize_gemm_decode(int64_t m, int64_t n, int64_t k, const void* x,
+                                 uint8_t* a_codes, uint8_t* a_scales, float* a_tscale,
+                                 const uint8_t* b_codes, const uint8_t* b_scales,
+                                 const float* b_tscale, void* c, int c_dtype, hipStream_t stream,
+                                 hipError_t* err) {
+  const bool aligned = ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(b_codes) |
+                         reinterpret_cast<uintptr_t>(b_scales) | reinterpret_cast<uintptr_t>(a_codes)) &
+                        15) == 0;
+  if (!(m >= 1 && m <= 8 && (k == 2048 || k == 4096) && n <= 16 * kStrTiles * 256 && aligned))
+    return false;
+  const int rows = (int)(8 * ((n + 2047) / 2048));
+  const dim3 grid((unsigned)((n + rows - 1) / rows));
+  if (k == 4096)
+    hipLaunchKernelGGL((gemm_nv_stream<2, true>), grid, dim3(64 * kStrWaves), 0, stream, (int)m, n,
+                       (int)k, rows, reinterpret_cast<const uint8_t*>(x), nullptr, nullptr, b_codes,
+                       b_scales, b_tscale, c, c_dtype, a_codes, a_scales, a_tscale);
+  else
+    hipLaunchKernelGGL((gemm_nv_stream<1, true>), grid, dim3(64 * kStrWaves), 0, stream, (int)m, n,
+                       (int)k, rows, reinterpret_cast<const uint8_t*>(x), nullptr, nullptr, b_codes,
+                       b_scales, b_tscale, c, c_dtype, a_codes, a_scales, a_tscale);
+  *err = hipGetLastError();
+  return true;
 }

@@ -34,3 +34,11 @@ hipError_t launch_gemm(int fmt, int64_t m, int64_t n, int64_t k,
                        const float* a_tscale, const uint8_t* b_codes,
                        const uint8_t* b_scales, const float* b_tscale, void* c,
                        int c_dtype, void* workspace, hipStream_t stream);
+
+// One-launch NVFP4 activation quantize (tensor scale from the data) + GEMM
+// for the decode shapes; false (nothing launched) for any other shape.
+bool launch_quantize_gemm_decode(int64_t m, int64_t n, int64_t k, const void* x,
+                                 uint8_t* a_codes, uint8_t* a_scales, float* a_tscale,
+                                 const uint8_t* b_codes, const uint8_t* b_scales,
+                                 const float* b_tscale, void* c, int c_dtype, hipStream_t stream,
+                                 hipError_t* err);

@@ -27,7 +27,7 @@ _OUT_DTYPES = {"f32": (F32, torch.float32), "bf16": (BF16, torch.bfloat16),
 
 EXPORTS = ("fp4_status_string", "fp4_quantize_workspace_size", "fp4_quantize",
            "fp4_hadamard_quantize", "fp4_dequantize", "fp4_gemm_workspace_size",
-           "fp4_gemm")
+           "fp4_gemm", "fp4_quantize_gemm_workspace_size", "fp4_quantize_gemm")
 
 _lib = None
 
@@ -62,6 +62,11 @@ def lib():
     L.fp4_gemm_workspace_size.restype = sz
     L.fp4_gemm.argtypes = [i32, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp, i32, vp, sz, vp]
     L.fp4_gemm.restype = i32
+    L.fp4_quantize_gemm_workspace_size.argtypes = [i32, i64, i64, i64]
+    L.fp4_quantize_gemm_workspace_size.restype = sz
+    L.fp4_quantize_gemm.argtypes = [i32, vp, i32, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp, i32,
+                                    vp, sz, vp]
+    L.fp4_quantize_gemm.restype = i32
     _lib = L
     return L
 
@@ -151,3 +156,30 @@ def gemm(a, b, fmt="nvfp4", out_dtype="bf16", out=None):
                     _ptr(bt), _ptr(out), code, _ptr(ws), need, _stream(ac))
     _check(st, "fp4_gemm")
     return out
+
+
+def quantize_gemm(x, b, fmt="nvfp4", out_dtype="bf16", out=None):
+    """Quantize the activations x [m, k] (tensor scale from the data for
+    NVFP4) and multiply by the quantized B = (codes [n, k/2], scales, tscale).
+    Returns ((codes, scales, tscale) of x, C [m, n]); same results as
+    quantize() followed by gemm(), in one launch for the decode shapes."""
+    f = _fmt(fmt)
+    if x.dim() != 2:
+        raise ValueError("x must be [m, k]")
+    m, k = x.shape
+    bc, bsc, bt = b
+    n = bc.shape[0]
+    code, tdt = _OUT_DTYPES[out_dtype]
+    codes = torch.empty((m, k // 2), dtype=torch.uint8, device=x.device)
+    scales = torch.empty((m, k // BLOCK[f]), dtype=torch.uint8, device=x.device)
+    ts = torch.empty(1, dtype=torch.float32, device=x.device) if f == NVFP4 else None
+    if out is None:
+        out = torch.empty((m, n), dtype=tdt, device=x.device)
+    L = lib()
+    need = L.fp4_quantize_gemm_workspace_size(f, m, n, k)
+    ws = torch.empty(need, dtype=torch.uint8, device=x.device) if need else None
+    st = L.fp4_quantize_gemm(f, _ptr(x), _IN_DTYPES[x.dtype], m, n, k, _ptr(codes), _ptr(scales),
+                             _ptr(ts), _ptr(bc), _ptr(bsc), _ptr(bt), _ptr(out), code, _ptr(ws),
+                             need, _stream(x))
+    _check(st, "fp4_quantize_gemm")
+    return (codes, scales, ts), out

@@ -117,6 +117,32 @@ def test_gemm_rejects_bad_arguments():
     assert g(m=0, a=None, c=None) == fp4.OK
 
 
+def test_quantize_gemm_rejects_bad_arguments():
+    f = fp4.lib().fp4_quantize_gemm
+
+    def g(fmt=NV, x=FAKE, dt=fp4.BF16, m=8, n=8, k=64, ac=FAKE, asc=FAKE, at=FAKE, b=FAKE,
+          bsc=FAKE, bt=FAKE, c=FAKE, cdt=fp4.BF16, ws=FAKE, wsb=1 << 20):
+        return f(fmt, x, dt, m, n, k, ac, asc, at, b, bsc, bt, c, cdt, ws, wsb, None)
+
+    E = fp4.EINVAL
+    assert g(fmt=2) == E
+    assert g(k=48) == E                       # quantizes (k % 16) but the GEMM needs k % 32
+    assert g(k=40) == E
+    assert g(x=FAKE_ODD) == E
+    assert g(dt=fp4.E4M3) == E                # not an input dtype
+    assert g(at=None) == E                    # NVFP4 writes the tensor scale
+    assert g(ws=None, wsb=0) == E             # the computed tensor scale needs the workspace
+    assert g(b=None) == E
+    assert g(bt=None) == E
+    assert g(c=FAKE_ODD) == E
+    assert g(n=-1) == E
+    assert g(fmt=MX, at=None) == E            # MXFP4 takes no tensor scale for B either
+    assert g(cdt=fp4.F16) == fp4.EUNSUPPORTED
+    assert g(m=0, x=None, ac=None) == fp4.OK   # nothing to do, nothing enqueued
+    assert fp4.lib().fp4_quantize_gemm_workspace_size(NV, 8, 8, 64) >= \
+        fp4.lib().fp4_quantize_workspace_size(NV, fp4.TSCALE_COMPUTE, 8, 64)
+
+
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(fp4, "_lib", None)
     monkeypatch.setattr(fp4, "LIB_PATH", str(tmp_path / "missing.so"))

@@ -174,3 +174,35 @@ def test_rotated_full_size():
     d = workloads.rotated(device=DEV)
     full_size_case("nvfp4", d["x"], d["w"], True)
     full_size_case("mxfp4", d["x"], d["w"], True)
+
+
+@pytest.mark.parametrize("fmt,m,n,k,xdt", [
+    ("nvfp4", 8, 14336, 4096, torch.bfloat16),   # decode shape: one launch
+    ("nvfp4", 1, 100, 4096, torch.bfloat16),     # partial share of rows
+    ("nvfp4", 5, 333, 2048, torch.bfloat16),
+    ("nvfp4", 8, 16384, 4096, torch.bfloat16),   # largest n of the one-launch path
+    ("nvfp4", 16, 64, 256, torch.bfloat16),      # m > 8: quantize + GEMM calls
+    ("nvfp4", 3, 50, 96, torch.bfloat16),
+    ("nvfp4", 8, 200, 4096, torch.float32),      # not bf16: two calls
+    ("mxfp4", 8, 100, 4096, torch.bfloat16),
+])
+def test_quantize_gemm(fmt, m, n, k, xdt):
+    g = torch.Generator().manual_seed(4)
+    x = torch.randn((m, k), generator=g).to(xdt)
+    x[0, :16] = 0.0                                  # a zero block
+    w = (torch.randn((n, k), generator=g) * 0.02).to(torch.bfloat16)
+    qw = fq.quantize(w.to(DEV), fmt)
+    note("quantize_gemm %s m=%d n=%d k=%d %s" % (fmt, m, n, k, xdt))
+    qx, c = fq.quantize_gemm(x.to(DEV), qw, fmt, out_dtype="f32")
+    torch.cuda.synchronize()
+    xf = x.float().numpy()
+    if fmt == "nvfp4":
+        px, sx, tx = oracle.nvfp4_quantize(xf)
+        assert np.float32(qx[2].item()).tobytes() == np.float32(tx).tobytes()
+    else:
+        (px, sx), tx = oracle.mxfp4_quantize(xf), None
+    assert np.array_equal(np_u8(qx[0]), px)
+    assert np.array_equal(np_u8(qx[1]), sx)
+    pw, sw, tw = host_q(qw)
+    ref = oracle.gemm_ref(fmt, px, sx, tx, pw, sw, tw)
+    assert rel_fro(c.double().cpu().numpy(), ref) <= TOL
