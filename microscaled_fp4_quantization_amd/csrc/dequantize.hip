@@ -13,8 +13,10 @@
 // FP8 rounds to nearest even after a clamp to +-448 (the hardware conversion
 // rounds correctly inside that range but returns NaN beyond it).
 //
-// Lane t owns chunk base + t of 8 elements: one dword of codes in, 8 values
-// out (8 bytes FP8, 16 bytes bf16/fp16, 32 bytes fp32).
+// Lane t owns chunks 2p and 2p + 1 (16 elements, one NVFP4 block, half an
+// MXFP4 block): 8 bytes of codes and one scale byte in, 16 values out (16
+// bytes FP8, 32 bytes bf16/fp16, 64 bytes fp32), so the wave instructions
+// of the FP8 path read and write contiguous memory.
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -23,9 +25,7 @@ using namespace fp4dev;
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kUnroll = 4;
-constexpr int kChunksPerTrip = kThreads * kUnroll;
-constexpr int kMaxGrid = 4096;
+constexpr int kUnrollP = 4;          // chunk pairs per thread per loop trip
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -60,66 +60,115 @@ __device__ __forceinline__ uint32_t pack_e4m3x4(const float* y) {
   return (uint32_t)w;
 }
 
+// Chunk c (8 values, code word w, scale byte sbyte) -> out.
+template <int FMT, int OUT>
+__device__ __forceinline__ void dequant_chunk(uint32_t w, uint32_t sbyte, float s_t, int64_t c,
+                                              void* __restrict__ out) {
+  float sv;
+  if (FMT == kFmtNV) {
+    sv = e4m3_decode_pos(sbyte & 0x7Fu);
+    if (sbyte & 0x80u) sv = -sv;
+  } else {
+    sv = sbyte ? as_f(sbyte << 23) : as_f(0x00400000u);  // 2^(c-127); c = 0 is 2^-127
+  }
+  float y[8];
+  const v2f p0 = e2m1_unpack2<0>(w), p1 = e2m1_unpack2<1>(w);
+  const v2f p2 = e2m1_unpack2<2>(w), p3 = e2m1_unpack2<3>(w);
+  y[0] = p0.x; y[1] = p0.y; y[2] = p1.x; y[3] = p1.y;
+  y[4] = p2.x; y[5] = p2.y; y[6] = p3.x; y[7] = p3.y;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    if (FMT == kFmtNV) {
+      const float t = y[i] * sv;   // exact
+      y[i] = t * s_t;
+    } else {
+      y[i] = y[i] * sv;            // exact
+    }
+  }
+  if (OUT == kInF32) {
+    f32x4* o = reinterpret_cast<f32x4*>(out) + 2 * c;
+    __builtin_nontemporal_store((f32x4){y[0], y[1], y[2], y[3]}, o);
+    __builtin_nontemporal_store((f32x4){y[4], y[5], y[6], y[7]}, o + 1);
+  } else if (OUT == kInBF16) {
+    u32x4 o = {pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]),
+               pack_bf16x2(y[4], y[5]), pack_bf16x2(y[6], y[7])};
+    __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(out) + c);
+  } else if (OUT == kInF16) {
+    u32x4 o = {pack_f16x2(y[0], y[1]), pack_f16x2(y[2], y[3]),
+               pack_f16x2(y[4], y[5]), pack_f16x2(y[6], y[7])};
+    __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(out) + c);
+  } else {
+    u32x2 o = {pack_e4m3x4(y), pack_e4m3x4(y + 4)};
+    __builtin_nontemporal_store(o, reinterpret_cast<u32x2*>(out) + c);
+  }
+}
+
+// Chunk (code word w, scale byte sbyte) -> 8 FP8 E4M3 bytes.
+template <int FMT>
+__device__ __forceinline__ u32x2 dequant_e4m3(uint32_t w, uint32_t sbyte, float s_t) {
+  float sv;
+  if (FMT == kFmtNV) {
+    sv = e4m3_decode_pos(sbyte & 0x7Fu);
+    if (sbyte & 0x80u) sv = -sv;
+  } else {
+    sv = sbyte ? as_f(sbyte << 23) : as_f(0x00400000u);  // 2^(c-127); c = 0 is 2^-127
+  }
+  float y[8];
+  const v2f p0 = e2m1_unpack2<0>(w), p1 = e2m1_unpack2<1>(w);
+  const v2f p2 = e2m1_unpack2<2>(w), p3 = e2m1_unpack2<3>(w);
+  y[0] = p0.x; y[1] = p0.y; y[2] = p1.x; y[3] = p1.y;
+  y[4] = p2.x; y[5] = p2.y; y[6] = p3.x; y[7] = p3.y;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    if (FMT == kFmtNV) {
+      const float t = y[i] * sv;   // exact
+      y[i] = t * s_t;
+    } else {
+      y[i] = y[i] * sv;            // exact
+    }
+  }
+  return (u32x2){pack_e4m3x4(y), pack_e4m3x4(y + 4)};
+}
+
+// An odd last chunk goes alone.
 template <int FMT, int OUT>
 __global__ __launch_bounds__(kThreads) void dequantize_kernel(
     const uint32_t* __restrict__ codes, const uint8_t* __restrict__ scales,
     const float* __restrict__ tscale, int64_t nchunks, void* __restrict__ out) {
   const float s_t = (FMT == kFmtNV) ? *tscale : 1.0f;
-  for (int64_t base = (int64_t)blockIdx.x * kChunksPerTrip; base < nchunks;
-       base += (int64_t)gridDim.x * kChunksPerTrip) {
-    uint32_t w[kUnroll], sb[kUnroll];
+  const int64_t npairs = nchunks >> 1;
+  const u32x2* codes2 = reinterpret_cast<const u32x2*>(codes);
+  for (int64_t base = (int64_t)blockIdx.x * kThreads * kUnrollP; base < npairs;
+       base += (int64_t)gridDim.x * kThreads * kUnrollP) {
+    u32x2 w[kUnrollP];
+    uint32_t sb[kUnrollP];
 #pragma unroll
-    for (int j = 0; j < kUnroll; ++j) {
-      const int64_t c = base + j * kThreads + threadIdx.x;
-      w[j] = 0u;
+    for (int j = 0; j < kUnrollP; ++j) {
+      const int64_t p = base + j * kThreads + threadIdx.x;
+      w[j] = (u32x2){0u, 0u};
       sb[j] = 0u;
-      if (c < nchunks) {
-        w[j] = __builtin_nontemporal_load(codes + c);
-        sb[j] = scales[FMT == kFmtNV ? (c >> 1) : (c >> 2)];
+      if (p < npairs) {
+        w[j] = __builtin_nontemporal_load(codes2 + p);
+        sb[j] = scales[FMT == kFmtNV ? p : (p >> 1)];
       }
     }
 #pragma unroll
-    for (int j = 0; j < kUnroll; ++j) {
-      const int64_t c = base + j * kThreads + threadIdx.x;
-      if (c >= nchunks) continue;
-      float sv;
-      if (FMT == kFmtNV) {
-        sv = e4m3_decode_pos(sb[j] & 0x7Fu);
-        if (sb[j] & 0x80u) sv = -sv;
+    for (int j = 0; j < kUnrollP; ++j) {
+      const int64_t p = base + j * kThreads + threadIdx.x;
+      if (p >= npairs) continue;
+      if (OUT == kOutE4M3) {
+        const u32x2 a = dequant_e4m3<FMT>(w[j][0], sb[j], s_t);
+        const u32x2 b = dequant_e4m3<FMT>(w[j][1], sb[j], s_t);
+        __builtin_nontemporal_store((u32x4){a.x, a.y, b.x, b.y}, reinterpret_cast<u32x4*>(out) + p);
       } else {
-        sv = sb[j] ? as_f(sb[j] << 23) : as_f(0x00400000u);  // 2^(c-127); c = 0 is 2^-127
-      }
-      float y[8];
-      const v2f p0 = e2m1_unpack2<0>(w[j]), p1 = e2m1_unpack2<1>(w[j]);
-      const v2f p2 = e2m1_unpack2<2>(w[j]), p3 = e2m1_unpack2<3>(w[j]);
-      y[0] = p0.x; y[1] = p0.y; y[2] = p1.x; y[3] = p1.y;
-      y[4] = p2.x; y[5] = p2.y; y[6] = p3.x; y[7] = p3.y;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        if (FMT == kFmtNV) {
-          const float t = y[i] * sv;   // exact
-          y[i] = t * s_t;
-        } else {
-          y[i] = y[i] * sv;            // exact
-        }
-      }
-      if (OUT == kInF32) {
-        f32x4* o = reinterpret_cast<f32x4*>(out) + 2 * c;
-        __builtin_nontemporal_store((f32x4){y[0], y[1], y[2], y[3]}, o);
-        __builtin_nontemporal_store((f32x4){y[4], y[5], y[6], y[7]}, o + 1);
-      } else if (OUT == kInBF16) {
-        u32x4 o = {pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]),
-                   pack_bf16x2(y[4], y[5]), pack_bf16x2(y[6], y[7])};
-        __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(out) + c);
-      } else if (OUT == kInF16) {
-        u32x4 o = {pack_f16x2(y[0], y[1]), pack_f16x2(y[2], y[3]),
-                   pack_f16x2(y[4], y[5]), pack_f16x2(y[6], y[7])};
-        __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(out) + c);
-      } else {
-        u32x2 o = {pack_e4m3x4(y), pack_e4m3x4(y + 4)};
-        __builtin_nontemporal_store(o, reinterpret_cast<u32x2*>(out) + c);
+        dequant_chunk<FMT, OUT>(w[j][0], sb[j], s_t, 2 * p, out);
+        dequant_chunk<FMT, OUT>(w[j][1], sb[j], s_t, 2 * p + 1, out);
       }
     }
+  }
+  if (blockIdx.x == 0 && threadIdx.x == 0 && (nchunks & 1)) {
+    const int64_t c = nchunks - 1;
+    dequant_chunk<FMT, OUT>(codes[c], scales[FMT == kFmtNV ? (c >> 1) : (c >> 2)], s_t, c, out);
   }
 }
 
@@ -127,8 +176,9 @@ template <int FMT>
 hipError_t launch_fmt(const uint8_t* codes, const uint8_t* scales,
                       const float* tscale, int64_t nchunks, void* out,
                       int out_dtype, hipStream_t stream) {
-  const int64_t trips = (nchunks + kChunksPerTrip - 1) / kChunksPerTrip;
-  const dim3 grid((unsigned)(trips < kMaxGrid ? trips : kMaxGrid));
+  // one trip per workgroup (a grid-stride cap cost bandwidth on long tensors)
+  const int64_t trips = (nchunks / 2 + kThreads * kUnrollP - 1) / (kThreads * kUnrollP);
+  const dim3 grid((unsigned)(trips < 1 ? 1 : trips));
   const uint32_t* c32 = reinterpret_cast<const uint32_t*>(codes);
   switch (out_dtype) {
     case kInF32:
