@@ -136,6 +136,90 @@ struct Frags {
   uint32_t sb[TJ];
 };
 
+// Writes a workgroup's 256 x 256 tile of C = ts * acc.  The MFMAs take B as
+// the first operand, so in each 32x32 block a lane holds output row
+// r = lane % 32 and, in registers 4g .. 4g + 3, the four consecutive columns
+// 8g + 4h .. + 3.  The tile goes through LDS (ep: the workgroup's operand
+// ring, free once every wave is past its last fragment read) in row-major
+// order and leaves as 16-byte row chunks: direct stores of the fragments
+// would scatter 2- or 4-byte pieces over 32 rows.
+//
+// The tile starts at row m0 and column n0; only rows >= m_lo and columns >=
+// n_lo are this workgroup's (a last tile that was moved back so that all of
+// its rows exist leaves the overlap to its neighbour).
+template <int WMW, int WNW, int TI, int TJ>
+__device__ __forceinline__ void store_tile(const v16f (&acc)[TI][TJ], uint8_t* ep, float ts,
+                                           void* __restrict__ c, int c_dtype, int m, int n,
+                                           int m0, int n0, int m_lo, int n_lo) {
+  constexpr int NW = WMW * WNW, TM = BM / WMW, TN = BN / WNW;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WNW, wn = wave % WNW;
+  const int r = lane & 31, h = lane >> 5;
+  wait_lgkm0();
+  __asm__ volatile("s_barrier" ::: "memory");
+  const bool f32 = (c_dtype == kInF32);
+  // bf16: the whole 256 x 256 tile, rows of 528 bytes (512 + 16: 16-byte
+  // aligned, writes of the 32 rows of a block spread over the banks);
+  // f32: one 128-row band (the rows of the waves with wm = band) at a time,
+  // rows of 1040 bytes.
+  const int pitch = f32 ? 1040 : 528;
+  const int nband = f32 ? 2 : 1;
+  const int band_rows = BM / nband;
+  const bool vec_ok = f32 ? (n % 4 == 0) : (n % 8 == 0);
+  for (int band = 0; band < nband; ++band) {
+    if (!f32 || wm == band) {
+#pragma unroll
+      for (int i = 0; i < TI; ++i)
+#pragma unroll
+        for (int j = 0; j < TJ; ++j) {
+          const int row = (f32 ? 0 : wm * TM) + 32 * i + r;   // row within the band
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int col = wn * TN + 32 * j + 8 * g + 4 * h;
+            const float v0 = acc[i][j][4 * g] * ts, v1 = acc[i][j][4 * g + 1] * ts;
+            const float v2 = acc[i][j][4 * g + 2] * ts, v3 = acc[i][j][4 * g + 3] * ts;
+            if (f32) {
+              *reinterpret_cast<float4*>(ep + row * pitch + col * 4) = make_float4(v0, v1, v2, v3);
+            } else {
+              const __bf16 b0 = (__bf16)v0, b1 = (__bf16)v1, b2 = (__bf16)v2, b3 = (__bf16)v3;
+              uint2 u;
+              u.x = (uint32_t)__builtin_bit_cast(uint16_t, b0) | ((uint32_t)__builtin_bit_cast(uint16_t, b1) << 16);
+              u.y = (uint32_t)__builtin_bit_cast(uint16_t, b2) | ((uint32_t)__builtin_bit_cast(uint16_t, b3) << 16);
+              *reinterpret_cast<uint2*>(ep + row * pitch + col * 2) = u;
+            }
+          }
+        }
+    }
+    __syncthreads();
+    // 16-byte chunks: 32 (bf16) or 64 (f32) per row
+    const int cpr = f32 ? 64 : 32, epc = f32 ? 4 : 8;
+    const int row0 = m0 + band * band_rows;
+    for (int idx = tid; idx < band_rows * cpr; idx += 64 * NW) {
+      const int lr = idx / cpr, ch = idx % cpr;
+      const int grow = row0 + lr, gcol = n0 + ch * epc;
+      if (grow < m_lo || grow >= m || gcol + epc <= n_lo || gcol >= n) continue;
+      const uint4 v = *reinterpret_cast<const uint4*>(ep + lr * pitch + ch * 16);
+      const int64_t off = (int64_t)grow * n + gcol;
+      if (vec_ok && gcol >= n_lo && gcol + epc <= n) {
+        if (f32) *reinterpret_cast<uint4*>(reinterpret_cast<float*>(c) + off) = v;
+        else *reinterpret_cast<uint4*>(reinterpret_cast<__bf16*>(c) + off) = v;
+      } else if (f32) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (gcol + e >= n_lo && gcol + e < n) reinterpret_cast<uint32_t*>(c)[off + e] = e == 0 ? v.x : e == 1 ? v.y : e == 2 ? v.z : v.w;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t w = (e >> 1) == 0 ? v.x : (e >> 1) == 1 ? v.y : (e >> 1) == 2 ? v.z : v.w;
+          if (gcol + e >= n_lo && gcol + e < n) reinterpret_cast<uint16_t*>(c)[off + e] = (uint16_t)(w >> (16 * (e & 1)));
+        }
+      }
+    }
+    if (band + 1 < nband) __syncthreads();
+  }
+}
+
 template <int FMT, int WMW, int WNW>
 __global__ __launch_bounds__(64 * WMW * WNW, 1) void gemm_large(
     int m, int n, int k, const uint8_t* __restrict__ a,
@@ -406,75 +490,273 @@ __global__ __launch_bounds__(64 * WMW * WNW, 1) void gemm_large(
   wait_vm<0>();                 // no load may land in LDS after the workgroup ends
 
   // ---- epilogue -----------------------------------------------------------
-  // The MFMAs take B as the first operand, so in each 32x32 block a lane holds
-  // output row r = lane % 32 and, in registers 4g .. 4g + 3, the four
-  // consecutive columns 8g + 4h .. + 3.  The tile goes through LDS (the ring
-  // is free now) in row-major order and leaves as 16-byte row chunks: direct
-  // stores of the fragments would scatter 2- or 4-byte pieces over 32 rows.
-  wait_lgkm0();
-  __asm__ volatile("s_barrier" ::: "memory");
   const float ts = (FMT == kFmtNV) ? (*at) * (*bt) : 1.0f;
-  uint8_t* ep = reinterpret_cast<uint8_t*>(&smem);
-  const bool f32 = (c_dtype == kInF32);
-  // bf16: the whole 256 x 256 tile, rows of 528 bytes (512 + 16: 16-byte
-  // aligned, writes of the 32 rows of a block spread over the banks);
-  // f32: one 128-row band (the rows of the waves with wm = band) at a time,
-  // rows of 1040 bytes.
-  const int pitch = f32 ? 1040 : 528;
-  const int nband = f32 ? 2 : 1;
-  const int band_rows = BM / nband;
-  const bool vec_ok = f32 ? (n % 4 == 0) : (n % 8 == 0);
-  for (int band = 0; band < nband; ++band) {
-    if (!f32 || wm == band) {
+  store_tile<WMW, WNW>(acc, reinterpret_cast<uint8_t*>(&smem), ts, c, c_dtype, m, n, m0, n0, m0, n0);
+}
+
+// ---- MXFP4: 256-value stages ----------------------------------------------
+// A stage holds 256 k-values of every row: 128 code bytes, so one direct
+// load of 64 lanes covers 8 whole rows in full 128-byte lines.  (With
+// 64-byte rows every load touches twice the lines for the same bytes, and the
+// number of lines, not bytes, bounds the rate at which a CU's loads are
+// served.)  Two stage slots (128 KiB) hold the ring; the fragments of half a
+// stage (128 values) are read into registers while the previous half is
+// multiplied, so a slot is free once the second half of its stage is in
+// registers.  Scales come in groups of 32 bytes per row (4 stages) into a
+// 2-slot ring of their own (32 KiB): with 16-byte groups the scale loads
+// touch half as many lines as the codes and slow the stream by a third.
+constexpr int MXBK = 256;                 // k values per stage
+constexpr int MXROWB = MXBK / 2;          // code bytes per row per stage
+constexpr int MXG = 4;                    // stages per scale group
+constexpr int MXSGB = MXG * MXBK / 32;    // scale bytes per row per group
+
+struct MxStage {
+  uint8_t a[BM * MXROWB];
+  uint8_t b[BN * MXROWB];
+};
+struct MxScaleGroup {
+  uint8_t a[BM * MXSGB];
+  uint8_t b[BN * MXSGB];
+};
+struct MxSmem {                           // 160 KiB: the whole LDS of a CU
+  MxStage st[2];
+  MxScaleGroup sg[2];
+};
+
+// Stored position of 16-byte code chunk c (0..7) of row r: the 16 rows a
+// 16-lane read phase touches land on 16 different 16-byte bank groups.
+__device__ __forceinline__ int swz_mx(int r, int c) { return c ^ ((r >> 1) & 7); }
+// Stored position of 16-byte half hh of the 32-byte scale row r.
+__device__ __forceinline__ int swz_mxs(int r, int hh) { return hh ^ ((r >> 3) & 1); }
+
+template <int WMW, int WNW>
+__global__ __launch_bounds__(64 * WMW * WNW, 1) void gemm_large_mx(
+    int m, int n, int k, const uint8_t* __restrict__ a, const uint8_t* __restrict__ as,
+    const uint8_t* __restrict__ b, const uint8_t* __restrict__ bs, void* __restrict__ c,
+    int c_dtype, int tiles_m, int tiles_n) {
+  constexpr int NW = WMW * WNW;
+  constexpr int NL = BM * MXROWB / 1024 / NW;        // code loads per operand per wave per stage
+  constexpr int NSG = 2 * BM * MXSGB / 1024 / NW;    // scale loads per wave per group
+  constexpr int TM = BM / WMW, TN = BN / WNW;
+  constexpr int TI = TM / 32, TJ = TN / 32;
+  static_assert(BM == BN && NL * NW * 1024 == BM * MXROWB && NSG * NW * 1024 == 2 * BM * MXSGB, "tile shape");
+  static_assert(2 * NL + NSG < 64, "vmcnt range");
+  __shared__ __attribute__((aligned(16))) MxSmem smem;
+
+  const int ntiles = tiles_m * tiles_n;
+  const int wg = blockIdx.x;
+  int tile = wg;
+  if (ntiles % NXCD == 0) tile = (wg % NXCD) * (ntiles / NXCD) + wg / NXCD;
+  const int tm = tile % tiles_m, tn = tile / tiles_m;
+  // A last tile that would run past m or n is moved back to end at the last
+  // row or column (m, n >= 256): every row it loads exists, and the rows and
+  // columns it shares with its neighbour are left to the neighbour.
+  const int m_lo = tm * BM, n_lo = tn * BN;
+  const int m0 = m_lo + BM <= m ? m_lo : m - BM;
+  const int n0 = n_lo + BN <= n ? n_lo : n - BN;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kbytes = k / 2, srow = k / 32;
+  const int nst = k / MXBK;                          // even: k is a multiple of 512
+  const int ngr = (nst + MXG - 1) / MXG;
+
+  const __amdgpu_buffer_rsrc_t rs_a = __builtin_amdgcn_make_buffer_rsrc((void*)a, (short)0, m * kbytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rs_b = __builtin_amdgcn_make_buffer_rsrc((void*)b, (short)0, n * kbytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rs_as = __builtin_amdgcn_make_buffer_rsrc((void*)as, (short)0, m * srow, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rs_bs = __builtin_amdgcn_make_buffer_rsrc((void*)bs, (short)0, n * srow, 0x00020000);
+  // Code load i of the wave fills 1 KiB block q = i NW + wave of an operand's
+  // slot: rows 8q .. 8q + 7; lane p writes row 8q + p / 8 at stored position
+  // p % 8, i.e. fetches chunk (p % 8) ^ ((row >> 1) & 7), which does not
+  // depend on i.  The lane's offset is that of load 0; rows 32 i further on,
+  // the tile's first row and the stage go into the uniform offset.
+  const int crow = 8 * wave + (lane >> 3);
+  const int voff_c = crow * kbytes + swz_mx(crow, lane & 7) * 16;
+  // Scale load j of the wave fills 1 KiB block g = j NW + wave of a group
+  // slot: operand g / 8, rows 32 (g % 8) .. + 31, i.e. rows 32 wave + 128
+  // (j % 2) of operand j / 2; lane p writes row 32 (g % 8) + p / 2 at stored
+  // half p % 2, i.e. fetches half (p % 2) ^ ((row >> 3) & 1).
+  static_assert(NW == 4 && NSG == 4, "scale-load mapping");
+  const int srw = 32 * wave + (lane >> 1);
+  const int voff_s = srw * srow;
+  const int hoff_s = 16 * swz_mxs(srw, lane & 1);
+  // stage t (clamped to the last; a repeat is never read) into slot t % 2
+  auto issue_stage = [&](int t) {
+    MxStage& S = smem.st[t & 1];
+    const int kb = (t < nst ? t : nst - 1) * MXROWB;
 #pragma unroll
-      for (int i = 0; i < TI; ++i)
-#pragma unroll
-        for (int j = 0; j < TJ; ++j) {
-          const int row = (f32 ? 0 : wm * TM) + 32 * i + r;   // row within the band
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const int col = wn * TN + 32 * j + 8 * g + 4 * h;
-            const float v0 = acc[i][j][4 * g] * ts, v1 = acc[i][j][4 * g + 1] * ts;
-            const float v2 = acc[i][j][4 * g + 2] * ts, v3 = acc[i][j][4 * g + 3] * ts;
-            if (f32) {
-              *reinterpret_cast<float4*>(ep + row * pitch + col * 4) = make_float4(v0, v1, v2, v3);
-            } else {
-              const __bf16 b0 = (__bf16)v0, b1 = (__bf16)v1, b2 = (__bf16)v2, b3 = (__bf16)v3;
-              uint2 u;
-              u.x = (uint32_t)__builtin_bit_cast(uint16_t, b0) | ((uint32_t)__builtin_bit_cast(uint16_t, b1) << 16);
-              u.y = (uint32_t)__builtin_bit_cast(uint16_t, b2) | ((uint32_t)__builtin_bit_cast(uint16_t, b3) << 16);
-              *reinterpret_cast<uint2*>(ep + row * pitch + col * 2) = u;
-            }
-          }
-        }
+    for (int i = 0; i < NL; ++i) {
+      const int q = i * NW + wave;
+      load_lds16(rs_a, &S.a[q * 1024], voff_c, (m0 + 32 * i) * kbytes + kb);
+      load_lds16(rs_b, &S.b[q * 1024], voff_c, (n0 + 32 * i) * kbytes + kb);
     }
-    __syncthreads();
-    // 16-byte chunks: 32 (bf16) or 64 (f32) per row
-    const int cpr = f32 ? 64 : 32, epc = f32 ? 4 : 8;
-    const int row0 = m0 + band * band_rows;
-    for (int idx = tid; idx < band_rows * cpr; idx += 64 * NW) {
-      const int lr = idx / cpr, ch = idx % cpr;
-      const int grow = row0 + lr, gcol = n0 + ch * epc;
-      if (grow >= m || gcol >= n) continue;
-      const uint4 v = *reinterpret_cast<const uint4*>(ep + lr * pitch + ch * 16);
-      const int64_t off = (int64_t)grow * n + gcol;
-      if (vec_ok && gcol + epc <= n) {
-        if (f32) *reinterpret_cast<uint4*>(reinterpret_cast<float*>(c) + off) = v;
-        else *reinterpret_cast<uint4*>(reinterpret_cast<__bf16*>(c) + off) = v;
-      } else if (f32) {
+  };
+  // scale group g (clamped to the last) into group slot g % 2.  A last group
+  // of two stages has only its first half inside the row: the second half
+  // then repeats the first and is never read.
+  auto issue_group = [&](int g) {
+    MxScaleGroup& SG = smem.sg[g & 1];
+    const int gc = g < ngr ? g : ngr - 1;
+    const int gb = MXSGB * gc;
+    const bool whole = gb + MXSGB <= srow;
+    const int vo = voff_s + (whole ? hoff_s : 0);
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (gcol + e < n) reinterpret_cast<uint32_t*>(c)[off + e] = e == 0 ? v.x : e == 1 ? v.y : e == 2 ? v.z : v.w;
-      } else {
+    for (int j = 0; j < NSG; ++j) {
+      const int gw = j * NW + wave;
+      const bool isb = j >= 2;
+      load_lds16(isb ? rs_bs : rs_as, (isb ? SG.b : SG.a) + 1024 * (gw % 8), vo,
+                 ((isb ? n0 : m0) + 128 * (j & 1)) * srow + gb);
+    }
+  };
+
+  const int wm = wave / WNW, wn = wave % WNW;
+  const int r = lane & 31, h = lane >> 5;
+  // Half-stage u = 2 t + x: values [128 x, 128 x + 128) of stage t, k-steps
+  // ks = 0, 1 of 64 values.  Lane (r, h) takes chunk 4 x + 2 ks + h of its
+  // rows (block 4 x + 2 ks + h of the stage) and the scale word x of the
+  // stage's 8 scale bytes, whose bytes 2 ks + h it uses.
+  auto read_frags = [&](int u, Frags<TI, TJ>& F) {
+    const int t = u >> 1, x = u & 1;
+    const MxStage& S = smem.st[t & 1];
+    const MxScaleGroup& SG = smem.sg[(t / MXG) & 1];
+    const int sl = t % MXG;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const uint32_t w = (e >> 1) == 0 ? v.x : (e >> 1) == 1 ? v.y : (e >> 1) == 2 ? v.z : v.w;
-          if (gcol + e < n) reinterpret_cast<uint16_t*>(c)[off + e] = (uint16_t)(w >> (16 * (e & 1)));
-        }
+    for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+      for (int i = 0; i < TI; ++i) {
+        const int ra = wm * TM + 32 * i + r;
+        F.a[ks][i] = *reinterpret_cast<const u32x4*>(&S.a[ra * MXROWB + swz_mx(ra, 4 * x + 2 * ks + h) * 16]);
+      }
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) {
+        const int rb = wn * TN + 32 * j + r;
+        F.b[ks][j] = *reinterpret_cast<const u32x4*>(&S.b[rb * MXROWB + swz_mx(rb, 4 * x + 2 * ks + h) * 16]);
       }
     }
-    if (band + 1 < nband) __syncthreads();
+    const int wb = 8 * (sl & 1) + 4 * x;             // byte of the word within its 16-byte half
+#pragma unroll
+    for (int i = 0; i < TI; ++i) {
+      const int ra = wm * TM + 32 * i + r;
+      F.sa[i] = *reinterpret_cast<const uint32_t*>(&SG.a[ra * MXSGB + swz_mxs(ra, sl >> 1) * 16 + wb]);
+    }
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) {
+      const int rb = wn * TN + 32 * j + r;
+      F.sb[j] = *reinterpret_cast<const uint32_t*>(&SG.b[rb * MXSGB + swz_mxs(rb, sl >> 1) * 16 + wb]);
+    }
+  };
+
+  v16f acc[TI][TJ];
+#pragma unroll
+  for (int i = 0; i < TI; ++i)
+#pragma unroll
+    for (int j = 0; j < TJ; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+  // MFMAs [lo, hi) of a half-stage, in the order (k-step, i, j).  The lane's
+  // scale bytes 2 ks + h are moved to bytes 2 ks, so op_sel is 2 ks.
+  auto compute = [&](const Frags<TI, TJ>& F, auto LO, auto HI) {
+    constexpr int lo = decltype(LO)::value, hi = decltype(HI)::value;
+#pragma unroll
+    for (int q = lo; q < hi; ++q) {
+      const int ks = q / (TI * TJ), i = q / TJ % TI, j = q % TJ;
+      const int sa = (int)(F.sa[i] >> (8 * h)), sb = (int)(F.sb[j] >> (8 * h));
+      const v8i a8 = {(int)F.a[ks][i][0], (int)F.a[ks][i][1], (int)F.a[ks][i][2], (int)F.a[ks][i][3], 0, 0, 0, 0};
+      const v8i b8 = {(int)F.b[ks][j][0], (int)F.b[ks][j][1], (int)F.b[ks][j][2], (int)F.b[ks][j][3], 0, 0, 0, 0};
+      if (ks == 0)
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b8, a8, acc[i][j], 4, 4, 0, sb, 0, sa);
+      else
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b8, a8, acc[i][j], 4, 4, 2, sb, 2, sa);
+    }
+  };
+  using C0 = std::integral_constant<int, 0>;
+  using CE = std::integral_constant<int, 8>;                 // MFMAs ahead of a barrier
+  using CN = std::integral_constant<int, 2 * TI * TJ>;       // MFMAs per half-stage
+
+  // ---- software pipeline ----------------------------------------------------
+  // Half-step u multiplies half-stage u from registers while the fragments
+  // of half-stage u + 1 are read.  Each half-step starts with a few MFMAs so
+  // that the matrix core stays busy across its wait and barrier.
+  //   even u = 2 t: read the fragments of (t, 1), the last of stage t; once
+  //     every wave has them (barrier), load stage t + 2 into slot t % 2, and
+  //     with t % 4 == 3 the scale group of stages t + 5 .. t + 8 into the
+  //     slot of the group just read.
+  //   odd u = 2 t + 1: wait for stage t + 1 (own loads by count: issued after
+  //     it are stage t + 2 and maybe a group; everyone's at the barrier), then
+  //     read the fragments of (t + 1, 0).
+  // A stage is loaded about three half-steps before it is first read: the
+  // single stage in flight needs that long to land.
+  // Issue order: group 0, stages 0, 1, group 1, then per even half-step the
+  // stage and (every fourth) the group.
+  issue_group(0);
+  issue_stage(0);
+  issue_stage(1);
+  issue_group(1);
+  wait_vm<2 * NL + NSG>();                   // stage 0 and group 0
+  __asm__ volatile("s_barrier" ::: "memory");
+  Frags<TI, TJ> F0, F1;
+  read_frags(0, F0);
+
+  auto step = [&](auto J, int u, const Frags<TI, TJ>& Fc, Frags<TI, TJ>& Fn) {
+    constexpr int j = decltype(J)::value;      // u % 8
+    const int t = u >> 1;
+    if constexpr ((j & 1) == 0) {
+      read_frags(u + 1, Fn);
+      compute(Fc, C0{}, CE{});
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * TI + 2 * TJ + TI + TJ, 0);   // LDS reads
+      __builtin_amdgcn_sched_group_barrier(0x008, CE::value, 0);                   // MFMA
+      __builtin_amdgcn_sched_barrier(0);
+      wait_lgkm0();
+      __asm__ volatile("s_barrier" ::: "memory");
+      issue_stage(t + 2);
+      if constexpr (j == 6) issue_group((t + 2) / MXG + 1);
+      compute(Fc, CE{}, CN{});
+#pragma unroll
+      for (int g = 0; g < 8; ++g) {
+        __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);                        // global loads
+        __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);                        // MFMA
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    } else {
+      compute(Fc, C0{}, CE{});
+      __builtin_amdgcn_sched_barrier(0);
+      // stage t + 1; issued after it: stage t + 2 and, at j == 7, a group
+      if constexpr (j == 7) wait_vm<2 * NL + NSG>();
+      else wait_vm<2 * NL>();
+      __asm__ volatile("s_barrier" ::: "memory");
+      read_frags(u + 1, Fn);                   // past the end: a repeated stage, unused
+      compute(Fc, CE{}, CN{});
+#pragma unroll
+      for (int g = 0; g < 8; ++g) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);                        // LDS reads
+        __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);                        // MFMA
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  const int nfull = nst / MXG * MXG;
+  for (int t = 0; t < nfull; t += MXG) {
+    const int u = 2 * t;
+    step(std::integral_constant<int, 0>{}, u, F0, F1);
+    step(std::integral_constant<int, 1>{}, u + 1, F1, F0);
+    step(std::integral_constant<int, 2>{}, u + 2, F0, F1);
+    step(std::integral_constant<int, 3>{}, u + 3, F1, F0);
+    step(std::integral_constant<int, 4>{}, u + 4, F0, F1);
+    step(std::integral_constant<int, 5>{}, u + 5, F1, F0);
+    step(std::integral_constant<int, 6>{}, u + 6, F0, F1);
+    step(std::integral_constant<int, 7>{}, u + 7, F1, F0);
   }
+  if (nfull < nst) {                           // two stages left (k = 512 mod 1024)
+    const int u = 2 * nfull;
+    step(std::integral_constant<int, 0>{}, u, F0, F1);
+    step(std::integral_constant<int, 1>{}, u + 1, F1, F0);
+    step(std::integral_constant<int, 2>{}, u + 2, F0, F1);
+    step(std::integral_constant<int, 3>{}, u + 3, F1, F0);
+  }
+
+  wait_vm<0>();                 // no load may land in LDS after the workgroup ends
+  store_tile<WMW, WNW>(acc, reinterpret_cast<uint8_t*>(&smem), 1.0f, c, c_dtype, m, n, m0, n0, m_lo, n_lo);
 }
 
 }  // namespace
@@ -483,7 +765,9 @@ bool gemm_large_supported(int fmt, int64_t m, int64_t n, int64_t k) {
   const int64_t lim = int64_t(1) << 31;     // 32-bit buffer offsets
   // 16-byte scale rows: k a multiple of 512 (MXFP4) or 256 (NVFP4)
   const int64_t kq = (fmt == kFmtNV) ? 256 : 512;
-  return m >= 128 && n >= 128 && k % kq == 0 && m * (k / 2) < lim && n * (k / 2) < lim;
+  // MXFP4 tiles are moved back to lie inside the operands: m, n >= 256
+  const int64_t mn = (fmt == kFmtNV) ? 128 : 256;
+  return m >= mn && n >= mn && k % kq == 0 && m * (k / 2) < lim && n * (k / 2) < lim;
 }
 
 hipError_t launch_gemm_large(int fmt, int64_t m, int64_t n, int64_t k,
@@ -494,9 +778,9 @@ hipError_t launch_gemm_large(int fmt, int64_t m, int64_t n, int64_t k,
   const int tiles_m = (int)((m + BM - 1) / BM), tiles_n = (int)((n + BN - 1) / BN);
   const dim3 grid((unsigned)(tiles_m * tiles_n));
   if (fmt == kFmtMX) {
-    hipLaunchKernelGGL((gemm_large<kFmtMX, kMXWM, kMXWN>), grid, dim3(64 * kMXWM * kMXWN), 0, stream,
-                       (int)m, (int)n, (int)k, a_codes, a_scales, a_tscale, b_codes, b_scales,
-                       b_tscale, c, c_dtype, tiles_m, tiles_n);
+    hipLaunchKernelGGL((gemm_large_mx<kMXWM, kMXWN>), grid, dim3(64 * kMXWM * kMXWN), 0, stream,
+                       (int)m, (int)n, (int)k, a_codes, a_scales, b_codes, b_scales, c, c_dtype,
+                       tiles_m, tiles_n);
   } else {
     hipLaunchKernelGGL((gemm_large<kFmtNV, kNVWM, kNVWN>), grid, dim3(64 * kNVWM * kNVWN), 0, stream,
                        (int)m, (int)n, (int)k, a_codes, a_scales, a_tscale, b_codes, b_scales,
