@@ -103,6 +103,21 @@ def test_random_shapes(fmt, out_dtype):
         check_full(fmt, qx, qw, out_dtype)
 
 
+@pytest.mark.parametrize("m,n,k,out_dtype", [
+    (1100, 16000, 512, "bf16"),    # more tiles than CUs, k = 512 mod 1024
+    (2048, 9000, 1024, "f32"),     # tile count a multiple of 8: XCD-ordered tiles
+    (520, 30001, 1536, "bf16"),    # n not a multiple of 8
+])
+def test_mxfp4_many_tiles(m, n, k, out_dtype):
+    # the MXFP4 large-m kernel over more tiles than CUs, with tiles moved back
+    # at the edges and a half scale group at the end of k (k = 512 mod 1024)
+    g = torch.Generator().manual_seed(11)
+    x = torch.randn((m, k), generator=g).to(torch.bfloat16)
+    w = (torch.randn((n, k), generator=g) * 0.02).to(torch.bfloat16)
+    qx, qw = quant_pair("mxfp4", x, w)
+    check_full("mxfp4", qx, qw, out_dtype)
+
+
 def test_tiny_workload():
     d = workloads.tiny()
     qx, qw = quant_pair("nvfp4", d["x"], d["w"])
