@@ -28,6 +28,8 @@ Parity status per function (what pins it in the CPU tests):
   e4m3_decode / e4m3_encode   torch.float8_e4m3fn (library routine)
   e8m0_decode / e8m0_encode   math.ldexp closed form
   nvfp4_quantize              exact-rational properties, invariants, golden
+  nvfp4_quantize_mse          exact-rational argmin over all scale bytes,
+                              never worse than amax / 6, hand-worked golden
   mxfp4_quantize              brute-force exponent search, invariants, golden
   dequantize                  hand-built golden tensors, exact-rational check
   hadamard_blocks             scipy.linalg.hadamard matmul, involution
@@ -52,6 +54,8 @@ from .quant import (
     nvfp4_tensor_scale,
     nvfp4_tensor_scale_from_amax,
     nvfp4_quantize,
+    nvfp4_quantize_mse,
+    nvfp4_mse_block_error,
     mxfp4_quantize,
     dequantize,
     dequantize_exact_f64,
@@ -65,7 +69,7 @@ __all__ = [
     "E2M1_MAGNITUDES", "e2m1_decode", "e2m1_encode", "e4m3_decode",
     "e4m3_encode", "e4m3_encode_signed", "e8m0_decode", "e8m0_encode_exponent",
     "bf16_round", "NV_BLOCK", "MX_BLOCK", "NV_TSCALE_DIVISOR",
-    "nvfp4_tensor_scale", "nvfp4_tensor_scale_from_amax", "nvfp4_quantize", "mxfp4_quantize", "dequantize",
+    "nvfp4_tensor_scale", "nvfp4_tensor_scale_from_amax", "nvfp4_quantize", "nvfp4_quantize_mse", "nvfp4_mse_block_error", "mxfp4_quantize", "dequantize",
     "dequantize_exact_f64", "pack_nibbles", "unpack_nibbles",
     "hadamard_blocks", "HADAMARD_NORM", "gemm_ref", "gemm_ref_entries",
 ]
