@@ -132,6 +132,30 @@ fp4_status fp4_hadamard_quantize(fp4_format fmt, const void* x,
                                  void* stream);
 
 /*
+ * fp4_quantize_mse -- NVFP4 quantization whose block scale minimizes the
+ * block's squared error.
+ * Defines: the NVFP4 scaling of aisyndicate.ch "FP4 auf Blackwell", section
+ * "Was NVFP4 von frueheren 4-Bit-Formaten unterscheidet" (the E4M3 block
+ * scale is the factor with the least mean squared error over the block's 16
+ * values, instead of a rounded power of two).
+ *   Every positive finite E4M3 byte (1 .. 126) is tried as the block scale
+ *   under the tensor scale s_t; each quantizes the block as fp4_quantize does
+ *   for that byte (S_b = fp32(E4M3(sb) * s_t), q = x * fp32(1/S_b), E2M1
+ *   round to nearest even); its error sum_i (x_i - v_i S_b)^2 is summed in
+ *   fp64 in element order; the least error wins, ties going to the smaller
+ *   byte.  A block of zeros keeps byte 0.  The output is ordinary NVFP4
+ *   (fp4_dequantize and fp4_gemm take it as is).  About 10^4 fp64 operations
+ *   per block: meant for weights quantized once.
+ *   Arguments, alignment, workspace (fp4_quantize_workspace_size with
+ *   FP4_NVFP4) and errors as fp4_quantize with fmt = FP4_NVFP4.
+ */
+fp4_status fp4_quantize_mse(const void* x, fp4_dtype x_dtype, int64_t rows,
+                            int64_t k, uint8_t* codes, uint8_t* scales,
+                            float* tensor_scale, fp4_tscale_mode mode,
+                            void* workspace, size_t workspace_bytes,
+                            void* stream);
+
+/*
  * fp4_dequantize -- codes + scales -> values.
  * Defines: the inverse of the formats above; FP4_E4M3 output is the FP8 form
  * an NVFP4 KV cache is dequantized to before attention (hyper.ai story on the

@@ -104,6 +104,18 @@ fp4_status fp4_hadamard_quantize(fp4_format fmt, const void* x,
                          tensor_scale, mode, workspace, workspace_bytes, stream);
 }
 
+fp4_status fp4_quantize_mse(const void* x, fp4_dtype x_dtype, int64_t rows, int64_t k,
+                            uint8_t* codes, uint8_t* scales, float* tensor_scale,
+                            fp4_tscale_mode mode, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  fp4_status s = check_quantize(FP4_NVFP4, x, x_dtype, rows, k, codes, scales, tensor_scale,
+                                mode, workspace, workspace_bytes);
+  if (s != FP4_OK || rows == 0) return s;
+  return from_hip(launch_quantize_mse(x, (int)x_dtype, rows * k, codes, scales, tensor_scale,
+                                      mode == FP4_TSCALE_COMPUTE, workspace,
+                                      static_cast<hipStream_t>(stream)));
+}
+
 fp4_status fp4_dequantize(fp4_format fmt, const uint8_t* codes,
                           const uint8_t* scales, const float* tensor_scale,
                           int64_t rows, int64_t k, void* out,

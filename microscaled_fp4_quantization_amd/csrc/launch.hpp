@@ -22,6 +22,12 @@ hipError_t launch_quantize(int fmt, bool hadamard, const void* x, int dtype,
                            float* tscale, bool compute, void* workspace,
                            hipStream_t stream);
 
+// NVFP4 with the least-squared-error block scale; n = rows * k, a multiple
+// of 16.  Same workspace as launch_quantize in compute mode.
+hipError_t launch_quantize_mse(const void* x, int dtype, int64_t n, uint8_t* codes,
+                               uint8_t* scales, float* tscale, bool compute, void* workspace,
+                               hipStream_t stream);
+
 hipError_t launch_dequantize(int fmt, const uint8_t* codes,
                              const uint8_t* scales, const float* tscale,
                              int64_t n, void* out, int out_dtype,

@@ -265,6 +265,118 @@ __global__ __launch_bounds__(kSmallThreads) void quantize_small_kernel(
   }
 }
 
+// NVFP4 with the block scale of least squared error (aisyndicate.ch "FP4 auf
+// Blackwell", section "Was NVFP4 von frueheren 4-Bit-Formaten
+// unterscheidet": the E4M3 block scale is the factor that minimizes the mean
+// squared error over the block's 16 values).  A thread owns one block and
+// tries every positive finite E4M3 byte, 1 .. 126, in ascending order: each
+// quantizes the block as quantize_chunk does for that byte, its error
+// sum_i (x_i - v_i S_b)^2 is accumulated in fp64 in element order (v_i S_b is
+// exact in fp64, every other step rounds once), and only a strictly smaller
+// error replaces the best, so ties keep the smaller scale.  A block whose max
+// |x| is 0 keeps byte 0 and the sign bits, as in quantize_chunk.  The search
+// is compute-bound (about 10^4 fp64 operations per block); it is meant for
+// weights quantized once.
+constexpr int kMseThreads = 256;
+
+template <int DT, bool COMPUTE>
+__global__ __launch_bounds__(kMseThreads) void quantize_mse_kernel(
+    const void* __restrict__ x, int64_t nblocks, uint2* __restrict__ codes,
+    uint8_t* __restrict__ scales, float* __restrict__ tscale,
+    const float* __restrict__ partials, int npartials) {
+  float s_t;
+  if (COMPUTE) {
+    float m = 0.0f;
+    for (int i = threadIdx.x; i < npartials; i += kMseThreads) m = fmaxf(m, partials[i]);
+    const float A = block_max<kMseThreads>(m);
+    s_t = A / 2688.0f;                         // 6 * 448
+    if (s_t == 0.0f) s_t = 1.0f;
+    if (blockIdx.x == 0 && threadIdx.x == 0) *tscale = s_t;
+  } else {
+    s_t = *tscale;
+  }
+  const int64_t b = (int64_t)blockIdx.x * kMseThreads + threadIdx.x;
+  const bool valid = b < nblocks;
+  float v[16];
+  load_chunk<DT>(x, 2 * b, valid, v);
+  load_chunk<DT>(x, 2 * b + 1, valid, v + 8);
+  const float a = fmaxf(amax8(v), amax8(v + 8));
+
+  // byte 0 / sign bits for a zero block (and the start of the search)
+  uint32_t best_c = 0;
+  uint32_t best_w0 = e2m1_pack2<3>(e2m1_pack2<2>(e2m1_pack2<1>(e2m1_pack2<0>(0u, v[0] * 0.0f, v[1] * 0.0f),
+                                                              v[2] * 0.0f, v[3] * 0.0f),
+                                                 v[4] * 0.0f, v[5] * 0.0f),
+                                    v[6] * 0.0f, v[7] * 0.0f);
+  uint32_t best_w1 = e2m1_pack2<3>(e2m1_pack2<2>(e2m1_pack2<1>(e2m1_pack2<0>(0u, v[8] * 0.0f, v[9] * 0.0f),
+                                                              v[10] * 0.0f, v[11] * 0.0f),
+                                                 v[12] * 0.0f, v[13] * 0.0f),
+                                    v[14] * 0.0f, v[15] * 0.0f);
+  if (a != 0.0f) {
+    double best = __builtin_inf();
+    for (uint32_t c = 1; c < 127; ++c) {
+      const float S = e4m3_decode_pos(c) * s_t;
+      const float r = 1.0f / S;
+      if (!(S != 0.0f && r < __builtin_inff())) continue;     // uniform
+      float q[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) q[i] = v[i] * r;
+      uint32_t w[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        uint32_t t = e2m1_pack2<0>(0u, q[8 * h], q[8 * h + 1]);
+        t = e2m1_pack2<1>(t, q[8 * h + 2], q[8 * h + 3]);
+        t = e2m1_pack2<2>(t, q[8 * h + 4], q[8 * h + 5]);
+        w[h] = e2m1_pack2<3>(t, q[8 * h + 6], q[8 * h + 7]);
+      }
+      const double Sd = (double)S;
+      double err = 0.0;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const v2f p0 = e2m1_unpack2<0>(w[h]), p1 = e2m1_unpack2<1>(w[h]);
+        const v2f p2 = e2m1_unpack2<2>(w[h]), p3 = e2m1_unpack2<3>(w[h]);
+        const float dv[8] = {p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const double d = (double)v[8 * h + i] - (double)dv[i] * Sd;
+          err = err + d * d;
+        }
+      }
+      if (err < best) {
+        best = err;
+        best_c = c;
+        best_w0 = w[0];
+        best_w1 = w[1];
+      }
+    }
+  }
+  if (valid) {
+    codes[b] = make_uint2(best_w0, best_w1);
+    scales[b] = (uint8_t)best_c;
+  }
+}
+
+template <int DT>
+hipError_t launch_mse_typed(const void* x, int64_t nblocks, uint8_t* codes, uint8_t* scales,
+                            float* tscale, bool compute, void* workspace, hipStream_t stream) {
+  const int grid = (int)((nblocks + kMseThreads - 1) / kMseThreads);
+  uint2* codes64 = reinterpret_cast<uint2*>(codes);
+  if (compute) {
+    const int64_t nchunks = 2 * nblocks;
+    const int64_t trips = (nchunks + kChunksPerTrip - 1) / kChunksPerTrip;
+    const int g = (int)(trips < kMaxPartials ? trips : kMaxPartials);
+    float* partials = reinterpret_cast<float*>(workspace);
+    hipLaunchKernelGGL((amax_partial_kernel<DT, 0>), dim3(g), dim3(kThreads), 0, stream, x, nchunks,
+                       partials);
+    hipLaunchKernelGGL((quantize_mse_kernel<DT, true>), dim3(grid), dim3(kMseThreads), 0, stream, x,
+                       nblocks, codes64, scales, tscale, (const float*)partials, g);
+  } else {
+    hipLaunchKernelGGL((quantize_mse_kernel<DT, false>), dim3(grid), dim3(kMseThreads), 0, stream, x,
+                       nblocks, codes64, scales, tscale, (const float*)nullptr, 0);
+  }
+  return hipGetLastError();
+}
+
 template <int FMT, int DT, int HAD>
 hipError_t launch_typed(const void* x, int64_t nchunks, uint8_t* codes,
                         uint8_t* scales, float* tscale, bool compute,
@@ -324,4 +436,18 @@ hipError_t launch_quantize(int fmt, bool hadamard, const void* x, int dtype,
   }
   return hadamard ? launch_dtype<kFmtMX, 32>(dtype, x, nchunks, codes, scales, tscale, false, workspace, stream)
                   : launch_dtype<kFmtMX, 0>(dtype, x, nchunks, codes, scales, tscale, false, workspace, stream);
+}
+
+hipError_t launch_quantize_mse(const void* x, int dtype, int64_t n, uint8_t* codes,
+                               uint8_t* scales, float* tscale, bool compute, void* workspace,
+                               hipStream_t stream) {
+  const int64_t nblocks = n / 16;
+  switch (dtype) {
+    case kInF32:
+      return launch_mse_typed<kInF32>(x, nblocks, codes, scales, tscale, compute, workspace, stream);
+    case kInBF16:
+      return launch_mse_typed<kInBF16>(x, nblocks, codes, scales, tscale, compute, workspace, stream);
+    default:
+      return launch_mse_typed<kInF16>(x, nblocks, codes, scales, tscale, compute, workspace, stream);
+  }
 }

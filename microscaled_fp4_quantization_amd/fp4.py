@@ -27,7 +27,8 @@ _OUT_DTYPES = {"f32": (F32, torch.float32), "bf16": (BF16, torch.bfloat16),
 
 EXPORTS = ("fp4_status_string", "fp4_quantize_workspace_size", "fp4_quantize",
            "fp4_hadamard_quantize", "fp4_dequantize", "fp4_gemm_workspace_size",
-           "fp4_gemm", "fp4_quantize_gemm_workspace_size", "fp4_quantize_gemm")
+           "fp4_gemm", "fp4_quantize_gemm_workspace_size", "fp4_quantize_gemm",
+           "fp4_quantize_mse")
 
 _lib = None
 
@@ -56,6 +57,8 @@ def lib():
         f = getattr(L, name)
         f.argtypes = [i32, vp, i32, i64, i64, vp, vp, vp, i32, vp, sz, vp]
         f.restype = i32
+    L.fp4_quantize_mse.argtypes = [vp, i32, i64, i64, vp, vp, vp, i32, vp, sz, vp]
+    L.fp4_quantize_mse.restype = i32
     L.fp4_dequantize.argtypes = [i32, vp, vp, vp, i64, i64, vp, i32, vp]
     L.fp4_dequantize.restype = i32
     L.fp4_gemm_workspace_size.argtypes = [i32, i64, i64, i64]
@@ -118,6 +121,28 @@ def quantize(x, fmt="nvfp4", tensor_scale=None, hadamard=False, workspace=None):
     st = fn(f, _ptr(x), _IN_DTYPES[x.dtype], rows, k, _ptr(codes), _ptr(scales),
             _ptr(ts), mode, _ptr(workspace) if need else None, need, _stream(x))
     _check(st, "fp4_hadamard_quantize" if hadamard else "fp4_quantize")
+    return codes, scales, ts
+
+
+def quantize_mse(x, tensor_scale=None, workspace=None):
+    """NVFP4 quantization with the least-squared-error block scale (see
+    fp4_quantize_mse).  Arguments and result as quantize(x, "nvfp4", ...)."""
+    if x.dim() != 2:
+        raise ValueError("x must be [rows, k]")
+    rows, k = x.shape
+    codes = torch.empty((rows, k // 2), dtype=torch.uint8, device=x.device)
+    scales = torch.empty((rows, k // 16), dtype=torch.uint8, device=x.device)
+    if tensor_scale is None:
+        ts, mode = torch.empty(1, dtype=torch.float32, device=x.device), TSCALE_COMPUTE
+    else:
+        ts, mode = tensor_scale, TSCALE_GIVEN
+    L = lib()
+    need = L.fp4_quantize_workspace_size(NVFP4, mode, rows, k)
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    st = L.fp4_quantize_mse(_ptr(x), _IN_DTYPES[x.dtype], rows, k, _ptr(codes), _ptr(scales),
+                            _ptr(ts), mode, _ptr(workspace) if need else None, need, _stream(x))
+    _check(st, "fp4_quantize_mse")
     return codes, scales, ts
 
 

@@ -77,6 +77,27 @@ def test_quantize_rejects_bad_arguments(name):
     assert _q(f, rows=0, x=None, codes=None, scales=None) == fp4.OK
 
 
+def test_quantize_mse_rejects_bad_arguments():
+    f = fp4.lib().fp4_quantize_mse
+
+    def q(x=FAKE, dt=fp4.BF16, rows=4, k=64, codes=FAKE, scales=FAKE, ts=FAKE,
+          mode=fp4.TSCALE_GIVEN, ws=None, wsb=0):
+        return f(x, dt, rows, k, codes, scales, ts, mode, ws, wsb, None)
+
+    E = fp4.EINVAL
+    assert q(dt=fp4.E4M3) == E
+    assert q(k=40) == E                                  # k % 16
+    assert q(k=0) == E
+    assert q(rows=-1) == E
+    assert q(x=None) == E
+    assert q(codes=None) == E
+    assert q(ts=None) == E
+    assert q(x=FAKE_ODD) == E
+    assert q(mode=5) == E
+    assert q(mode=fp4.TSCALE_COMPUTE) == E               # no workspace
+    assert q(rows=0, x=None, codes=None, scales=None) == fp4.OK
+
+
 def test_dequantize_rejects_bad_arguments():
     f = fp4.lib().fp4_dequantize
     E = fp4.EINVAL
