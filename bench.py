@@ -16,6 +16,9 @@ every input already resident in HBM:
            GEMM vs the offline-rotated W [28672, 8192].
   kv       NVFP4 quantize of K and V [32*8*32768, 128] bf16 with their given
            tensor scales + dequantize of both to FP8 E4M3.
+  mse      NVFP4 quantization of the weight W [14336, 4096] bf16 with the
+           least-squared-error block scale (fp4_quantize_mse, tensor scale
+           computed from the data): compute-bound, fp64 error sums.
 Prints one JSON line.  The timed region is K steps back to back between one
 pair of HIP events (value, ms_per_step).  The dominant kernel is then timed
 the same way over the K steps' launches of it alone; its algorithmic bytes
@@ -36,6 +39,12 @@ sys.path.insert(0, ROOT)
 METRIC = "W4A4 NVFP4 GEMM TFLOPS + quantize GB/s, % of MI355X roofline"
 HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = {"fp4": 10100.0, "f16": 2500.0}
+# fp64 vector: 78.6 TFLOP/s counts a fused multiply-add as two; the search's
+# separate multiplies and adds issue at half that rate (256 CUs x 64 lanes x
+# 2.4 GHz = 39.3 T operations/s).
+FP64_PEAK_TOPS = 39.3
+MSE_CANDIDATES = 126            # positive finite E4M3 scale bytes
+MSE_FLOPS_PER_VALUE = 4         # per candidate: v S_b, x - ., d d, err + .
 MALL_BYTES = 256 << 20
 
 
@@ -45,7 +54,7 @@ def parse():
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", default="decode",
-                   choices=["decode", "prefill", "rotated_nv", "rotated_mx", "kv"])
+                   choices=["decode", "prefill", "rotated_nv", "rotated_mx", "kv", "mse"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--copy-bytes", type=int, default=0,
@@ -64,8 +73,9 @@ DOMINANT = {
     "decode": ("gemm_nv_stream", ["gemm_skinny.hip"]),
     "prefill": ("gemm_large<0", ["gemm_large.hip"]),
     "rotated_nv": ("gemm_large<0", ["gemm_large.hip"]),
-    "rotated_mx": ("gemm_large<1", ["gemm_large.hip"]),
+    "rotated_mx": ("gemm_large_mx<", ["gemm_large.hip"]),
     "kv": ("quantize_kernel<0, 1, 0, false>", ["quantize.hip", "device_common.hpp"]),
+    "mse": ("quantize_mse_kernel<1, true>", ["quantize.hip", "device_common.hpp"]),
 }
 COPY_KERNEL = "copyBuffer"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
@@ -170,6 +180,15 @@ class Lib:
         fn = self.L.fp4_quantize_gemm
         return lambda: self.check(fn(*args), "quantize_gemm")
 
+    def quantize_mse_call(self, x, codes, scales, ts, mode, ws):
+        from microscaled_fp4_quantization_amd import fp4
+        dt = {self.torch.bfloat16: fp4.BF16, self.torch.float32: fp4.F32, self.torch.float16: fp4.F16}[x.dtype]
+        need = self.L.fp4_quantize_workspace_size(fp4.NVFP4, mode, x.shape[0], x.shape[1])
+        args = (self.p(x), dt, x.shape[0], x.shape[1], self.p(codes), self.p(scales), self.p(ts), mode,
+                self.p(ws) if need else None, need, self.stream)
+        fn = self.L.fp4_quantize_mse
+        return lambda: self.check(fn(*args), "quantize_mse")
+
     def dequant_call(self, fmt, codes, scales, ts, out, out_dtype):
         rows, k = codes.shape[0], codes.shape[1] * 2
         args = (fmt, self.p(codes), self.p(scales), self.p(ts), rows, k, self.p(out), out_dtype, self.stream)
@@ -255,6 +274,24 @@ def setup(workload, torch, fq, lib):
                  else "e2m1 x e4m3 -> f16 mfma, f32 acc",
                  host=dict(x=x.float().cpu().numpy(), w=w.float().cpu().numpy(), fmt=fmt,
                            hadamard=True))
+    elif workload == "mse":
+        w = workloads.decode(device=dev)["w"]
+        n, k = w.shape
+        codes = torch.empty((n, k // 2), dtype=torch.uint8, device=dev)
+        scales = torch.empty((n, k // 16), dtype=torch.uint8, device=dev)
+        ts = torch.empty(1, dtype=torch.float32, device=dev)
+        ws = torch.empty(4096, dtype=torch.uint8, device=dev)
+        q = lib.quantize_mse_call(w, codes, scales, ts, fp4.TSCALE_COMPUTE, ws)
+        nblocks = n * k // 16
+        W.update(pre=[], dominant=[q], post=[], flops=0,
+                 dom_name="fp4_quantize_mse (NVFP4, bf16 [%d, %d])" % (n, k),
+                 dom_units=nblocks * MSE_CANDIDATES * 16 * MSE_FLOPS_PER_VALUE,
+                 dom_bound="alu", dom_peak=FP64_PEAK_TOPS,
+                 quant_bytes=quant_bytes(n, k, "nvfp4", 2),
+                 config={"workload": "mse", "rows": n, "k": k, "format": "nvfp4",
+                         "scale_rule": "least squared error", "x_dtype": "bf16"},
+                 dtype="f32 quantize, f64 error sums",
+                 host=dict(w=w))
     else:  # kv
         d = workloads.kv(device=dev)
         calls_q, calls_d, outs = [], [], []
@@ -293,6 +330,20 @@ def cpu_baseline(workload, W, seconds):
     except Exception:
         cores = 1
     h = W["host"]
+    if workload == "mse":
+        rows = 32                        # bounded sample: the first rows of W
+        x = h["w"][:rows].float().cpu().numpy()
+        st = oracle.nvfp4_tensor_scale(h["w"].float().cpu().numpy())
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            oracle.nvfp4_quantize_mse(x, st)
+            reps += 1
+            if time.perf_counter() - t0 >= seconds:
+                break
+        dt = (time.perf_counter() - t0) / reps
+        return {"value": rows * x.shape[1] * 2.5625 / dt / 1e9, "unit": "GB/s", "cores": 1,
+                "kind": "oracle", "sample": "MSE quantize of %d of the %d W rows, %d reps" % (
+                    rows, h["w"].shape[0], reps)}
     if workload == "kv":
         # bounded sample: the first rows of K, quantized and dequantized
         rows = 1 << 16
@@ -434,11 +485,17 @@ def main():
     if W["dom_bound"] == "hbm":
         achieved = W["dom_units"] / (dom_avg * 1e-3) / 1e9
         unit = "GB/s"
+    elif W["dom_bound"] == "alu":
+        achieved = W["dom_units"] / (dom_avg * 1e-3) / 1e12
+        unit = "TFLOP/s (fp64, unfused)"
     else:
         achieved = W["dom_units"] / (dom_avg * 1e-3) / 1e12
         unit = "TFLOP/s"
     if args.workload == "kv":
         value = 2 * (W["quant_bytes"] + W["dequant_bytes"]) / (ms_step * 1e-3) / 1e9
+        vunit = "GB/s"
+    elif args.workload == "mse":
+        value = W["quant_bytes"] / (ms_step * 1e-3) / 1e9
         vunit = "GB/s"
     else:
         value = W["flops"] / (ms_step * 1e-3) / 1e12
@@ -462,7 +519,7 @@ def main():
         "host_enqueue_ms_per_step": round(enqueue_s * 1e3 / args.steps, 4),
         "gpu_fed_by_host": bool(gpu_fed),
     }
-    if args.workload != "kv":
+    if args.workload not in ("kv", "mse"):
         out["quantize_bytes_per_step"] = W["quant_bytes"]
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.workload, W, args.cpu_seconds)
