@@ -34,6 +34,8 @@ Parity status per function (what pins it in the CPU tests):
   dequantize                  hand-built golden tensors, exact-rational check
   hadamard_blocks             scipy.linalg.hadamard matmul, involution
   gemm_ref                    integer matmul special case, Fraction brute force
+  gemm_w4a16_ref              integer special case, Fraction brute force,
+                              equals gemm_ref when X is itself NVFP4-exact
 """
 
 from .formats import (
@@ -63,7 +65,7 @@ from .quant import (
     unpack_nibbles,
 )
 from .hadamard import hadamard_blocks, HADAMARD_NORM
-from .gemm import gemm_ref, gemm_ref_entries
+from .gemm import gemm_ref, gemm_ref_entries, gemm_w4a16_ref
 
 __all__ = [
     "E2M1_MAGNITUDES", "e2m1_decode", "e2m1_encode", "e4m3_decode",
@@ -71,5 +73,5 @@ __all__ = [
     "bf16_round", "NV_BLOCK", "MX_BLOCK", "NV_TSCALE_DIVISOR",
     "nvfp4_tensor_scale", "nvfp4_tensor_scale_from_amax", "nvfp4_quantize", "nvfp4_quantize_mse", "nvfp4_mse_block_error", "mxfp4_quantize", "dequantize",
     "dequantize_exact_f64", "pack_nibbles", "unpack_nibbles",
-    "hadamard_blocks", "HADAMARD_NORM", "gemm_ref", "gemm_ref_entries",
+    "hadamard_blocks", "HADAMARD_NORM", "gemm_ref", "gemm_ref_entries", "gemm_w4a16_ref",
 ]

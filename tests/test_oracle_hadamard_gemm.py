@@ -130,3 +130,66 @@ def test_gemm_matches_exact_triple_loop(fmt):
             assert abs(Fraction(C[i, j]) - exact[i][j]) <= abs(exact[i][j]) * Fraction(1, 2 ** 45) + Fraction(1, 2 ** 80)
     ent = oracle.gemm_ref_entries(fmt, pa, sa, ta, pb, sb, tb, [0, 2, 1], [3, 0, 1])
     assert np.allclose(ent, [C[0, 3], C[2, 0], C[1, 1]], rtol=1e-12, atol=0)
+
+
+# --- W4A16 --------------------------------------------------------------------
+
+def test_w4a16_integer_special_case():
+    # MXFP4 weights with scale code 127 (scale 1) are half-integers 2v in
+    # [-12, 12]/2; integer activations: 2 C is an integer matmul, exactly.
+    rng = np.random.default_rng(21)
+    m, n, k = 5, 7, 256
+    x = rng.integers(-50, 51, size=(m, k)).astype(np.float32)
+    cb = rng.integers(0, 16, size=(n, k)).astype(np.uint8)
+    pb = oracle.pack_nibbles(cb)
+    sb = np.full((n, k // 32), 127, dtype=np.uint8)
+    C = oracle.gemm_w4a16_ref("mxfp4", x, pb, sb, None)
+    ib = (2 * oracle.e2m1_decode(cb)).astype(np.int64)
+    assert np.array_equal((2 * C).astype(np.int64), x.astype(np.int64) @ ib.T)
+    assert np.array_equal(2 * C, (x.astype(np.int64) @ ib.T).astype(np.float64))
+
+
+@pytest.mark.parametrize("fmt", ["nvfp4", "mxfp4"])
+def test_w4a16_matches_exact_triple_loop(fmt):
+    rng = np.random.default_rng(22)
+    x = rng.standard_normal((3, 64)).astype(np.float32)
+    w = (rng.standard_normal((4, 64)) * 0.05).astype(np.float32)
+    if fmt == "nvfp4":
+        pb, sb, tb = oracle.nvfp4_quantize(w)
+    else:
+        (pb, sb), tb = oracle.mxfp4_quantize(w), None
+    C = oracle.gemm_w4a16_ref(fmt, x, pb, sb, tb)
+    cb = oracle.unpack_nibbles(pb)
+    mags = [Fraction(0), Fraction(1, 2), Fraction(1), Fraction(3, 2), Fraction(2), Fraction(3), Fraction(4), Fraction(6)]
+    bs = 16 if fmt == "nvfp4" else 32
+    for i in range(3):
+        for j in range(4):
+            acc = Fraction(0)
+            for kk in range(64):
+                c = int(cb[j, kk])
+                v = -mags[c & 7] if c & 8 else mags[c & 7]
+                s = int(sb[j, kk // bs])
+                if fmt == "mxfp4":
+                    sc = Fraction(2) ** (s - 127)
+                else:
+                    e, mt = (s >> 3) & 15, s & 7
+                    sc = Fraction(mt, 512) if e == 0 else (1 + Fraction(mt, 8)) * Fraction(2) ** (e - 7)
+                acc += Fraction(float(x[i, kk])) * v * sc
+            exact = acc * (Fraction(float(tb)) if tb is not None else 1)
+            assert abs(Fraction(C[i, j]) - exact) <= abs(exact) * Fraction(1, 2 ** 40) + Fraction(1, 2 ** 80)
+
+
+def test_w4a16_equals_w4a4_on_quantized_activations():
+    # when the activations are exactly an NVFP4 tensor's values, W4A16 and
+    # W4A4 compute the same product (tensor scale 1: the values v * E4M3 have
+    # at most 6 significant bits, so float32 holds them exactly)
+    rng = np.random.default_rng(23)
+    x0 = rng.standard_normal((4, 128)).astype(np.float32)
+    w = (rng.standard_normal((6, 128)) * 0.02).astype(np.float32)
+    pa, sa, ta = oracle.nvfp4_quantize(x0, np.float32(1.0))
+    x = oracle.dequantize("nvfp4", pa, sa, ta, "f32")
+    assert np.array_equal(oracle.dequantize_exact_f64("nvfp4", pa, sa, ta), x.astype(np.float64))
+    pb, sb, tb = oracle.nvfp4_quantize(w)
+    a = oracle.gemm_w4a16_ref("nvfp4", x, pb, sb, tb)
+    b = oracle.gemm_ref("nvfp4", pa, sa, ta, pb, sb, tb)
+    assert np.allclose(a, b, rtol=1e-13, atol=1e-300)
