@@ -16,6 +16,9 @@ every input already resident in HBM:
            GEMM vs the offline-rotated W [28672, 8192].
   kv       NVFP4 quantize of K and V [32*8*32768, 128] bf16 with their given
            tensor scales + dequantize of both to FP8 E4M3.
+  w4a16    W4A16 decode: X bf16 [8, 4096] as it is times the NVFP4 weight
+           W [14336, 4096] (fp4_gemm_w4a16), bf16 out; weight copies cycled
+           as for decode.
   mse      NVFP4 quantization of the weight W [14336, 4096] bf16 with the
            least-squared-error block scale (fp4_quantize_mse, tensor scale
            computed from the data): compute-bound, fp64 error sums.
@@ -54,7 +57,7 @@ def parse():
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", default="decode",
-                   choices=["decode", "prefill", "rotated_nv", "rotated_mx", "kv", "mse"])
+                   choices=["decode", "prefill", "rotated_nv", "rotated_mx", "kv", "mse", "w4a16"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--copy-bytes", type=int, default=0,
@@ -70,12 +73,13 @@ def parse():
 # sources its code comes from: a recorded HBM traffic figure is used only
 # while these files are unchanged.
 DOMINANT = {
-    "decode": ("gemm_nv_stream", ["gemm_skinny.hip"]),
+    "decode": ("gemm_nv_stream<2, 1>", ["gemm_skinny.hip"]),
     "prefill": ("gemm_large<0", ["gemm_large.hip"]),
     "rotated_nv": ("gemm_large<0", ["gemm_large.hip"]),
     "rotated_mx": ("gemm_large_mx<", ["gemm_large.hip"]),
     "kv": ("quantize_kernel<0, 1, 0, false>", ["quantize.hip", "device_common.hpp"]),
     "mse": ("quantize_mse_kernel<1, true>", ["quantize.hip", "device_common.hpp"]),
+    "w4a16": ("gemm_nv_stream<2, 2>", ["gemm_skinny.hip"]),
 }
 COPY_KERNEL = "copyBuffer"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
@@ -189,6 +193,16 @@ class Lib:
         fn = self.L.fp4_quantize_mse
         return lambda: self.check(fn(*args), "quantize_mse")
 
+    def w4a16_call(self, fmt, x, b, c, c_dtype):
+        from microscaled_fp4_quantization_amd import fp4
+        bc, bsc, bt = b
+        m, k, n = x.shape[0], x.shape[1], bc.shape[0]
+        dt = {self.torch.bfloat16: fp4.BF16, self.torch.float32: fp4.F32, self.torch.float16: fp4.F16}[x.dtype]
+        args = (fmt, self.p(x), dt, m, n, k, self.p(bc), self.p(bsc), self.p(bt), self.p(c), c_dtype,
+                self.stream)
+        fn = self.L.fp4_gemm_w4a16
+        return lambda: self.check(fn(*args), "gemm_w4a16")
+
     def dequant_call(self, fmt, codes, scales, ts, out, out_dtype):
         rows, k = codes.shape[0], codes.shape[1] * 2
         args = (fmt, self.p(codes), self.p(scales), self.p(ts), rows, k, self.p(out), out_dtype, self.stream)
@@ -274,6 +288,25 @@ def setup(workload, torch, fq, lib):
                  else "e2m1 x e4m3 -> f16 mfma, f32 acc",
                  host=dict(x=x.float().cpu().numpy(), w=w.float().cpu().numpy(), fmt=fmt,
                            hadamard=True))
+    elif workload == "w4a16":
+        d = workloads.decode(device=dev)
+        x, w = d["x"], d["w"]
+        m, k = x.shape
+        n = w.shape[0]
+        wq = fq.quantize(w, "nvfp4")
+        copies = max(1, -(-2 * MALL_BYTES // (n * k // 2 + n * k // 16)))
+        wqs = [wq] + [tuple(t.clone() for t in wq) for _ in range(copies - 1)]
+        c = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+        gs = [lib.w4a16_call(NV, x, wqi, c, fp4.BF16) for wqi in wqs]
+        per = (n * (k // 2 + k // 16) + 4) + 2 * m * k + 2 * m * n
+        W.update(pre=[], dominant=gs, post=[], flops=2 * m * n * k,
+                 dom_name="fp4_gemm_w4a16 (NVFP4 weights, bf16 X, m=%d)" % m, dom_units=per,
+                 dom_bound="hbm", dom_peak=HBM_PEAK_GBS, quant_bytes=0,
+                 config={"workload": "w4a16", "m": m, "n": n, "k": k, "format": "nvfp4",
+                         "x_dtype": "bf16", "out_dtype": "bf16", "weight_copies": copies},
+                 dtype="e2m1 x e4m3 -> f16, bf16 X -> f16 (power-of-two prescale), f16 mfma, f32 acc",
+                 host=dict(x=x.float().cpu().numpy(), w=w.float().cpu().numpy(), fmt="nvfp4",
+                           hadamard=False, w4a16=True))
     elif workload == "mse":
         w = workloads.decode(device=dev)["w"]
         n, k = w.shape
@@ -362,6 +395,18 @@ def cpu_baseline(workload, W, seconds):
                 "sample": "quantize + FP8 dequantize of %d of the 2^23 K rows, %d reps" % (rows, reps)}
     fmt = h["fmt"]
     x, w = h["x"], h["w"]
+    if h.get("w4a16"):
+        pw, sw, tw = oracle.nvfp4_quantize(w)
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            oracle.gemm_w4a16_ref(fmt, x, pw, sw, tw)
+            reps += 1
+            if time.perf_counter() - t0 >= seconds:
+                break
+        dt = (time.perf_counter() - t0) / reps
+        return {"value": 2.0 * x.shape[0] * w.shape[0] * w.shape[1] / dt / 1e12, "unit": "TFLOP/s",
+                "cores": cores, "kind": "oracle",
+                "sample": "w4a16 step (X %dx%d, W %dx%d), %d reps" % (x.shape + w.shape + (reps,))}
     if workload in ("prefill", "rotated_nv", "rotated_mx"):
         x = x[:64]                        # bounded sample: 64 activation rows
     b = 16 if fmt == "nvfp4" else 32
@@ -519,7 +564,7 @@ def main():
         "host_enqueue_ms_per_step": round(enqueue_s * 1e3 / args.steps, 4),
         "gpu_fed_by_host": bool(gpu_fed),
     }
-    if args.workload not in ("kv", "mse"):
+    if args.workload not in ("kv", "mse", "w4a16"):
         out["quantize_bytes_per_step"] = W["quant_bytes"]
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.workload, W, args.cpu_seconds)

@@ -204,6 +204,34 @@ fp4_status fp4_gemm(fp4_format fmt, int64_t m, int64_t n, int64_t k,
                     fp4_dtype c_dtype, void* workspace, size_t workspace_bytes,
                     void* stream);
 
+/*
+ * fp4_gemm_w4a16 -- C = X B^T with 16-bit activations and 4-bit weights.
+ * Defines: W4A16, where only the weights are 4-bit and the products stay
+ * 16-bit -- the form that speeds up token-by-token generation, whose
+ * bottleneck is reading the weights (pimento.cloud "FP8, NVFP4 czy AWQ?",
+ * section "Dlaczego W8A8 i W4A16 to nie to samo?").
+ *   fmt           FP4_NVFP4 or FP4_MXFP4 (the weights' format).
+ *   x, x_dtype    activations [m, k], FP4_BF16 / FP4_F16 / FP4_F32,
+ *                 row-major, aligned to their element size.
+ *   b_*           weights [n, k] as fp4_gemm's B; b_tscale NVFP4 only.
+ *   c, c_dtype    out [m, n], FP4_F32 or FP4_BF16 (FP4_F16 / FP4_E4M3:
+ *                 FP4_EUNSUPPORTED).
+ *   Numerics: the weights are widened exactly (v * E4M3 scale in fp16 or
+ *   fp32, v * 2^e); NVFP4 with bf16 X, k in {2048, 4096} and 16-byte aligned
+ *   x / codes / scales takes the streaming path: X is scaled by the power of
+ *   two that brings max |X| into [1, 2) and rounded to fp16 (exact for every
+ *   value above 2^-15 max |X|), the products accumulate in fp32 on the matrix
+ *   cores and C is scaled back; other shapes sum fp32 products.  Tolerance
+ *   against the float64 reference: relative Frobenius error <= 1e-3.
+ *   m = 0 or n = 0 enqueues nothing.  Returns FP4_OK, FP4_EINVAL,
+ *   FP4_EUNSUPPORTED or FP4_EHIP.
+ */
+fp4_status fp4_gemm_w4a16(fp4_format fmt, const void* x, fp4_dtype x_dtype,
+                          int64_t m, int64_t n, int64_t k,
+                          const uint8_t* b_codes, const uint8_t* b_scales,
+                          const float* b_tscale, void* c, fp4_dtype c_dtype,
+                          void* stream);
+
 /* Bytes of device workspace fp4_quantize_gemm needs for these sizes. */
 size_t fp4_quantize_gemm_workspace_size(fp4_format fmt, int64_t m, int64_t n,
                                         int64_t k);

@@ -5,6 +5,8 @@ include/fp4.h); `fp4` is its Python binding.
 """
 
 from . import fp4
-from .fp4 import quantize, quantize_mse, hadamard_quantize, dequantize, gemm, quantize_gemm, lib
+from .fp4 import (quantize, quantize_mse, hadamard_quantize, dequantize, gemm, gemm_w4a16,
+                  quantize_gemm, lib)
 
-__all__ = ["fp4", "quantize", "quantize_mse", "hadamard_quantize", "dequantize", "gemm", "quantize_gemm", "lib"]
+__all__ = ["fp4", "quantize", "quantize_mse", "hadamard_quantize", "dequantize", "gemm", "gemm_w4a16",
+           "quantize_gemm", "lib"]

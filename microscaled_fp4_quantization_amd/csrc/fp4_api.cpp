@@ -174,6 +174,30 @@ fp4_status fp4_gemm(fp4_format fmt, int64_t m, int64_t n, int64_t k,
                               workspace, static_cast<hipStream_t>(stream)));
 }
 
+fp4_status fp4_gemm_w4a16(fp4_format fmt, const void* x, fp4_dtype x_dtype, int64_t m, int64_t n,
+                          int64_t k, const uint8_t* b_codes, const uint8_t* b_scales,
+                          const float* b_tscale, void* c, fp4_dtype c_dtype, void* stream) {
+  if (!valid_format(fmt)) return FP4_EINVAL;
+  if (x_dtype != FP4_F32 && x_dtype != FP4_BF16 && x_dtype != FP4_F16) return FP4_EINVAL;
+  if (c_dtype != FP4_F32 && c_dtype != FP4_BF16) {
+    return (c_dtype == FP4_F16 || c_dtype == FP4_E4M3) ? FP4_EUNSUPPORTED : FP4_EINVAL;
+  }
+  if (m < 0 || n < 0 || k <= 0 || k % block_of(fmt) != 0) return FP4_EINVAL;
+  if ((m > 0 && k > kMaxElements / m) || (n > 0 && k > kMaxElements / n)) return FP4_EINVAL;
+  if (m > 0 && n > kMaxElements / m) return FP4_EINVAL;
+  if (m == 0 || n == 0) return FP4_OK;
+  if (!x || !b_codes || !b_scales || !c) return FP4_EINVAL;
+  const int xs = x_dtype == FP4_F32 ? 4 : 2;
+  if (!aligned(x, xs) || !aligned(b_codes, 4) || !aligned(c, c_dtype == FP4_F32 ? 4 : 2)) return FP4_EINVAL;
+  if (fmt == FP4_NVFP4) {
+    if (!b_tscale || !aligned(b_tscale, 4)) return FP4_EINVAL;
+  } else if (b_tscale) {
+    return FP4_EINVAL;
+  }
+  return from_hip(launch_gemm_w4a16((int)fmt, m, n, k, x, (int)x_dtype, b_codes, b_scales,
+                                    b_tscale, c, (int)c_dtype, static_cast<hipStream_t>(stream)));
+}
+
 size_t fp4_quantize_gemm_workspace_size(fp4_format fmt, int64_t m, int64_t n, int64_t k) {
   if (!valid_format(fmt)) return 0;
   const size_t q = fp4_quantize_workspace_size(fmt, FP4_TSCALE_COMPUTE, m, k);

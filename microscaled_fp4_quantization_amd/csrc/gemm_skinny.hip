@@ -358,13 +358,25 @@ struct StreamLds {
   uint8_t w[kStrWaves][16 * kStrTiles][kStrPitch];    // weight scale slices
 };
 
-// QX: the activations come in as bf16 X [m, k] (`a`) and are quantized here,
-// NVFP4 with the tensor scale computed from the data, exactly as
-// quantize_chunk does it: every workgroup reduces max |X| over the whole
-// tensor (16 slices, one per wave) and quantizes its own slices; workgroup 0
-// also writes the codes, scales and tensor scale out (qcodes, qscales,
-// qtscale).  `as` and `at` are unused then.
-template <int NSTEP, bool QX>
+// The activations (XM):
+//   kXCodes  NVFP4 codes, scales and tensor scale (`a`, `as`, `at`).
+//   kXQuant  bf16 X [m, k] (`a`), quantized here to NVFP4 with the tensor
+//            scale computed from the data, exactly as quantize_chunk does it:
+//            every workgroup reduces max |X| over the whole tensor (16
+//            slices, one per wave) and quantizes its own slices; workgroup 0
+//            also writes the codes, scales and tensor scale out (qcodes,
+//            qscales, qtscale).
+//   kXRaw    bf16 X [m, k] (`a`) used as it is: W4A16 (pimento.cloud "FP8,
+//            NVFP4 czy AWQ?", section "Dlaczego W8A8 i W4A16 to nie to
+//            samo?": only the weights are 4-bit, the products stay 16-bit).
+//            X is scaled by the power of two 2^-E that brings max |X| into
+//            [1, 2) (reduced as for kXQuant) and rounded to fp16: exact for
+//            every value above 2^-15 max |X| (bf16 has 8 significant bits, fp16
+//            11), the rest within 2^-25 max |X|; C is scaled back by 2^E.
+// `as` and `at` are unused but for kXCodes.
+constexpr int kXCodes = 0, kXQuant = 1, kXRaw = 2;
+
+template <int NSTEP, int XM>
 __global__ __launch_bounds__(64 * kStrWaves) void gemm_nv_stream(
     int m, int64_t n, int k, int rows_per_wg, const uint8_t* __restrict__ a,
     const uint8_t* __restrict__ as, const float* __restrict__ at,
@@ -373,6 +385,7 @@ __global__ __launch_bounds__(64 * kStrWaves) void gemm_nv_stream(
     uint8_t* __restrict__ qcodes, uint8_t* __restrict__ qscales, float* __restrict__ qtscale) {
   __shared__ StreamLds L;
   __shared__ float red[kStrWaves];
+  constexpr bool QX = XM != kXCodes;                  // bf16 X loaded here
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = lane & 15, g = lane >> 4;
@@ -483,33 +496,48 @@ __global__ __launch_bounds__(64 * kStrWaves) void gemm_nv_stream(
     float s_t = A / 2688.0f;                          // 6 * 448
     if (s_t == 0.0f) s_t = 1.0f;
     const float dd = 6.0f * s_t;
-    xscale = s_t;
+    xscale = s_t;                                    // kXRaw: replaced below
     const bool out = blockIdx.x == 0 && live;
+    if (XM == kXRaw) {
+      // 2^-E with max |X| in [2^E, 2^(E+1)); 1 for a zero tensor
+      const int eb = (int)(as_u(A) >> 23);
+      const int pe = A == 0.0f ? 127 : (254 - eb < 1 ? 1 : 254 - eb);
+      const float p2 = as_f((uint32_t)pe << 23);
+      xscale = as_f((uint32_t)(254 - pe) << 23);        // 2^E, exact
 #pragma unroll
-    for (int bl = 0; bl < NSTEP; ++bl) {
-      const uint32_t sbyte = e4m3_encode_pos(am[bl] / dd);
-      const float S = e4m3_decode_pos(sbyte) * s_t;
-      float r = 1.0f / S;
-      if (!(S != 0.0f && r < __builtin_inff())) r = 0.0f;   // zero block or overflowing reciprocal
-      uint32_t wd[2];
+      for (int i = 0; i < 2 * NSTEP; ++i) {
+        v8h f;
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const float* q = &xv[16 * bl + 8 * h];
-        uint32_t w = e2m1_pack2<0>(0u, q[0] * r, q[1] * r);
-        w = e2m1_pack2<1>(w, q[2] * r, q[3] * r);
-        w = e2m1_pack2<2>(w, q[4] * r, q[5] * r);
-        w = e2m1_pack2<3>(w, q[6] * r, q[7] * r);
-        wd[h] = w;
-        v8h f = dequant8(w, (_Float16)e4m3_decode_pos(sbyte));
-        if (!live) f = (v8h){0, 0, 0, 0, 0, 0, 0, 0};
-        *reinterpret_cast<v8h*>(&L.x[wave][xrow][16 * NSTEP * xc + 16 * bl + 8 * h]) = f;
+        for (int j = 0; j < 8; ++j) f[j] = live ? (_Float16)(xv[8 * i + j] * p2) : (_Float16)0.0f;
+        *reinterpret_cast<v8h*>(&L.x[wave][xrow][16 * NSTEP * xc + 8 * i]) = f;
       }
-      if (out) {
-        *reinterpret_cast<u32x2*>(qcodes + xsrc * kbytes + (xv0 + 16 * bl) / 2) = (u32x2){wd[0], wd[1]};
-        qscales[xsrc * kblocks + (xv0 + 16 * bl) / 16] = (uint8_t)sbyte;
+    } else {
+#pragma unroll
+      for (int bl = 0; bl < NSTEP; ++bl) {
+        const uint32_t sbyte = e4m3_encode_pos(am[bl] / dd);
+        const float S = e4m3_decode_pos(sbyte) * s_t;
+        float r = 1.0f / S;
+        if (!(S != 0.0f && r < __builtin_inff())) r = 0.0f;   // zero block or overflowing reciprocal
+        uint32_t wd[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const float* q = &xv[16 * bl + 8 * h];
+          uint32_t w = e2m1_pack2<0>(0u, q[0] * r, q[1] * r);
+          w = e2m1_pack2<1>(w, q[2] * r, q[3] * r);
+          w = e2m1_pack2<2>(w, q[4] * r, q[5] * r);
+          w = e2m1_pack2<3>(w, q[6] * r, q[7] * r);
+          wd[h] = w;
+          v8h f = dequant8(w, (_Float16)e4m3_decode_pos(sbyte));
+          if (!live) f = (v8h){0, 0, 0, 0, 0, 0, 0, 0};
+          *reinterpret_cast<v8h*>(&L.x[wave][xrow][16 * NSTEP * xc + 16 * bl + 8 * h]) = f;
+        }
+        if (out) {
+          *reinterpret_cast<u32x2*>(qcodes + xsrc * kbytes + (xv0 + 16 * bl) / 2) = (u32x2){wd[0], wd[1]};
+          qscales[xsrc * kblocks + (xv0 + 16 * bl) / 16] = (uint8_t)sbyte;
+        }
       }
     }
-    if (blockIdx.x == 0 && tid == 0) *qtscale = s_t;
+    if (XM == kXQuant && blockIdx.x == 0 && tid == 0) *qtscale = s_t;
     store_ws();
   } else {
     const bool live = xrow < m;
@@ -571,6 +599,47 @@ __global__ __launch_bounds__(64 * kStrWaves) void gemm_nv_stream(
   }
 }
 
+// W4A16 for any shape: thread -> one weight row j and up to 8 activation
+// rows; the weights are widened exactly in fp32 (v * E4M3 scale, or v * 2^e)
+// and the products summed in fp32.  The fallback of the streaming kernel.
+template <int FMT, int DT>
+__global__ __launch_bounds__(256) void gemm_w4a16_simple(
+    int m, int64_t n, int k, const void* __restrict__ x, const uint8_t* __restrict__ b,
+    const uint8_t* __restrict__ bs, const float* __restrict__ bt, void* __restrict__ c,
+    int c_dtype) {
+  constexpr int BS = FMT == kFmtNV ? 16 : 32;
+  const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int i0 = blockIdx.y * 8;
+  if (j >= n) return;
+  const int rows = m - i0 < 8 ? m - i0 : 8;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  const uint8_t* wr = b + j * (int64_t)(k / 2);
+  const uint8_t* sr = bs + j * (int64_t)(k / BS);
+  for (int kb = 0; kb < k; kb += BS) {
+    const uint32_t sb = sr[kb / BS];
+    const float S = FMT == kFmtNV ? e4m3_decode_pos(sb) : as_f(sb == 0 ? 0x00400000u : sb << 23);
+    for (int t = 0; t < BS; t += 8) {
+      const uint32_t w = *reinterpret_cast<const uint32_t*>(wr + (kb + t) / 2);
+      const v2f p0 = e2m1_unpack2<0>(w), p1 = e2m1_unpack2<1>(w);
+      const v2f p2 = e2m1_unpack2<2>(w), p3 = e2m1_unpack2<3>(w);
+      const float wv[8] = {p0.x * S, p0.y * S, p1.x * S, p1.y * S, p2.x * S, p2.y * S, p3.x * S, p3.y * S};
+      for (int i = 0; i < rows; ++i) {
+        const int64_t xo = (int64_t)(i0 + i) * k + kb + t;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          float xv;
+          if (DT == kInF32) xv = reinterpret_cast<const float*>(x)[xo + e];
+          else if (DT == kInBF16) xv = as_f((uint32_t)reinterpret_cast<const uint16_t*>(x)[xo + e] << 16);
+          else xv = (float)reinterpret_cast<const _Float16*>(x)[xo + e];
+          acc[i] = acc[i] + xv * wv[e];
+        }
+      }
+    }
+  }
+  const float ts = FMT == kFmtNV ? *bt : 1.0f;
+  for (int i = 0; i < rows; ++i) store_out(c, c_dtype, (int64_t)(i0 + i) * n + j, acc[i] * ts);
+}
+
 }  // namespace
 
 hipError_t launch_gemm_skinny(int fmt, int64_t m, int64_t n, int64_t k,
@@ -586,11 +655,11 @@ hipError_t launch_gemm_skinny(int fmt, int64_t m, int64_t n, int64_t k,
     const int rows = (int)(8 * ((n + 2047) / 2048));
     const dim3 grid((unsigned)((n + rows - 1) / rows));
     if (k == 4096)
-      hipLaunchKernelGGL((gemm_nv_stream<2, false>), grid, dim3(64 * kStrWaves), 0, stream, (int)m, n,
+      hipLaunchKernelGGL((gemm_nv_stream<2, kXCodes>), grid, dim3(64 * kStrWaves), 0, stream, (int)m, n,
                          (int)k, rows, a_codes, a_scales, a_tscale, b_codes, b_scales, b_tscale, c,
                          c_dtype, nullptr, nullptr, nullptr);
     else
-      hipLaunchKernelGGL((gemm_nv_stream<1, false>), grid, dim3(64 * kStrWaves), 0, stream, (int)m, n,
+      hipLaunchKernelGGL((gemm_nv_stream<1, kXCodes>), grid, dim3(64 * kStrWaves), 0, stream, (int)m, n,
                          (int)k, rows, a_codes, a_scales, a_tscale, b_codes, b_scales, b_tscale, c,
                          c_dtype, nullptr, nullptr, nullptr);
     return hipGetLastError();
@@ -628,13 +697,58 @@ bool launch_quantize_gemm_decode(int64_t m, int64_t n, int64_t k, const void* x,
   const int rows = (int)(8 * ((n + 2047) / 2048));
   const dim3 grid((unsigned)((n + rows - 1) / rows));
   if (k == 4096)
-    hipLaunchKernelGGL((gemm_nv_stream<2, true>), grid, dim3(64 * kStrWaves), 0, stream, (int)m, n,
+    hipLaunchKernelGGL((gemm_nv_stream<2, kXQuant>), grid, dim3(64 * kStrWaves), 0, stream, (int)m, n,
                        (int)k, rows, reinterpret_cast<const uint8_t*>(x), nullptr, nullptr, b_codes,
                        b_scales, b_tscale, c, c_dtype, a_codes, a_scales, a_tscale);
   else
-    hipLaunchKernelGGL((gemm_nv_stream<1, true>), grid, dim3(64 * kStrWaves), 0, stream, (int)m, n,
+    hipLaunchKernelGGL((gemm_nv_stream<1, kXQuant>), grid, dim3(64 * kStrWaves), 0, stream, (int)m, n,
                        (int)k, rows, reinterpret_cast<const uint8_t*>(x), nullptr, nullptr, b_codes,
                        b_scales, b_tscale, c, c_dtype, a_codes, a_scales, a_tscale);
   *err = hipGetLastError();
   return true;
+}
+
+hipError_t launch_gemm_w4a16(int fmt, int64_t m, int64_t n, int64_t k, const void* x, int x_dtype,
+                             const uint8_t* b_codes, const uint8_t* b_scales,
+                             const float* b_tscale, void* c, int c_dtype, hipStream_t stream) {
+  const bool aligned = ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(b_codes) |
+                         reinterpret_cast<uintptr_t>(b_scales)) & 15) == 0;
+  if (fmt == kFmtNV && x_dtype == kInBF16 && (k == 2048 || k == 4096) &&
+      n <= 16 * kStrTiles * 256 && aligned) {
+    // streaming kernel, 8 activation rows per launch
+    const int rows = (int)(8 * ((n + 2047) / 2048));
+    const dim3 grid((unsigned)((n + rows - 1) / rows));
+    const int64_t osz = c_dtype == kInF32 ? 4 : 2;
+    for (int64_t i0 = 0; i0 < m; i0 += 8) {
+      const int mc = (int)(m - i0 < 8 ? m - i0 : 8);
+      const uint8_t* xa = reinterpret_cast<const uint8_t*>(x) + i0 * k * 2;
+      void* ca = reinterpret_cast<char*>(c) + i0 * n * osz;
+      if (k == 4096)
+        hipLaunchKernelGGL((gemm_nv_stream<2, kXRaw>), grid, dim3(64 * kStrWaves), 0, stream, mc, n,
+                           (int)k, rows, xa, nullptr, nullptr, b_codes, b_scales, b_tscale, ca, c_dtype,
+                           nullptr, nullptr, nullptr);
+      else
+        hipLaunchKernelGGL((gemm_nv_stream<1, kXRaw>), grid, dim3(64 * kStrWaves), 0, stream, mc, n,
+                           (int)k, rows, xa, nullptr, nullptr, b_codes, b_scales, b_tscale, ca, c_dtype,
+                           nullptr, nullptr, nullptr);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  }
+  const dim3 grid((unsigned)((n + 255) / 256), (unsigned)((m + 7) / 8));
+#define W4A16_SIMPLE(F, D)                                                                        \
+  hipLaunchKernelGGL((gemm_w4a16_simple<F, D>), grid, dim3(256), 0, stream, (int)m, n, (int)k, x, \
+                     b_codes, b_scales, b_tscale, c, c_dtype)
+  if (fmt == kFmtNV) {
+    if (x_dtype == kInF32) W4A16_SIMPLE(kFmtNV, kInF32);
+    else if (x_dtype == kInBF16) W4A16_SIMPLE(kFmtNV, kInBF16);
+    else W4A16_SIMPLE(kFmtNV, kInF16);
+  } else {
+    if (x_dtype == kInF32) W4A16_SIMPLE(kFmtMX, kInF32);
+    else if (x_dtype == kInBF16) W4A16_SIMPLE(kFmtMX, kInBF16);
+    else W4A16_SIMPLE(kFmtMX, kInF16);
+  }
+#undef W4A16_SIMPLE
+  return hipGetLastError();
 }

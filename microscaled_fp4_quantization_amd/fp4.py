@@ -28,7 +28,7 @@ _OUT_DTYPES = {"f32": (F32, torch.float32), "bf16": (BF16, torch.bfloat16),
 EXPORTS = ("fp4_status_string", "fp4_quantize_workspace_size", "fp4_quantize",
            "fp4_hadamard_quantize", "fp4_dequantize", "fp4_gemm_workspace_size",
            "fp4_gemm", "fp4_quantize_gemm_workspace_size", "fp4_quantize_gemm",
-           "fp4_quantize_mse")
+           "fp4_quantize_mse", "fp4_gemm_w4a16")
 
 _lib = None
 
@@ -59,6 +59,8 @@ def lib():
         f.restype = i32
     L.fp4_quantize_mse.argtypes = [vp, i32, i64, i64, vp, vp, vp, i32, vp, sz, vp]
     L.fp4_quantize_mse.restype = i32
+    L.fp4_gemm_w4a16.argtypes = [i32, vp, i32, i64, i64, i64, vp, vp, vp, vp, i32, vp]
+    L.fp4_gemm_w4a16.restype = i32
     L.fp4_dequantize.argtypes = [i32, vp, vp, vp, i64, i64, vp, i32, vp]
     L.fp4_dequantize.restype = i32
     L.fp4_gemm_workspace_size.argtypes = [i32, i64, i64, i64]
@@ -180,6 +182,24 @@ def gemm(a, b, fmt="nvfp4", out_dtype="bf16", out=None):
     st = L.fp4_gemm(f, m, n, k, _ptr(ac), _ptr(asc), _ptr(at), _ptr(bc), _ptr(bsc),
                     _ptr(bt), _ptr(out), code, _ptr(ws), need, _stream(ac))
     _check(st, "fp4_gemm")
+    return out
+
+
+def gemm_w4a16(x, b, fmt="nvfp4", out_dtype="bf16", out=None):
+    """C = X B^T with X [m, k] as it is (bf16 / fp16 / fp32) and the
+    quantized weights B = (codes [n, k/2], scales, tscale).  Returns C [m, n]."""
+    f = _fmt(fmt)
+    if x.dim() != 2:
+        raise ValueError("x must be [m, k]")
+    m, k = x.shape
+    bc, bsc, bt = b
+    n = bc.shape[0]
+    code, tdt = _OUT_DTYPES[out_dtype]
+    if out is None:
+        out = torch.empty((m, n), dtype=tdt, device=x.device)
+    st = lib().fp4_gemm_w4a16(f, _ptr(x), _IN_DTYPES[x.dtype], m, n, k, _ptr(bc), _ptr(bsc),
+                              _ptr(bt), _ptr(out), code, _stream(x))
+    _check(st, "fp4_gemm_w4a16")
     return out
 
 

@@ -20,7 +20,7 @@ FAKE_ODD = ctypes.c_void_p(0x10001)    # misaligned
 def header_functions():
     src = open(os.path.join(ROOT, "include", "fp4.h")).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(fp4_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(fp4_[a-z0-9_]+)\s*\(", src)))
 
 
 def test_library_exports_every_declared_function():
@@ -96,6 +96,29 @@ def test_quantize_mse_rejects_bad_arguments():
     assert q(mode=5) == E
     assert q(mode=fp4.TSCALE_COMPUTE) == E               # no workspace
     assert q(rows=0, x=None, codes=None, scales=None) == fp4.OK
+
+
+def test_gemm_w4a16_rejects_bad_arguments():
+    f = fp4.lib().fp4_gemm_w4a16
+
+    def g(fmt=NV, x=FAKE, dt=fp4.BF16, m=8, n=64, k=256, bc=FAKE, bs=FAKE, bt=FAKE, c=FAKE,
+          cdt=fp4.BF16):
+        return f(fmt, x, dt, m, n, k, bc, bs, bt, c, cdt, None)
+
+    E = fp4.EINVAL
+    assert g(fmt=9) == E
+    assert g(dt=fp4.E4M3) == E
+    assert g(cdt=fp4.F16) == fp4.EUNSUPPORTED
+    assert g(cdt=7) == E
+    assert g(k=40) == E                                  # k % 16
+    assert g(fmt=MX, bt=None, k=48) == E                 # k % 32
+    assert g(m=-1) == E
+    assert g(x=None) == E
+    assert g(bc=None) == E
+    assert g(bt=None) == E                               # NVFP4 needs the weights' tensor scale
+    assert g(fmt=MX) == E                                # MXFP4 takes none
+    assert g(x=FAKE_ODD) == E
+    assert g(m=0, x=None, c=None) == fp4.OK
 
 
 def test_dequantize_rejects_bad_arguments():
