@@ -31,6 +31,11 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+// Scalars for LDS bytes written and read at different widths: without
+// may_alias, type-based alias analysis lets a 16-bit read move above the
+// 32-bit write of the same bytes.
+typedef uint32_t __attribute__((may_alias)) u32_alias;
+typedef uint16_t __attribute__((may_alias)) u16_alias;
 
 constexpr int kWaves = 4;
 constexpr int kRows = 16;
@@ -476,7 +481,7 @@ __global__ __launch_bounds__(64 * kStrWaves) void gemm_nv_stream(
 
   // ---- this wave's LDS regions (loads complete in issue order) ---------------
   auto store_ws = [&]() {
-    uint32_t* dd = reinterpret_cast<uint32_t*>(&L.w[wave][lane][0]);
+    u32_alias* dd = reinterpret_cast<u32_alias*>(&L.w[wave][lane][0]);
     dd[0] = sv[0]; dd[1] = sv[1];
     if (NSTEP == 2) { dd[2] = sv[2]; dd[3] = sv[3]; }
   };
@@ -561,7 +566,7 @@ __global__ __launch_bounds__(64 * kStrWaves) void gemm_nv_stream(
     v2h s[kStrTiles];
 #pragma unroll
     for (int tl = 0; tl < kStrTiles; ++tl) {
-      const uint32_t p = *reinterpret_cast<const uint16_t*>(&L.w[wave][16 * tl + r][8 * t + 2 * g]);
+      const uint32_t p = *reinterpret_cast<const u16_alias*>(&L.w[wave][16 * tl + r][8 * t + 2 * g]);
       s[tl] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(p, 1.0f, false);
     }
 #pragma unroll
