@@ -20,8 +20,8 @@ Sources (the web pages this method is described on):
     ~4.5 bits per value, MXFP4 = OCP blocks of 32 with an E8M0 scale).
   * hyper.ai, paper 2509.23202 (MR-GPTQ), Abstract (blockwise Hadamard
     transforms, rotation fused into the weights, online for activations).
-  * hyper.ai story on the NVFP4 KV cache (dequantization to FP8 before
-    attention).
+  * hyper.ai story on the NVFP4 KV cache (new K/V written to the cache in
+    NVFP4, dequantization to FP8 before attention).
 
 Parity status per function (what pins it in the CPU tests):
   e2m1_decode / e2m1_encode   closed form + brute-force nearest-value search
@@ -36,6 +36,10 @@ Parity status per function (what pins it in the CPU tests):
   gemm_ref                    integer matmul special case, Fraction brute force
   gemm_w4a16_ref              integer special case, Fraction brute force,
                               equals gemm_ref when X is itself NVFP4-exact
+  kv_append_ref               hand-worked NVFP4 / MXFP4 rows at their
+                              positions, dropped out-of-range rows
+  attention_decode_ref        exact rows, means, 3:1 weights, GQA head map,
+                              FP8 ties and saturation, one-hot key
 """
 
 from .formats import (
@@ -66,6 +70,7 @@ from .quant import (
 )
 from .hadamard import hadamard_blocks, HADAMARD_NORM
 from .gemm import gemm_ref, gemm_ref_entries, gemm_w4a16_ref
+from .attention import kv_append_ref, kv_fp8_values, attention_decode_ref
 
 __all__ = [
     "E2M1_MAGNITUDES", "e2m1_decode", "e2m1_encode", "e4m3_decode",
@@ -74,4 +79,5 @@ __all__ = [
     "nvfp4_tensor_scale", "nvfp4_tensor_scale_from_amax", "nvfp4_quantize", "nvfp4_quantize_mse", "nvfp4_mse_block_error", "mxfp4_quantize", "dequantize",
     "dequantize_exact_f64", "pack_nibbles", "unpack_nibbles",
     "hadamard_blocks", "HADAMARD_NORM", "gemm_ref", "gemm_ref_entries", "gemm_w4a16_ref",
+    "kv_append_ref", "kv_fp8_values", "attention_decode_ref",
 ]
