@@ -266,6 +266,73 @@ fp4_status fp4_quantize_gemm(fp4_format fmt, const void* x, fp4_dtype x_dtype,
                              void* workspace, size_t workspace_bytes,
                              void* stream);
 
+/*
+ * fp4_kv_append -- write new K (or V) vectors into a 4-bit KV cache.
+ * Defines: the write side of the hyper.ai story on the NVFP4 KV cache (new
+ * K/V vectors go into the cache in NVFP4 form).
+ *   x, x_dtype    new rows [batch, heads, t_new, k], FP4_F32 / FP4_BF16 /
+ *                 FP4_F16, row-major, 16-byte aligned.
+ *   positions     device int32 [batch]: row (b, h, i) is written at cache
+ *                 position positions[b] + i; a position outside [0, t_max)
+ *                 writes nothing (checked on the device, no error).
+ *   codes         cache [batch, heads, t_max, k/2], 16-byte aligned.
+ *   scales        cache [batch, heads, t_max, k/block], 4-byte aligned.
+ *   tensor_scale  NVFP4: one device float, used as given (a cache keeps one
+ *                 tensor scale for the tokens it already holds); MXFP4: NULL.
+ *   Each row is quantized exactly as fp4_quantize quantizes it (GIVEN mode
+ *   for NVFP4); rows of the cache that are not written are not touched.
+ *   k % block == 0; batch, heads or t_new of 0 enqueue nothing.
+ *   Returns FP4_OK, FP4_EINVAL or FP4_EHIP.
+ */
+fp4_status fp4_kv_append(fp4_format fmt, const void* x, fp4_dtype x_dtype, int64_t batch,
+                         int64_t heads, int64_t t_new, int64_t k, const int32_t* positions,
+                         uint8_t* codes, uint8_t* scales, const float* tensor_scale,
+                         int64_t t_max, void* stream);
+
+/* Bytes of device workspace fp4_attention_decode needs for these sizes. */
+size_t fp4_attention_workspace_size(int64_t batch, int64_t q_heads, int64_t kv_heads,
+                                    int64_t head_dim, int64_t t_max);
+
+/*
+ * fp4_attention_decode -- one query token per sequence attending over a
+ * 4-bit KV cache dequantized to FP8.
+ * Defines: the read side of the hyper.ai story on the NVFP4 KV cache (the
+ * cached K and V are dequantized to FP8 before attention).  Each cached
+ * element enters as exactly the E4M3 byte fp4_dequantize(..., FP4_E4M3)
+ * gives it; then
+ *   out[b, j, :] = sum_{t < seq_lens[b]} softmax_t(softmax_scale *
+ *                  K[b, j/G, t, :] . q[b, j, :]) V[b, j/G, t, :]
+ * with G = q_heads / kv_heads (grouped query heads); a sequence of length 0
+ * gives zeros.
+ *   fmt           FP4_NVFP4 or FP4_MXFP4 (both caches).
+ *   q, q_dtype    [batch, q_heads, head_dim], FP4_BF16 or FP4_F16 (FP4_F32:
+ *                 FP4_EUNSUPPORTED), 16-byte aligned.
+ *   k_codes, k_scales, k_tscale, v_codes, v_scales, v_tscale
+ *                 caches [batch, kv_heads, t_max, head_dim/2] (16-byte
+ *                 aligned) and [.., head_dim/block] (4-byte aligned), as
+ *                 fp4_kv_append writes them; tensor scales are device floats
+ *                 (NVFP4) or NULL (MXFP4).
+ *   seq_lens      device int32 [batch]; values are clamped to [0, t_max].
+ *   out, out_dtype  [batch, q_heads, head_dim], FP4_F32 or FP4_BF16
+ *                 (nearest even), 16-byte aligned.
+ *   workspace     at least fp4_attention_workspace_size() bytes, 16-byte
+ *                 aligned (split-token partial results).
+ *   head_dim must be 128 and q_heads / kv_heads at most 16 (else
+ *   FP4_EUNSUPPORTED); q_heads must be a multiple of kv_heads.
+ *   Numerics: K . q on the matrix cores with FP8 K widened exactly to the
+ *   16-bit type of q, fp32 sums; fp32 softmax; the weights rounded to fp16
+ *   (nearest even) for the weighted sum of V, fp32 sums.
+ *   Returns FP4_OK, FP4_EINVAL, FP4_EUNSUPPORTED or FP4_EHIP.
+ */
+fp4_status fp4_attention_decode(fp4_format fmt, const void* q, fp4_dtype q_dtype,
+                                int64_t batch, int64_t q_heads, int64_t kv_heads,
+                                int64_t head_dim, const uint8_t* k_codes,
+                                const uint8_t* k_scales, const float* k_tscale,
+                                const uint8_t* v_codes, const uint8_t* v_scales,
+                                const float* v_tscale, int64_t t_max, const int32_t* seq_lens,
+                                float softmax_scale, void* out, fp4_dtype out_dtype,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

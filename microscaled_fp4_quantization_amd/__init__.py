@@ -6,7 +6,7 @@ include/fp4.h); `fp4` is its Python binding.
 
 from . import fp4
 from .fp4 import (quantize, quantize_mse, hadamard_quantize, dequantize, gemm, gemm_w4a16,
-                  quantize_gemm, lib)
+                  quantize_gemm, kv_cache, kv_append, attention_decode, lib)
 
 __all__ = ["fp4", "quantize", "quantize_mse", "hadamard_quantize", "dequantize", "gemm", "gemm_w4a16",
-           "quantize_gemm", "lib"]
+           "quantize_gemm", "kv_cache", "kv_append", "attention_decode", "lib"]

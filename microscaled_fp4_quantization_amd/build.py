@@ -22,6 +22,7 @@ SOURCES = [
     "gemm_skinny.hip",
     "gemm_large.hip",
     "gemm.hip",
+    "attention.hip",
 ]
 
 # -ffp-contract=off: every a*b and a+b rounds on its own (no fused

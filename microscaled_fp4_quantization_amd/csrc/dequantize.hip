@@ -51,26 +51,11 @@ __device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
          ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
 }
 
-__device__ __forceinline__ uint32_t pack_e4m3x4(const float* y) {
-  float c[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) c[i] = __builtin_amdgcn_fmed3f(y[i], -448.0f, 448.0f);
-  int w = __builtin_amdgcn_cvt_pk_fp8_f32(c[0], c[1], 0, false);
-  w = __builtin_amdgcn_cvt_pk_fp8_f32(c[2], c[3], w, true);
-  return (uint32_t)w;
-}
-
 // Chunk c (8 values, code word w, scale byte sbyte) -> out.
 template <int FMT, int OUT>
 __device__ __forceinline__ void dequant_chunk(uint32_t w, uint32_t sbyte, float s_t, int64_t c,
                                               void* __restrict__ out) {
-  float sv;
-  if (FMT == kFmtNV) {
-    sv = e4m3_decode_pos(sbyte & 0x7Fu);
-    if (sbyte & 0x80u) sv = -sv;
-  } else {
-    sv = sbyte ? as_f(sbyte << 23) : as_f(0x00400000u);  // 2^(c-127); c = 0 is 2^-127
-  }
+  const float sv = block_scale_value<FMT == kFmtNV>(sbyte);
   float y[8];
   const v2f p0 = e2m1_unpack2<0>(w), p1 = e2m1_unpack2<1>(w);
   const v2f p2 = e2m1_unpack2<2>(w), p3 = e2m1_unpack2<3>(w);
@@ -106,13 +91,7 @@ __device__ __forceinline__ void dequant_chunk(uint32_t w, uint32_t sbyte, float 
 // Chunk (code word w, scale byte sbyte) -> 8 FP8 E4M3 bytes.
 template <int FMT>
 __device__ __forceinline__ u32x2 dequant_e4m3(uint32_t w, uint32_t sbyte, float s_t) {
-  float sv;
-  if (FMT == kFmtNV) {
-    sv = e4m3_decode_pos(sbyte & 0x7Fu);
-    if (sbyte & 0x80u) sv = -sv;
-  } else {
-    sv = sbyte ? as_f(sbyte << 23) : as_f(0x00400000u);  // 2^(c-127); c = 0 is 2^-127
-  }
+  const float sv = block_scale_value<FMT == kFmtNV>(sbyte);
   float y[8];
   const v2f p0 = e2m1_unpack2<0>(w), p1 = e2m1_unpack2<1>(w);
   const v2f p2 = e2m1_unpack2<2>(w), p3 = e2m1_unpack2<3>(w);

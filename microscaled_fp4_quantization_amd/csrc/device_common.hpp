@@ -71,6 +71,30 @@ __device__ __forceinline__ v2f e2m1_unpack2(uint32_t w) {
   return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, SEL);
 }
 
+// ---- FP8 E4M3 output --------------------------------------------------------
+// Four fp32 values -> four E4M3 bytes, round to nearest even after a clamp to
+// +-448 (the hardware conversion rounds correctly inside that range but
+// returns NaN beyond it).
+__device__ __forceinline__ uint32_t pack_e4m3x4(const float* y) {
+  float c[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) c[i] = __builtin_amdgcn_fmed3f(y[i], -448.0f, 448.0f);
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(c[0], c[1], 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c[2], c[3], w, true);
+  return (uint32_t)w;
+}
+
+// Block scale byte -> its fp32 value.  NVFP4 (NV = true): E4M3, sign bit
+// honoured.  MXFP4: E8M0 2^(c-127), the byte 0 giving 2^-127.
+template <bool NV>
+__device__ __forceinline__ float block_scale_value(uint32_t sbyte) {
+  if (NV) {
+    const float sv = e4m3_decode_pos(sbyte & 0x7Fu);
+    return (sbyte & 0x80u) ? -sv : sv;
+  }
+  return sbyte ? as_f(sbyte << 23) : as_f(0x00400000u);
+}
+
 // ---- MXFP4 block exponent --------------------------------------------------
 // Smallest k with a <= 6 * 2^k for a > 0, clamped to [-127, 127].  With
 // a = 1.f * 2^(E-127) = m * 2^e, m in [0.5, 1), e = E - 126: k = e - 3 when

@@ -247,4 +247,81 @@ fp4_status fp4_quantize_gemm(fp4_format fmt, const void* x, fp4_dtype x_dtype,
                               b_scales, b_tscale, c, (int)c_dtype, workspace, st));
 }
 
+fp4_status fp4_kv_append(fp4_format fmt, const void* x, fp4_dtype x_dtype, int64_t batch,
+                         int64_t heads, int64_t t_new, int64_t k, const int32_t* positions,
+                         uint8_t* codes, uint8_t* scales, const float* tensor_scale,
+                         int64_t t_max, void* stream) {
+  if (!valid_format(fmt)) return FP4_EINVAL;
+  if (x_dtype != FP4_F32 && x_dtype != FP4_BF16 && x_dtype != FP4_F16) return FP4_EINVAL;
+  if (batch < 0 || heads < 0 || t_new < 0 || t_max <= 0) return FP4_EINVAL;
+  if (k <= 0 || k % block_of(fmt) != 0) return FP4_EINVAL;
+  if (batch > 0 && heads > kMaxElements / batch) return FP4_EINVAL;
+  const int64_t bh = batch * heads;
+  if (bh > 0 && (t_max > kMaxElements / bh || t_new > kMaxElements / bh)) return FP4_EINVAL;
+  if (bh > 0 && (k > kMaxElements / (bh * t_max) || (t_new > 0 && k > kMaxElements / (bh * t_new))))
+    return FP4_EINVAL;
+  if (bh == 0 || t_new == 0) return FP4_OK;
+  if (!x || !positions || !codes || !scales) return FP4_EINVAL;
+  if (!aligned(x, 16) || !aligned(codes, 16) || !aligned(scales, 4) || !aligned(positions, 4))
+    return FP4_EINVAL;
+  if (fmt == FP4_NVFP4) {
+    if (!tensor_scale || !aligned(tensor_scale, 4)) return FP4_EINVAL;
+  } else if (tensor_scale) {
+    return FP4_EINVAL;
+  }
+  return from_hip(launch_kv_append((int)fmt, x, (int)x_dtype, batch, heads, t_new, k, positions,
+                                   t_max, codes, scales, tensor_scale,
+                                   static_cast<hipStream_t>(stream)));
+}
+
+size_t fp4_attention_workspace_size(int64_t batch, int64_t q_heads, int64_t kv_heads,
+                                    int64_t head_dim, int64_t t_max) {
+  if (batch <= 0 || kv_heads <= 0 || q_heads <= 0 || q_heads % kv_heads != 0 || t_max <= 0 ||
+      head_dim != 128 || q_heads / kv_heads > 16)
+    return 0;
+  return attention_workspace_bytes(batch, q_heads, kv_heads, t_max);
+}
+
+fp4_status fp4_attention_decode(fp4_format fmt, const void* q, fp4_dtype q_dtype,
+                                int64_t batch, int64_t q_heads, int64_t kv_heads,
+                                int64_t head_dim, const uint8_t* k_codes,
+                                const uint8_t* k_scales, const float* k_tscale,
+                                const uint8_t* v_codes, const uint8_t* v_scales,
+                                const float* v_tscale, int64_t t_max, const int32_t* seq_lens,
+                                float softmax_scale, void* out, fp4_dtype out_dtype,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  if (!valid_format(fmt)) return FP4_EINVAL;
+  if (q_dtype != FP4_BF16 && q_dtype != FP4_F16) {
+    return q_dtype == FP4_F32 ? FP4_EUNSUPPORTED : FP4_EINVAL;
+  }
+  if (out_dtype != FP4_F32 && out_dtype != FP4_BF16) {
+    return (out_dtype == FP4_F16 || out_dtype == FP4_E4M3) ? FP4_EUNSUPPORTED : FP4_EINVAL;
+  }
+  if (batch < 0 || q_heads <= 0 || kv_heads <= 0 || t_max <= 0 || head_dim <= 0) return FP4_EINVAL;
+  if (q_heads % kv_heads != 0 || head_dim % block_of(fmt) != 0) return FP4_EINVAL;
+  if (head_dim != 128 || q_heads / kv_heads > 16) return FP4_EUNSUPPORTED;
+  if (q_heads > (int64_t(1) << 20) || kv_heads > (int64_t(1) << 20)) return FP4_EINVAL;
+  if (batch > 0 && (kv_heads > kMaxElements / batch || q_heads > kMaxElements / batch))
+    return FP4_EINVAL;
+  if (batch > 0 && t_max > kMaxElements / (batch * kv_heads * head_dim)) return FP4_EINVAL;
+  if (batch > (int64_t(1) << 31) / kv_heads || batch > (int64_t(1) << 31) / q_heads) return FP4_EINVAL;
+  if (batch == 0) return FP4_OK;
+  if (!q || !k_codes || !k_scales || !v_codes || !v_scales || !seq_lens || !out) return FP4_EINVAL;
+  if (!aligned(q, 16) || !aligned(k_codes, 16) || !aligned(v_codes, 16) || !aligned(k_scales, 4) ||
+      !aligned(v_scales, 4) || !aligned(seq_lens, 4) || !aligned(out, 16))
+    return FP4_EINVAL;
+  if (fmt == FP4_NVFP4) {
+    if (!k_tscale || !v_tscale || !aligned(k_tscale, 4) || !aligned(v_tscale, 4)) return FP4_EINVAL;
+  } else if (k_tscale || v_tscale) {
+    return FP4_EINVAL;
+  }
+  const size_t need = attention_workspace_bytes(batch, q_heads, kv_heads, t_max);
+  if (!workspace || workspace_bytes < need || !aligned(workspace, 16)) return FP4_EINVAL;
+  return from_hip(launch_attention_decode((int)fmt, q, (int)q_dtype, batch, q_heads, kv_heads,
+                                          k_codes, k_scales, k_tscale, v_codes, v_scales,
+                                          v_tscale, t_max, seq_lens, softmax_scale, out,
+                                          (int)out_dtype, workspace,
+                                          static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -54,3 +54,22 @@ bool launch_quantize_gemm_decode(int64_t m, int64_t n, int64_t k, const void* x,
 hipError_t launch_gemm_w4a16(int fmt, int64_t m, int64_t n, int64_t k, const void* x, int x_dtype,
                              const uint8_t* b_codes, const uint8_t* b_scales,
                              const float* b_tscale, void* c, int c_dtype, hipStream_t stream);
+
+// KV cache append: rows of x [batch, heads, t_new, k] quantized (NVFP4 with
+// the given tensor scale) into a [batch, heads, t_max, ...] cache at
+// positions[b] + i; rows outside [0, t_max) are not stored.
+hipError_t launch_kv_append(int fmt, const void* x, int dtype, int64_t batch, int64_t heads,
+                            int64_t t_new, int64_t k, const int32_t* positions, int64_t t_max,
+                            uint8_t* codes, uint8_t* scales, const float* tscale,
+                            hipStream_t stream);
+
+// Decode attention over an FP4 KV cache (head_dim 128, q_heads a multiple
+// of kv_heads by at most 16), K and V dequantized to FP8 E4M3 on the fly.
+size_t attention_workspace_bytes(int64_t batch, int64_t q_heads, int64_t kv_heads, int64_t t_max);
+hipError_t launch_attention_decode(int fmt, const void* q, int q_dtype, int64_t batch,
+                                   int64_t q_heads, int64_t kv_heads, const uint8_t* k_codes,
+                                   const uint8_t* k_scales, const float* k_tscale,
+                                   const uint8_t* v_codes, const uint8_t* v_scales,
+                                   const float* v_tscale, int64_t t_max, const int32_t* seq_lens,
+                                   float softmax_scale, void* out, int out_dtype, void* workspace,
+                                   hipStream_t stream);

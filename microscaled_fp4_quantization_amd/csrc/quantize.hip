@@ -231,6 +231,50 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
   }
 }
 
+// KV cache append (hyper.ai story on the NVFP4 KV cache: new K/V vectors are
+// written into the cache in 4-bit form).  The rows of x [batch, heads,
+// t_new, k] are quantized exactly as quantize_kernel quantizes them (NVFP4
+// with the given tensor scale) and row (b, h, i) is stored at position
+// positions[b] + i of the [batch, heads, t_max, ...] cache; a position
+// outside [0, t_max) stores nothing.  k is a multiple of 16 (32 for
+// MXFP4), so cpr = k / 8 keeps a block's lane pair (quad) and the parity of
+// the chunk index from source to destination.
+template <int FMT, int DT>
+__global__ __launch_bounds__(kThreads) void kv_append_kernel(
+    const void* __restrict__ x, int64_t nchunks, int cpr, int64_t t_new, int64_t heads,
+    const int32_t* __restrict__ positions, int64_t t_max, uint32_t* __restrict__ codes,
+    uint8_t* __restrict__ scales, const float* __restrict__ tscale) {
+  const int lane = threadIdx.x & 63;
+  float s_t = 1.0f, d = 6.0f;
+  if (FMT == kFmtNV) {
+    s_t = *tscale;
+    d = 6.0f * s_t;
+  }
+  for (int64_t base = (int64_t)blockIdx.x * kChunksPerTrip; base < nchunks;
+       base += (int64_t)gridDim.x * kChunksPerTrip) {
+    float v[kUnroll][8];
+#pragma unroll
+    for (int j = 0; j < kUnroll; ++j) {
+      const int64_t c = base + j * kThreads + threadIdx.x;
+      load_chunk<DT>(x, c, c < nchunks, v[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < kUnroll; ++j) {
+      const int64_t c = base + j * kThreads + threadIdx.x;
+      int64_t cdst = 0;
+      bool ok = false;
+      if (c < nchunks) {
+        const int64_t row = c / cpr, cr = c - row * cpr;
+        const int64_t bh = row / t_new, i = row - bh * t_new;
+        const int64_t p = (int64_t)positions[bh / heads] + i;
+        ok = p >= 0 && p < t_max;
+        cdst = (bh * t_max + (ok ? p : 0)) * cpr + cr;
+      }
+      quantize_chunk<FMT>(v[j], lane, s_t, d, cdst, ok, codes, scales);
+    }
+  }
+}
+
 // NVFP4 with the tensor scale computed from the data, for small tensors
 // (decode activations): one workgroup holds the whole tensor in registers,
 // reduces its max |x| and quantizes, in a single launch instead of two.
@@ -436,6 +480,30 @@ hipError_t launch_quantize(int fmt, bool hadamard, const void* x, int dtype,
   }
   return hadamard ? launch_dtype<kFmtMX, 32>(dtype, x, nchunks, codes, scales, tscale, false, workspace, stream)
                   : launch_dtype<kFmtMX, 0>(dtype, x, nchunks, codes, scales, tscale, false, workspace, stream);
+}
+
+hipError_t launch_kv_append(int fmt, const void* x, int dtype, int64_t batch, int64_t heads,
+                            int64_t t_new, int64_t k, const int32_t* positions, int64_t t_max,
+                            uint8_t* codes, uint8_t* scales, const float* tscale,
+                            hipStream_t stream) {
+  const int64_t nchunks = batch * heads * t_new * (k / 8);
+  const int grid = (int)((nchunks + kChunksPerTrip - 1) / kChunksPerTrip);
+  uint32_t* c32 = reinterpret_cast<uint32_t*>(codes);
+  const int cpr = (int)(k / 8);
+#define FP4_KV_APPEND(F, D)                                                                  \
+  hipLaunchKernelGGL((kv_append_kernel<F, D>), dim3(grid), dim3(kThreads), 0, stream, x,     \
+                     nchunks, cpr, t_new, heads, positions, t_max, c32, scales, tscale)
+  if (fmt == kFmtNV) {
+    if (dtype == kInF32) FP4_KV_APPEND(kFmtNV, kInF32);
+    else if (dtype == kInBF16) FP4_KV_APPEND(kFmtNV, kInBF16);
+    else FP4_KV_APPEND(kFmtNV, kInF16);
+  } else {
+    if (dtype == kInF32) FP4_KV_APPEND(kFmtMX, kInF32);
+    else if (dtype == kInBF16) FP4_KV_APPEND(kFmtMX, kInBF16);
+    else FP4_KV_APPEND(kFmtMX, kInF16);
+  }
+#undef FP4_KV_APPEND
+  return hipGetLastError();
 }
 
 hipError_t launch_quantize_mse(const void* x, int dtype, int64_t n, uint8_t* codes,

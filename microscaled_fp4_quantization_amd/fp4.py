@@ -28,7 +28,8 @@ _OUT_DTYPES = {"f32": (F32, torch.float32), "bf16": (BF16, torch.bfloat16),
 EXPORTS = ("fp4_status_string", "fp4_quantize_workspace_size", "fp4_quantize",
            "fp4_hadamard_quantize", "fp4_dequantize", "fp4_gemm_workspace_size",
            "fp4_gemm", "fp4_quantize_gemm_workspace_size", "fp4_quantize_gemm",
-           "fp4_quantize_mse", "fp4_gemm_w4a16")
+           "fp4_quantize_mse", "fp4_gemm_w4a16", "fp4_kv_append",
+           "fp4_attention_workspace_size", "fp4_attention_decode")
 
 _lib = None
 
@@ -72,6 +73,13 @@ def lib():
     L.fp4_quantize_gemm.argtypes = [i32, vp, i32, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp, i32,
                                     vp, sz, vp]
     L.fp4_quantize_gemm.restype = i32
+    L.fp4_kv_append.argtypes = [i32, vp, i32, i64, i64, i64, i64, vp, vp, vp, vp, i64, vp]
+    L.fp4_kv_append.restype = i32
+    L.fp4_attention_workspace_size.argtypes = [i64, i64, i64, i64, i64]
+    L.fp4_attention_workspace_size.restype = sz
+    L.fp4_attention_decode.argtypes = [i32, vp, i32, i64, i64, i64, i64, vp, vp, vp, vp, vp, vp,
+                                       i64, vp, ctypes.c_float, vp, i32, vp, sz, vp]
+    L.fp4_attention_decode.restype = i32
     _lib = L
     return L
 
@@ -228,3 +236,62 @@ def quantize_gemm(x, b, fmt="nvfp4", out_dtype="bf16", out=None):
                              need, _stream(x))
     _check(st, "fp4_quantize_gemm")
     return (codes, scales, ts), out
+
+
+def kv_cache(batch, heads, t_max, head_dim=128, fmt="nvfp4", device="cuda"):
+    """An empty 4-bit KV cache: (codes [batch, heads, t_max, head_dim/2],
+    scales [batch, heads, t_max, head_dim/block]), zero-filled."""
+    f = _fmt(fmt)
+    codes = torch.zeros((batch, heads, t_max, head_dim // 2), dtype=torch.uint8, device=device)
+    scales = torch.zeros((batch, heads, t_max, head_dim // BLOCK[f]), dtype=torch.uint8,
+                         device=device)
+    return codes, scales
+
+
+def kv_append(x, cache, positions, fmt="nvfp4", tensor_scale=None):
+    """Quantize the new rows x [batch, heads, t_new, head_dim] into
+    cache = (codes, scales) at positions[b] + i (int32 CUDA tensor [batch]);
+    NVFP4 needs tensor_scale (one-element float32 CUDA tensor).  Rows whose
+    position is outside the cache are not written.  Returns the cache."""
+    f = _fmt(fmt)
+    if x.dim() != 4:
+        raise ValueError("x must be [batch, heads, t_new, head_dim]")
+    codes, scales = cache
+    B, H, tn, d = x.shape
+    st = lib().fp4_kv_append(f, _ptr(x), _IN_DTYPES[x.dtype], B, H, tn, d, _ptr(positions),
+                             _ptr(codes), _ptr(scales), _ptr(tensor_scale), codes.shape[2],
+                             _stream(x))
+    _check(st, "fp4_kv_append")
+    return cache
+
+
+def attention_decode(q, k_cache, v_cache, seq_lens, fmt="nvfp4", k_tscale=None, v_tscale=None,
+                     softmax_scale=None, out_dtype="bf16", out=None, workspace=None):
+    """One query token per sequence, q [batch, q_heads, head_dim] (bf16 /
+    fp16), over the 4-bit caches k_cache, v_cache = (codes, scales) of shape
+    [batch, kv_heads, t_max, ...] dequantized to FP8; seq_lens int32 CUDA
+    tensor [batch].  softmax_scale defaults to 1 / sqrt(head_dim).  Returns
+    out [batch, q_heads, head_dim]."""
+    f = _fmt(fmt)
+    if q.dim() != 3:
+        raise ValueError("q must be [batch, q_heads, head_dim]")
+    B, hq, d = q.shape
+    kc, ks = k_cache
+    vc, vs = v_cache
+    hkv, t_max = kc.shape[1], kc.shape[2]
+    if softmax_scale is None:
+        softmax_scale = 1.0 / float(d) ** 0.5
+    code, tdt = _OUT_DTYPES[out_dtype]
+    if out is None:
+        out = torch.empty((B, hq, d), dtype=tdt, device=q.device)
+    L = lib()
+    need = L.fp4_attention_workspace_size(B, hq, hkv, d, t_max)
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    st = L.fp4_attention_decode(f, _ptr(q), _IN_DTYPES[q.dtype], B, hq, hkv, d, _ptr(kc), _ptr(ks),
+                                _ptr(k_tscale), _ptr(vc), _ptr(vs), _ptr(v_tscale), t_max,
+                                _ptr(seq_lens), float(softmax_scale), _ptr(out), code,
+                                _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                _stream(q))
+    _check(st, "fp4_attention_decode")
+    return out

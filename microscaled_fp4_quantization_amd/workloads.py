@@ -17,9 +17,19 @@ rounded to bfloat16 (round to nearest even) where the workload is bf16.
            multiplier c ~ U(0.5, 4) per (head, head_dim channel), shared by
            batch and tokens; drawn c_K, K, c_V, V.
 
+  attention  the kv workload's K and V (the cache contents) and the query of
+           one decode step, Q bf16 [32, 64, 128] ~ N(0,1) (64 query heads over
+           8 KV heads: grouped-query attention with 8 query heads per KV
+           head), drawn after K and V.
+  random_cache  uniformly random cache bytes (codes 0..255; NVFP4 scale
+           bytes uniform in [0x30, 0x50), i.e. 0.5 .. 7.5; MXFP4 scale bytes
+           uniform in [120, 130), i.e. 2^-7 .. 2^2) from numpy's PCG64 with
+           the given seed: the input of full-size attention checks.
+
 Draw order inside a workload: X, then W, then outlier positions.
 """
 
+import numpy as np
 import torch
 
 SHAPES = {
@@ -100,6 +110,26 @@ def kv(device="cpu", seed=0, batch=32, heads=8, tokens=32768, head_dim=128):
         out[name] = t
         out["c_" + name] = c
     return out
+
+
+def attention(device="cpu", seed=0, batch=32, kv_heads=8, q_heads=64, tokens=32768,
+              head_dim=128):
+    out = kv(device, seed, batch, kv_heads, tokens, head_dim)
+    g = _gen(device, seed + 1)
+    out["q"] = torch.randn((batch, q_heads, head_dim), generator=g, device=device).to(torch.bfloat16)
+    return out
+
+
+def random_cache(batch, heads, tokens, head_dim, fmt="nvfp4", seed=0):
+    """(codes [batch, heads, tokens, head_dim/2], scales [.., head_dim/block])
+    as numpy uint8 arrays of random bytes."""
+    rng = np.random.default_rng(seed)
+    codes = rng.integers(0, 256, size=(batch, heads, tokens, head_dim // 2), dtype=np.uint8)
+    if fmt == "nvfp4":
+        scales = rng.integers(0x30, 0x50, size=(batch, heads, tokens, head_dim // 16), dtype=np.uint8)
+    else:
+        scales = rng.integers(120, 130, size=(batch, heads, tokens, head_dim // 32), dtype=np.uint8)
+    return codes, scales
 
 
 WORKLOADS = {"tiny": tiny, "decode": decode, "prefill": prefill,

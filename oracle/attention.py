@@ -88,8 +88,10 @@ def attention_decode_ref(fmt, q, k_codes, k_scales, k_tscale, v_codes, v_scales,
     q [B, Hq, D] (exact values); caches [B, Hkv, T_max, ...]; seq_lens [B].
     out[b, j] = sum_t p_t V[t] with p = softmax(softmax_scale * K q) over
     t < seq_lens[b], K and V the FP8 values of kv head j // G; a sequence of
-    length 0 gives zeros.  with_abs also returns sum_t p_t |V[t]| (the scale
-    of the rounding error of a weighted sum), same shape.
+    length 0 gives zeros.  with_abs also returns the two scales of the
+    rounding error of a weighted sum, same shape: sum_t p_t |V[t]| (errors
+    relative to each weight) and max_t p_t * sum_t |V[t]| (errors absolute
+    against the largest weight).
     """
     q = np.asarray(q, dtype=np.float64)
     B, Hq, D = q.shape
@@ -100,6 +102,7 @@ def attention_decode_ref(fmt, q, k_codes, k_scales, k_tscale, v_codes, v_scales,
     scale = float(np.float32(softmax_scale))
     out = np.zeros((B, Hq, D), dtype=np.float64)
     absw = np.zeros((B, Hq, D), dtype=np.float64)
+    flat = np.zeros((B, Hq, D), dtype=np.float64)
     for b in range(B):
         L = int(seq_lens[b])
         if L <= 0:
@@ -114,6 +117,7 @@ def attention_decode_ref(fmt, q, k_codes, k_scales, k_tscale, v_codes, v_scales,
                 w /= np.sum(w)
                 out[b, hq] = w @ V
                 absw[b, hq] = w @ np.abs(V)
+                flat[b, hq] = np.max(w) * np.sum(np.abs(V), axis=0)
     if with_abs:
-        return out, absw
+        return out, absw, flat
     return out

@@ -187,6 +187,62 @@ def test_quantize_gemm_rejects_bad_arguments():
         fp4.lib().fp4_quantize_workspace_size(NV, fp4.TSCALE_COMPUTE, 8, 64)
 
 
+def test_kv_append_rejects_bad_arguments():
+    f = fp4.lib().fp4_kv_append
+
+    def g(fmt=NV, x=FAKE, dt=fp4.BF16, b=2, h=8, tn=1, k=128, pos=FAKE, codes=FAKE, scales=FAKE,
+          ts=FAKE, t_max=64):
+        return f(fmt, x, dt, b, h, tn, k, pos, codes, scales, ts, t_max, None)
+
+    E = fp4.EINVAL
+    assert g(fmt=2) == E
+    assert g(k=24) == E                       # not whole NVFP4 blocks
+    assert g(fmt=MX, ts=None, k=48) == E      # not whole MXFP4 blocks
+    assert g(dt=fp4.E4M3) == E
+    assert g(x=FAKE_ODD) == E
+    assert g(codes=FAKE_ODD) == E
+    assert g(pos=None) == E
+    assert g(ts=None) == E                    # NVFP4 uses the cache's given tensor scale
+    assert g(fmt=MX) == E                     # MXFP4 has none
+    assert g(t_max=0) == E
+    assert g(tn=-1) == E
+    assert g(tn=0, x=None, pos=None) == fp4.OK
+    assert g(b=0, x=None) == fp4.OK
+
+
+def test_attention_decode_rejects_bad_arguments():
+    L = fp4.lib()
+    f = L.fp4_attention_decode
+    need = L.fp4_attention_workspace_size(2, 16, 2, 128, 1000)
+    assert need > 0
+
+    def g(fmt=NV, q=FAKE, qdt=fp4.BF16, b=2, hq=16, hkv=2, d=128, kc=FAKE, ks=FAKE, kt=FAKE,
+          vc=FAKE, vs=FAKE, vt=FAKE, t_max=1000, lens=FAKE, scale=0.088, out=FAKE,
+          odt=fp4.BF16, ws=FAKE, wsb=None):
+        return f(fmt, q, qdt, b, hq, hkv, d, kc, ks, kt, vc, vs, vt, t_max, lens, scale, out, odt,
+                 ws, need if wsb is None else wsb, None)
+
+    E, U = fp4.EINVAL, fp4.EUNSUPPORTED
+    assert g(fmt=2) == E
+    assert g(hq=15) == E                      # q heads not a multiple of kv heads
+    assert g(d=64) == U                       # head_dim 128 only
+    assert g(hq=34) == U                      # more than 16 query heads per kv head
+    assert g(qdt=fp4.F32) == U
+    assert g(qdt=fp4.E4M3) == E
+    assert g(odt=fp4.F16) == U
+    assert g(q=FAKE_ODD) == E
+    assert g(kc=FAKE_ODD) == E
+    assert g(vs=None) == E
+    assert g(lens=None) == E
+    assert g(kt=None) == E                    # NVFP4 caches carry tensor scales
+    assert g(fmt=MX) == E                     # MXFP4 caches do not
+    assert g(ws=None) == E
+    assert g(wsb=need - 1) == E
+    assert g(t_max=0) == E
+    assert g(b=0, q=None, out=None) == fp4.OK
+    assert L.fp4_attention_workspace_size(2, 16, 2, 64, 1000) == 0
+
+
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(fp4, "_lib", None)
     monkeypatch.setattr(fp4, "LIB_PATH", str(tmp_path / "missing.so"))

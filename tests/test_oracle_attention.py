@@ -190,10 +190,12 @@ def test_abs_weighted_sum_bounds_the_output():
     v = rng.integers(0, 16, size=(2, 2, 9, 16))
     kc, ks = _nv_cache(k)
     vc, vs = _nv_cache(v)
-    out, absw = attention_decode_ref("nvfp4", rng.standard_normal((2, 4, 16)), kc, ks, 1.0,
-                                     vc, vs, 1.0, [9, 4], 0.4, with_abs=True)
+    out, absw, flat = attention_decode_ref("nvfp4", rng.standard_normal((2, 4, 16)), kc, ks, 1.0,
+                                           vc, vs, 1.0, [9, 4], 0.4, with_abs=True)
     assert np.all(np.abs(out) <= absw + 1e-12)
     assert np.all(absw <= 6.0 + 1e-12)
+    # max_t p_t sum_t |V_t| >= sum_t p_t |V_t| >= |out|
+    assert np.all(absw <= flat + 1e-12)
 
 
 def _golden():
