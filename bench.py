@@ -22,6 +22,11 @@ every input already resident in HBM:
   mse      NVFP4 quantization of the weight W [14336, 4096] bf16 with the
            least-squared-error block scale (fp4_quantize_mse, tensor scale
            computed from the data): compute-bound, fp64 error sums.
+  attention  one decode step over the NVFP4 KV cache of the kv workload
+           ([32, 8, 32768, 128], quantized once): append the new token's K
+           and V (fp4_kv_append, given tensor scales) + attention of 64 query
+           heads (8 per KV head, bf16 q) over all 32768 tokens with the cache
+           dequantized to FP8 (fp4_attention_decode), bf16 out.
 Prints one JSON line.  The timed region is K steps back to back between one
 pair of HIP events (value, ms_per_step).  The dominant kernel is then timed
 the same way over the K steps' launches of it alone; its algorithmic bytes
@@ -57,7 +62,8 @@ def parse():
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", default="decode",
-                   choices=["decode", "prefill", "rotated_nv", "rotated_mx", "kv", "mse", "w4a16"])
+                   choices=["decode", "prefill", "rotated_nv", "rotated_mx", "kv", "mse", "w4a16",
+                            "attention"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--copy-bytes", type=int, default=0,
@@ -80,6 +86,7 @@ DOMINANT = {
     "kv": ("quantize_kernel<0, 1, 0, false>", ["quantize.hip", "device_common.hpp"]),
     "mse": ("quantize_mse_kernel<1, true>", ["quantize.hip", "device_common.hpp"]),
     "w4a16": ("gemm_nv_stream<2, 2>", ["gemm_skinny.hip"]),
+    "attention": ("attn_decode_kernel<0, 1>", ["attention.hip", "device_common.hpp"]),
 }
 COPY_KERNEL = "copyBuffer"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
@@ -203,6 +210,27 @@ class Lib:
         fn = self.L.fp4_gemm_w4a16
         return lambda: self.check(fn(*args), "gemm_w4a16")
 
+    def kv_append_call(self, fmt, x, cache, positions, ts):
+        from microscaled_fp4_quantization_amd import fp4
+        codes, scales = cache
+        B, H, tn, d = x.shape
+        dt = {self.torch.bfloat16: fp4.BF16, self.torch.float32: fp4.F32, self.torch.float16: fp4.F16}[x.dtype]
+        args = (fmt, self.p(x), dt, B, H, tn, d, self.p(positions), self.p(codes), self.p(scales),
+                self.p(ts), codes.shape[2], self.stream)
+        fn = self.L.fp4_kv_append
+        return lambda: self.check(fn(*args), "kv_append")
+
+    def attention_call(self, fmt, q, kcache, kts, vcache, vts, lens, scale, out, out_dtype, ws):
+        from microscaled_fp4_quantization_amd import fp4
+        B, hq, d = q.shape
+        (kc, ks), (vc, vs) = kcache, vcache
+        dt = {self.torch.bfloat16: fp4.BF16, self.torch.float16: fp4.F16}[q.dtype]
+        args = (fmt, self.p(q), dt, B, hq, kc.shape[1], d, self.p(kc), self.p(ks), self.p(kts),
+                self.p(vc), self.p(vs), self.p(vts), kc.shape[2], self.p(lens), ctypes.c_float(scale),
+                self.p(out), out_dtype, self.p(ws), ws.numel(), self.stream)
+        fn = self.L.fp4_attention_decode
+        return lambda: self.check(fn(*args), "attention_decode")
+
     def dequant_call(self, fmt, codes, scales, ts, out, out_dtype):
         rows, k = codes.shape[0], codes.shape[1] * 2
         args = (fmt, self.p(codes), self.p(scales), self.p(ts), rows, k, self.p(out), out_dtype, self.stream)
@@ -325,6 +353,51 @@ def setup(workload, torch, fq, lib):
                          "scale_rule": "least squared error", "x_dtype": "bf16"},
                  dtype="f32 quantize, f64 error sums",
                  host=dict(w=w))
+    elif workload == "attention":
+        B, H, T, D, G = 32, 8, 32768, 128, 8
+        d = workloads.attention(device=dev, batch=B, kv_heads=H, q_heads=H * G, tokens=T,
+                                head_dim=D)
+        caches, news, tss, host = [], [], [], {}
+        ws = torch.empty(4096, dtype=torch.uint8, device=dev)
+        for name in ("k", "v"):
+            x = d.pop(name)
+            codes = torch.empty((B, H, T, D // 2), dtype=torch.uint8, device=dev)
+            scales = torch.empty((B, H, T, D // 16), dtype=torch.uint8, device=dev)
+            ts = torch.empty(1, dtype=torch.float32, device=dev)
+            # the cache as it stands before the step (offline, untimed)
+            lib.quantize_call(NV, x.view(-1, D), codes.view(-1, D // 2), scales.view(-1, D // 16),
+                              ts, fp4.TSCALE_COMPUTE, ws)()
+            news.append(x[:, :, T - 1:T, :].contiguous())        # the step's new token
+            host[name] = x[0, 0].float().cpu().numpy()           # CPU-baseline sample
+            caches.append((codes, scales))
+            tss.append(ts)
+            del x
+        torch.cuda.synchronize()
+        q = d["q"]
+        host["q"] = q[0, :G].float().cpu().numpy()
+        pos = torch.full((B,), T - 1, dtype=torch.int32, device=dev)
+        lens = torch.full((B,), T, dtype=torch.int32, device=dev)
+        out = torch.empty((B, H * G, D), dtype=torch.bfloat16, device=dev)
+        wsa = torch.empty(max(16, fq.lib().fp4_attention_workspace_size(B, H * G, H, D, T)),
+                          dtype=torch.uint8, device=dev)
+        scale = 1.0 / (D ** 0.5)
+        pre = [lib.kv_append_call(NV, news[0], caches[0], pos, tss[0]),
+               lib.kv_append_call(NV, news[1], caches[1], pos, tss[1])]
+        att = lib.attention_call(NV, q, caches[0], tss[0], caches[1], tss[1], lens, scale, out,
+                                 fp4.BF16, wsa)
+        attn_bytes = 2 * B * H * T * (D // 2 + D // 16) + 2 * q.numel() + 2 * out.numel() + 4 * B + 8
+        append_bytes = 2 * (B * H * D * 2 + B * H * (D // 2 + D // 16)) + 4 * B + 8
+        W.update(pre=pre, dominant=[att], post=[], flops=0,
+                 dom_name="fp4_attention_decode (NVFP4 cache [32,8,32768,128], 64 query heads; "
+                          "split kernel + merge kernel)",
+                 dom_units=attn_bytes, dom_bound="hbm", dom_peak=HBM_PEAK_GBS,
+                 step_bytes=attn_bytes + append_bytes, quant_bytes=0,
+                 config={"workload": "attention", "batch": B, "kv_heads": H, "q_heads": H * G,
+                         "tokens": T, "head_dim": D, "format": "nvfp4", "q_dtype": "bf16",
+                         "out_dtype": "bf16"},
+                 dtype="e2m1 x e4m3 -> fp8 e4m3 (table) -> bf16 mfma (q.K), f32 softmax, "
+                       "f16 weights x f16 V mfma, f32 acc",
+                 host=dict(attention=host))
     else:  # kv
         d = workloads.kv(device=dev)
         calls_q, calls_d, outs = [], [], []
@@ -377,6 +450,27 @@ def cpu_baseline(workload, W, seconds):
         return {"value": rows * x.shape[1] * 2.5625 / dt / 1e9, "unit": "GB/s", "cores": 1,
                 "kind": "oracle", "sample": "MSE quantize of %d of the %d W rows, %d reps" % (
                     rows, h["w"].shape[0], reps)}
+    if workload == "attention":
+        # bounded sample: one (sequence, KV head) of the 256, all 32768 tokens,
+        # its 8 query heads; the cache rows quantized on the host
+        a = h["attention"]
+        T, D = a["k"].shape
+        kc, ks, kts = oracle.nvfp4_quantize(a["k"])
+        vc, vs, vts = oracle.nvfp4_quantize(a["v"])
+        kc, ks = kc.reshape(1, 1, T, D // 2), ks.reshape(1, 1, T, D // 16)
+        vc, vs = vc.reshape(1, 1, T, D // 2), vs.reshape(1, 1, T, D // 16)
+        q = a["q"][None]
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            oracle.attention_decode_ref("nvfp4", q, kc, ks, kts, vc, vs, vts, [T], 1.0 / D ** 0.5)
+            reps += 1
+            if time.perf_counter() - t0 >= seconds:
+                break
+        dt = (time.perf_counter() - t0) / reps
+        nbytes = 2 * T * (D // 2 + D // 16) + 2 * 2 * q.size
+        return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": cores, "kind": "oracle",
+                "sample": "attention of 8 query heads over one of the 256 (sequence, KV head) "
+                          "caches, 32768 tokens, %d reps" % reps}
     if workload == "kv":
         # bounded sample: the first rows of K, quantized and dequantized
         rows = 1 << 16
@@ -542,6 +636,9 @@ def main():
     elif args.workload == "mse":
         value = W["quant_bytes"] / (ms_step * 1e-3) / 1e9
         vunit = "GB/s"
+    elif args.workload == "attention":
+        value = W["step_bytes"] / (ms_step * 1e-3) / 1e9
+        vunit = "GB/s"
     else:
         value = W["flops"] / (ms_step * 1e-3) / 1e12
         vunit = "TFLOP/s"
@@ -564,7 +661,7 @@ def main():
         "host_enqueue_ms_per_step": round(enqueue_s * 1e3 / args.steps, 4),
         "gpu_fed_by_host": bool(gpu_fed),
     }
-    if args.workload not in ("kv", "mse", "w4a16"):
+    if args.workload not in ("kv", "mse", "w4a16", "attention"):
         out["quantize_bytes_per_step"] = W["quant_bytes"]
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.workload, W, args.cpu_seconds)

@@ -317,8 +317,8 @@ size_t fp4_attention_workspace_size(int64_t batch, int64_t q_heads, int64_t kv_h
  *                 (nearest even), 16-byte aligned.
  *   workspace     at least fp4_attention_workspace_size() bytes, 16-byte
  *                 aligned (split-token partial results).
- *   head_dim must be 128 and q_heads / kv_heads at most 16 (else
- *   FP4_EUNSUPPORTED); q_heads must be a multiple of kv_heads.
+ *   head_dim must be 128, q_heads / kv_heads at most 16 and t_max at most
+ *   2^26 (else FP4_EUNSUPPORTED); q_heads must be a multiple of kv_heads.
  *   Numerics: K . q on the matrix cores with FP8 K widened exactly to the
  *   16-bit type of q, fp32 sums; fp32 softmax; the weights rounded to fp16
  *   (nearest even) for the weighted sum of V, fp32 sums.

@@ -52,6 +52,7 @@ constexpr int kMaxGroup = 16;             // query heads per KV head (MFMA width
 constexpr int kPartPitch = kHeadDim + 4;
 constexpr int64_t kTargetWorkgroups = 2048;
 constexpr int64_t kMinChunk = 256;
+constexpr float kLazy = 8.0f;             // log2 headroom before the running max moves
 
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
@@ -106,6 +107,15 @@ __device__ __forceinline__ void transpose4(uint32_t x0, uint32_t x1, uint32_t x2
   t[3] = perm(u23h, u01h, 0x07060302u);
 }
 
+// Max over the 4 lane groups of 16 (lanes l, l ^ 16, l ^ 32, l ^ 48):
+// gfx950's row swaps, no LDS round trip.
+__device__ __forceinline__ float max_over_groups(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(c[0]), __uint_as_float(c[1]));
+}
+
 // FP8 bytes 2 HI, 2 HI + 1 of x -> two f16 / bf16 (exact).
 template <bool HI>
 __device__ __forceinline__ uint32_t f8_to_f16x2(uint32_t x) {
@@ -125,6 +135,146 @@ __device__ __forceinline__ v4f mfma_qk(u32x4 a, u32x4 b, v4f c) {
   }
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, a),
                                                __builtin_bit_cast(v8h, b), c, 0, 0, 0);
+}
+
+struct AttnState {
+  float m;                  // running max of the scaled scores (log2 domain)
+  v4f ol;                   // sum of the weights (every row of this tile holds it)
+  v4f o[8];                 // unnormalized output: o[i] row 4 g + e = element 32 g + 8 e + i
+};
+
+struct AttnPtrs {
+  const uint8_t* kc;        // this (sequence, head)'s K codes, K scales, V codes, V scales
+  const uint8_t* ks;
+  const uint8_t* vc;
+  const uint8_t* vs;
+  uint32_t koff, voff;      // this lane's byte offsets (token 0 of the step)
+  int t_end;
+};
+
+// One 32-token step of a wave at tokens t0 .. t0 + 31.  TAIL: the step runs
+// past t_end; its loads read token t_end - 1 instead (finite values) and its
+// scores are masked to weight 0.
+template <int FMT, int QDT, bool TAIL>
+__device__ __forceinline__ void attn_step(const AttnLds& L, const AttnPtrs& P, const u32x4 qf[4],
+                                          float c2, int t0, int r, int g, AttnState& st) {
+  constexpr bool NV = FMT == kFmtNV;
+  constexpr int kScaleBytes = NV ? kHeadDim / 16 : kHeadDim / 32;
+  constexpr int kSShift = NV ? 3 : 4;       // code offset -> scale offset
+  u32x4 kw[2];
+  uint32_t ksb[2], vw[8], vsb[8];
+  if (!TAIL) {
+    const uint8_t* kc = P.kc + (uint32_t)t0 * kRowBytes;
+    const uint8_t* ks = P.ks + (uint32_t)t0 * kScaleBytes;
+    const uint8_t* vc = P.vc + (uint32_t)t0 * kRowBytes;
+    const uint8_t* vs = P.vs + (uint32_t)t0 * kScaleBytes;
+    const uint32_t kso = P.koff >> kSShift, vso = P.voff >> kSShift;
+#pragma unroll
+    for (int T = 0; T < 2; ++T) {
+      kw[T] = *reinterpret_cast<const u32x4*>(kc + P.koff + 4 * T * kRowBytes);
+      if (NV) ksb[T] = *reinterpret_cast<const uint16_t*>(ks + kso + 4 * T * kScaleBytes);
+      else ksb[T] = ks[kso + 4 * T * kScaleBytes];
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      vw[j] = *reinterpret_cast<const uint32_t*>(vc + P.voff + j * kRowBytes);
+      vsb[j] = vs[vso + j * kScaleBytes];
+    }
+  } else {
+    const int t_last = P.t_end - 1;
+#pragma unroll
+    for (int T = 0; T < 2; ++T) {
+      int tk = t0 + 8 * (r >> 2) + 4 * T + (r & 3);
+      tk = tk < t_last ? tk : t_last;
+      const uint32_t o = (uint32_t)tk * kRowBytes + 16 * g;
+      kw[T] = *reinterpret_cast<const u32x4*>(P.kc + o);
+      if (NV) ksb[T] = *reinterpret_cast<const uint16_t*>(P.ks + (o >> kSShift));
+      else ksb[T] = P.ks[o >> kSShift];
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      int tv = t0 + 8 * g + j;
+      tv = tv < t_last ? tv : t_last;
+      const uint32_t o = (uint32_t)tv * kRowBytes + 4 * r;
+      vw[j] = *reinterpret_cast<const uint32_t*>(P.vc + o);
+      vsb[j] = P.vs[o >> kSShift];
+    }
+  }
+
+  // ---- S = K Q^T ----------------------------------------------------------------
+  v4f s[2];
+#pragma unroll
+  for (int T = 0; T < 2; ++T) {
+    s[T] = (v4f){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const uint32_t sb = NV ? ((c < 2) ? (ksb[T] & 0xFFu) : (ksb[T] >> 8)) : ksb[T];
+      uint32_t ev, od;
+      lookup8(kw[T][c], L.lut[0][sb], ev, od);
+      u32x4 kf;
+      if (QDT == kInBF16) {
+        kf = (u32x4){f8_to_bf16x2<false>(ev), f8_to_bf16x2<true>(ev),
+                     f8_to_bf16x2<false>(od), f8_to_bf16x2<true>(od)};
+      } else {
+        kf = (u32x4){f8_to_f16x2<false>(ev), f8_to_f16x2<true>(ev),
+                     f8_to_f16x2<false>(od), f8_to_f16x2<true>(od)};
+      }
+      s[T] = mfma_qk<QDT>(kf, qf[c], s[T]);
+    }
+  }
+
+  // ---- V fragments: element 8 r + i of tokens 8 g .. 8 g + 7 ----------------------
+  uint32_t ev[8], od[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) lookup8(vw[j], L.lut[1][vsb[j]], ev[j], od[j]);
+  uint32_t te0[4], te1[4], to0[4], to1[4];
+  transpose4(ev[0], ev[1], ev[2], ev[3], te0);
+  transpose4(ev[4], ev[5], ev[6], ev[7], te1);
+  transpose4(od[0], od[1], od[2], od[3], to0);
+  transpose4(od[4], od[5], od[6], od[7], to1);
+
+  // ---- online softmax, log2 domain: weight 2^(c2 s - m).  The running max m
+  // moves only when the step's scores exceed it by more than kLazy, so the
+  // weights stay below 2^kLazy (well inside fp16) and rescales are rare ------
+  float sv[8];
+  float mx = -__builtin_inff();
+#pragma unroll
+  for (int T = 0; T < 2; ++T)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      float v = s[T][e];
+      if (TAIL && t0 + 8 * g + 4 * T + e >= P.t_end) v = -__builtin_inff();
+      sv[4 * T + e] = v;
+      mx = fmaxf(mx, v);
+    }
+  mx = max_over_groups(mx) * c2;
+  if (__any(mx > st.m + kLazy)) {
+    const float m_new = fmaxf(st.m, mx);
+    const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);
+    st.ol *= alpha;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) st.o[i] *= alpha;
+    st.m = m_new;
+  }
+  const float nm = -st.m;
+  float p[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) p[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[j], c2, nm));
+  const v8h pf = {(_Float16)p[0], (_Float16)p[1], (_Float16)p[2], (_Float16)p[3],
+                  (_Float16)p[4], (_Float16)p[5], (_Float16)p[6], (_Float16)p[7]};
+
+  // ---- O += P V; the weights' sum on the matrix cores as well (ones x P) ------------
+  const v8h ones = {1, 1, 1, 1, 1, 1, 1, 1};
+  st.ol = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pf, st.ol, 0, 0, 0);
+#pragma unroll
+  for (int a = 0; a < 4; ++a) {
+    const u32x4 fe = {f8_to_f16x2<false>(te0[a]), f8_to_f16x2<true>(te0[a]),
+                      f8_to_f16x2<false>(te1[a]), f8_to_f16x2<true>(te1[a])};
+    st.o[2 * a] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, fe), pf, st.o[2 * a], 0, 0, 0);
+    const u32x4 fo = {f8_to_f16x2<false>(to0[a]), f8_to_f16x2<true>(to0[a]),
+                      f8_to_f16x2<false>(to1[a]), f8_to_f16x2<true>(to1[a])};
+    st.o[2 * a + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, fo), pf, st.o[2 * a + 1], 0, 0, 0);
+  }
 }
 
 template <int FMT, int QDT>
@@ -159,13 +309,18 @@ __global__ __launch_bounds__(kThreads) void attn_decode_kernel(AttnArgs A) {
     }
   }
 
-  // ---- this workgroup's tokens ------------------------------------------------------
+  // ---- this workgroup's tokens (offsets inside this (sequence, head)'s cache) --------
   int64_t len = A.seq_lens[b];
   if (len < 0) len = 0;
   if (len > A.t_max) len = A.t_max;
-  const int64_t t_begin = (int64_t)split * A.chunk;
-  const int64_t t_end = t_begin + A.chunk < len ? t_begin + A.chunk : len;
+  const int64_t tb = (int64_t)split * A.chunk;
+  const int t_begin = (int)(tb < len ? tb : len);
+  const int t_end = (int)(tb + A.chunk < len ? tb + A.chunk : len);
   const int64_t row0 = bh * A.t_max;
+  const uint8_t* kcb = A.kc + row0 * kRowBytes;
+  const uint8_t* ksb_ = A.ks + row0 * kScaleBytes;
+  const uint8_t* vcb = A.vc + row0 * kRowBytes;
+  const uint8_t* vsb_ = A.vs + row0 * kScaleBytes;
 
   // ---- Q fragments: query head r (zero for r >= G), elements 32 g + 8 c + {0,2,4,6,1,3,5,7}
   u32x4 qf[4];
@@ -178,120 +333,35 @@ __global__ __launch_bounds__(kThreads) void attn_decode_kernel(AttnArgs A) {
       if (live) w = *reinterpret_cast<const u32x4*>(qrow + 8 * c);
       qf[c] = (u32x4){perm(w.y, w.x, 0x05040100u), perm(w.w, w.z, 0x05040100u),
                       perm(w.y, w.x, 0x07060302u), perm(w.w, w.z, 0x07060302u)};
+      if (A.scale_log2 < 0.0f) qf[c] ^= 0x80008000u;  // scale * (K . q) = |scale| * (K . -q), exact
     }
   }
+  const float c2 = fabsf(A.scale_log2);
   __syncthreads();                                    // the table is complete
 
-  float m = -__builtin_inff(), l = 0.0f;
-  v4f o[8];
+  AttnState st;
+  st.m = -__builtin_inff();
+  st.ol = (v4f){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int i = 0; i < 8; ++i) o[i] = (v4f){0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < 8; ++i) st.o[i] = (v4f){0.f, 0.f, 0.f, 0.f};
+  // loop-invariant byte offsets of this lane's first K row (tile T adds 4 T
+  // rows), first V row (token j adds j rows) and their scale bytes
+  const uint32_t koff = (uint32_t)(8 * (r >> 2) + (r & 3)) * kRowBytes + 16 * g;
+  const uint32_t voff = (uint32_t)(8 * g) * kRowBytes + 4 * r;
+  const AttnPtrs P = {kcb, ksb_, vcb, vsb_, koff, voff, t_end};
 
-  for (int64_t t0 = t_begin + (int64_t)wave * kStep; t0 < t_end; t0 += kWaves * kStep) {
-    // ---- loads (masked tokens read the last live token: always in bounds) ----
-    u32x4 kw[2];
-    uint32_t ksb[2];
-#pragma unroll
-    for (int T = 0; T < 2; ++T) {
-      int64_t tk = t0 + 8 * (r >> 2) + 4 * T + (r & 3);
-      if (tk >= t_end) tk = t_end - 1;
-      kw[T] = *reinterpret_cast<const u32x4*>(A.kc + (row0 + tk) * kRowBytes + 16 * g);
-      if (NV) ksb[T] = *reinterpret_cast<const uint16_t*>(A.ks + (row0 + tk) * kScaleBytes + 2 * g);
-      else ksb[T] = A.ks[(row0 + tk) * kScaleBytes + g];
-    }
-    uint32_t vw[8], vsb[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int64_t tv = t0 + 8 * g + j;
-      const int64_t ta = tv < t_end ? tv : t_end - 1;
-      vw[j] = *reinterpret_cast<const uint32_t*>(A.vc + (row0 + ta) * kRowBytes + 4 * r);
-      vsb[j] = A.vs[(row0 + ta) * kScaleBytes + (NV ? (r >> 1) : (r >> 2))];
-      if (tv >= t_end) { vw[j] = 0u; vsb[j] = 0u; }   // exact zeros, whatever the cache holds
-    }
-
-    // ---- S = K Q^T ----------------------------------------------------------------
-    v4f s[2];
-#pragma unroll
-    for (int T = 0; T < 2; ++T) {
-      s[T] = (v4f){0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const uint32_t sb = NV ? ((c < 2) ? (ksb[T] & 0xFFu) : (ksb[T] >> 8)) : ksb[T];
-        uint32_t ev, od;
-        lookup8(kw[T][c], L.lut[0][sb], ev, od);
-        u32x4 kf;
-        if (QDT == kInBF16) {
-          kf = (u32x4){f8_to_bf16x2<false>(ev), f8_to_bf16x2<true>(ev),
-                       f8_to_bf16x2<false>(od), f8_to_bf16x2<true>(od)};
-        } else {
-          kf = (u32x4){f8_to_f16x2<false>(ev), f8_to_f16x2<true>(ev),
-                       f8_to_f16x2<false>(od), f8_to_f16x2<true>(od)};
-        }
-        s[T] = mfma_qk<QDT>(kf, qf[c], s[T]);
-      }
-    }
-
-    // ---- V fragments: element 8 r + i of tokens 8 g .. 8 g + 7 ----------------------
-    uint32_t ev[8], od[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) lookup8(vw[j], L.lut[1][vsb[j]], ev[j], od[j]);
-    uint32_t te0[4], te1[4], to0[4], to1[4];
-    transpose4(ev[0], ev[1], ev[2], ev[3], te0);
-    transpose4(ev[4], ev[5], ev[6], ev[7], te1);
-    transpose4(od[0], od[1], od[2], od[3], to0);
-    transpose4(od[4], od[5], od[6], od[7], to1);
-
-    // ---- online softmax (log2 domain) ------------------------------------------------
-    float x[8];
-    float mx = -__builtin_inff();
-#pragma unroll
-    for (int T = 0; T < 2; ++T)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int64_t tok = t0 + 8 * g + 4 * T + e;
-        const float v = s[T][e] * A.scale_log2;
-        x[4 * T + e] = tok < t_end ? v : -__builtin_inff();
-        mx = fmaxf(mx, x[4 * T + e]);
-      }
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m, mx);
-    if (__any(m_new > m)) {
-      const float alpha = __builtin_amdgcn_exp2f(m - m_new);
-      l *= alpha;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) o[i] *= alpha;
-      m = m_new;
-    }
-    float p[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      p[j] = __builtin_amdgcn_exp2f(x[j] - m);
-      l += p[j];
-    }
-    const v8h pf = {(_Float16)p[0], (_Float16)p[1], (_Float16)p[2], (_Float16)p[3],
-                    (_Float16)p[4], (_Float16)p[5], (_Float16)p[6], (_Float16)p[7]};
-
-    // ---- O += P V --------------------------------------------------------------------
-#pragma unroll
-    for (int a = 0; a < 4; ++a) {
-      const u32x4 fe = {f8_to_f16x2<false>(te0[a]), f8_to_f16x2<true>(te0[a]),
-                        f8_to_f16x2<false>(te1[a]), f8_to_f16x2<true>(te1[a])};
-      o[2 * a] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, fe), pf, o[2 * a], 0, 0, 0);
-      const u32x4 fo = {f8_to_f16x2<false>(to0[a]), f8_to_f16x2<true>(to0[a]),
-                        f8_to_f16x2<false>(to1[a]), f8_to_f16x2<true>(to1[a])};
-      o[2 * a + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, fo), pf, o[2 * a + 1], 0, 0, 0);
-    }
-  }
+  int t0 = t_begin + wave * kStep;
+  for (; t0 + kStep <= t_end; t0 += kWaves * kStep) attn_step<FMT, QDT, false>(L, P, qf, c2, t0, r, g, st);
+  if (t0 < t_end) attn_step<FMT, QDT, true>(L, P, qf, c2, t0, r, g, st);
+  const float m = st.m;
+  const float l = st.ol[0];                           // sum of the fp16 weights, all lane groups
 
   // ---- merge the 4 waves, write this split's partial ----------------------------------
-  l += __shfl_xor(l, 16);
-  l += __shfl_xor(l, 32);
   if (r < A.g) {
 #pragma unroll
     for (int i = 0; i < 8; ++i)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) L.part[wave][r][32 * g + 8 * e + i] = o[i][e];
+      for (int e = 0; e < 4; ++e) L.part[wave][r][32 * g + 8 * e + i] = st.o[i][e];
     if (g == 0) {
       L.pm[wave][r] = m;
       L.pl[wave][r] = l;

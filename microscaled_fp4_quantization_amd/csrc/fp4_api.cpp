@@ -277,7 +277,7 @@ fp4_status fp4_kv_append(fp4_format fmt, const void* x, fp4_dtype x_dtype, int64
 size_t fp4_attention_workspace_size(int64_t batch, int64_t q_heads, int64_t kv_heads,
                                     int64_t head_dim, int64_t t_max) {
   if (batch <= 0 || kv_heads <= 0 || q_heads <= 0 || q_heads % kv_heads != 0 || t_max <= 0 ||
-      head_dim != 128 || q_heads / kv_heads > 16)
+      head_dim != 128 || q_heads / kv_heads > 16 || t_max > (int64_t(1) << 26))
     return 0;
   return attention_workspace_bytes(batch, q_heads, kv_heads, t_max);
 }
@@ -299,7 +299,7 @@ fp4_status fp4_attention_decode(fp4_format fmt, const void* q, fp4_dtype q_dtype
   }
   if (batch < 0 || q_heads <= 0 || kv_heads <= 0 || t_max <= 0 || head_dim <= 0) return FP4_EINVAL;
   if (q_heads % kv_heads != 0 || head_dim % block_of(fmt) != 0) return FP4_EINVAL;
-  if (head_dim != 128 || q_heads / kv_heads > 16) return FP4_EUNSUPPORTED;
+  if (head_dim != 128 || q_heads / kv_heads > 16 || t_max > (int64_t(1) << 26)) return FP4_EUNSUPPORTED;
   if (q_heads > (int64_t(1) << 20) || kv_heads > (int64_t(1) << 20)) return FP4_EINVAL;
   if (batch > 0 && (kv_heads > kMaxElements / batch || q_heads > kMaxElements / batch))
     return FP4_EINVAL;

@@ -227,6 +227,7 @@ def test_attention_decode_rejects_bad_arguments():
     assert g(hq=15) == E                      # q heads not a multiple of kv heads
     assert g(d=64) == U                       # head_dim 128 only
     assert g(hq=34) == U                      # more than 16 query heads per kv head
+    assert g(t_max=(1 << 26) + 1) == U        # token offsets are 32-bit inside a sequence
     assert g(qdt=fp4.F32) == U
     assert g(qdt=fp4.E4M3) == E
     assert g(odt=fp4.F16) == U
