@@ -281,8 +281,9 @@ fp4_status fp4_quantize_gemm(fp4_format fmt, const void* x, fp4_dtype x_dtype,
  *                 tensor scale for the tokens it already holds); MXFP4: NULL.
  *   Each row is quantized exactly as fp4_quantize quantizes it (GIVEN mode
  *   for NVFP4); rows of the cache that are not written are not touched.
- *   k % block == 0; batch, heads or t_new of 0 enqueue nothing.
- *   Returns FP4_OK, FP4_EINVAL or FP4_EHIP.
+ *   k % block == 0; batch, heads or t_new of 0 enqueue nothing; one call
+ *   appends fewer than 2^34 values (else FP4_EUNSUPPORTED).
+ *   Returns FP4_OK, FP4_EINVAL, FP4_EUNSUPPORTED or FP4_EHIP.
  */
 fp4_status fp4_kv_append(fp4_format fmt, const void* x, fp4_dtype x_dtype, int64_t batch,
                          int64_t heads, int64_t t_new, int64_t k, const int32_t* positions,

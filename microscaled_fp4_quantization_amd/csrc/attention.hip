@@ -26,16 +26,19 @@
 //
 // One 32-token step of a wave (lane l: r = l % 16, g = l / 16):
 //   S = K Q^T, v_mfma_f32_16x16x32_{bf16,f16}, two 16-token tiles.  Row m
-//     of tile T is token 8 (m / 4) + 4 T + m % 4, so the C layout (lane l
-//     holds rows 4 g + e) leaves lane l the scores of tokens 8 g .. 8 g + 7
-//     for query head r: exactly the k-slots of the B operand of P V.  Lane
+//     of tile T is token 16 T + 4 (m % 4) + m / 4, so the C layout (lane l
+//     holds rows 4 g + e) leaves lane l the scores of tokens 4 j + g
+//     (j = 4 T + e = 0..7) for query head r: exactly the k-slots of the B
+//     operand of P V.  Lane
 //     group g holds head-dim elements 32 g .. 32 g + 31 (16 code bytes);
 //     inside a lane the k-slots follow the even/odd split of the table
 //     lookup ({0, 2, 4, 6, 1, 3, 5, 7}) and Q is loaded in that order.
 //   O += P V, v_mfma_f32_16x16x32_f16, 8 MFMAs: MFMA i has head-dim element
 //     8 r + i in row r.  Lane l loads the 4 code bytes at 4 r of tokens
-//     8 g + j (j = 0..7), looks them up and transposes the 8 x 8 FP8 bytes
-//     so that fragment i holds element 8 r + i of those 8 tokens.
+//     4 j + g (j = 0..7), looks them up and transposes the 8 x 8 FP8 bytes
+//     so that fragment i holds element 8 r + i of those 8 tokens.  Every
+//     cache load of a wave reads whole rows of consecutive tokens: 16 rows
+//     (1 KiB) for a K tile, 4 rows for a V word.
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -152,54 +155,87 @@ struct AttnPtrs {
   int t_end;
 };
 
-// One 32-token step of a wave at tokens t0 .. t0 + 31.  TAIL: the step runs
-// past t_end; its loads read token t_end - 1 instead (finite values) and its
-// scores are masked to weight 0.
-template <int FMT, int QDT, bool TAIL>
-__device__ __forceinline__ void attn_step(const AttnLds& L, const AttnPtrs& P, const u32x4 qf[4],
-                                          float c2, int t0, int r, int g, AttnState& st) {
+// The cache words of one step, loaded a step ahead.
+struct StepRegs {
+  u32x4 kw[2];              // K codes: tiles T = 0, 1
+  uint32_t ksb[2];          // their scale bytes (NVFP4: two blocks in 16 bits)
+  uint32_t vw[8];           // V codes of tokens 4 j + g
+  uint32_t vsb[8];          // their scale bytes
+};
+
+// K (V) words of the step at tokens t0 .. t0 + 31.  A step inside the live
+// range addresses the cache through a uniform base plus this lane's
+// offsets; a step running past t_end reads token t_end - 1 for the tokens
+// beyond it (finite values; their weights are 0).
+template <int FMT>
+__device__ __forceinline__ void load_k(const AttnPtrs& P, int t0, int r, int g, StepRegs& R) {
   constexpr bool NV = FMT == kFmtNV;
   constexpr int kScaleBytes = NV ? kHeadDim / 16 : kHeadDim / 32;
   constexpr int kSShift = NV ? 3 : 4;       // code offset -> scale offset
-  u32x4 kw[2];
-  uint32_t ksb[2], vw[8], vsb[8];
-  if (!TAIL) {
+  if (t0 + kStep <= P.t_end) {
     const uint8_t* kc = P.kc + (uint32_t)t0 * kRowBytes;
     const uint8_t* ks = P.ks + (uint32_t)t0 * kScaleBytes;
-    const uint8_t* vc = P.vc + (uint32_t)t0 * kRowBytes;
-    const uint8_t* vs = P.vs + (uint32_t)t0 * kScaleBytes;
-    const uint32_t kso = P.koff >> kSShift, vso = P.voff >> kSShift;
+    const uint32_t kso = P.koff >> kSShift;
 #pragma unroll
     for (int T = 0; T < 2; ++T) {
-      kw[T] = *reinterpret_cast<const u32x4*>(kc + P.koff + 4 * T * kRowBytes);
-      if (NV) ksb[T] = *reinterpret_cast<const uint16_t*>(ks + kso + 4 * T * kScaleBytes);
-      else ksb[T] = ks[kso + 4 * T * kScaleBytes];
-    }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      vw[j] = *reinterpret_cast<const uint32_t*>(vc + P.voff + j * kRowBytes);
-      vsb[j] = vs[vso + j * kScaleBytes];
+      R.kw[T] = *reinterpret_cast<const u32x4*>(kc + P.koff + 16 * T * kRowBytes);
+      if (NV) R.ksb[T] = *reinterpret_cast<const uint16_t*>(ks + kso + 16 * T * kScaleBytes);
+      else R.ksb[T] = ks[kso + 16 * T * kScaleBytes];
     }
   } else {
     const int t_last = P.t_end - 1;
 #pragma unroll
     for (int T = 0; T < 2; ++T) {
-      int tk = t0 + 8 * (r >> 2) + 4 * T + (r & 3);
+      int tk = t0 + 16 * T + 4 * (r & 3) + (r >> 2);
       tk = tk < t_last ? tk : t_last;
       const uint32_t o = (uint32_t)tk * kRowBytes + 16 * g;
-      kw[T] = *reinterpret_cast<const u32x4*>(P.kc + o);
-      if (NV) ksb[T] = *reinterpret_cast<const uint16_t*>(P.ks + (o >> kSShift));
-      else ksb[T] = P.ks[o >> kSShift];
-    }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      int tv = t0 + 8 * g + j;
-      tv = tv < t_last ? tv : t_last;
-      const uint32_t o = (uint32_t)tv * kRowBytes + 4 * r;
-      vw[j] = *reinterpret_cast<const uint32_t*>(P.vc + o);
-      vsb[j] = P.vs[o >> kSShift];
+      R.kw[T] = *reinterpret_cast<const u32x4*>(P.kc + o);
+      if (NV) R.ksb[T] = *reinterpret_cast<const uint16_t*>(P.ks + (o >> kSShift));
+      else R.ksb[T] = P.ks[o >> kSShift];
     }
   }
+}
+
+template <int FMT>
+__device__ __forceinline__ void load_v(const AttnPtrs& P, int t0, int r, int g, StepRegs& R) {
+  constexpr bool NV = FMT == kFmtNV;
+  constexpr int kScaleBytes = NV ? kHeadDim / 16 : kHeadDim / 32;
+  constexpr int kSShift = NV ? 3 : 4;
+  if (t0 + kStep <= P.t_end) {
+    const uint8_t* vc = P.vc + (uint32_t)t0 * kRowBytes;
+    const uint8_t* vs = P.vs + (uint32_t)t0 * kScaleBytes;
+    const uint32_t vso = P.voff >> kSShift;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      R.vw[j] = *reinterpret_cast<const uint32_t*>(vc + P.voff + 4 * j * kRowBytes);
+      R.vsb[j] = vs[vso + 4 * j * kScaleBytes];
+    }
+  } else {
+    const int t_last = P.t_end - 1;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      int tv = t0 + 4 * j + g;
+      tv = tv < t_last ? tv : t_last;
+      const uint32_t o = (uint32_t)tv * kRowBytes + 4 * r;
+      R.vw[j] = *reinterpret_cast<const uint32_t*>(P.vc + o);
+      R.vsb[j] = P.vs[o >> kSShift];
+    }
+  }
+}
+
+// One 32-token step of a wave at tokens t0 .. t0 + 31 on the words in R;
+// refills R with the words of the wave's next step tn as soon as each part
+// has been used (K after the scores, V after its table lookups), so those
+// loads run under this step's arithmetic.  TAIL: the step runs past t_end
+// and its scores beyond it are masked to weight 0.
+template <int FMT, int QDT, bool TAIL>
+__device__ __forceinline__ void attn_step(const AttnLds& L, const AttnPtrs& P, const u32x4 qf[4],
+                                          float c2, int t0, int tn, int r, int g, StepRegs& R,
+                                          AttnState& st) {
+  constexpr bool NV = FMT == kFmtNV;
+  const bool more = tn < P.t_end;
+  const u32x4 kw[2] = {R.kw[0], R.kw[1]};
+  const uint32_t ksb[2] = {R.ksb[0], R.ksb[1]};
 
   // ---- S = K Q^T ----------------------------------------------------------------
   v4f s[2];
@@ -222,11 +258,13 @@ __device__ __forceinline__ void attn_step(const AttnLds& L, const AttnPtrs& P, c
       s[T] = mfma_qk<QDT>(kf, qf[c], s[T]);
     }
   }
+  if (more) load_k<FMT>(P, tn, r, g, R);
 
-  // ---- V fragments: element 8 r + i of tokens 8 g .. 8 g + 7 ----------------------
+  // ---- V fragments: element 8 r + i of tokens 4 j + g, j = 0..7 ---------------------
   uint32_t ev[8], od[8];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) lookup8(vw[j], L.lut[1][vsb[j]], ev[j], od[j]);
+  for (int j = 0; j < 8; ++j) lookup8(R.vw[j], L.lut[1][R.vsb[j]], ev[j], od[j]);
+  if (more) load_v<FMT>(P, tn, r, g, R);
   uint32_t te0[4], te1[4], to0[4], to1[4];
   transpose4(ev[0], ev[1], ev[2], ev[3], te0);
   transpose4(ev[4], ev[5], ev[6], ev[7], te1);
@@ -243,7 +281,7 @@ __device__ __forceinline__ void attn_step(const AttnLds& L, const AttnPtrs& P, c
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       float v = s[T][e];
-      if (TAIL && t0 + 8 * g + 4 * T + e >= P.t_end) v = -__builtin_inff();
+      if (TAIL && t0 + 16 * T + 4 * e + g >= P.t_end) v = -__builtin_inff();
       sv[4 * T + e] = v;
       mx = fmaxf(mx, v);
     }
@@ -277,8 +315,11 @@ __device__ __forceinline__ void attn_step(const AttnLds& L, const AttnPtrs& P, c
   }
 }
 
+// 4 waves per SIMD (16 per CU, 4 workgroups: the LDS of a CU holds 4): the
+// register budget that leaves keeps the accumulators out of AGPRs.
 template <int FMT, int QDT>
-__global__ __launch_bounds__(kThreads) void attn_decode_kernel(AttnArgs A) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3)))
+void attn_decode_kernel(AttnArgs A) {
   __shared__ AttnLds L;
   constexpr bool NV = FMT == kFmtNV;
   constexpr int kScaleBytes = NV ? kHeadDim / 16 : kHeadDim / 32;
@@ -344,15 +385,21 @@ __global__ __launch_bounds__(kThreads) void attn_decode_kernel(AttnArgs A) {
   st.ol = (v4f){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int i = 0; i < 8; ++i) st.o[i] = (v4f){0.f, 0.f, 0.f, 0.f};
-  // loop-invariant byte offsets of this lane's first K row (tile T adds 4 T
-  // rows), first V row (token j adds j rows) and their scale bytes
-  const uint32_t koff = (uint32_t)(8 * (r >> 2) + (r & 3)) * kRowBytes + 16 * g;
-  const uint32_t voff = (uint32_t)(8 * g) * kRowBytes + 4 * r;
+  // loop-invariant byte offsets of this lane's first K row (tile T adds 16 T
+  // rows), first V row (word j adds 4 j rows) and their scale bytes
+  const uint32_t koff = (uint32_t)(4 * (r & 3) + (r >> 2)) * kRowBytes + 16 * g;
+  const uint32_t voff = (uint32_t)g * kRowBytes + 4 * r;
   const AttnPtrs P = {kcb, ksb_, vcb, vsb_, koff, voff, t_end};
 
   int t0 = t_begin + wave * kStep;
-  for (; t0 + kStep <= t_end; t0 += kWaves * kStep) attn_step<FMT, QDT, false>(L, P, qf, c2, t0, r, g, st);
-  if (t0 < t_end) attn_step<FMT, QDT, true>(L, P, qf, c2, t0, r, g, st);
+  StepRegs R;
+  if (t0 < t_end) {
+    load_k<FMT>(P, t0, r, g, R);
+    load_v<FMT>(P, t0, r, g, R);
+  }
+  for (; t0 + kStep <= t_end; t0 += kWaves * kStep)
+    attn_step<FMT, QDT, false>(L, P, qf, c2, t0, t0 + kWaves * kStep, r, g, R, st);
+  if (t0 < t_end) attn_step<FMT, QDT, true>(L, P, qf, c2, t0, t_end, r, g, R, st);
   const float m = st.m;
   const float l = st.ol[0];                           // sum of the fp16 weights, all lane groups
 

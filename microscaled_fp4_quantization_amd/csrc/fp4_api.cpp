@@ -261,6 +261,7 @@ fp4_status fp4_kv_append(fp4_format fmt, const void* x, fp4_dtype x_dtype, int64
   if (bh > 0 && (k > kMaxElements / (bh * t_max) || (t_new > 0 && k > kMaxElements / (bh * t_new))))
     return FP4_EINVAL;
   if (bh == 0 || t_new == 0) return FP4_OK;
+  if (bh * t_new > (int64_t(1) << 31) / (k / 8) - 1) return FP4_EUNSUPPORTED;
   if (!x || !positions || !codes || !scales) return FP4_EINVAL;
   if (!aligned(x, 16) || !aligned(codes, 16) || !aligned(scales, 4) || !aligned(positions, 4))
     return FP4_EINVAL;

@@ -57,7 +57,8 @@ hipError_t launch_gemm_w4a16(int fmt, int64_t m, int64_t n, int64_t k, const voi
 
 // KV cache append: rows of x [batch, heads, t_new, k] quantized (NVFP4 with
 // the given tensor scale) into a [batch, heads, t_max, ...] cache at
-// positions[b] + i; rows outside [0, t_max) are not stored.
+// positions[b] + i; rows outside [0, t_max) are not stored.  At most 2^31 - 1
+// chunks of 8 values per call.
 hipError_t launch_kv_append(int fmt, const void* x, int dtype, int64_t batch, int64_t heads,
                             int64_t t_new, int64_t k, const int32_t* positions, int64_t t_max,
                             uint8_t* codes, uint8_t* scales, const float* tscale,

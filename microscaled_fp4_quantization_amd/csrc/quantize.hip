@@ -241,38 +241,30 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
 // the chunk index from source to destination.
 template <int FMT, int DT>
 __global__ __launch_bounds__(kThreads) void kv_append_kernel(
-    const void* __restrict__ x, int64_t nchunks, int cpr, int64_t t_new, int64_t heads,
+    const void* __restrict__ x, uint32_t nchunks, uint32_t cpr, uint32_t t_new, uint32_t heads,
     const int32_t* __restrict__ positions, int64_t t_max, uint32_t* __restrict__ codes,
     uint8_t* __restrict__ scales, const float* __restrict__ tscale) {
+  // one chunk per thread: an append is a few rows, so the grid, not a loop,
+  // covers it (32-bit index arithmetic: fewer than 2^31 chunks per call)
   const int lane = threadIdx.x & 63;
   float s_t = 1.0f, d = 6.0f;
   if (FMT == kFmtNV) {
     s_t = *tscale;
     d = 6.0f * s_t;
   }
-  for (int64_t base = (int64_t)blockIdx.x * kChunksPerTrip; base < nchunks;
-       base += (int64_t)gridDim.x * kChunksPerTrip) {
-    float v[kUnroll][8];
-#pragma unroll
-    for (int j = 0; j < kUnroll; ++j) {
-      const int64_t c = base + j * kThreads + threadIdx.x;
-      load_chunk<DT>(x, c, c < nchunks, v[j]);
-    }
-#pragma unroll
-    for (int j = 0; j < kUnroll; ++j) {
-      const int64_t c = base + j * kThreads + threadIdx.x;
-      int64_t cdst = 0;
-      bool ok = false;
-      if (c < nchunks) {
-        const int64_t row = c / cpr, cr = c - row * cpr;
-        const int64_t bh = row / t_new, i = row - bh * t_new;
-        const int64_t p = (int64_t)positions[bh / heads] + i;
-        ok = p >= 0 && p < t_max;
-        cdst = (bh * t_max + (ok ? p : 0)) * cpr + cr;
-      }
-      quantize_chunk<FMT>(v[j], lane, s_t, d, cdst, ok, codes, scales);
-    }
+  const uint32_t c = blockIdx.x * (uint32_t)kThreads + threadIdx.x;
+  float v[8];
+  load_chunk<DT>(x, c, c < nchunks, v);
+  int64_t cdst = 0;
+  bool ok = false;
+  if (c < nchunks) {
+    const uint32_t row = c / cpr, cr = c - row * cpr;
+    const uint32_t bh = row / t_new, i = row - bh * t_new;
+    const int64_t p = (int64_t)positions[bh / heads] + i;
+    ok = p >= 0 && p < t_max;
+    cdst = ((int64_t)bh * t_max + (ok ? p : 0)) * cpr + cr;
   }
+  quantize_chunk<FMT>(v, lane, s_t, d, cdst, ok, codes, scales);
 }
 
 // NVFP4 with the tensor scale computed from the data, for small tensors
@@ -486,13 +478,14 @@ hipError_t launch_kv_append(int fmt, const void* x, int dtype, int64_t batch, in
                             int64_t t_new, int64_t k, const int32_t* positions, int64_t t_max,
                             uint8_t* codes, uint8_t* scales, const float* tscale,
                             hipStream_t stream) {
-  const int64_t nchunks = batch * heads * t_new * (k / 8);
-  const int grid = (int)((nchunks + kChunksPerTrip - 1) / kChunksPerTrip);
+  const uint32_t nchunks = (uint32_t)(batch * heads * t_new * (k / 8));
+  const uint32_t grid = (nchunks + kThreads - 1) / kThreads;
   uint32_t* c32 = reinterpret_cast<uint32_t*>(codes);
-  const int cpr = (int)(k / 8);
+  const uint32_t cpr = (uint32_t)(k / 8);
 #define FP4_KV_APPEND(F, D)                                                                  \
   hipLaunchKernelGGL((kv_append_kernel<F, D>), dim3(grid), dim3(kThreads), 0, stream, x,     \
-                     nchunks, cpr, t_new, heads, positions, t_max, c32, scales, tscale)
+                     nchunks, cpr, (uint32_t)t_new, (uint32_t)heads, positions, t_max, c32,  \
+                     scales, tscale)
   if (fmt == kFmtNV) {
     if (dtype == kInF32) FP4_KV_APPEND(kFmtNV, kInF32);
     else if (dtype == kInBF16) FP4_KV_APPEND(kFmtNV, kInBF16);

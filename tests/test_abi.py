@@ -207,6 +207,7 @@ def test_kv_append_rejects_bad_arguments():
     assert g(t_max=0) == E
     assert g(tn=-1) == E
     assert g(tn=0, x=None, pos=None) == fp4.OK
+    assert g(b=1 << 14, h=64, tn=1 << 10, t_max=1 << 10) == fp4.EUNSUPPORTED   # 2^34 values
     assert g(b=0, x=None) == fp4.OK
 
 
