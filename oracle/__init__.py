@@ -19,7 +19,10 @@ Sources (the web pages this method is described on):
     MXFP4 i AWQ?" (E4M3 = 4 exponent / 3 mantissa bits, E2M1 range about +-6,
     ~4.5 bits per value, MXFP4 = OCP blocks of 32 with an E8M0 scale).
   * hyper.ai, paper 2509.23202 (MR-GPTQ), Abstract (blockwise Hadamard
-    transforms, rotation fused into the weights, online for activations).
+    transforms, rotation fused into the weights, online for activations;
+    MR-GPTQ as a variant of GPTQ).
+  * pimento.cloud, section "Czym roznia sie FP8, NVFP4, MXFP4 i AWQ?" (GPTQ
+    quantizes layer by layer with error correction).
   * hyper.ai story on the NVFP4 KV cache (new K/V written to the cache in
     NVFP4, dequantization to FP8 before attention).
 
@@ -40,6 +43,9 @@ Parity status per function (what pins it in the CPU tests):
                               positions, dropped out-of-range rows
   attention_decode_ref        exact rows, means, 3:1 weights, GQA head map,
                               FP8 ties and saturation, one-hot key
+  gptq_quantize               diagonal Hessian = plain quantizer (bit-exact),
+                              equals the surgeon form with fresh sub-Hessian
+                              inverses, beats round-to-nearest, dead features
 """
 
 from .formats import (
@@ -71,6 +77,7 @@ from .quant import (
 from .hadamard import hadamard_blocks, HADAMARD_NORM
 from .gemm import gemm_ref, gemm_ref_entries, gemm_w4a16_ref
 from .attention import kv_append_ref, kv_fp8_values, attention_decode_ref
+from .gptq import gptq_hessian, gptq_factor, gptq_quantize, gptq_layer_error
 
 __all__ = [
     "E2M1_MAGNITUDES", "e2m1_decode", "e2m1_encode", "e4m3_decode",
@@ -80,4 +87,5 @@ __all__ = [
     "dequantize_exact_f64", "pack_nibbles", "unpack_nibbles",
     "hadamard_blocks", "HADAMARD_NORM", "gemm_ref", "gemm_ref_entries", "gemm_w4a16_ref",
     "kv_append_ref", "kv_fp8_values", "attention_decode_ref",
+    "gptq_hessian", "gptq_factor", "gptq_quantize", "gptq_layer_error",
 ]
