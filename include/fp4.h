@@ -334,6 +334,44 @@ fp4_status fp4_attention_decode(fp4_format fmt, const void* q, fp4_dtype q_dtype
                                 float softmax_scale, void* out, fp4_dtype out_dtype,
                                 void* workspace, size_t workspace_bytes, void* stream);
 
+/* Bytes of device workspace fp4_gptq_quantize needs (0: sizes not accepted). */
+size_t fp4_gptq_workspace_size(int64_t n, int64_t k, int64_t n_calib);
+
+/*
+ * fp4_gptq_quantize -- MR-GPTQ: quantize a weight matrix to FP4 with GPTQ's
+ * error correction on blockwise-Hadamard-rotated weights.
+ * Defines: hyper.ai, paper 2509.23202 (MR-GPTQ), Abstract (GPTQ adapted to
+ * FP4 with blockwise Hadamard transforms, the rotation fused into the
+ * weights); pimento.cloud "FP8, NVFP4 czy AWQ?", section "Czym roznia sie
+ * FP8, NVFP4, MXFP4 i AWQ?" (GPTQ: layer-wise quantization with error
+ * correction).
+ *   w, w_dtype    weights [n, k] (F32 / BF16 / F16), 16-byte aligned.
+ *   x, x_dtype    calibration activations [n_calib, k], 16-byte aligned.
+ *   damp          H_jj += damp * mean(diag H) (GPTQ's damping; 0.01 typical).
+ *   rotate        nonzero: W and X rotated by the format's blockwise
+ *                 Hadamard (16 NVFP4, 32 MXFP4) first; the result is then
+ *                 the operand for activations quantized with
+ *                 fp4_hadamard_quantize.  0: no rotation (plain GPTQ).
+ *   codes, scales, tensor_scale  out: as fp4_quantize writes them for the
+ *                 (rotated) weights; NVFP4's tensor scale max |W| / 2688
+ *                 (device float), MXFP4: must be NULL.
+ *   Computes H = 2/N X^T X (fp64), zeroes the weights of features with
+ *   H_jj = 0, damps, takes U = the upper Cholesky factor of H^-1 and walks
+ *   the columns: each quantization block's scale from its current weights
+ *   (the quantizer's rule), each column quantized as the quantizer does it
+ *   (fp32), err = (w - q) / U_jj corrected into the later columns.  Linear
+ *   algebra in fp64.  k % 128 == 0, k <= 16384 (else FP4_EUNSUPPORTED).
+ *   workspace     at least fp4_gptq_workspace_size() bytes, 16-byte aligned
+ *                 (fp64 copies of W and X, two k x k matrices).
+ *   Returns FP4_OK, FP4_EINVAL, FP4_EUNSUPPORTED or FP4_EHIP.  A Hessian
+ *   that is not positive definite after damping gives NaN weights.
+ */
+fp4_status fp4_gptq_quantize(fp4_format fmt, const void* w, fp4_dtype w_dtype, int64_t n,
+                             int64_t k, const void* x, fp4_dtype x_dtype, int64_t n_calib,
+                             double damp, int rotate, uint8_t* codes, uint8_t* scales,
+                             float* tensor_scale, void* workspace, size_t workspace_bytes,
+                             void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -6,7 +6,8 @@ include/fp4.h); `fp4` is its Python binding.
 
 from . import fp4
 from .fp4 import (quantize, quantize_mse, hadamard_quantize, dequantize, gemm, gemm_w4a16,
-                  quantize_gemm, kv_cache, kv_append, attention_decode, lib)
+                  quantize_gemm, kv_cache, kv_append, attention_decode, gptq_quantize, lib)
 
 __all__ = ["fp4", "quantize", "quantize_mse", "hadamard_quantize", "dequantize", "gemm", "gemm_w4a16",
-           "quantize_gemm", "kv_cache", "kv_append", "attention_decode", "lib"]
+           "quantize_gemm", "kv_cache", "kv_append", "attention_decode", "gptq_quantize",
+           "lib"]

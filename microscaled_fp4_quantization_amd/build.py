@@ -23,6 +23,7 @@ SOURCES = [
     "gemm_large.hip",
     "gemm.hip",
     "attention.hip",
+    "gptq.hip",
 ]
 
 # -ffp-contract=off: every a*b and a+b rounds on its own (no fused

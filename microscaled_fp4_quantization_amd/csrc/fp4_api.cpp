@@ -325,4 +325,40 @@ fp4_status fp4_attention_decode(fp4_format fmt, const void* q, fp4_dtype q_dtype
                                           static_cast<hipStream_t>(stream)));
 }
 
+size_t fp4_gptq_workspace_size(int64_t n, int64_t k, int64_t n_calib) {
+  if (n <= 0 || k <= 0 || n_calib <= 0 || k % 128 != 0 || k > 16384) return 0;
+  if (n > kMaxElements / k || n_calib > kMaxElements / k) return 0;
+  return gptq_workspace_bytes(n, k, n_calib);
+}
+
+fp4_status fp4_gptq_quantize(fp4_format fmt, const void* w, fp4_dtype w_dtype, int64_t n,
+                             int64_t k, const void* x, fp4_dtype x_dtype, int64_t n_calib,
+                             double damp, int rotate, uint8_t* codes, uint8_t* scales,
+                             float* tensor_scale, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  if (!valid_format(fmt)) return FP4_EINVAL;
+  if (w_dtype != FP4_F32 && w_dtype != FP4_BF16 && w_dtype != FP4_F16) return FP4_EINVAL;
+  if (x_dtype != FP4_F32 && x_dtype != FP4_BF16 && x_dtype != FP4_F16) return FP4_EINVAL;
+  if (n <= 0 || k <= 0 || n_calib <= 0 || k % 128 != 0) return FP4_EINVAL;
+  if (!(damp >= 0.0) || damp > 1e30) return FP4_EINVAL;
+  if (k > 16384) return FP4_EUNSUPPORTED;
+  if (n > kMaxElements / k || n_calib > kMaxElements / k) return FP4_EINVAL;
+  if ((n + 63) / 64 > (int64_t(1) << 31) || n * k / 8 > (int64_t(1) << 31) * 256 ||
+      n_calib * k / 8 > (int64_t(1) << 31) * 256)
+    return FP4_EUNSUPPORTED;
+  if (!w || !x || !codes || !scales || !workspace) return FP4_EINVAL;
+  if (!aligned(w, 16) || !aligned(x, 16) || !aligned(codes, 16) || !aligned(scales, 4) ||
+      !aligned(workspace, 16))
+    return FP4_EINVAL;
+  if (fmt == FP4_NVFP4) {
+    if (!tensor_scale || !aligned(tensor_scale, 4)) return FP4_EINVAL;
+  } else if (tensor_scale) {
+    return FP4_EINVAL;
+  }
+  if (workspace_bytes < gptq_workspace_bytes(n, k, n_calib)) return FP4_EINVAL;
+  return from_hip(launch_gptq((int)fmt, w, (int)w_dtype, n, k, x, (int)x_dtype, n_calib, damp,
+                              rotate != 0, codes, scales, tensor_scale, workspace,
+                              static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

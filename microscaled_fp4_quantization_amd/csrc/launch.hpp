@@ -74,3 +74,14 @@ hipError_t launch_attention_decode(int fmt, const void* q, int q_dtype, int64_t 
                                    const float* v_tscale, int64_t t_max, const int32_t* seq_lens,
                                    float softmax_scale, void* out, int out_dtype, void* workspace,
                                    hipStream_t stream);
+
+// Blockwise Hadamard (hadamard = 16 or 32; 0 copies) of n values, fp32
+// arithmetic, widened to fp64.
+hipError_t launch_rotate_f64(const void* x, int dtype, int64_t n, int hadamard, double* out,
+                             hipStream_t stream);
+
+// MR-GPTQ of W [n, k] with calibration X [n_calib, k] (k % 128 == 0).
+size_t gptq_workspace_bytes(int64_t n, int64_t k, int64_t n_calib);
+hipError_t launch_gptq(int fmt, const void* w, int w_dtype, int64_t n, int64_t k, const void* x,
+                       int x_dtype, int64_t n_calib, double damp, bool rotate, uint8_t* codes,
+                       uint8_t* scales, float* tscale, void* workspace, hipStream_t stream);

@@ -267,6 +267,24 @@ __global__ __launch_bounds__(kThreads) void kv_append_kernel(
   quantize_chunk<FMT>(v, lane, s_t, d, cdst, ok, codes, scales);
 }
 
+// Blockwise Hadamard rotation alone (HAD = 16 or 32; 0 copies), fp32
+// arithmetic exactly as in the fused quantizer, widened to fp64: the
+// rotated weights and calibration activations of GPTQ.
+template <int DT, int HAD>
+__global__ __launch_bounds__(kThreads) void rotate_f64_kernel(const void* __restrict__ x,
+                                                              int64_t nchunks,
+                                                              double* __restrict__ out) {
+  const int lane = threadIdx.x & 63;
+  const int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  float v[8];
+  load_chunk<DT>(x, c, c < nchunks, v);
+  if (HAD) fwht_chunk<HAD>(v, lane);
+  if (c < nchunks) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) out[8 * c + i] = (double)v[i];
+  }
+}
+
 // NVFP4 with the tensor scale computed from the data, for small tensors
 // (decode activations): one workgroup holds the whole tensor in registers,
 // reduces its max |x| and quantizes, in a single launch instead of two.
@@ -496,6 +514,24 @@ hipError_t launch_kv_append(int fmt, const void* x, int dtype, int64_t batch, in
     else FP4_KV_APPEND(kFmtMX, kInF16);
   }
 #undef FP4_KV_APPEND
+  return hipGetLastError();
+}
+
+hipError_t launch_rotate_f64(const void* x, int dtype, int64_t n, int hadamard, double* out,
+                             hipStream_t stream) {
+  const int64_t nchunks = n / 8;
+  const dim3 grid((unsigned)((nchunks + kThreads - 1) / kThreads));
+#define FP4_ROT(D, H) \
+  hipLaunchKernelGGL((rotate_f64_kernel<D, H>), grid, dim3(kThreads), 0, stream, x, nchunks, out)
+#define FP4_ROT_H(D)                    \
+  if (hadamard == 16) FP4_ROT(D, 16);   \
+  else if (hadamard == 32) FP4_ROT(D, 32); \
+  else FP4_ROT(D, 0)
+  if (dtype == kInF32) { FP4_ROT_H(kInF32); }
+  else if (dtype == kInBF16) { FP4_ROT_H(kInBF16); }
+  else { FP4_ROT_H(kInF16); }
+#undef FP4_ROT_H
+#undef FP4_ROT
   return hipGetLastError();
 }
 

@@ -29,7 +29,8 @@ EXPORTS = ("fp4_status_string", "fp4_quantize_workspace_size", "fp4_quantize",
            "fp4_hadamard_quantize", "fp4_dequantize", "fp4_gemm_workspace_size",
            "fp4_gemm", "fp4_quantize_gemm_workspace_size", "fp4_quantize_gemm",
            "fp4_quantize_mse", "fp4_gemm_w4a16", "fp4_kv_append",
-           "fp4_attention_workspace_size", "fp4_attention_decode")
+           "fp4_attention_workspace_size", "fp4_attention_decode", "fp4_gptq_workspace_size",
+           "fp4_gptq_quantize")
 
 _lib = None
 
@@ -80,6 +81,11 @@ def lib():
     L.fp4_attention_decode.argtypes = [i32, vp, i32, i64, i64, i64, i64, vp, vp, vp, vp, vp, vp,
                                        i64, vp, ctypes.c_float, vp, i32, vp, sz, vp]
     L.fp4_attention_decode.restype = i32
+    L.fp4_gptq_workspace_size.argtypes = [i64, i64, i64]
+    L.fp4_gptq_workspace_size.restype = sz
+    L.fp4_gptq_quantize.argtypes = [i32, vp, i32, i64, i64, vp, i32, i64, ctypes.c_double, i32,
+                                    vp, vp, vp, vp, sz, vp]
+    L.fp4_gptq_quantize.restype = i32
     _lib = L
     return L
 
@@ -295,3 +301,27 @@ def attention_decode(q, k_cache, v_cache, seq_lens, fmt="nvfp4", k_tscale=None, 
                                 _stream(q))
     _check(st, "fp4_attention_decode")
     return out
+
+
+def gptq_quantize(w, x, fmt="nvfp4", damp=0.01, rotate=True, workspace=None):
+    """MR-GPTQ of the weights w [n, k] with calibration activations x
+    [n_calib, k] (CUDA tensors, fp32 / bf16 / fp16).  Returns (codes,
+    scales, tensor scale or None) of the (rotated) weights."""
+    f = _fmt(fmt)
+    if w.dim() != 2 or x.dim() != 2 or w.shape[1] != x.shape[1]:
+        raise ValueError("w must be [n, k] and x [n_calib, k]")
+    n, k = w.shape
+    N = x.shape[0]
+    codes = torch.empty((n, k // 2), dtype=torch.uint8, device=w.device)
+    scales = torch.empty((n, k // BLOCK[f]), dtype=torch.uint8, device=w.device)
+    ts = torch.empty(1, dtype=torch.float32, device=w.device) if f == NVFP4 else None
+    L = lib()
+    need = L.fp4_gptq_workspace_size(n, k, N)
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=w.device)
+    st = L.fp4_gptq_quantize(f, _ptr(w), _IN_DTYPES[w.dtype], n, k, _ptr(x), _IN_DTYPES[x.dtype], N,
+                             float(damp), 1 if rotate else 0, _ptr(codes), _ptr(scales), _ptr(ts),
+                             _ptr(workspace), workspace.numel() * workspace.element_size(),
+                             _stream(w))
+    _check(st, "fp4_gptq_quantize")
+    return codes, scales, ts

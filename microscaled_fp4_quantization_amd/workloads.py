@@ -21,6 +21,10 @@ rounded to bfloat16 (round to nearest even) where the workload is bf16.
            one decode step, Q bf16 [32, 64, 128] ~ N(0,1) (64 query heads over
            8 KV heads: grouped-query attention with 8 query heads per KV
            head), drawn after K and V.
+  calibration  GPTQ calibration activations X bf16 [n_calib, k]: per-channel
+           scales c ~ U(0.5, 4) times N(0,1) plus a shared rank-32 part
+           (N(0,1) [n_calib, 32] @ N(0, 1/32) [32, k]), so that X^T X has
+           off-diagonal structure; drawn c, Z, then the two rank-32 factors.
   random_cache  uniformly random cache bytes (codes 0..255; NVFP4 scale
            bytes uniform in [0x30, 0x50), i.e. 0.5 .. 7.5; MXFP4 scale bytes
            uniform in [120, 130), i.e. 2^-7 .. 2^2) from numpy's PCG64 with
@@ -118,6 +122,15 @@ def attention(device="cpu", seed=0, batch=32, kv_heads=8, q_heads=64, tokens=327
     g = _gen(device, seed + 1)
     out["q"] = torch.randn((batch, q_heads, head_dim), generator=g, device=device).to(torch.bfloat16)
     return out
+
+
+def calibration(device="cpu", seed=0, n_calib=2048, k=4096, rank=32):
+    g = _gen(device, seed)
+    c = torch.rand((k,), generator=g, device=device) * 3.5 + 0.5
+    z = torch.randn((n_calib, k), generator=g, device=device)
+    a = torch.randn((n_calib, rank), generator=g, device=device)
+    b = torch.randn((rank, k), generator=g, device=device) / rank ** 0.5
+    return (z * c + a @ b).to(torch.bfloat16)
 
 
 def random_cache(batch, heads, tokens, head_dim, fmt="nvfp4", seed=0):

@@ -94,12 +94,14 @@ def _group_scale(fmt, wg, s_t):
     return sb, r, deq, nonzero
 
 
-def gptq_quantize(fmt, w, x, damp=0.01, rotate=True):
+def gptq_quantize(fmt, w, x, damp=0.01, rotate=True, rows=None):
     """MR-GPTQ of the weights w [n, k] with calibration activations x [N, k].
 
     Returns (packed codes [n, k/2], scale bytes [n, k/block], tensor scale
     (NVFP4; None for MXFP4)) of the (rotated) weights: the operand the W4A4
     GEMM takes with activations quantized by the fused Hadamard quantizer.
+    rows: only these rows (the rows are independent once H and the tensor
+    scale, which are computed from all of w and x, are fixed).
     """
     b = _block(fmt)
     W32 = np.asarray(w, dtype=np.float32)
@@ -112,6 +114,9 @@ def gptq_quantize(fmt, w, x, damp=0.01, rotate=True):
     W = W32.astype(np.float64)
     W[:, dead] = 0.0
     s_t = np.float32(nvfp4_tensor_scale(W.astype(np.float32))) if fmt == "nvfp4" else None
+    if rows is not None:
+        W = W[np.asarray(rows)]
+        n = W.shape[0]
     codes = np.zeros((n, k), dtype=np.uint8)
     scales = np.zeros((n, k // b), dtype=np.uint8)
     for j in range(k):

@@ -245,6 +245,35 @@ def test_attention_decode_rejects_bad_arguments():
     assert L.fp4_attention_workspace_size(2, 16, 2, 64, 1000) == 0
 
 
+def test_gptq_rejects_bad_arguments():
+    L = fp4.lib()
+    f = L.fp4_gptq_quantize
+    need = L.fp4_gptq_workspace_size(64, 256, 128)
+    assert need > 64 * 256 * 8
+
+    def g(fmt=NV, w=FAKE, wdt=fp4.BF16, n=64, k=256, x=FAKE, xdt=fp4.BF16, N=128, damp=0.01,
+          rot=1, codes=FAKE, scales=FAKE, ts=FAKE, ws=FAKE, wsb=None):
+        return f(fmt, w, wdt, n, k, x, xdt, N, damp, rot, codes, scales, ts, ws,
+                 need if wsb is None else wsb, None)
+
+    E = fp4.EINVAL
+    assert g(fmt=2) == E
+    assert g(k=192) == E                      # k % 128
+    assert g(n=0) == E
+    assert g(N=0) == E
+    assert g(damp=-1.0) == E
+    assert g(damp=float("nan")) == E
+    assert g(wdt=fp4.E4M3) == E
+    assert g(w=FAKE_ODD) == E
+    assert g(x=None) == E
+    assert g(ts=None) == E                    # NVFP4 writes its tensor scale
+    assert g(fmt=MX) == E                     # MXFP4 has none
+    assert g(ws=None) == E
+    assert g(wsb=need - 1) == E
+    assert g(k=16384 + 128) == fp4.EUNSUPPORTED
+    assert L.fp4_gptq_workspace_size(64, 100, 128) == 0
+
+
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(fp4, "_lib", None)
     monkeypatch.setattr(fp4, "LIB_PATH", str(tmp_path / "missing.so"))
