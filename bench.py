@@ -27,6 +27,9 @@ every input already resident in HBM:
            and V (fp4_kv_append, given tensor scales) + attention of 64 query
            heads (8 per KV head, bf16 q) over all 32768 tokens with the cache
            dequantized to FP8 (fp4_attention_decode), bf16 out.
+  gptq     MR-GPTQ of the decode workload's weight W [14336, 4096] to NVFP4
+           (blockwise Hadamard, 2048 calibration rows, fp4_gptq_quantize):
+           the offline weight path; fp64 arithmetic (roofline "alu").
 Prints one JSON line.  The timed region is K steps back to back between one
 pair of HIP events (value, ms_per_step).  The dominant kernel is then timed
 the same way over the K steps' launches of it alone; its algorithmic bytes
@@ -47,6 +50,7 @@ sys.path.insert(0, ROOT)
 METRIC = "W4A4 NVFP4 GEMM TFLOPS + quantize GB/s, % of MI355X roofline"
 HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = {"fp4": 10100.0, "f16": 2500.0}
+FP64_FMA_PEAK_TFLOPS = 78.6    # fp64 vector with fused multiply-adds (GPTQ's products)
 # fp64 vector: 78.6 TFLOP/s counts a fused multiply-add as two; the search's
 # separate multiplies and adds issue at half that rate (256 CUs x 64 lanes x
 # 2.4 GHz = 39.3 T operations/s).
@@ -63,7 +67,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", default="decode",
                    choices=["decode", "prefill", "rotated_nv", "rotated_mx", "kv", "mse", "w4a16",
-                            "attention"])
+                            "attention", "gptq"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--copy-bytes", type=int, default=0,
@@ -87,6 +91,7 @@ DOMINANT = {
     "mse": ("quantize_mse_kernel<1, true>", ["quantize.hip", "device_common.hpp"]),
     "w4a16": ("gemm_nv_stream<2, 2>", ["gemm_skinny.hip"]),
     "attention": ("attn_decode_kernel<0, 1>", ["attention.hip", "device_common.hpp"]),
+    "gptq": ("gemm_f64_kernel", ["gptq.hip", "quantize.hip", "device_common.hpp"]),
 }
 COPY_KERNEL = "copyBuffer"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
@@ -231,6 +236,16 @@ class Lib:
         fn = self.L.fp4_attention_decode
         return lambda: self.check(fn(*args), "attention_decode")
 
+    def gptq_call(self, fmt, w, x, codes, scales, ts, ws):
+        from microscaled_fp4_quantization_amd import fp4
+        n, k = w.shape
+        dt = {self.torch.bfloat16: fp4.BF16, self.torch.float32: fp4.F32, self.torch.float16: fp4.F16}
+        args = (fmt, self.p(w), dt[w.dtype], n, k, self.p(x), dt[x.dtype], x.shape[0],
+                ctypes.c_double(0.01), 1, self.p(codes), self.p(scales), self.p(ts), self.p(ws),
+                ws.numel(), self.stream)
+        fn = self.L.fp4_gptq_quantize
+        return lambda: self.check(fn(*args), "gptq_quantize")
+
     def dequant_call(self, fmt, codes, scales, ts, out, out_dtype):
         rows, k = codes.shape[0], codes.shape[1] * 2
         args = (fmt, self.p(codes), self.p(scales), self.p(ts), rows, k, self.p(out), out_dtype, self.stream)
@@ -353,6 +368,26 @@ def setup(workload, torch, fq, lib):
                          "scale_rule": "least squared error", "x_dtype": "bf16"},
                  dtype="f32 quantize, f64 error sums",
                  host=dict(w=w))
+    elif workload == "gptq":
+        w = workloads.decode(device=dev)["w"]
+        n, k = w.shape
+        N = 2048
+        x = workloads.calibration(device=dev, n_calib=N, k=k)
+        codes = torch.empty((n, k // 2), dtype=torch.uint8, device=dev)
+        scales = torch.empty((n, k // 16), dtype=torch.uint8, device=dev)
+        ts = torch.empty(1, dtype=torch.float32, device=dev)
+        ws = torch.empty(fq.lib().fp4_gptq_workspace_size(n, k, N), dtype=torch.uint8, device=dev)
+        q = lib.gptq_call(NV, w, x, codes, scales, ts, ws)
+        flops = 2 * N * k * k + 2 * k ** 3 // 3 + n * k * k
+        W.update(pre=[], dominant=[q], post=[], flops=flops,
+                 dom_name="fp4_gptq_quantize (NVFP4, W bf16 [%d, %d], %d calibration rows; all "
+                          "its kernels)" % (n, k, N),
+                 dom_units=flops, dom_bound="alu", dom_peak=FP64_FMA_PEAK_TFLOPS, quant_bytes=0,
+                 config={"workload": "gptq", "rows": n, "k": k, "n_calib": N, "format": "nvfp4",
+                         "hadamard": 16, "damp": 0.01, "w_dtype": "bf16", "x_dtype": "bf16"},
+                 dtype="f64 (Hessian, Cholesky, inverse, error correction), f32 quantize",
+                 host=dict(gptq=dict(w=w[:64].float().cpu().numpy(), x=x.float().cpu().numpy(),
+                                     w_amax_rows=w.float().abs().amax().item())))
     elif workload == "attention":
         B, H, T, D, G = 32, 8, 32768, 128, 8
         d = workloads.attention(device=dev, batch=B, kv_heads=H, q_heads=H * G, tokens=T,
@@ -450,6 +485,23 @@ def cpu_baseline(workload, W, seconds):
         return {"value": rows * x.shape[1] * 2.5625 / dt / 1e9, "unit": "GB/s", "cores": 1,
                 "kind": "oracle", "sample": "MSE quantize of %d of the %d W rows, %d reps" % (
                     rows, h["w"].shape[0], reps)}
+    if workload == "gptq":
+        # bounded sample: the full Hessian and factor, error correction of the
+        # first 64 weight rows (rows are independent once the factor exists)
+        g = h["gptq"]
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            oracle.gptq_quantize("nvfp4", g["w"], g["x"])
+            reps += 1
+            if time.perf_counter() - t0 >= seconds:
+                break
+        dt = (time.perf_counter() - t0) / reps
+        N, k = g["x"].shape
+        rows = g["w"].shape[0]
+        flops = 2 * N * k * k + 2 * k ** 3 // 3 + rows * k * k
+        return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+                "sample": "GPTQ of %d of the 14336 weight rows with the full %dx%d Hessian and "
+                          "its factor, %d reps" % (rows, k, k, reps)}
     if workload == "attention":
         # bounded sample: one (sequence, KV head) of the 256, all 32768 tokens,
         # its 8 query heads; the cache rows quantized on the host
@@ -626,7 +678,7 @@ def main():
         unit = "GB/s"
     elif W["dom_bound"] == "alu":
         achieved = W["dom_units"] / (dom_avg * 1e-3) / 1e12
-        unit = "TFLOP/s (fp64, unfused)"
+        unit = "TFLOP/s (fp64, unfused)" if args.workload == "mse" else "TFLOP/s (fp64)"
     else:
         achieved = W["dom_units"] / (dom_avg * 1e-3) / 1e12
         unit = "TFLOP/s"
@@ -639,6 +691,9 @@ def main():
     elif args.workload == "attention":
         value = W["step_bytes"] / (ms_step * 1e-3) / 1e9
         vunit = "GB/s"
+    elif args.workload == "gptq":
+        value = W["flops"] / (ms_step * 1e-3) / 1e12
+        vunit = "TFLOP/s (fp64)"
     else:
         value = W["flops"] / (ms_step * 1e-3) / 1e12
         vunit = "TFLOP/s"
@@ -661,7 +716,7 @@ def main():
         "host_enqueue_ms_per_step": round(enqueue_s * 1e3 / args.steps, 4),
         "gpu_fed_by_host": bool(gpu_fed),
     }
-    if args.workload not in ("kv", "mse", "w4a16", "attention"):
+    if args.workload not in ("kv", "mse", "w4a16", "attention", "gptq"):
         out["quantize_bytes_per_step"] = W["quant_bytes"]
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.workload, W, args.cpu_seconds)

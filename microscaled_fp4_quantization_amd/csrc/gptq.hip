@@ -37,12 +37,17 @@ constexpr int kNB = 32;          // Cholesky / inverse panel width
 constexpr int kBC = 128;         // GPTQ column block
 constexpr int kRows = 64;        // rows per GPTQ workgroup
 constexpr int kGT = 64;          // gemm_f64 tile
-constexpr int kGK = 16;          // gemm_f64 k-chunk
+constexpr int kGK = 32;          // gemm_f64 k-chunk
 
 // ---- C = beta C + alpha A B, general strides ------------------------------------
 // A(i, t) = a[i * sa0 + t * sa1] (M x K), B(t, j) = b[t * sb0 + j * sb1]
 // (K x N), C[i * ldc + j] (M x N).  beta == 0 never reads C.  64 x 64 tile
-// per workgroup, 4 x 4 per thread (rows ty + 16 a, columns tx + 16 b).
+// per workgroup of 4 waves, each wave a 32 x 32 quarter as 2 x 2
+// v_mfma_f64_16x16x4_f64 tiles (lane l: A row l % 16 / B column l % 16 at
+// k-slot l / 16; C column l % 16).  The tiles go through LDS in
+// chunks of 32 k; the next chunk's global loads are in flight while the
+// current chunk is multiplied.  (Unlike the fp32 16 x 16 MFMAs, the fp64
+// one leaves item e of lane l at row 4 e + l / 16.)
 struct GemmArgs {
   const double* a;
   const double* b;
@@ -52,59 +57,72 @@ struct GemmArgs {
   double alpha, beta;
 };
 
+typedef double v4d __attribute__((ext_vector_type(4)));
+
 __global__ __launch_bounds__(256) void gemm_f64_kernel(GemmArgs G) {
   __shared__ double As[kGK][kGT + 1];
   __shared__ double Bs[kGK][kGT + 1];
-  const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int i0 = blockIdx.y * kGT, j0 = blockIdx.x * kGT;
-  // loaders: the 1024 elements of a tile, fastest along the unit-stride side
+  const int wr = 32 * (wave >> 1), wc = 32 * (wave & 1);
+  // loaders: 2048 elements of each tile, fastest along the unit-stride side
   const bool a_i_fast = (G.sa0 < 0 ? -G.sa0 : G.sa0) <= (G.sa1 < 0 ? -G.sa1 : G.sa1);
   const bool b_j_fast = (G.sb1 < 0 ? -G.sb1 : G.sb1) <= (G.sb0 < 0 ? -G.sb0 : G.sb0);
-  double acc[4][4];
+  double ra[8], rb[8];
+  auto fetch = [&](int t0) {
 #pragma unroll
-  for (int x = 0; x < 4; ++x)
+    for (int e = 0; e < 8; ++e) {
+      const int idx = tid + 256 * e;
+      const int ii = a_i_fast ? (idx & 63) : (idx >> 5);
+      const int tt = a_i_fast ? (idx >> 6) : (idx & 31);
+      const int gi = i0 + ii, gt = t0 + tt;
+      ra[e] = (gi < G.m && gt < G.k) ? G.a[gi * G.sa0 + gt * G.sa1] : 0.0;
+      const int jj = b_j_fast ? (idx & 63) : (idx >> 5);
+      const int tb = b_j_fast ? (idx >> 6) : (idx & 31);
+      const int gj = j0 + jj, gtb = t0 + tb;
+      rb[e] = (gj < G.n && gtb < G.k) ? G.b[gtb * G.sb0 + gj * G.sb1] : 0.0;
+    }
+  };
+  v4d acc[2][2];
 #pragma unroll
-    for (int y = 0; y < 4; ++y) acc[x][y] = 0.0;
+  for (int x = 0; x < 2; ++x)
+#pragma unroll
+    for (int y = 0; y < 2; ++y) acc[x][y] = (v4d){0.0, 0.0, 0.0, 0.0};
+  fetch(0);
   for (int t0 = 0; t0 < G.k; t0 += kGK) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
+    for (int e = 0; e < 8; ++e) {
       const int idx = tid + 256 * e;
-      const int ii = a_i_fast ? (idx & 63) : (idx >> 4);
-      const int tt = a_i_fast ? (idx >> 6) : (idx & 15);
-      const int gi = i0 + ii, gt = t0 + tt;
-      As[tt][ii] = (gi < G.m && gt < G.k) ? G.a[gi * G.sa0 + gt * G.sa1] : 0.0;
-      const int jj = b_j_fast ? (idx & 63) : (idx >> 4);
-      const int tb = b_j_fast ? (idx >> 6) : (idx & 15);
-      const int gj = j0 + jj, gtb = t0 + tb;
-      Bs[tb][jj] = (gj < G.n && gtb < G.k) ? G.b[gtb * G.sb0 + gj * G.sb1] : 0.0;
+      As[a_i_fast ? (idx >> 6) : (idx & 31)][a_i_fast ? (idx & 63) : (idx >> 5)] = ra[e];
+      Bs[b_j_fast ? (idx >> 6) : (idx & 31)][b_j_fast ? (idx & 63) : (idx >> 5)] = rb[e];
     }
     __syncthreads();
+    if (t0 + kGK < G.k) fetch(t0 + kGK);
 #pragma unroll
-    for (int t = 0; t < kGK; ++t) {
-      double av[4], bv[4];
-#pragma unroll
-      for (int x = 0; x < 4; ++x) av[x] = As[t][ty + 16 * x];
-#pragma unroll
-      for (int y = 0; y < 4; ++y) bv[y] = Bs[t][tx + 16 * y];
-#pragma unroll
-      for (int x = 0; x < 4; ++x)
-#pragma unroll
-        for (int y = 0; y < 4; ++y) acc[x][y] = __builtin_fma(av[x], bv[y], acc[x][y]);
+    for (int ks = 0; ks < kGK; ks += 4) {
+      const int kk = ks + (lane >> 4), r = lane & 15;
+      const double a0 = As[kk][wr + r], a1 = As[kk][wr + 16 + r];
+      const double b0 = Bs[kk][wc + r], b1 = Bs[kk][wc + 16 + r];
+      acc[0][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(a0, b0, acc[0][0], 0, 0, 0);
+      acc[0][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(a0, b1, acc[0][1], 0, 0, 0);
+      acc[1][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(a1, b0, acc[1][0], 0, 0, 0);
+      acc[1][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(a1, b1, acc[1][1], 0, 0, 0);
     }
     __syncthreads();
   }
 #pragma unroll
-  for (int x = 0; x < 4; ++x) {
-    const int gi = i0 + ty + 16 * x;
-    if (gi >= G.m) continue;
+  for (int x = 0; x < 2; ++x)
 #pragma unroll
-    for (int y = 0; y < 4; ++y) {
-      const int gj = j0 + tx + 16 * y;
-      if (gj >= G.n) continue;
-      double* p = G.c + gi * G.ldc + gj;
-      *p = G.beta == 0.0 ? G.alpha * acc[x][y] : G.beta * *p + G.alpha * acc[x][y];
-    }
-  }
+    for (int y = 0; y < 2; ++y)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int gi = i0 + wr + 16 * x + 4 * e + (lane >> 4);
+        const int gj = j0 + wc + 16 * y + (lane & 15);
+        if (gi < G.m && gj < G.n) {
+          double* p = G.c + gi * G.ldc + gj;
+          *p = G.beta == 0.0 ? G.alpha * acc[x][y][e] : G.beta * *p + G.alpha * acc[x][y][e];
+        }
+      }
 }
 
 hipError_t gemm_f64(const GemmArgs& G, hipStream_t stream) {
@@ -163,20 +181,36 @@ __global__ __launch_bounds__(256) void fill_f64_kernel(double* __restrict__ p, i
   if (idx < count) p[idx] = 0.0;
 }
 
-// max |W| (as fp32, a monotone rounding) -> NVFP4 tensor scale fp32(A) / 2688.
-__global__ __launch_bounds__(1024) void gptq_tscale_kernel(const double* __restrict__ W,
-                                                           int64_t count, float* __restrict__ ts) {
-  __shared__ float part[1024];
+// max |W| (as fp32, a monotone rounding) -> NVFP4 tensor scale fp32(A) / 2688,
+// in two passes: one partial maximum per workgroup, then one workgroup.
+constexpr int kMaxParts = 1024;
+
+__global__ __launch_bounds__(256) void gptq_amax_kernel(const double* __restrict__ W, int64_t count,
+                                                        float* __restrict__ parts) {
+  __shared__ float red[256];
   float m = 0.0f;
-  for (int64_t i = threadIdx.x; i < count; i += 1024) m = fmaxf(m, fabsf((float)W[i]));
-  part[threadIdx.x] = m;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < count; i += (int64_t)gridDim.x * 256)
+    m = fmaxf(m, fabsf((float)W[i]));
+  red[threadIdx.x] = m;
   __syncthreads();
-  for (int w = 512; w >= 1; w >>= 1) {
-    if ((int)threadIdx.x < w) part[threadIdx.x] = fmaxf(part[threadIdx.x], part[threadIdx.x + w]);
+  for (int w = 128; w >= 1; w >>= 1) {
+    if ((int)threadIdx.x < w) red[threadIdx.x] = fmaxf(red[threadIdx.x], red[threadIdx.x + w]);
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) parts[blockIdx.x] = red[0];
+}
+
+__global__ __launch_bounds__(kMaxParts) void gptq_tscale_kernel(const float* __restrict__ parts,
+                                                                int nparts, float* __restrict__ ts) {
+  __shared__ float red[kMaxParts];
+  red[threadIdx.x] = (int)threadIdx.x < nparts ? parts[threadIdx.x] : 0.0f;
+  __syncthreads();
+  for (int w = kMaxParts / 2; w >= 1; w >>= 1) {
+    if ((int)threadIdx.x < w) red[threadIdx.x] = fmaxf(red[threadIdx.x], red[threadIdx.x + w]);
     __syncthreads();
   }
   if (threadIdx.x == 0) {
-    float s_t = part[0] / 2688.0f;                 // 6 * 448
+    const float s_t = red[0] / 2688.0f;             // 6 * 448
     ts[0] = s_t == 0.0f ? 1.0f : s_t;
   }
 }
@@ -401,8 +435,13 @@ hipError_t launch_gptq(int fmt, const void* w, int w_dtype, int64_t n, int64_t k
     }
   }
   float* ts = tscale;
-  if (fmt == kFmtNV)
-    hipLaunchKernelGGL(gptq_tscale_kernel, dim3(1), dim3(1024), 0, stream, Wr, n * k, ts);
+  if (fmt == kFmtNV) {
+    float* parts = reinterpret_cast<float*>(T);     // the strip buffer is free again
+    const int64_t want = (n * k + 256 * 64 - 1) / (256 * 64);
+    const int np = (int)(want < kMaxParts ? want : kMaxParts);
+    hipLaunchKernelGGL(gptq_amax_kernel, dim3(np), dim3(256), 0, stream, Wr, n * k, parts);
+    hipLaunchKernelGGL(gptq_tscale_kernel, dim3(1), dim3(kMaxParts), 0, stream, parts, np, ts);
+  }
   FP4_TRY(hipGetLastError());
   // the columns, 128 at a time
   const dim3 bgrid((unsigned)((n + kRows - 1) / kRows));
