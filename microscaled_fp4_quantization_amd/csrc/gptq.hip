@@ -14,18 +14,18 @@
 //   3. Dead features (H_jj = 0): H_jj = 1 and their weights zeroed; then
 //      H_jj += damp * mean(diag H).  The damped H is stored flipped,
 //      H'[i][j] = H[k-1-i][k-1-j].
-//   4. L' = cholesky(H') (lower, blocked: 32-wide panels), X = L'^-1
-//      (blocked by 32-row strips).  The upper Cholesky factor U of H^-1 is
-//      then U[i][j] = X[k-1-i][k-1-j]: with J the reversal, H^-1 =
-//      J (J H J)^-1 J = (J L'^-1 J)^T (J L'^-1 J).
+//   4. X = L'^-1 for L' = cholesky(H'), recursively (cholinv: 128 x 128
+//      leaves in one workgroup each, everything above them large GEMMs).
+//      The upper Cholesky factor U of H^-1 is then U[i][j] = X[k-1-i][k-1-j]:
+//      with J the reversal, H^-1 = J (J H J)^-1 J = (J L'^-1 J)^T (J L'^-1 J).
 //   5. NVFP4 tensor scale max |Wr| / 2688.
 //   6. The columns in blocks of 128: gptq_block_kernel walks a block's
-//      columns for 64 rows per workgroup (the block in LDS, U read with
-//      uniform loads): block scale from the current weights at each
-//      quantization block start, code, err = (w - q) / U_jj, the block's
-//      later columns take -err U_jj'; then the columns right of the block
-//      take -E U[block, right] in one gemm_f64 (the error correction of all
-//      later columns, deferred to the block's end as one product).
+//      columns for 64 rows per wave (weights in registers and LDS, U's block
+//      in LDS): block scale from the current weights at each quantization
+//      block start, code, err = (w - q) / U_jj, the block's later columns
+//      take -err U_jj'; then the columns right of the block take
+//      -E U[block, right] in one gemm_f64 (the error correction of all later
+//      columns, deferred to the block's end as one product).
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -33,7 +33,6 @@ using namespace fp4dev;
 
 namespace {
 
-constexpr int kNB = 32;          // Cholesky / inverse panel width
 constexpr int kBC = 128;         // GPTQ column block
 constexpr int kRows = 64;        // rows per GPTQ workgroup
 constexpr int kGT = 64;          // gemm_f64 tile
@@ -48,6 +47,15 @@ constexpr int kGK = 32;          // gemm_f64 k-chunk
 // chunks of 32 k; the next chunk's global loads are in flight while the
 // current chunk is multiplied.  (Unlike the fp32 16 x 16 MFMAs, the fp64
 // one leaves item e of lane l at row 4 e + l / 16.)
+// Triangular operands narrow each tile's k-range (the skipped products are
+// zeros); kLowerTiles computes only the tiles that meet the lower triangle.
+enum : int {
+  kTriBTransLower = 1,   // B(t, j) = 0 for t > j: k ends at the tile's last column
+  kTriBLower = 2,        // B(t, j) = 0 for t < j: k starts at the tile's first column
+  kTriALower = 4,        // A(i, t) = 0 for t > i: k ends at the tile's last row
+  kLowerTiles = 8,       // C: tiles strictly above the diagonal are left alone
+};
+
 struct GemmArgs {
   const double* a;
   const double* b;
@@ -55,6 +63,7 @@ struct GemmArgs {
   int64_t sa0, sa1, sb0, sb1, ldc;
   int m, n, k;
   double alpha, beta;
+  int tri;
 };
 
 typedef double v4d __attribute__((ext_vector_type(4)));
@@ -65,6 +74,11 @@ __global__ __launch_bounds__(256) void gemm_f64_kernel(GemmArgs G) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int i0 = blockIdx.y * kGT, j0 = blockIdx.x * kGT;
   const int wr = 32 * (wave >> 1), wc = 32 * (wave & 1);
+  if ((G.tri & kLowerTiles) && j0 > i0) return;
+  int kb = 0, ke = G.k;
+  if (G.tri & kTriBTransLower) ke = min(ke, j0 + kGT);
+  if (G.tri & kTriBLower) kb = j0;
+  if (G.tri & kTriALower) ke = min(ke, i0 + kGT);
   // loaders: 2048 elements of each tile, fastest along the unit-stride side
   const bool a_i_fast = (G.sa0 < 0 ? -G.sa0 : G.sa0) <= (G.sa1 < 0 ? -G.sa1 : G.sa1);
   const bool b_j_fast = (G.sb1 < 0 ? -G.sb1 : G.sb1) <= (G.sb0 < 0 ? -G.sb0 : G.sb0);
@@ -88,8 +102,8 @@ __global__ __launch_bounds__(256) void gemm_f64_kernel(GemmArgs G) {
   for (int x = 0; x < 2; ++x)
 #pragma unroll
     for (int y = 0; y < 2; ++y) acc[x][y] = (v4d){0.0, 0.0, 0.0, 0.0};
-  fetch(0);
-  for (int t0 = 0; t0 < G.k; t0 += kGK) {
+  if (kb < ke) fetch(kb);
+  for (int t0 = kb; t0 < ke; t0 += kGK) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int idx = tid + 256 * e;
@@ -97,7 +111,7 @@ __global__ __launch_bounds__(256) void gemm_f64_kernel(GemmArgs G) {
       Bs[b_j_fast ? (idx >> 6) : (idx & 31)][b_j_fast ? (idx & 63) : (idx >> 5)] = rb[e];
     }
     __syncthreads();
-    if (t0 + kGK < G.k) fetch(t0 + kGK);
+    if (t0 + kGK < ke) fetch(t0 + kGK);
 #pragma unroll
     for (int ks = 0; ks < kGK; ks += 4) {
       const int kk = ks + (lane >> 4), r = lane & 15;
@@ -163,7 +177,7 @@ __global__ __launch_bounds__(256) void gptq_flip_kernel(const double* __restrict
   if (idx >= (int64_t)k * k) return;
   const int i = (int)(idx / k), j = (int)(idx - (int64_t)i * k);
   const int si = k - 1 - i, sj = k - 1 - j;
-  double v = H[(int64_t)si * k + sj];
+  double v = si >= sj ? H[(int64_t)si * k + sj] : H[(int64_t)sj * k + si];   // lower part of H
   if (i == j) v = (dead[si] ? 1.0 : v) + scal[0];
   Hf[idx] = v;
 }
@@ -215,168 +229,294 @@ __global__ __launch_bounds__(kMaxParts) void gptq_tscale_kernel(const float* __r
   }
 }
 
-// ---- Cholesky of the flipped Hessian, in place (lower) ----------------------------
-// Diagonal block at (p0, p0): unblocked, in LDS.
-__global__ __launch_bounds__(256) void chol_diag_kernel(double* __restrict__ A, int k, int p0) {
-  __shared__ double S[kNB][kNB + 1];
-  const int tid = threadIdx.x;
-  for (int e = tid; e < kNB * kNB; e += 256) {
-    const int i = e / kNB, j = e % kNB;
-    S[i][j] = A[(int64_t)(p0 + i) * k + p0 + j];
-  }
-  __syncthreads();
-  for (int c = 0; c < kNB; ++c) {
-    if (tid == 0) S[c][c] = sqrt(S[c][c]);
-    __syncthreads();
-    if (tid > c && tid < kNB) S[tid][c] = S[tid][c] / S[c][c];
-    __syncthreads();
-    for (int e = tid; e < kNB * kNB; e += 256) {
-      const int i = e / kNB, j = e % kNB;
-      if (j > c && i >= j) S[i][j] -= S[i][c] * S[j][c];
-    }
-    __syncthreads();
-  }
-  for (int e = tid; e < kNB * kNB; e += 256) {
-    const int i = e / kNB, j = e % kNB;
-    if (j <= i) A[(int64_t)(p0 + i) * k + p0 + j] = S[i][j];
-  }
-}
+// ---- Cholesky factor and its inverse, recursively -----------------------------------
+// cholinv(A) for the symmetric positive definite block A (lower part read):
+// with A = [[A11, .], [A21, A22]],
+//   L11, X11 = cholinv(A11)           (X11 = L11^-1)
+//   L21 = A21 X11^T                   (= A21 L11^-T)
+//   L22, X22 = cholinv(A22 - L21 L21^T)
+//   X21 = -X22 L21 X11
+// so every step above the 128 x 128 leaves is one large GEMM.  Only X = L^-1
+// is kept: L21 lives in the X21 slot until X21 replaces it, the product
+// L21 X11 in the (consumed) A21 slot.
+constexpr int kLeaf = 128;
 
-// Rows below the panel: L_ip = A_ip L_pp^-T, one thread per row.
-__global__ __launch_bounds__(256) void chol_trsm_kernel(double* __restrict__ A, int k, int p0) {
-  __shared__ double P[kNB][kNB + 1];
-  for (int e = threadIdx.x; e < kNB * kNB; e += 256) {
-    const int i = e / kNB, j = e % kNB;
-    P[i][j] = j <= i ? A[(int64_t)(p0 + i) * k + p0 + j] : 0.0;
+// Leaf: the 128 x 128 diagonal block at (p, p) of A, in one workgroup.  X =
+// L^-1 comes out of one right-looking sweep that never forms L: thread
+// (i, jj) keeps a[t] = A'[i][jj + 8t] (the trailing matrix) and
+// x[t] = B'[i][jj + 8t] (B' = I minus the rows already eliminated) in
+// registers.  With d_c = A'[c][c], step c takes, for every row r > c,
+//   A'[r][j] -= A'[r][c] A'[j][c] / d_c   (c < j <= r)
+//   B'[r]    -= A'[r][c] B'[c] / d_c
+// and X's row r is B'[r] / sqrt(d_r) once step r - 1 is done (L's column c
+// is A'[., c] / sqrt(d_c), so these are the usual updates with both factors
+// unscaled).  The values step c reads (A'[., c] below the diagonal, B'[c]
+// left of it: one LDS vector, as B'[c] is zero right of c) are published by
+// their owners at the end of step c - 1, so each step has one barrier.  The
+// whole 128 x 128 block of X is written, zeros above the diagonal included.
+__global__ __launch_bounds__(1024) void cholinv_leaf_kernel(const double* __restrict__ A,
+                                                            double* __restrict__ X, int k, int p) {
+  __shared__ double v[2][kLeaf];
+  __shared__ double inv_d[kLeaf];        // 1 / d_c
+  __shared__ double inv_s[kLeaf];        // 1 / sqrt(d_c)
+  const int tid = threadIdx.x, i = tid >> 3, jj = tid & 7;
+  double a[kLeaf / 8], x[kLeaf / 8];
+#pragma unroll
+  for (int t = 0; t < kLeaf / 8; ++t) {
+    const int col = jj + 8 * t;
+    a[t] = col <= i ? A[(int64_t)(p + i) * k + p + col] : 0.0;
+    x[t] = col == i ? 1.0 : 0.0;
+  }
+  // step 0's inputs: A'[., 0] and B'[0] = e_0
+  if (jj == 0) v[0][i] = i == 0 ? 1.0 : a[0];
+  if (i == 0 && jj == 0) {
+    inv_d[0] = 1.0 / a[0];
+    inv_s[0] = 1.0 / sqrt(a[0]);
   }
   __syncthreads();
-  const int row = p0 + kNB + blockIdx.x * 256 + threadIdx.x;
-  if (row >= k) return;
-  double* a = A + (int64_t)row * k + p0;
-  double x[kNB];
 #pragma unroll
-  for (int c = 0; c < kNB; ++c) {
-    double v = a[c];
+  for (int tc = 0; tc < kLeaf / 8; ++tc) {
+#pragma unroll 1
+    for (int cj = 0; cj < 8; ++cj) {
+      const int c = 8 * tc + cj, b = c & 1;
+      if (i > c) {
+        const double li = v[b][i] * inv_d[c];
 #pragma unroll
-    for (int t = 0; t < c; ++t) v -= x[t] * P[c][t];
-    x[c] = v / P[c][c];
-  }
+        for (int t = 0; t < kLeaf / 8; ++t) {
+          const int col = jj + 8 * t;
+          const double u = v[b][col];
+          if (t > tc) {
+            a[t] = col <= i ? fma(-li, u, a[t]) : a[t];
+          } else if (t < tc) {
+            x[t] = fma(-li, u, x[t]);
+          } else {
+            const bool right = jj > cj;
+            a[t] = right && col <= i ? fma(-li, u, a[t]) : a[t];
+            x[t] = right ? x[t] : fma(-li, u, x[t]);
+          }
+        }
+        // publish step c + 1's inputs: A'[., c+1] (owner jj == (c+1) & 7)
+        // and B'[c + 1] (row c + 1)
+        const int n1 = c + 1;
+        const double an = cj < 7 ? a[tc] : a[tc + 1 < kLeaf / 8 ? tc + 1 : tc];
+        if (jj == (n1 & 7)) {
+          if (i > n1) v[b ^ 1][i] = an;
+          if (i == n1) {
+            inv_d[n1] = 1.0 / an;
+            inv_s[n1] = 1.0 / sqrt(an);
+          }
+        }
+        if (i == n1) {
 #pragma unroll
-  for (int c = 0; c < kNB; ++c) a[c] = x[c];
-}
-
-// ---- inverse of the lower factor, by 32-row strips ----------------------------------
-// X_ii = L_ii^-1 (lower 32 x 32, zeros above its diagonal).
-__global__ __launch_bounds__(256) void trtri_diag_kernel(const double* __restrict__ L,
-                                                         double* __restrict__ X, int k, int i0) {
-  __shared__ double S[kNB][kNB + 1];
-  __shared__ double R[kNB][kNB + 1];
-  const int tid = threadIdx.x;
-  for (int e = tid; e < kNB * kNB; e += 256) {
-    const int i = e / kNB, j = e % kNB;
-    S[i][j] = j <= i ? L[(int64_t)(i0 + i) * k + i0 + j] : 0.0;
-    R[i][j] = 0.0;
-  }
-  __syncthreads();
-  // column c of the inverse by forward substitution, one thread per column
-  if (tid < kNB) {
-    const int c = tid;
-    R[c][c] = 1.0 / S[c][c];
-    for (int r = c + 1; r < kNB; ++r) {
-      double v = 0.0;
-      for (int t = c; t < r; ++t) v += S[r][t] * R[t][c];
-      R[r][c] = -v / S[r][r];
+          for (int t = 0; t <= tc + 1 && t < kLeaf / 8; ++t)
+            if (jj + 8 * t <= n1) v[b ^ 1][jj + 8 * t] = x[t];
+        }
+      }
+      __syncthreads();
     }
   }
-  __syncthreads();
-  for (int e = tid; e < kNB * kNB; e += 256) {
-    const int i = e / kNB, j = e % kNB;
-    X[(int64_t)(i0 + i) * k + i0 + j] = R[i][j];
-  }
+  const double sc = inv_s[i];
+#pragma unroll
+  for (int t = 0; t < kLeaf / 8; ++t) X[(int64_t)(p + i) * k + p + jj + 8 * t] = x[t] * sc;
 }
 
 // ---- the GPTQ column block ---------------------------------------------------------
-// Workgroup = 64 rows (one thread each) x the block's 128 columns, kept in
-// LDS as Ws[column][row].  U[i][j] = Xi[(k-1-i) k + (k-1-j)] is uniform over
-// the workgroup.  Codes and scale bytes go out as they are decided; E
-// [n, 128] receives err for the deferred update of the later columns.
+// One wave per 64 rows, one row per lane.  The block's 128 columns are walked
+// in four sub-blocks of 32: the sub-block's weights sit in registers, its
+// columns are quantized in order and each err is corrected into the
+// sub-block's later columns at once; then the sub-block's 32 errs correct
+// the later sub-blocks' weights (kept in LDS), 32 columns at a time, in the
+// errs' order.  U's block (uniform over the rows) is staged in LDS as 32 x 32
+// tiles by rows and read with the same address in every lane.
+constexpr int kSub = 32;
+
+struct BlockLds {
+  double ud[kBC / kSub][kSub][kSub];       // ud[s][i][c] = U[32s+i][32s+c] (0 for c < i)
+  double uo[6][kSub][kSub];                // uo[t(s,s2)][i][c] = U[32s+i][32s2+c], s < s2
+  double ws[kBC][kRows];                   // the block's current weights, [column][row]
+};
+
+__device__ __forceinline__ int off_tile(int s, int s2) { return 3 * s - (s * (s - 1)) / 2 + (s2 - s - 1); }
+
 template <int FMT>
-__global__ __launch_bounds__(kRows) void gptq_block_kernel(double* __restrict__ W, int64_t n, int k,
-                                                           int c0, const double* __restrict__ Xi,
+__global__ __launch_bounds__(kRows) __attribute__((amdgpu_waves_per_eu(1, 1))) void gptq_block_kernel(const double* __restrict__ W, int64_t n,
+                                                           int k, int c0,
+                                                           const double* __restrict__ Xi,
                                                            const float* __restrict__ tscale,
                                                            double* __restrict__ E,
                                                            uint8_t* __restrict__ codes,
                                                            uint8_t* __restrict__ scales) {
   constexpr bool NV = FMT == kFmtNV;
   constexpr int B = NV ? 16 : 32;
-  __shared__ double Ws[kBC][kRows];
-  const int t = threadIdx.x;
-  const int64_t row = (int64_t)blockIdx.x * kRows + t;
+  __shared__ BlockLds L;
+  const int lane = threadIdx.x;
+  const int64_t row = (int64_t)blockIdx.x * kRows + lane;
   const bool live = row < n;
   const int64_t rr = live ? row : n - 1;
-  for (int j = 0; j < kBC; ++j) Ws[j][t] = W[rr * k + c0 + j];
+  // U[c0 + a][c0 + b] = Xi[(k-1-c0-a) k + (k-1-c0-b)]
+  const double* ub = Xi + (int64_t)(k - 1 - c0) * k + (k - 1 - c0);
+  for (int s = 0; s < kBC / kSub; ++s)
+    for (int e = lane; e < kSub * kSub; e += kRows) {
+      const int i = e >> 5, c = e & (kSub - 1);
+      const int a = kSub * s + i, b = kSub * s + c;
+      L.ud[s][i][c] = c >= i ? ub[-(int64_t)a * k - b] : 0.0;
+    }
+  for (int s = 0; s < kBC / kSub; ++s)
+    for (int s2 = s + 1; s2 < kBC / kSub; ++s2)
+      for (int e = lane; e < kSub * kSub; e += kRows) {
+        const int i = e >> 5, c = e & (kSub - 1);
+        L.uo[off_tile(s, s2)][i][c] = ub[-(int64_t)(kSub * s + i) * k - (kSub * s2 + c)];
+      }
+  const double* wrow = W + rr * k + c0;
+#pragma unroll 4
+  for (int c = 0; c < kBC; ++c) L.ws[c][lane] = wrow[c];
+  __syncthreads();
   const float s_t = NV ? *tscale : 1.0f;
   const float d6 = 6.0f * s_t;
-  float r = 0.0f;
-  double deq = 0.0;
-  bool usable = false;
-  uint32_t pending = 0;
-  for (int j = 0; j < kBC; ++j) {
-    const int col = c0 + j;
-    if ((j & (B - 1)) == 0) {
-      // the block scale from the block's current weights, the quantizer's rule
-      float a = 0.0f;
-      for (int q = 0; q < B; ++q) a = fmaxf(a, fabsf((float)Ws[j + q][t]));
-      uint32_t sbyte;
-      if (NV) {
-        sbyte = e4m3_encode_pos(a / d6);
-        const float S = e4m3_decode_pos(sbyte) * s_t;
-        r = 1.0f / S;
-        usable = S != 0.0f && r < __builtin_inff();
-        if (!usable) r = 0.0f;
-        deq = (double)e4m3_decode_pos(sbyte) * (double)s_t;
-      } else {
-        usable = a > 0.0f;
-        const int kx = usable ? mx_block_exponent(a) : -127;
-        sbyte = (uint32_t)(kx + 127);
-        r = usable ? as_f((uint32_t)(127 - kx) << 23) : 0.0f;
-        deq = (double)block_scale_value<false>(sbyte);
+#pragma unroll 1
+  for (int s = 0; s < kBC / kSub; ++s) {
+    double w[kSub];
+#pragma unroll
+    for (int c = 0; c < kSub; ++c) w[c] = L.ws[kSub * s + c][lane];
+    double e[kSub];
+    uint32_t cw[4] = {0u, 0u, 0u, 0u};
+    float r = 0.0f;
+    double deq = 0.0;
+    bool usable = false;
+    // U's rows for the walk, one row ahead (row i+1 is read while column i
+    // is worked on)
+    const double2* ud2 = reinterpret_cast<const double2*>(&L.ud[s][0][0]);
+    double2 uc[kSub / 2];
+#pragma unroll
+    for (int h = 0; h < kSub / 2; ++h) uc[h] = ud2[h];
+#pragma unroll
+    for (int i = 0; i < kSub; ++i) {
+      const int col = c0 + kSub * s + i;
+      double2 un[kSub / 2];
+      if (i + 1 < kSub) {
+#pragma unroll
+        for (int h = (i + 1) / 2; h < kSub / 2; ++h) un[h] = ud2[(i + 1) * (kSub / 2) + h];
       }
-      if (live) scales[row * (k / B) + col / B] = (uint8_t)sbyte;
-    }
-    const double w = Ws[j][t];
-    const float wf = (float)w;
-    uint32_t code;
-    double q;
-    if (usable) {
+      if ((i & (B - 1)) == 0) {
+        // the block scale from the block's current weights, the quantizer's rule
+        float a = 0.0f;
+#pragma unroll
+        for (int q = 0; q < B; ++q) a = fmaxf(a, fabsf((float)w[i + q]));
+        uint32_t sbyte;
+        if (NV) {
+          sbyte = e4m3_encode_pos(a / d6);
+          const float S = e4m3_decode_pos(sbyte) * s_t;
+          r = 1.0f / S;
+          usable = S != 0.0f && r < __builtin_inff();
+          if (!usable) r = 0.0f;
+          deq = (double)e4m3_decode_pos(sbyte) * (double)s_t;
+        } else {
+          usable = a > 0.0f;
+          const int kx = usable ? mx_block_exponent(a) : -127;
+          sbyte = (uint32_t)(kx + 127);
+          r = usable ? as_f((uint32_t)(127 - kx) << 23) : 0.0f;
+          deq = (double)block_scale_value<false>(sbyte);
+        }
+        if (live) scales[row * (k / B) + col / B] = (uint8_t)sbyte;
+      }
+      const float wf = (float)w[i];
       const uint32_t pk = e2m1_pack2<0>(0u, wf * r, 0.0f) & 0xFu;
-      code = pk;
-      const v2f dv = e2m1_unpack2<0>(pk);
-      q = (double)dv.x * deq;
-    } else {
-      code = (as_u(wf) >> 31) << 3;                  // sign only
-      q = 0.0;
+      const uint32_t code = usable ? pk : (as_u(wf) >> 31) << 3;   // sign only
+      const double q = usable ? (double)e2m1_unpack2<0>(pk).x * deq : 0.0;
+      cw[i >> 3] |= code << (4 * (i & 7));
+      const double err = (w[i] - q) / ((i & 1) ? uc[i / 2].y : uc[i / 2].x);
+      e[i] = err;
+#pragma unroll
+      for (int c = i + 1; c < kSub; ++c) {
+        w[c] = fma(-err, (c & 1) ? uc[c / 2].y : uc[c / 2].x, w[c]);
+        // apply the update here: left to the compiler, the products sink
+        // towards the next block-scale maximum and their operands pile up
+        // in registers
+        __asm__ volatile("" : "+v"(w[c]));
+      }
+#pragma unroll
+      for (int h = (i + 1) / 2; h < kSub / 2; ++h) uc[h] = un[h];
     }
-    if (j & 1) {
-      if (live) codes[row * (k / 2) + col / 2] = (uint8_t)(pending | (code << 4));
-    } else {
-      pending = code;
+    if (live) {
+      *reinterpret_cast<uint4*>(codes + row * (k / 2) + (c0 + kSub * s) / 2) =
+          make_uint4(cw[0], cw[1], cw[2], cw[3]);
+      double* er = E + row * kBC + kSub * s;
+#pragma unroll
+      for (int i = 0; i < kSub; i += 2)
+        *reinterpret_cast<double2*>(er + i) = make_double2(e[i], e[i + 1]);
     }
-    const double* urow = Xi + (int64_t)(k - 1 - col) * k + (k - 1 - col);   // U[col][col - x] backwards
-    const double err = (w - q) / urow[0];
-    if (live) E[row * kBC + j] = err;
-    for (int jj = j + 1; jj < kBC; ++jj) Ws[jj][t] -= err * urow[-(jj - j)];
+    for (int s2 = s + 1; s2 < kBC / kSub; ++s2) {
+      const int t = off_tile(s, s2);
+      double v[kSub];
+#pragma unroll
+      for (int c = 0; c < kSub; ++c) v[c] = L.ws[kSub * s2 + c][lane];
+      const double2* uo2 = reinterpret_cast<const double2*>(&L.uo[t][0][0]);
+      double2 uc2[kSub / 2];
+#pragma unroll
+      for (int h = 0; h < kSub / 2; ++h) uc2[h] = uo2[h];
+#pragma unroll
+      for (int i = 0; i < kSub; ++i) {
+        double2 un2[kSub / 2];
+        if (i + 1 < kSub) {
+#pragma unroll
+          for (int h = 0; h < kSub / 2; ++h) un2[h] = uo2[(i + 1) * (kSub / 2) + h];
+        }
+#pragma unroll
+        for (int h = 0; h < kSub / 2; ++h) {
+          v[2 * h] = fma(-e[i], uc2[h].x, v[2 * h]);
+          v[2 * h + 1] = fma(-e[i], uc2[h].y, v[2 * h + 1]);
+        }
+#pragma unroll
+        for (int h = 0; h < kSub / 2; ++h) uc2[h] = un2[h];
+      }
+#pragma unroll
+      for (int c = 0; c < kSub; ++c) L.ws[kSub * s2 + c][lane] = v[c];
+    }
   }
 }
 
 }  // namespace
 
 size_t gptq_workspace_bytes(int64_t n, int64_t k, int64_t n_calib) {
-  // Wr [n, k], Xr [N, k], two k x k matrices, E [n, 128], the inverse's
-  // strip product [32, k], dead flags and scalars
-  const int64_t doubles = n * k + n_calib * k + 2 * k * k + n * kBC + (int64_t)kNB * k + 4;
+  // Wr [n, k], Xr [N, k], two k x k matrices, E [n, 128], the partial
+  // maxima, scalars and the dead flags
+  const int64_t doubles = n * k + n_calib * k + 2 * k * k + n * kBC + kMaxParts / 2 + 4;
   return (size_t)doubles * sizeof(double) + (size_t)k * sizeof(int) + 256;
 }
+
+namespace {
+
+// L^-1 of the Cholesky factor of the n x n block at (p, p) of A into the same
+// block of X (A's block is consumed); n a multiple of 128.
+hipError_t cholinv(double* A, double* X, int k, int p, int n, hipStream_t stream) {
+  if (n == kLeaf) {
+    hipLaunchKernelGGL(cholinv_leaf_kernel, dim3(1), dim3(1024), 0, stream, A, X, k, p);
+    return hipGetLastError();
+  }
+  const int h = kLeaf * ((n / kLeaf + 1) / 2), r = n - h;
+  const int64_t K = k;
+  double* A21 = A + (p + h) * K + p;
+  double* A22 = A + (p + h) * K + p + h;
+  double* X11 = X + p * K + p;
+  double* X21 = X + (p + h) * K + p;
+  double* X22 = X + (p + h) * K + p + h;
+  hipError_t e = cholinv(A, X, k, p, h, stream);
+  if (e != hipSuccess) return e;
+  // L21 = A21 X11^T into the X21 slot
+  const GemmArgs g1 = {A21, X11, X21, K, 1, 1, K, K, r, h, h, 1.0, 0.0, kTriBTransLower};
+  if ((e = gemm_f64(g1, stream)) != hipSuccess) return e;
+  // A22 -= L21 L21^T (its lower part)
+  const GemmArgs g2 = {X21, X21, A22, K, 1, 1, K, K, r, r, h, -1.0, 1.0, kLowerTiles};
+  if ((e = gemm_f64(g2, stream)) != hipSuccess) return e;
+  if ((e = cholinv(A, X, k, p + h, r, stream)) != hipSuccess) return e;
+  // L21 X11 into the A21 slot, then X21 = -X22 (L21 X11)
+  const GemmArgs g3 = {X21, X11, A21, K, 1, K, 1, K, r, h, h, 1.0, 0.0, kTriBLower};
+  if ((e = gemm_f64(g3, stream)) != hipSuccess) return e;
+  const GemmArgs g4 = {X22, A21, X21, K, 1, K, 1, K, r, h, r, -1.0, 0.0, kTriALower};
+  return gemm_f64(g4, stream);
+}
+
+}  // namespace
 
 hipError_t launch_gptq(int fmt, const void* w, int w_dtype, int64_t n, int64_t k, const void* x,
                        int x_dtype, int64_t n_calib, double damp, bool rotate, uint8_t* codes,
@@ -385,10 +525,10 @@ hipError_t launch_gptq(int fmt, const void* w, int w_dtype, int64_t n, int64_t k
   double* Wr = reinterpret_cast<double*>(workspace);
   double* Xr = Wr + n * k;
   double* H = Xr + n_calib * k;          // H, then the inverse of the factor
-  double* Lf = H + k * k;                // flipped damped H, then its factor
+  double* Lf = H + k * k;                // flipped damped H (consumed by the factorization)
   double* E = Lf + k * k;
-  double* T = E + n * kBC;               // [32, k] strip product of the inverse
-  double* scal = T + (int64_t)kNB * k;
+  float* parts = reinterpret_cast<float*>(E + n * kBC);
+  double* scal = E + n * kBC + kMaxParts / 2;
   int* dead = reinterpret_cast<int*>(scal + 4);
   const int ki = (int)k;
   hipError_t e;
@@ -396,9 +536,10 @@ hipError_t launch_gptq(int fmt, const void* w, int w_dtype, int64_t n, int64_t k
   if ((e = (call)) != hipSuccess) return e
   FP4_TRY(launch_rotate_f64(w, w_dtype, n * k, rotate ? bsz : 0, Wr, stream));
   FP4_TRY(launch_rotate_f64(x, x_dtype, n_calib * k, rotate ? bsz : 0, Xr, stream));
-  // H = 2 / N Xr^T Xr: A(i, t) = Xr[t][i], B(t, j) = Xr[t][j]
+  // H = 2 / N Xr^T Xr (lower tiles): A(i, t) = Xr[t][i], B(t, j) = Xr[t][j]
   {
-    GemmArgs G = {Xr, Xr, H, 1, k, k, 1, k, ki, ki, (int)n_calib, 2.0 / (double)n_calib, 0.0};
+    GemmArgs G = {Xr, Xr, H, 1, k, k, 1, k, ki, ki, (int)n_calib, 2.0 / (double)n_calib, 0.0,
+                  kLowerTiles};
     FP4_TRY(gemm_f64(G, stream));
   }
   hipLaunchKernelGGL(gptq_damp_kernel, dim3(1), dim3(1024), 0, stream, H, ki, damp, dead, scal);
@@ -406,37 +547,12 @@ hipError_t launch_gptq(int fmt, const void* w, int w_dtype, int64_t n, int64_t k
   hipLaunchKernelGGL(gptq_flip_kernel, dim3(kk_grid), dim3(256), 0, stream, H, ki, dead, scal, Lf);
   const unsigned nk_grid = (unsigned)((n * k + 255) / 256);
   hipLaunchKernelGGL(gptq_zero_dead_kernel, dim3(nk_grid), dim3(256), 0, stream, Wr, n, ki, dead);
-  FP4_TRY(hipGetLastError());
-  // Cholesky of the flipped H in place
-  for (int p0 = 0; p0 < ki; p0 += kNB) {
-    hipLaunchKernelGGL(chol_diag_kernel, dim3(1), dim3(256), 0, stream, Lf, ki, p0);
-    const int below = ki - p0 - kNB;
-    if (below > 0) {
-      hipLaunchKernelGGL(chol_trsm_kernel, dim3((unsigned)((below + 255) / 256)), dim3(256), 0,
-                         stream, Lf, ki, p0);
-      // trailing A22 -= L21 L21^T over the full square (only its lower part is read later)
-      const double* L21 = Lf + (int64_t)(p0 + kNB) * k + p0;
-      GemmArgs G = {L21, L21, Lf + (int64_t)(p0 + kNB) * k + p0 + kNB, k, 1, 1, k, k,
-                    below, below, kNB, -1.0, 1.0};
-      FP4_TRY(gemm_f64(G, stream));
-    }
-  }
-  // the inverse of the factor into H (zeros above the diagonal first)
+  // the inverse of the factor into H: zeros above the diagonal first
   hipLaunchKernelGGL(fill_f64_kernel, dim3(kk_grid), dim3(256), 0, stream, H, k * k);
-  for (int i0 = 0; i0 < ki; i0 += kNB) {
-    hipLaunchKernelGGL(trtri_diag_kernel, dim3(1), dim3(256), 0, stream, Lf, H, ki, i0);
-    if (i0 > 0) {
-      // T = L[i0.., 0:i0] X[0:i0, 0:i0]; X[i0.., 0:i0] = -X_ii T
-      GemmArgs G1 = {Lf + (int64_t)i0 * k, H, T, k, 1, k, 1, k, kNB, i0, i0, 1.0, 0.0};
-      FP4_TRY(gemm_f64(G1, stream));
-      GemmArgs G2 = {H + (int64_t)i0 * k + i0, T, H + (int64_t)i0 * k, k, 1, k, 1, k,
-                     kNB, i0, kNB, -1.0, 0.0};
-      FP4_TRY(gemm_f64(G2, stream));
-    }
-  }
+  FP4_TRY(hipGetLastError());
+  FP4_TRY(cholinv(Lf, H, ki, 0, ki, stream));
   float* ts = tscale;
   if (fmt == kFmtNV) {
-    float* parts = reinterpret_cast<float*>(T);     // the strip buffer is free again
     const int64_t want = (n * k + 256 * 64 - 1) / (256 * 64);
     const int np = (int)(want < kMaxParts ? want : kMaxParts);
     hipLaunchKernelGGL(gptq_amax_kernel, dim3(np), dim3(256), 0, stream, Wr, n * k, parts);
@@ -456,7 +572,7 @@ hipError_t launch_gptq(int fmt, const void* w, int w_dtype, int64_t n, int64_t k
     if (right > 0) {
       // W[:, c0+128:] -= E U[c0:c0+128, c0+128:], U[i][j] = X[k-1-i][k-1-j]
       const double* ub = H + (int64_t)(k - 1 - c0) * k + (k - 1 - c0 - kBC);
-      GemmArgs G = {E, ub, Wr + c0 + kBC, kBC, 1, -k, -1, k, (int)n, right, kBC, -1.0, 1.0};
+      GemmArgs G = {E, ub, Wr + c0 + kBC, kBC, 1, -k, -1, k, (int)n, right, kBC, -1.0, 1.0, 0};
       FP4_TRY(gemm_f64(G, stream));
     }
   }
