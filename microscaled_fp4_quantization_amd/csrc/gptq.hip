@@ -23,9 +23,10 @@
 //      columns for 64 rows per wave (weights in registers and LDS, U's block
 //      in LDS): block scale from the current weights at each quantization
 //      block start, code, err = (w - q) / U_jj, the block's later columns
-//      take -err U_jj'; then the columns right of the block take
-//      -E U[block, right] in one gemm_f64 (the error correction of all later
-//      columns, deferred to the block's end as one product).
+//      take -err U_jj'; then the rest of the block's group of 512 columns
+//      takes -E_block U[block, rest] in one gemm_f64, and after the group's
+//      last block the columns right of the group take -E_group U[group,
+//      right] in one more (GPTQ's deferred error correction, in two levels).
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -34,19 +35,19 @@ using namespace fp4dev;
 namespace {
 
 constexpr int kBC = 128;         // GPTQ column block
+constexpr int kOuter = 512;      // group of column blocks whose corrections of the
+                                 // columns right of the group go out as one product
 constexpr int kRows = 64;        // rows per GPTQ workgroup
-constexpr int kGT = 64;          // gemm_f64 tile
-constexpr int kGK = 32;          // gemm_f64 k-chunk
 
 // ---- C = beta C + alpha A B, general strides ------------------------------------
 // A(i, t) = a[i * sa0 + t * sa1] (M x K), B(t, j) = b[t * sb0 + j * sb1]
-// (K x N), C[i * ldc + j] (M x N).  beta == 0 never reads C.  64 x 64 tile
-// per workgroup of 4 waves, each wave a 32 x 32 quarter as 2 x 2
-// v_mfma_f64_16x16x4_f64 tiles (lane l: A row l % 16 / B column l % 16 at
-// k-slot l / 16; C column l % 16).  The tiles go through LDS in
-// chunks of 32 k; the next chunk's global loads are in flight while the
-// current chunk is multiplied.  (Unlike the fp32 16 x 16 MFMAs, the fp64
-// one leaves item e of lane l at row 4 e + l / 16.)
+// (K x N), C[i * ldc + j] (M x N).  beta == 0 never reads C.  A T x T tile
+// (T = 64 or 128) per workgroup of 4 waves, each wave a T/2 x T/2 quarter as
+// (T/32) x (T/32) v_mfma_f64_16x16x4_f64 tiles (lane l: A row l % 16 / B
+// column l % 16 at k-slot l / 16; C column l % 16).  The tiles go through
+// LDS in chunks of 2048 / T k; the next chunk's global loads are in flight
+// while the current chunk is multiplied.  (Unlike the fp32 16 x 16 MFMAs,
+// the fp64 one leaves item e of lane l at row 4 e + l / 16.)
 // Triangular operands narrow each tile's k-range (the skipped products are
 // zeros); kLowerTiles computes only the tiles that meet the lower triangle.
 enum : int {
@@ -68,81 +69,120 @@ struct GemmArgs {
 
 typedef double v4d __attribute__((ext_vector_type(4)));
 
+template <int T>
 __global__ __launch_bounds__(256) void gemm_f64_kernel(GemmArgs G) {
-  __shared__ double As[kGK][kGT + 1];
-  __shared__ double Bs[kGK][kGT + 1];
+  constexpr int KC = 2048 / T;           // k-chunk: 8 elements of A and of B per thread
+  constexpr int NT = T / 32;             // MFMA tiles per wave along each side
+  __shared__ double As[KC][T + 1];
+  __shared__ double Bs[KC][T + 1];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int i0 = blockIdx.y * kGT, j0 = blockIdx.x * kGT;
-  const int wr = 32 * (wave >> 1), wc = 32 * (wave & 1);
+  const int i0 = blockIdx.y * T, j0 = blockIdx.x * T;
+  const int wr = (T / 2) * (wave >> 1), wc = (T / 2) * (wave & 1);
   if ((G.tri & kLowerTiles) && j0 > i0) return;
   int kb = 0, ke = G.k;
-  if (G.tri & kTriBTransLower) ke = min(ke, j0 + kGT);
+  if (G.tri & kTriBTransLower) ke = min(ke, j0 + T);
   if (G.tri & kTriBLower) kb = j0;
-  if (G.tri & kTriALower) ke = min(ke, i0 + kGT);
-  // loaders: 2048 elements of each tile, fastest along the unit-stride side
+  if (G.tri & kTriALower) ke = min(ke, i0 + T);
+  // loaders: T * KC elements of each tile, fastest along the unit-stride side.
+  // Element e of a thread sits at a fixed offset (along the tile's row or k
+  // side) from the thread's first one, so one base pointer per operand and a
+  // uniform step per element give every address.
   const bool a_i_fast = (G.sa0 < 0 ? -G.sa0 : G.sa0) <= (G.sa1 < 0 ? -G.sa1 : G.sa1);
   const bool b_j_fast = (G.sb1 < 0 ? -G.sb1 : G.sb1) <= (G.sb0 < 0 ? -G.sb0 : G.sb0);
+  const int a_i = a_i_fast ? tid % T : tid / KC, a_t = a_i_fast ? tid / T : tid % KC;
+  const int a_di = a_i_fast ? 0 : 256 / KC, a_dt = a_i_fast ? 256 / T : 0;
+  const int b_j = b_j_fast ? tid % T : tid / KC, b_t = b_j_fast ? tid / T : tid % KC;
+  const int b_dj = b_j_fast ? 0 : 256 / KC, b_dt = b_j_fast ? 256 / T : 0;
+  const double* a_base = G.a + (int64_t)(i0 + a_i) * G.sa0 + (int64_t)a_t * G.sa1;
+  const double* b_base = G.b + (int64_t)b_t * G.sb0 + (int64_t)(j0 + b_j) * G.sb1;
+  const int64_t a_step = a_di * G.sa0 + a_dt * G.sa1, b_step = b_dt * G.sb0 + b_dj * G.sb1;
   double ra[8], rb[8];
+  const bool inner = i0 + T <= G.m && j0 + T <= G.n;   // no row or column bound
   auto fetch = [&](int t0) {
+    const double* pa = a_base + (int64_t)t0 * G.sa1;
+    const double* pb = b_base + (int64_t)t0 * G.sb0;
+    if (inner && t0 + KC <= G.k) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        ra[e] = pa[e * a_step];
+        rb[e] = pb[e * b_step];
+      }
+      return;
+    }
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const int idx = tid + 256 * e;
-      const int ii = a_i_fast ? (idx & 63) : (idx >> 5);
-      const int tt = a_i_fast ? (idx >> 6) : (idx & 31);
-      const int gi = i0 + ii, gt = t0 + tt;
-      ra[e] = (gi < G.m && gt < G.k) ? G.a[gi * G.sa0 + gt * G.sa1] : 0.0;
-      const int jj = b_j_fast ? (idx & 63) : (idx >> 5);
-      const int tb = b_j_fast ? (idx >> 6) : (idx & 31);
-      const int gj = j0 + jj, gtb = t0 + tb;
-      rb[e] = (gj < G.n && gtb < G.k) ? G.b[gtb * G.sb0 + gj * G.sb1] : 0.0;
+      const bool oka = i0 + a_i + a_di * e < G.m && t0 + a_t + a_dt * e < G.k;
+      ra[e] = oka ? pa[e * a_step] : 0.0;
+      const bool okb = j0 + b_j + b_dj * e < G.n && t0 + b_t + b_dt * e < G.k;
+      rb[e] = okb ? pb[e * b_step] : 0.0;
     }
   };
-  v4d acc[2][2];
+  v4d acc[NT][NT];
 #pragma unroll
-  for (int x = 0; x < 2; ++x)
+  for (int x = 0; x < NT; ++x)
 #pragma unroll
-    for (int y = 0; y < 2; ++y) acc[x][y] = (v4d){0.0, 0.0, 0.0, 0.0};
+    for (int y = 0; y < NT; ++y) acc[x][y] = (v4d){0.0, 0.0, 0.0, 0.0};
   if (kb < ke) fetch(kb);
-  for (int t0 = kb; t0 < ke; t0 += kGK) {
+  for (int t0 = kb; t0 < ke; t0 += KC) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const int idx = tid + 256 * e;
-      As[a_i_fast ? (idx >> 6) : (idx & 31)][a_i_fast ? (idx & 63) : (idx >> 5)] = ra[e];
-      Bs[b_j_fast ? (idx >> 6) : (idx & 31)][b_j_fast ? (idx & 63) : (idx >> 5)] = rb[e];
+      As[a_t + a_dt * e][a_i + a_di * e] = ra[e];
+      Bs[b_t + b_dt * e][b_j + b_dj * e] = rb[e];
     }
     __syncthreads();
-    if (t0 + kGK < ke) fetch(t0 + kGK);
+    if (t0 + KC < ke) fetch(t0 + KC);
 #pragma unroll
-    for (int ks = 0; ks < kGK; ks += 4) {
+    for (int ks = 0; ks < KC; ks += 4) {
       const int kk = ks + (lane >> 4), r = lane & 15;
-      const double a0 = As[kk][wr + r], a1 = As[kk][wr + 16 + r];
-      const double b0 = Bs[kk][wc + r], b1 = Bs[kk][wc + 16 + r];
-      acc[0][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(a0, b0, acc[0][0], 0, 0, 0);
-      acc[0][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(a0, b1, acc[0][1], 0, 0, 0);
-      acc[1][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(a1, b0, acc[1][0], 0, 0, 0);
-      acc[1][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(a1, b1, acc[1][1], 0, 0, 0);
+      double av[NT], bv[NT];
+#pragma unroll
+      for (int x = 0; x < NT; ++x) av[x] = As[kk][wr + 16 * x + r];
+#pragma unroll
+      for (int y = 0; y < NT; ++y) bv[y] = Bs[kk][wc + 16 * y + r];
+#pragma unroll
+      for (int x = 0; x < NT; ++x)
+#pragma unroll
+        for (int y = 0; y < NT; ++y)
+          acc[x][y] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[x], bv[y], acc[x][y], 0, 0, 0);
     }
     __syncthreads();
   }
+  // all of C's old values are read before the first store (a store ahead of
+  // a load of the same array would make every element a round trip)
+  if (G.beta != 0.0) {
 #pragma unroll
-  for (int x = 0; x < 2; ++x)
+    for (int x = 0; x < NT; ++x)
 #pragma unroll
-    for (int y = 0; y < 2; ++y)
+      for (int y = 0; y < NT; ++y)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int gi = i0 + wr + 16 * x + 4 * e + (lane >> 4);
+          const int gj = j0 + wc + 16 * y + (lane & 15);
+          const double old = (gi < G.m && gj < G.n) ? G.c[gi * G.ldc + gj] : 0.0;
+          acc[x][y][e] = G.beta * old + G.alpha * acc[x][y][e];
+        }
+  } else {
+#pragma unroll
+    for (int x = 0; x < NT; ++x)
+#pragma unroll
+      for (int y = 0; y < NT; ++y) acc[x][y] *= G.alpha;
+  }
+#pragma unroll
+  for (int x = 0; x < NT; ++x)
+#pragma unroll
+    for (int y = 0; y < NT; ++y)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int gi = i0 + wr + 16 * x + 4 * e + (lane >> 4);
         const int gj = j0 + wc + 16 * y + (lane & 15);
-        if (gi < G.m && gj < G.n) {
-          double* p = G.c + gi * G.ldc + gj;
-          *p = G.beta == 0.0 ? G.alpha * acc[x][y][e] : G.beta * *p + G.alpha * acc[x][y][e];
-        }
+        if (gi < G.m && gj < G.n) G.c[gi * G.ldc + gj] = acc[x][y][e];
       }
 }
 
 hipError_t gemm_f64(const GemmArgs& G, hipStream_t stream) {
   if (G.m <= 0 || G.n <= 0) return hipSuccess;
-  const dim3 grid((unsigned)((G.n + kGT - 1) / kGT), (unsigned)((G.m + kGT - 1) / kGT));
-  hipLaunchKernelGGL(gemm_f64_kernel, grid, dim3(256), 0, stream, G);
+  const dim3 grid((unsigned)((G.n + 63) / 64), (unsigned)((G.m + 63) / 64));
+  hipLaunchKernelGGL(gemm_f64_kernel<64>, grid, dim3(256), 0, stream, G);
   return hipGetLastError();
 }
 
@@ -440,7 +480,7 @@ __global__ __launch_bounds__(kRows) __attribute__((amdgpu_waves_per_eu(1, 1))) v
     if (live) {
       *reinterpret_cast<uint4*>(codes + row * (k / 2) + (c0 + kSub * s) / 2) =
           make_uint4(cw[0], cw[1], cw[2], cw[3]);
-      double* er = E + row * kBC + kSub * s;
+      double* er = E + row * kOuter + kSub * s;
 #pragma unroll
       for (int i = 0; i < kSub; i += 2)
         *reinterpret_cast<double2*>(er + i) = make_double2(e[i], e[i + 1]);
@@ -478,9 +518,9 @@ __global__ __launch_bounds__(kRows) __attribute__((amdgpu_waves_per_eu(1, 1))) v
 }  // namespace
 
 size_t gptq_workspace_bytes(int64_t n, int64_t k, int64_t n_calib) {
-  // Wr [n, k], Xr [N, k], two k x k matrices, E [n, 128], the partial
+  // Wr [n, k], Xr [N, k], two k x k matrices, E [n, 512], the partial
   // maxima, scalars and the dead flags
-  const int64_t doubles = n * k + n_calib * k + 2 * k * k + n * kBC + kMaxParts / 2 + 4;
+  const int64_t doubles = n * k + n_calib * k + 2 * k * k + n * kOuter + kMaxParts / 2 + 4;
   return (size_t)doubles * sizeof(double) + (size_t)k * sizeof(int) + 256;
 }
 
@@ -527,8 +567,8 @@ hipError_t launch_gptq(int fmt, const void* w, int w_dtype, int64_t n, int64_t k
   double* H = Xr + n_calib * k;          // H, then the inverse of the factor
   double* Lf = H + k * k;                // flipped damped H (consumed by the factorization)
   double* E = Lf + k * k;
-  float* parts = reinterpret_cast<float*>(E + n * kBC);
-  double* scal = E + n * kBC + kMaxParts / 2;
+  float* parts = reinterpret_cast<float*>(E + n * kOuter);
+  double* scal = E + n * kOuter + kMaxParts / 2;
   int* dead = reinterpret_cast<int*>(scal + 4);
   const int ki = (int)k;
   hipError_t e;
@@ -559,20 +599,33 @@ hipError_t launch_gptq(int fmt, const void* w, int w_dtype, int64_t n, int64_t k
     hipLaunchKernelGGL(gptq_tscale_kernel, dim3(1), dim3(kMaxParts), 0, stream, parts, np, ts);
   }
   FP4_TRY(hipGetLastError());
-  // the columns, 128 at a time
+  // the columns, 128 at a time, in groups of 512: each block's errs correct
+  // the rest of its group at once, the group's errs (E [n, 512]) the columns
+  // right of the group in one product with k = 512.  U[i][j] = X[k-1-i][k-1-j]
   const dim3 bgrid((unsigned)((n + kRows - 1) / kRows));
-  for (int c0 = 0; c0 < ki; c0 += kBC) {
-    if (fmt == kFmtNV)
-      hipLaunchKernelGGL((gptq_block_kernel<kFmtNV>), bgrid, dim3(kRows), 0, stream, Wr, n, ki, c0,
-                         H, ts, E, codes, scales);
-    else
-      hipLaunchKernelGGL((gptq_block_kernel<kFmtMX>), bgrid, dim3(kRows), 0, stream, Wr, n, ki, c0,
-                         H, ts, E, codes, scales);
-    const int right = ki - c0 - kBC;
+  for (int o0 = 0; o0 < ki; o0 += kOuter) {
+    const int oe = o0 + kOuter < ki ? o0 + kOuter : ki;
+    for (int c0 = o0; c0 < oe; c0 += kBC) {
+      double* Eb = E + (c0 - o0);
+      if (fmt == kFmtNV)
+        hipLaunchKernelGGL((gptq_block_kernel<kFmtNV>), bgrid, dim3(kRows), 0, stream, Wr, n, ki,
+                           c0, H, ts, Eb, codes, scales);
+      else
+        hipLaunchKernelGGL((gptq_block_kernel<kFmtMX>), bgrid, dim3(kRows), 0, stream, Wr, n, ki,
+                           c0, H, ts, Eb, codes, scales);
+      const int right = oe - c0 - kBC;
+      if (right > 0) {
+        // W[:, c0+128 : oe] -= E_b U[c0 : c0+128, c0+128 : oe]
+        const double* ub = H + (int64_t)(k - 1 - c0) * k + (k - 1 - c0 - kBC);
+        GemmArgs G = {Eb, ub, Wr + c0 + kBC, kOuter, 1, -k, -1, k, (int)n, right, kBC, -1.0, 1.0, 0};
+        FP4_TRY(gemm_f64(G, stream));
+      }
+    }
+    const int right = ki - oe;
     if (right > 0) {
-      // W[:, c0+128:] -= E U[c0:c0+128, c0+128:], U[i][j] = X[k-1-i][k-1-j]
-      const double* ub = H + (int64_t)(k - 1 - c0) * k + (k - 1 - c0 - kBC);
-      GemmArgs G = {E, ub, Wr + c0 + kBC, kBC, 1, -k, -1, k, (int)n, right, kBC, -1.0, 1.0, 0};
+      // W[:, oe:] -= E U[o0 : oe, oe:]
+      const double* ub = H + (int64_t)(k - 1 - o0) * k + (k - 1 - oe);
+      GemmArgs G = {E, ub, Wr + oe, kOuter, 1, -k, -1, k, (int)n, right, oe - o0, -1.0, 1.0, 0};
       FP4_TRY(gemm_f64(G, stream));
     }
   }
