@@ -370,13 +370,22 @@ __global__ __launch_bounds__(1024) void cholinv_leaf_kernel(const double* __rest
 // tiles by rows and read with the same address in every lane.
 constexpr int kSub = 32;
 
+// U's tiles: ut[s] = the diagonal tile s (ut[s][i][c] = U[32s+i][32s+c], 0 for
+// c < i), ut[4 + off_tile(s, s2)] = the tile (s, s2), s < s2, by rows.
+constexpr int kTiles = 10;
+
 struct BlockLds {
-  double ud[kBC / kSub][kSub][kSub];       // ud[s][i][c] = U[32s+i][32s+c] (0 for c < i)
-  double uo[6][kSub][kSub];                // uo[t(s,s2)][i][c] = U[32s+i][32s2+c], s < s2
+  double ut[kTiles][kSub][kSub];
   double ws[kBC][kRows];                   // the block's current weights, [column][row]
 };
 
 __device__ __forceinline__ int off_tile(int s, int s2) { return 3 * s - (s * (s - 1)) / 2 + (s2 - s - 1); }
+
+// (s, s2) of tile slot t
+__device__ __forceinline__ int tile_row(int t) { return t < 4 ? t : (t < 7 ? 0 : (t < 9 ? 1 : 2)); }
+__device__ __forceinline__ int tile_col(int t) {
+  return t < 4 ? t : (t < 7 ? t - 3 : (t < 9 ? t - 5 : 3));
+}
 
 template <int FMT>
 __global__ __launch_bounds__(kRows) __attribute__((amdgpu_waves_per_eu(1, 1))) void gptq_block_kernel(const double* __restrict__ W, int64_t n,
@@ -395,21 +404,34 @@ __global__ __launch_bounds__(kRows) __attribute__((amdgpu_waves_per_eu(1, 1))) v
   const int64_t rr = live ? row : n - 1;
   // U[c0 + a][c0 + b] = Xi[(k-1-c0-a) k + (k-1-c0-b)]
   const double* ub = Xi + (int64_t)(k - 1 - c0) * k + (k - 1 - c0);
-  for (int s = 0; s < kBC / kSub; ++s)
-    for (int e = lane; e < kSub * kSub; e += kRows) {
-      const int i = e >> 5, c = e & (kSub - 1);
-      const int a = kSub * s + i, b = kSub * s + c;
-      L.ud[s][i][c] = c >= i ? ub[-(int64_t)a * k - b] : 0.0;
+  // staged in batches, all of a batch's loads in flight before its stores
+  constexpr int kStage = 32;               // elements per lane per batch
+  for (int base = 0; base < kTiles * kSub * kSub; base += kRows * kStage) {
+    double val[kStage];
+#pragma unroll
+    for (int q = 0; q < kStage; ++q) {
+      const int e = base + kRows * q + lane;
+      const int t = e >> 10, i = (e >> 5) & (kSub - 1), c = e & (kSub - 1);
+      const int a = kSub * tile_row(t) + i, b = kSub * tile_col(t) + c;
+      val[q] = (e < kTiles * kSub * kSub && (t >= 4 || c >= i)) ? ub[-(int64_t)a * k - b] : 0.0;
     }
-  for (int s = 0; s < kBC / kSub; ++s)
-    for (int s2 = s + 1; s2 < kBC / kSub; ++s2)
-      for (int e = lane; e < kSub * kSub; e += kRows) {
-        const int i = e >> 5, c = e & (kSub - 1);
-        L.uo[off_tile(s, s2)][i][c] = ub[-(int64_t)(kSub * s + i) * k - (kSub * s2 + c)];
-      }
-  const double* wrow = W + rr * k + c0;
-#pragma unroll 4
-  for (int c = 0; c < kBC; ++c) L.ws[c][lane] = wrow[c];
+#pragma unroll
+    for (int q = 0; q < kStage; ++q) {
+      const int e = base + kRows * q + lane;
+      if (e < kTiles * kSub * kSub) (&L.ut[0][0][0])[e] = val[q];
+    }
+  }
+  const double2* wrow = reinterpret_cast<const double2*>(W + rr * k + c0);
+  for (int base = 0; base < kBC / 2; base += kStage / 2) {
+    double2 val[kStage / 2];
+#pragma unroll
+    for (int q = 0; q < kStage / 2; ++q) val[q] = wrow[base + q];
+#pragma unroll
+    for (int q = 0; q < kStage / 2; ++q) {
+      L.ws[2 * (base + q)][lane] = val[q].x;
+      L.ws[2 * (base + q) + 1][lane] = val[q].y;
+    }
+  }
   __syncthreads();
   const float s_t = NV ? *tscale : 1.0f;
   const float d6 = 6.0f * s_t;
@@ -425,7 +447,7 @@ __global__ __launch_bounds__(kRows) __attribute__((amdgpu_waves_per_eu(1, 1))) v
     bool usable = false;
     // U's rows for the walk, one row ahead (row i+1 is read while column i
     // is worked on)
-    const double2* ud2 = reinterpret_cast<const double2*>(&L.ud[s][0][0]);
+    const double2* ud2 = reinterpret_cast<const double2*>(&L.ut[s][0][0]);
     double2 uc[kSub / 2];
 #pragma unroll
     for (int h = 0; h < kSub / 2; ++h) uc[h] = ud2[h];
@@ -490,7 +512,7 @@ __global__ __launch_bounds__(kRows) __attribute__((amdgpu_waves_per_eu(1, 1))) v
       double v[kSub];
 #pragma unroll
       for (int c = 0; c < kSub; ++c) v[c] = L.ws[kSub * s2 + c][lane];
-      const double2* uo2 = reinterpret_cast<const double2*>(&L.uo[t][0][0]);
+      const double2* uo2 = reinterpret_cast<const double2*>(&L.ut[4 + t][0][0]);
       double2 uc2[kSub / 2];
 #pragma unroll
       for (int h = 0; h < kSub / 2; ++h) uc2[h] = uo2[h];
