@@ -321,18 +321,18 @@ __global__ __launch_bounds__(1024) void cholinv_leaf_kernel(const double* __rest
       const int c = 8 * tc + cj, b = c & 1;
       if (i > c) {
         const double li = v[b][i] * inv_d[c];
+        // a[t] right of the row's diagonal (and left of c) is never read
+        // again, so those entries take the update unguarded
 #pragma unroll
         for (int t = 0; t < kLeaf / 8; ++t) {
-          const int col = jj + 8 * t;
-          const double u = v[b][col];
+          const double u = v[b][jj + 8 * t];
           if (t > tc) {
-            a[t] = col <= i ? fma(-li, u, a[t]) : a[t];
+            a[t] = fma(-li, u, a[t]);
           } else if (t < tc) {
             x[t] = fma(-li, u, x[t]);
           } else {
-            const bool right = jj > cj;
-            a[t] = right && col <= i ? fma(-li, u, a[t]) : a[t];
-            x[t] = right ? x[t] : fma(-li, u, x[t]);
+            a[t] = fma(-li, u, a[t]);
+            x[t] = jj > cj ? x[t] : fma(-li, u, x[t]);
           }
         }
         // publish step c + 1's inputs: A'[., c+1] (owner jj == (c+1) & 7)
@@ -342,8 +342,15 @@ __global__ __launch_bounds__(1024) void cholinv_leaf_kernel(const double* __rest
         if (jj == (n1 & 7)) {
           if (i > n1) v[b ^ 1][i] = an;
           if (i == n1) {
-            inv_d[n1] = 1.0 / an;
-            inv_s[n1] = 1.0 / sqrt(an);
+            // v_rcp_f64 / v_rsq_f64 refined by two Newton steps each
+            double r = __builtin_amdgcn_rcp(an);
+            r = fma(r, fma(-an, r, 1.0), r);
+            r = fma(r, fma(-an, r, 1.0), r);
+            double q = __builtin_amdgcn_rsq(an);
+            q = q * fma(-0.5 * an * q, q, 1.5);
+            q = q * fma(-0.5 * an * q, q, 1.5);
+            inv_d[n1] = r;
+            inv_s[n1] = q;
           }
         }
         if (i == n1) {
