@@ -2,9 +2,10 @@
 
 Both sides run GPTQ's linear algebra in float64 and take every quantization
 decision in float32 on the float32 value of the current weight, exactly as
-the quantizer does.  They differ only in the order of their float64
-operations (the GPU's Hessian and Cholesky are blocked, the oracle's are
-NumPy/LAPACK), so a decision can differ only where a weight lies within
+the quantizer does.  They differ only in the order and the fusion of their
+float64 operations (the GPU's Hessian and factorization are blocked and its
+multiply-adds fused; the oracle's are NumPy/LAPACK with each product
+rounded), so a decision can differ only where a weight lies within
 ~1e-12 of a rounding boundary; a differing code then shifts that row's
 later errors.  The gate: codes and scales identical in at least 99 % of the
 rows (in practice all of them), and the layer error ||X W^T - X Q^T||^2 of
