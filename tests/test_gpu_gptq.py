@@ -71,6 +71,23 @@ def test_gptq_matches_oracle(fmt, rotate, dtype):
     assert abs(e_gpu / e_ora - 1.0) <= 1e-3, (e_gpu, e_ora)
 
 
+@pytest.mark.parametrize("fmt,k", [("nvfp4", 640), ("mxfp4", 384), ("nvfp4", 1152)])
+def test_gptq_uneven_splits(fmt, k):
+    # k = 640: two groups of column blocks, the second partial (512 + 128),
+    # and a factorization split 384 + 256; k = 384: 256 + 128; k = 1152:
+    # 640 + 512 down to three-leaf halves; 80 rows leave a ragged 64-row tile
+    n, N = 80, 300
+    w, x = _inputs(n, k, N, seed=6)
+    note("gptq uneven %s n=%d k=%d N=%d" % (fmt, n, k, N))
+    c, s, t = fq.gptq_quantize(w.to(DEV), x.to(DEV), fmt)
+    torch.cuda.synchronize()
+    oc, os_, ot, same = _compare(fmt, w, x, c, s, t)
+    e_gpu = oracle.gptq_layer_error(fmt, host_f32(w), host_f32(x), np_u8(c), np_u8(s),
+                                    None if t is None else np.float32(t.item()))
+    e_ora = oracle.gptq_layer_error(fmt, host_f32(w), host_f32(x), oc, os_, ot)
+    assert abs(e_gpu / e_ora - 1.0) <= 1e-3, (e_gpu, e_ora)
+
+
 @pytest.mark.parametrize("fmt", ["nvfp4", "mxfp4"])
 def test_gptq_diagonal_hessian_is_the_plain_quantizer(fmt):
     k = 128
