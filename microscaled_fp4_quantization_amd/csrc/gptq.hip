@@ -70,13 +70,28 @@ struct GemmArgs {
 typedef double v4d __attribute__((ext_vector_type(4)));
 
 template <int T>
-__global__ __launch_bounds__(256) void gemm_f64_kernel(GemmArgs G) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) void gemm_f64_kernel(
+    GemmArgs G) {
   constexpr int KC = 2048 / T;           // k-chunk: 8 elements of A and of B per thread
   constexpr int NT = T / 32;             // MFMA tiles per wave along each side
   __shared__ double As[KC][T + 1];
   __shared__ double Bs[KC][T + 1];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int i0 = blockIdx.y * T, j0 = blockIdx.x * T;
+  // a triangular operand makes the tiles' k-ranges unequal: the longest go
+  // out first (tile columns or rows in order of their k-range, slowest index)
+  int bx = blockIdx.x, by = blockIdx.y;
+  const int lin = by * gridDim.x + bx;
+  if (G.tri & kTriBTransLower) {
+    bx = gridDim.x - 1 - lin / gridDim.y;
+    by = lin % gridDim.y;
+  } else if (G.tri & kTriBLower) {
+    bx = lin / gridDim.y;
+    by = lin % gridDim.y;
+  } else if (G.tri & kTriALower) {
+    by = gridDim.y - 1 - lin / gridDim.x;
+    bx = lin % gridDim.x;
+  }
+  const int i0 = by * T, j0 = bx * T;
   const int wr = (T / 2) * (wave >> 1), wc = (T / 2) * (wave & 1);
   if ((G.tri & kLowerTiles) && j0 > i0) return;
   int kb = 0, ke = G.k;
