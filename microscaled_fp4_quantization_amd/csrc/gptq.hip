@@ -42,7 +42,7 @@ constexpr int kRows = 64;        // rows per GPTQ workgroup
 // ---- C = beta C + alpha A B, general strides ------------------------------------
 // A(i, t) = a[i * sa0 + t * sa1] (M x K), B(t, j) = b[t * sb0 + j * sb1]
 // (K x N), C[i * ldc + j] (M x N).  beta == 0 never reads C.  A T x T tile
-// (T = 64 or 128) per workgroup of 4 waves, each wave a T/2 x T/2 quarter as
+// (T = 32 or 64) per workgroup of 4 waves, each wave a T/2 x T/2 quarter as
 // (T/32) x (T/32) v_mfma_f64_16x16x4_f64 tiles (lane l: A row l % 16 / B
 // column l % 16 at k-slot l / 16; C column l % 16).  The tiles go through
 // LDS in chunks of 2048 / T k; the next chunk's global loads are in flight
@@ -194,8 +194,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
       }
 }
 
+// A 32 x 32 tile (64-k chunks) where 64 x 64 tiles would leave most of the
+// chip idle: the small products at the bottom of the factorization's
+// recursion, bound by the latency of their k-loop.
 hipError_t gemm_f64(const GemmArgs& G, hipStream_t stream) {
   if (G.m <= 0 || G.n <= 0) return hipSuccess;
+  const int64_t t64 = (int64_t)((G.m + 63) / 64) * ((G.n + 63) / 64);
+  if (t64 < 64) {
+    const dim3 grid((unsigned)((G.n + 31) / 32), (unsigned)((G.m + 31) / 32));
+    hipLaunchKernelGGL(gemm_f64_kernel<32>, grid, dim3(256), 0, stream, G);
+    return hipGetLastError();
+  }
   const dim3 grid((unsigned)((G.n + 63) / 64), (unsigned)((G.m + 63) / 64));
   hipLaunchKernelGGL(gemm_f64_kernel<64>, grid, dim3(256), 0, stream, G);
   return hipGetLastError();
