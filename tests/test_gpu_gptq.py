@@ -88,6 +88,18 @@ def test_gptq_uneven_splits(fmt, k):
     assert abs(e_gpu / e_ora - 1.0) <= 1e-3, (e_gpu, e_ora)
 
 
+def test_gptq_is_deterministic():
+    # no atomics and a fixed order of every fp64 sum: two calls give the same bytes
+    n, k, N = 200, 1024, 512
+    w, x = _inputs(n, k, N, seed=7)
+    note("gptq determinism")
+    wd, xd = w.to(DEV), x.to(DEV)
+    c1, s1, t1 = fq.gptq_quantize(wd, xd, "nvfp4")
+    c2, s2, t2 = fq.gptq_quantize(wd, xd, "nvfp4")
+    torch.cuda.synchronize()
+    assert torch.equal(c1, c2) and torch.equal(s1, s2) and torch.equal(t1, t2)
+
+
 @pytest.mark.parametrize("fmt", ["nvfp4", "mxfp4"])
 def test_gptq_diagonal_hessian_is_the_plain_quantizer(fmt):
     k = 128
