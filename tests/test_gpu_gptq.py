@@ -88,6 +88,17 @@ def test_gptq_uneven_splits(fmt, k):
     assert abs(e_gpu / e_ora - 1.0) <= 1e-3, (e_gpu, e_ora)
 
 
+@pytest.mark.parametrize("n,k,N", [(1, 128, 64), (24, 256, 1)])
+def test_gptq_degenerate_shapes(n, k, N):
+    # one weight row (a single, mostly idle row tile); one calibration row
+    # (H of rank one: only the damping makes it invertible)
+    w, x = _inputs(n, k, N, seed=8)
+    note("gptq degenerate n=%d k=%d N=%d" % (n, k, N))
+    c, s, t = fq.gptq_quantize(w.to(DEV), x.to(DEV), "nvfp4")
+    torch.cuda.synchronize()
+    _compare("nvfp4", w, x, c, s, t)
+
+
 def test_gptq_is_deterministic():
     # no atomics and a fixed order of every fp64 sum: two calls give the same bytes
     n, k, N = 200, 1024, 512
