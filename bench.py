@@ -4,16 +4,20 @@ python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
 A step is one pass of the hot path over one batch of synthetic input with
 every input already resident in HBM:
-  decode   (default) online NVFP4 quantize of X bf16 [8, 4096] (tensor scale
+  rotated_nv (default) fused blockwise Hadamard (16) + NVFP4 quantize of the
+           activations X bf16 [2048, 8192] with the tensor scale computed
+           from the data, then the NVFP4 W4A4 GEMM against the offline-rotated
+           and quantized W [28672, 8192], bf16 out: the largest W4A4
+           configuration (962 GFLOP per step).
+  rotated_mx the same step in MXFP4 (Hadamard 32, E8M0 scales).
+  prefill  NVFP4 quantize of X [4096, 4096] + GEMM vs W [14336, 4096].
+  decode   online NVFP4 quantize of X bf16 [8, 4096] (tensor scale
            computed from the data) + NVFP4 W4A4 GEMM against a pre-quantized
            W [14336, 4096], bf16 out, as one fp4_quantize_gemm call (a single
            launch; it also writes X's codes, scales and tensor scale).
-           Steps cycle over 17 distinct weight
-           copies (over 2x the 256 MB last-level cache) so the weights
-           stream from HBM as they do layer after layer.
-  prefill  NVFP4 quantize of X [4096, 4096] + GEMM vs W [14336, 4096].
-  rotated_nv / rotated_mx  fused Hadamard+quantize of X [2048, 8192] +
-           GEMM vs the offline-rotated W [28672, 8192].
+           Steps cycle over 17 distinct weight copies (over 2x the 256 MB
+           last-level cache) so the weights stream from HBM as they do layer
+           after layer.
   kv       NVFP4 quantize of K and V [32*8*32768, 128] bf16 with their given
            tensor scales + dequantize of both to FP8 E4M3.
   w4a16    W4A16 decode: X bf16 [8, 4096] as it is times the NVFP4 weight
@@ -33,8 +37,14 @@ every input already resident in HBM:
 Prints one JSON line.  The timed region is K steps back to back between one
 pair of HIP events (value, ms_per_step).  The dominant kernel is then timed
 the same way over the K steps' launches of it alone; its algorithmic bytes
-(or flops) per launch over that duration give the roofline figure.  The CPU
-oracle is timed on a bounded sample of the same workload on the host.
+(or flops) per launch over that duration give the roofline figure.  A
+separate sampling phase (at least 100 launches or 200 ms, in 10 windows of
+back-to-back launches) gives the median, p10 and p90 per launch of the step,
+the dominant kernel and, where the step launches it on its own, the
+activation quantize (reported with its algorithmic bytes and HBM fraction).
+HBM-bound workloads also report the warm figure (one weight copy, resident in
+the last-level cache).  The CPU oracle is timed on a bounded sample of the
+same workload on the host.
 """
 
 import argparse
@@ -65,11 +75,14 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
-    p.add_argument("--workload", default="decode",
+    p.add_argument("--workload", default="rotated_nv",
                    choices=["decode", "prefill", "rotated_nv", "rotated_mx", "kv", "mse", "w4a16",
                             "attention", "gptq"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
+    p.add_argument("--stat-ms", type=float, default=200.0,
+                   help="least GPU time of each sampling phase (median / p10 / p90)")
+    p.add_argument("--no-stats", action="store_true", help="skip the sampling phases")
     p.add_argument("--copy-bytes", type=int, default=0,
                    help="after the timed region, copy this many bytes device to device three "
                         "times: the plain copy that scales rocprofv3 FETCH_SIZE / WRITE_SIZE")
@@ -293,6 +306,11 @@ def setup(workload, torch, fq, lib):
             pre = [lib.quantize_call(NV, x, xc, xs, xt, fp4.TSCALE_COMPUTE, ws)]
             gs = [lib.gemm_call(NV, (xc, xs, xt), wqi, c, fp4.BF16) for wqi in wqs]
             name = "fp4_gemm (NVFP4, m=%d)" % m
+        if workload == "prefill":
+            W["quant"] = dict(calls=pre, bytes=quant_bytes(m, k, "nvfp4", 2),
+                              name="fp4_quantize (NVFP4, bf16 [%d, %d], tensor scale computed)" % (m, k))
+        else:
+            W["warm"] = [gs[0]]              # one weight copy: resident in the last-level cache
         W.update(pre=pre, dominant=gs, post=[], flops=2 * m * n * k,
                  dom_name=name,
                  dom_units=per if workload == "decode" else 2 * m * n * k,
@@ -320,6 +338,10 @@ def setup(workload, torch, fq, lib):
         c = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
         q = lib.quantize_call(f, x, xc, xs, xt, fp4.TSCALE_COMPUTE, ws, hadamard=True)
         g = lib.gemm_call(f, (xc, xs, xt), wq, c, fp4.BF16)
+        W["quant"] = dict(calls=[q], bytes=quant_bytes(m, k, fmt, 2),
+                          name="fp4_hadamard_quantize (%s, Hadamard %d, bf16 [%d, %d]%s)" % (
+                              fmt.upper(), bs, m, k,
+                              ", tensor scale computed" if fmt == "nvfp4" else ""))
         W.update(pre=[q], dominant=[g], post=[], flops=2 * m * n * k,
                  dom_name="fp4_gemm (%s, m=%d)" % (fmt.upper(), m), dom_units=2 * m * n * k,
                  dom_bound="mfma",
@@ -341,6 +363,7 @@ def setup(workload, torch, fq, lib):
         wqs = [wq] + [tuple(t.clone() for t in wq) for _ in range(copies - 1)]
         c = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
         gs = [lib.w4a16_call(NV, x, wqi, c, fp4.BF16) for wqi in wqs]
+        W["warm"] = [gs[0]]
         per = (n * (k // 2 + k // 16) + 4) + 2 * m * k + 2 * m * n
         W.update(pre=[], dominant=gs, post=[], flops=2 * m * n * k,
                  dom_name="fp4_gemm_w4a16 (NVFP4 weights, bf16 X, m=%d)" % m, dom_units=per,
@@ -462,14 +485,27 @@ def setup(workload, torch, fq, lib):
     return W
 
 
-def cpu_baseline(workload, W, seconds):
-    import numpy as np
-    import oracle
+def blas_threads():
     try:
         from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        return max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:
-        cores = 1
+        return 1
+
+
+def cpu_baseline(workload, W, seconds):
+    """The oracle timed on a bounded sample of the workload.  `cores` is the
+    number of threads the sample runs on: 1 for the elementwise NumPy stages,
+    NumPy's BLAS threads where the sample includes an fp64 matrix product."""
+    res = _cpu_baseline(workload, W, seconds, blas_threads())
+    res["host_cores"] = len(os.sched_getaffinity(0))
+    res["blas_threads"] = blas_threads()
+    return res
+
+
+def _cpu_baseline(workload, W, seconds, cores):
+    import numpy as np
+    import oracle
     h = W["host"]
     if workload == "mse":
         rows = 32                        # bounded sample: the first rows of W
@@ -555,6 +591,8 @@ def cpu_baseline(workload, W, seconds):
                 "sample": "w4a16 step (X %dx%d, W %dx%d), %d reps" % (x.shape + w.shape + (reps,))}
     if workload in ("prefill", "rotated_nv", "rotated_mx"):
         x = x[:64]                        # bounded sample: 64 activation rows
+    if workload in ("rotated_nv", "rotated_mx"):
+        w = w[:4096]                      # and 4096 of the 28672 weight rows
     b = 16 if fmt == "nvfp4" else 32
     wr = oracle.hadamard_blocks(w, b) if h["hadamard"] else w
     if fmt == "nvfp4":
@@ -575,8 +613,46 @@ def cpu_baseline(workload, W, seconds):
     dt = (time.perf_counter() - t0) / reps
     flops = 2.0 * x.shape[0] * w.shape[0] * w.shape[1]
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "sample": "%s step on X rows %d of %d (full W %dx%d), %d reps" % (
-                workload, x.shape[0], h["x"].shape[0], w.shape[0], w.shape[1], reps)}
+            "sample": "%s step (activation %squantize + GEMM reference) on X rows %d of %d and "
+                      "W rows %d of %d (W quantized offline, untimed), %d reps" % (
+                          workload, "Hadamard + " if h["hadamard"] else "", x.shape[0],
+                          h["x"].shape[0], w.shape[0], h["w"].shape[0], reps)}
+
+
+def sample(torch, fn, per_call, min_ms, cycles_per_ms, windows=10):
+    """GPU time of one call of fn: the median, p10 and p90 over `windows`
+    windows of back-to-back calls, each between its own HIP event pair, with
+    at least 100 calls or min_ms of GPU time in all.  A GPU spin ahead of
+    the windows keeps the host's enqueueing out of the measurement."""
+    import math
+    import numpy as np
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0, e1 = ev(), ev()
+    t0 = time.perf_counter()
+    e0.record()
+    for i in range(5):
+        fn(i)
+    e1.record()
+    host_ms = (time.perf_counter() - t0) * 1e3 / 5
+    torch.cuda.synchronize()
+    est = max(e0.elapsed_time(e1) / 5, 1e-3)
+    n = max(100, int(math.ceil(min_ms / est)))
+    n = min(int(math.ceil(n / windows)) * windows, 20000)
+    per = n // windows
+    evs = [ev() for _ in range(windows + 1)]
+    torch.cuda.synchronize()
+    torch.cuda._sleep(int((2.0 * host_ms * n + 2.0) * cycles_per_ms))
+    evs[0].record()
+    for w in range(windows):
+        for i in range(w * per, (w + 1) * per):
+            fn(i)
+        evs[w + 1].record()
+    torch.cuda.synchronize()
+    v = np.array([evs[w].elapsed_time(evs[w + 1]) / (per * per_call) for w in range(windows)])
+    return {"median_ms": round(float(np.median(v)), 5), "p10_ms": round(float(np.percentile(v, 10)), 5),
+            "p90_ms": round(float(np.percentile(v, 90)), 5), "mean_ms": round(float(v.mean()), 5),
+            "windows": windows, "calls": n}
 
 
 def main():
@@ -586,8 +662,8 @@ def main():
                       args.copy_bytes)
         return
     if args.gpus != 1:
-        print("bench.py: this build runs on one GPU only; --gpus %d is not supported "
-              "(the sharded path is described in DESIGN.md, not built)" % args.gpus, file=sys.stderr)
+        print("bench.py: this library runs on one GPU; --gpus %d is not supported (the "
+              "multi-GPU sharding of the path is not built)" % args.gpus, file=sys.stderr)
         sys.exit(2)
     import torch
     import microscaled_fp4_quantization_amd as fq
@@ -635,7 +711,7 @@ def main():
     torch.cuda.synchronize()
     ms_per_cycle = c0.elapsed_time(c1) / float(1 << 20)
     spin_ms = 2.0 * host_step * 1e3 * (args.steps + 4) + 2.0
-    spin_cycles = int(spin_ms / ms_per_cycle)
+    spin_cycles = int(1.0 / ms_per_cycle)
     # Timed region: K whole steps back to back, one event pair around them.
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -661,6 +737,19 @@ def main():
     d1.record()
     torch.cuda.synchronize()
     dom_avg = d0.elapsed_time(d1) / (args.steps * launches_per_step)
+    stats = {}
+    if not args.no_stats:
+        stats["step"] = sample(torch, step, 1, args.stat_ms, 1.0 / ms_per_cycle)
+        stats["dominant"] = sample(torch, dominant, launches_per_step, args.stat_ms,
+                                   1.0 / ms_per_cycle)
+        if "quant" in W:
+            qc = W["quant"]["calls"]
+            stats["quantize"] = sample(torch, lambda i: qc[i % len(qc)](), 1, args.stat_ms,
+                                       1.0 / ms_per_cycle)
+        if "warm" in W:
+            wc = W["warm"]
+            stats["warm"] = sample(torch, lambda i: wc[i % len(wc)](), 1, args.stat_ms,
+                                   1.0 / ms_per_cycle)
     if args.copy_bytes:
         # the plain copy of known size that calibrates the HBM byte counters
         src = torch.empty(args.copy_bytes, dtype=torch.uint8, device="cuda:0")
@@ -716,8 +805,48 @@ def main():
         "host_enqueue_ms_per_step": round(enqueue_s * 1e3 / args.steps, 4),
         "gpu_fed_by_host": bool(gpu_fed),
     }
-    if args.workload not in ("kv", "mse", "w4a16", "attention", "gptq"):
-        out["quantize_bytes_per_step"] = W["quant_bytes"]
+    if W["dom_bound"] == "mfma":
+        rf = out["roofline"]
+        rf["frac_fp4"] = round(achieved / MFMA_PEAK_TFLOPS["fp4"], 4)
+        if W["config"].get("format") == "nvfp4":
+            rf["peak_unit_used"] = "f16 matrix cores"
+            rf["note"] = ("NVFP4 runs as exact fp16 products (E2M1 x E4M3 is exact in fp16; the "
+                          "scaled FP4 MFMA takes only E8M0 scales per 32 values) on the f16 matrix "
+                          "cores: frac is against their %.0f TFLOP/s; against the FP4 peak the "
+                          "ceiling is %.3f" % (MFMA_PEAK_TFLOPS["f16"],
+                                               MFMA_PEAK_TFLOPS["f16"] / MFMA_PEAK_TFLOPS["fp4"]))
+    if stats:
+        out["stats"] = stats
+    if "quant" in W:
+        qb = W["quant"]["bytes"]
+        q = {"kernel": W["quant"]["name"], "bytes_per_launch": qb,
+             "bytes_rule": "input read once + codes + scales (+4 B tensor scale)"}
+        if "quantize" in stats:
+            qms = stats["quantize"]["median_ms"]
+            q.update({"median_ms": qms, "achieved_gbs": round(qb / (qms * 1e-3) / 1e9, 1),
+                      "peak_gbs": HBM_PEAK_GBS,
+                      "frac": round(qb / (qms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                      "timing": "median over windows of back-to-back launches of it alone "
+                                "(all its kernels)"})
+        out["quantize"] = q
+    elif args.workload == "decode":
+        out["quantize"] = {"kernel": "inside the fp4_quantize_gemm launch (not timed alone)",
+                           "bytes_per_launch": W["quant_bytes"]}
+    elif args.workload == "kv" and "dominant" in stats:
+        qms = stats["dominant"]["median_ms"]
+        out["quantize"] = {"kernel": W["dom_name"], "bytes_per_launch": W["dom_units"],
+                           "median_ms": qms,
+                           "achieved_gbs": round(W["dom_units"] / (qms * 1e-3) / 1e9, 1),
+                           "peak_gbs": HBM_PEAK_GBS,
+                           "frac": round(W["dom_units"] / (qms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                           "timing": "median over windows of back-to-back launches of it alone"}
+    if "warm" in stats and W["dom_bound"] == "hbm":
+        wms = stats["warm"]["median_ms"]
+        out["warm"] = {"median_ms": wms,
+                       "achieved_gbs": round(W["dom_units"] / (wms * 1e-3) / 1e9, 1),
+                       "frac": round(W["dom_units"] / (wms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                       "note": "one weight copy, resident in the 256 MB last-level cache: not an "
+                               "HBM figure"}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.workload, W, args.cpu_seconds)
     print(json.dumps(out), flush=True)

@@ -29,7 +29,12 @@
  *            a multiple of the block size (16 or 32).
  *   codes    uint8 [rows, k/2]: byte j of a row holds element 2j in its low
  *            nibble and element 2j+1 in its high nibble.
- *   scales   uint8 [rows, k/block], row-major, one byte per block.
+ *   scales   uint8 [rows, k/block], row-major, one byte per block.  The
+ *            quantizers write NVFP4 bytes 0x00..0x7E and MXFP4 bytes
+ *            0x00..0xFE; every call that reads scales accepts any byte:
+ *            E4M3 with its sign bit (0x7F and 0xFF are NaN), E8M0 with
+ *            0xFF NaN.  A NaN scale makes its block's values NaN (and the
+ *            GEMM outputs they reach); FP8 output of a NaN is unspecified.
  *   tensor scale (NVFP4 only): one float in device memory.
  *
  * Rounding (the pages state none; these are the library's definitions):

@@ -54,6 +54,15 @@ __device__ __forceinline__ float e4m3_decode_pos(uint32_t c) {
   return e ? as_f(((e + 120u) << 23) | (m << 20)) : (float)m * 0.001953125f;
 }
 
+// Any E4M3 byte -> its fp32 value: sign in bit 7, S.1111.111 is NaN (the
+// format has no infinity).  Every kernel that reads caller-supplied NVFP4
+// block-scale bytes decodes them through this (or through the hardware
+// fp8 conversion, which has the same rule).
+__device__ __forceinline__ float e4m3_decode(uint32_t c) {
+  const float v = ((c & 0x7Fu) == 0x7Fu) ? __builtin_nanf("") : e4m3_decode_pos(c & 0x7Fu);
+  return (c & 0x80u) ? -v : v;
+}
+
 // ---- E2M1 ------------------------------------------------------------------
 // Two fp32 -> two E2M1 codes (round to nearest even, ties to the even code,
 // saturating at 6, sign of zero kept) written into byte `SEL` of `old`.
@@ -84,14 +93,13 @@ __device__ __forceinline__ uint32_t pack_e4m3x4(const float* y) {
   return (uint32_t)w;
 }
 
-// Block scale byte -> its fp32 value.  NVFP4 (NV = true): E4M3, sign bit
-// honoured.  MXFP4: E8M0 2^(c-127), the byte 0 giving 2^-127.
+// Block scale byte -> its fp32 value.  NVFP4 (NV = true): E4M3 with its
+// sign, 0x7F / 0xFF NaN.  MXFP4: E8M0 2^(c-127), the byte 0 giving 2^-127,
+// 0xFF NaN.
 template <bool NV>
 __device__ __forceinline__ float block_scale_value(uint32_t sbyte) {
-  if (NV) {
-    const float sv = e4m3_decode_pos(sbyte & 0x7Fu);
-    return (sbyte & 0x80u) ? -sv : sv;
-  }
+  if (NV) return e4m3_decode(sbyte);
+  if (sbyte == 0xFFu) return __builtin_nanf("");
   return sbyte ? as_f(sbyte << 23) : as_f(0x00400000u);
 }
 

@@ -153,8 +153,8 @@ __global__ __launch_bounds__(256) void gemm_nv_simple(
         ca = as[arow[i] * kb + kk / 16];
         cb = bs[brow[i] * kb + kk / 16];
       }
-      fa[i] = dequant8_f16(wa, (_Float16)e4m3_decode_pos(ca & 0x7Fu));
-      fb[i] = dequant8_f16(wb, (_Float16)e4m3_decode_pos(cb & 0x7Fu));
+      fa[i] = dequant8_f16(wa, (_Float16)e4m3_decode(ca));
+      fb[i] = dequant8_f16(wb, (_Float16)e4m3_decode(cb));
     }
 #pragma unroll
     for (int i = 0; i < 2; ++i)

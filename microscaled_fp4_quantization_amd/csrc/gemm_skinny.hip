@@ -41,7 +41,7 @@ constexpr int kWaves = 4;
 constexpr int kRows = 16;
 
 __device__ __forceinline__ _Float16 e4m3_to_f16(uint32_t c) {
-  return (_Float16)e4m3_decode_pos(c & 0x7Fu);
+  return (_Float16)e4m3_decode(c);
 }
 
 __device__ __forceinline__ v8h dequant8(uint32_t w, _Float16 s) {
@@ -112,14 +112,23 @@ __global__ __launch_bounds__(256) void gemm_nv_skinny(
     uint32_t wsv[UNROLL], asv[UNROLL];
 #pragma unroll
     for (int u = 0; u < UNROLL; ++u) {
+      // lanes past k load nothing (their 32 values may lie past the row, or
+      // past the buffer) and take zero codes with a zero scale: a scale byte
+      // from elsewhere could be NaN, and NaN * 0 is NaN
       const bool ok = (ch + u < c1) && ((ch + u) * 4 + g < k32);
-      const int64_t cc = ok ? ch + u : 0;
-      wv[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wp + cc * 64));
-      wsv[u] = *reinterpret_cast<const uint16_t*>(wsp + cc * 8);
-      av[u] = *reinterpret_cast<const u32x4*>(ap + cc * 64);
-      asv[u] = *reinterpret_cast<const uint16_t*>(asp + cc * 8);
-      if (!ok || !arow_ok) av[u] = (u32x4){0u, 0u, 0u, 0u};
-      if (!ok) wv[u] = (u32x4){0u, 0u, 0u, 0u};
+      const int64_t cc = ch + u;
+      wv[u] = (u32x4){0u, 0u, 0u, 0u};
+      av[u] = (u32x4){0u, 0u, 0u, 0u};
+      wsv[u] = 0u;
+      asv[u] = 0u;
+      if (ok) {
+        wv[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wp + cc * 64));
+        wsv[u] = *reinterpret_cast<const uint16_t*>(wsp + cc * 8);
+        if (arow_ok) {
+          av[u] = *reinterpret_cast<const u32x4*>(ap + cc * 64);
+          asv[u] = *reinterpret_cast<const uint16_t*>(asp + cc * 8);
+        }
+      }
     }
 #pragma unroll
     for (int u = 0; u < UNROLL; ++u) {
@@ -160,14 +169,20 @@ __global__ __launch_bounds__(256) void gemm_mx_skinny(
 #pragma unroll
     for (int u = 0; u < UNROLL; ++u) {
       const int64_t blk = (ch + u) * 4 + g;
+      // lanes past k (and rows past m) take zero codes with scale 2^0
       const bool ok = (ch + u < c1) && blk < kblocks;
-      const int64_t bb = ok ? blk : 0;
-      wv[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(b + wrow * kbytes + bb * 16));
-      av[u] = *reinterpret_cast<const u32x4*>(a + arow * kbytes + bb * 16);
-      wsv[u] = bs[wrow * kblocks + bb];
-      asv[u] = as[arow * kblocks + bb];
-      if (!ok || !arow_ok) av[u] = (u32x4){0u, 0u, 0u, 0u};
-      if (!ok) wv[u] = (u32x4){0u, 0u, 0u, 0u};
+      wv[u] = (u32x4){0u, 0u, 0u, 0u};
+      av[u] = (u32x4){0u, 0u, 0u, 0u};
+      wsv[u] = 127;
+      asv[u] = 127;
+      if (ok) {
+        wv[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(b + wrow * kbytes + blk * 16));
+        wsv[u] = bs[wrow * kblocks + blk];
+        if (arow_ok) {
+          av[u] = *reinterpret_cast<const u32x4*>(a + arow * kbytes + blk * 16);
+          asv[u] = as[arow * kblocks + blk];
+        }
+      }
     }
 #pragma unroll
     for (int u = 0; u < UNROLL; ++u) {
@@ -622,7 +637,7 @@ __global__ __launch_bounds__(256) void gemm_w4a16_simple(
   const uint8_t* sr = bs + j * (int64_t)(k / BS);
   for (int kb = 0; kb < k; kb += BS) {
     const uint32_t sb = sr[kb / BS];
-    const float S = FMT == kFmtNV ? e4m3_decode_pos(sb) : as_f(sb == 0 ? 0x00400000u : sb << 23);
+    const float S = block_scale_value<FMT == kFmtNV>(sb);
     for (int t = 0; t < BS; t += 8) {
       const uint32_t w = *reinterpret_cast<const uint32_t*>(wr + (kb + t) / 2);
       const v2f p0 = e2m1_unpack2<0>(w), p1 = e2m1_unpack2<1>(w);

@@ -89,32 +89,42 @@ def test_quantize_dequantize_round_trip_error():
         assert err < (0.11 if fmt == "nvfp4" else 0.13)
 
 
-def test_kv_stream_full_size_sampled():
-    # K, V [32, 8, 32768, 128] bf16; NVFP4 along head_dim with a given tensor
-    # scale (the cache keeps one fixed scale per tensor), dequantized to FP8.
+@pytest.mark.parametrize("name", ["k", "v"])
+def test_kv_stream_full_size(name):
+    # K or V [32, 8, 32768, 128] bf16 (2^30 values); NVFP4 along head_dim
+    # with a given tensor scale (the cache keeps one fixed scale per tensor),
+    # dequantized to FP8: every row of the codes, scales and FP8 bytes against
+    # the oracle (rows checked in parallel host processes).
+    from oracle_pool import OracleRun
     d = workloads.kv(device=DEV)
-    rng = np.random.default_rng(0)
-    for name in ("k", "v"):
-        t = d[name]
-        x2 = t.view(-1, 128)
-        rows = x2.shape[0]
-        amax = np.float32(torch.max(torch.abs(x2)).float().item())    # input preparation
-        s_t = oracle.nvfp4_tensor_scale_from_amax(amax)
-        ts = torch.tensor([float(s_t)], dtype=torch.float32, device=DEV)
-        note("kv quantize %s" % name)
-        codes, scales, _ = fq.quantize(x2, "nvfp4", tensor_scale=ts)
-        note("kv dequantize %s" % name)
-        y8 = fq.dequantize(codes, scales, ts, "nvfp4", "e4m3")
+    x2 = d[name].view(-1, 128)
+    del d
+    amax = np.float32(torch.max(torch.abs(x2)).float().item())    # input preparation
+    s_t = oracle.nvfp4_tensor_scale_from_amax(amax)
+    ts = torch.tensor([float(s_t)], dtype=torch.float32, device=DEV)
+    note("kv quantize %s" % name)
+    codes, scales, _ = fq.quantize(x2, "nvfp4", tensor_scale=ts)
+    note("kv dequantize %s" % name)
+    y8 = fq.dequantize(codes, scales, ts, "nvfp4", "e4m3")
+    torch.cuda.synchronize()
+    xb = x2.view(torch.int16).cpu().numpy().view(np.uint16)
+    del x2
+    with OracleRun(xb, "bf16", np_u8(codes), np_u8(scales), deq=y8.view(torch.uint8).cpu().numpy(),
+                   deq_dtype="e4m3", chunk_rows=1 << 15) as run:
+        del codes, scales, y8, xb
+        assert run.check("nvfp4", s_t) is None
+
+
+def test_rounding_worked_examples(golden_dir):
+    # the hand-derived bf16 / f16 roundings (ties, f16 overflow, subnormals)
+    from test_oracle_quant import rounding_case_expected, rounding_case_inputs
+    g = json.load(open(os.path.join(golden_dir, "dequant_rounding_worked.json")))
+    for case in g["cases"]:
+        packed, scales, ts = rounding_case_inputs(case)
+        note("dequantize rounding case: %s" % case["name"])
+        tst = None if ts is None else torch.tensor([float(ts)], dtype=torch.float32, device=DEV)
+        y = fq.dequantize(torch.from_numpy(packed).to(DEV), torch.from_numpy(scales).to(DEV), tst,
+                          case["fmt"], case["out"])
         torch.cuda.synchronize()
-        for r0 in rng.integers(0, rows - 4096, size=6):
-            sl = slice(int(r0), int(r0) + 4096)
-            p, s, _ = oracle.nvfp4_quantize(host_f32(x2[sl]), s_t)
-            assert np.array_equal(np_u8(scales[sl]), s)
-            assert np.array_equal(np_u8(codes[sl]), p)
-            e8 = oracle.dequantize("nvfp4", p, s, s_t, "e4m3")
-            assert np.array_equal(y8[sl].view(torch.uint8).cpu().numpy(), e8)
-        # last rows (tail of the flat range)
-        sl = slice(rows - 64, rows)
-        p, s, _ = oracle.nvfp4_quantize(host_f32(x2[sl]), s_t)
-        assert np.array_equal(np_u8(codes[sl]), p)
-        del codes, scales, y8
+        got = gpu_bits(y, case["out"])
+        assert np.array_equal(got, rounding_case_expected(case)), (case["name"], got)

@@ -297,3 +297,43 @@ def test_nvfp4_more_accurate_than_mxfp4_on_gaussian():
     pm, sm = oracle.mxfp4_quantize(x)
     e_mx = np.linalg.norm(x - oracle.dequantize("mxfp4", pm, sm)) / np.linalg.norm(x)
     assert e_nv < e_mx
+
+
+def _scale_of(case):
+    """Tensor scale of a rounding case: a sum of terms like "1", "2^-8",
+    "3*2^-11", or the fp32 bit pattern in hex."""
+    if "tensor_scale_bits" in case:
+        return np.array([int(case["tensor_scale_bits"], 16)], dtype=np.uint32).view(np.float32)[0]
+    if "tensor_scale" not in case:
+        return None
+    total = sum(_num(term) for term in case["tensor_scale"].split("+"))
+    s = np.float32(total)
+    assert float(s) == total          # every scale in the file is exact in fp32
+    return s
+
+
+def rounding_case_inputs(case):
+    """(packed codes [1, k/2], scale bytes [1, k/block], tensor scale) of a
+    case in dequant_rounding_worked.json."""
+    packed = _codes_to_packed([case["codes"]])
+    scales = _hex([case["scales"]])
+    return packed, scales, _scale_of(case)
+
+
+def rounding_case_expected(case):
+    k = len(case["codes"])
+    exp = np.zeros((1, k), dtype=np.uint16)
+    for i, v in case["expected"].items():
+        exp[0, int(i)] = int(v, 16)
+    return exp
+
+
+def test_dequantize_rounding_worked(golden_dir):
+    # bf16 / f16 output rounding: ties to even, f16 overflow to infinity at
+    # 65520, f16 subnormals, bf16 of fp32 subnormals (hand-derived)
+    g = _load(golden_dir, "dequant_rounding_worked.json")
+    for case in g["cases"]:
+        packed, scales, ts = rounding_case_inputs(case)
+        y = oracle.dequantize(case["fmt"], packed, scales, ts, case["out"])
+        assert y.dtype == np.uint16, case["name"]
+        assert np.array_equal(y, rounding_case_expected(case)), (case["name"], y)
