@@ -295,7 +295,7 @@ def setup(workload, torch, fq, lib):
         xc = torch.empty((m, k // 2), dtype=torch.uint8, device=dev)
         xs = torch.empty((m, k // 16), dtype=torch.uint8, device=dev)
         xt = torch.empty(1, dtype=torch.float32, device=dev)
-        ws = torch.empty(4096, dtype=torch.uint8, device=dev)
+        ws = torch.empty(1 << 16, dtype=torch.uint8, device=dev)   # quantize workspace
         c = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
         if workload == "decode":
             # one call: the activations are quantized inside the GEMM launch
@@ -334,7 +334,7 @@ def setup(workload, torch, fq, lib):
         xc = torch.empty((m, k // 2), dtype=torch.uint8, device=dev)
         xs = torch.empty((m, k // bs), dtype=torch.uint8, device=dev)
         xt = torch.empty(1, dtype=torch.float32, device=dev) if fmt == "nvfp4" else None
-        ws = torch.empty(4096, dtype=torch.uint8, device=dev)
+        ws = torch.empty(1 << 16, dtype=torch.uint8, device=dev)   # quantize workspace
         c = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
         q = lib.quantize_call(f, x, xc, xs, xt, fp4.TSCALE_COMPUTE, ws, hadamard=True)
         g = lib.gemm_call(f, (xc, xs, xt), wq, c, fp4.BF16)
@@ -379,7 +379,7 @@ def setup(workload, torch, fq, lib):
         codes = torch.empty((n, k // 2), dtype=torch.uint8, device=dev)
         scales = torch.empty((n, k // 16), dtype=torch.uint8, device=dev)
         ts = torch.empty(1, dtype=torch.float32, device=dev)
-        ws = torch.empty(4096, dtype=torch.uint8, device=dev)
+        ws = torch.empty(1 << 16, dtype=torch.uint8, device=dev)   # quantize workspace
         q = lib.quantize_mse_call(w, codes, scales, ts, fp4.TSCALE_COMPUTE, ws)
         nblocks = n * k // 16
         W.update(pre=[], dominant=[q], post=[], flops=0,
@@ -416,7 +416,7 @@ def setup(workload, torch, fq, lib):
         d = workloads.attention(device=dev, batch=B, kv_heads=H, q_heads=H * G, tokens=T,
                                 head_dim=D)
         caches, news, tss, host = [], [], [], {}
-        ws = torch.empty(4096, dtype=torch.uint8, device=dev)
+        ws = torch.empty(1 << 16, dtype=torch.uint8, device=dev)   # quantize workspace
         for name in ("k", "v"):
             x = d.pop(name)
             codes = torch.empty((B, H, T, D // 2), dtype=torch.uint8, device=dev)

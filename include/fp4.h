@@ -86,9 +86,10 @@ typedef enum {
 /* Human-readable name of a status code (static string, never NULL). */
 const char* fp4_status_string(fp4_status s);
 
-/* Bytes of device workspace fp4_quantize / fp4_hadamard_quantize need for
- * these arguments: nonzero only for NVFP4 in FP4_TSCALE_COMPUTE mode (the
- * per-workgroup partial maxima of the tensor amax pass). */
+/* Bytes of device workspace fp4_quantize / fp4_hadamard_quantize /
+ * fp4_quantize_mse need for these arguments: nonzero only for NVFP4 in
+ * FP4_TSCALE_COMPUTE mode (the per-workgroup partial maxima of the tensor
+ * amax pass, read back by the quantizing pass). */
 size_t fp4_quantize_workspace_size(fp4_format fmt, fp4_tscale_mode mode,
                                    int64_t rows, int64_t k);
 
@@ -108,6 +109,8 @@ size_t fp4_quantize_workspace_size(fp4_format fmt, fp4_tscale_mode mode,
  *   mode          FP4_TSCALE_COMPUTE or FP4_TSCALE_GIVEN (ignored for MXFP4).
  *   workspace     device scratch of at least fp4_quantize_workspace_size()
  *                 bytes (may be NULL when that size is 0); 16-byte aligned.
+ *                 Its contents on entry do not matter; calls that overlap
+ *                 in time (other streams) must not share a workspace.
  * Returns FP4_OK, FP4_EINVAL or FP4_EHIP.
  */
 fp4_status fp4_quantize(fp4_format fmt, const void* x, fp4_dtype x_dtype,

@@ -9,14 +9,17 @@
 // computed online for activations).
 //
 // Work decomposition.  A [rows, k] tensor with k a multiple of the block size
-// is a flat run of blocks, so the kernels see it as n = rows*k elements cut
-// into chunks of 8.  Lane t of a wave owns chunk base + t: one 16-byte load
-// for bf16/fp16 input (two for fp32), so every load instruction of a wave
-// reads 1 KiB (bf16) of contiguous memory.  An NVFP4 block is a lane pair
-// (t, t^1), an MXFP4 block a lane quad; block max and the cross-lane
-// butterfly stages use DPP quad permutes.  Each lane writes its 8 codes as
-// one dword (contiguous across the wave) and the first lane of a block writes
-// the scale byte.
+// is a flat run of blocks.  The bulk kernels (blocks_kernel and its max pass)
+// give each lane one whole block: its 16 or 32 contiguous values in 16-byte
+// loads, the rotation's butterfly stages inside the lane, the block's scale
+// arithmetic once per block, its codes as one 8- or 16-byte store and its
+// scale byte.  The kernels for short inputs (the single-workgroup
+// compute-mode kernel for decode activations, the KV append, the rotation
+// alone) cut the elements into chunks of 8 instead: lane t of a wave owns
+// chunk base + t, an NVFP4 block is a lane pair (t, t^1), an MXFP4 block a
+// lane quad, and the block max and the cross-lane butterfly stages use DPP
+// quad permutes.  Both orders of arithmetic are the same, so both give the
+// same bits.
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -25,11 +28,10 @@ using namespace fp4dev;
 namespace {
 
 constexpr int kThreads = 256;        // 4 waves of 64
-constexpr int kUnroll = 8;           // chunks per thread per loop trip
-constexpr int kChunksPerTrip = kThreads * kUnroll;
 constexpr int kMaxPartials = 1024;   // amax partials (workspace floats)
 
 typedef uint32_t u32x4e __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2e __attribute__((ext_vector_type(2)));
 typedef float f32x4e __attribute__((ext_vector_type(4)));
 
 // 8 elements of chunk c widened to fp32 (exact); zeros when !valid.
@@ -168,37 +170,146 @@ __device__ __forceinline__ void quantize_chunk(const float v[8], int lane, float
   }
 }
 
-// Pass 1 of dynamic NVFP4 scaling: per-workgroup max |x| (of the rotated
-// values when HAD > 0) into partials[blockIdx.x].
-template <int DT, int HAD>
-__global__ __launch_bounds__(kThreads) void amax_partial_kernel(
-    const void* __restrict__ x, int64_t nchunks, float* __restrict__ partials) {
-  const int lane = threadIdx.x & 63;
-  float m = 0.0f;
-  for (int64_t base = (int64_t)blockIdx.x * kChunksPerTrip; base < nchunks;
-       base += (int64_t)gridDim.x * kChunksPerTrip) {
+// ---- block-per-lane kernels ----------------------------------------------
+// The bulk quantize path: lane l of a wave owns one whole block (BS = 16
+// NVFP4 or 32 MXFP4 values, BS * element-size bytes of contiguous input),
+// so the rotation's butterfly stages all run inside the lane and the block's
+// scale arithmetic (two IEEE divisions for NVFP4) runs once per block.  The
+// arithmetic, and its order, is that of quantize_chunk / fwht_chunk.
+
+template <int DT, int BS, bool NT>
+__device__ __forceinline__ void load_block(const void* __restrict__ x, int64_t b, bool valid,
+                                           float v[BS]) {
+  constexpr int L = BS * (DT == kInF32 ? 4 : 2) / 16;     // 16-byte pieces
+  const u32x4e* p = reinterpret_cast<const u32x4e*>(x) + b * L;
+  u32x4e w[L];
 #pragma unroll
-    for (int j = 0; j < kUnroll; ++j) {
-      const int64_t c = base + j * kThreads + threadIdx.x;
-      float v[8];
-      load_chunk<DT>(x, c, c < nchunks, v);
-      if (HAD) fwht_chunk<HAD>(v, lane);
-      m = fmaxf(m, amax8(v));
+  for (int i = 0; i < L; ++i) {
+    w[i] = (u32x4e){0u, 0u, 0u, 0u};
+    if (valid) w[i] = NT ? __builtin_nontemporal_load(p + i) : p[i];
+  }
+#pragma unroll
+  for (int i = 0; i < L; ++i) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (DT == kInF32) {
+        v[4 * i + j] = as_f(w[i][j]);
+      } else if (DT == kInBF16) {
+        v[8 * i + 2 * j] = bf16_lo(w[i][j]);
+        v[8 * i + 2 * j + 1] = bf16_hi(w[i][j]);
+      } else {
+        // through a scalar: clang's bit cast of a vector-element lvalue reads
+        // the vector's first element whatever the index
+        const uint32_t wd = w[i][j];
+        const v2h h = __builtin_bit_cast(v2h, wd);
+        v[8 * i + 2 * j] = (float)h.x;
+        v[8 * i + 2 * j + 1] = (float)h.y;
+      }
+    }
+  }
+}
+
+// Blockwise Hadamard of one whole block in the lane: stages h = 1, 2, 4, ...,
+// BS/2, each pair (j, j + h) -> (lower + upper, lower - upper), then one
+// multiply by fp32(1/sqrt(BS)).
+template <int BS>
+__device__ __forceinline__ void fwht_block(float v[BS]) {
+#pragma unroll
+  for (int h = 1; h < BS; h *= 2) {
+#pragma unroll
+    for (int s = 0; s < BS; s += 2 * h) {
+#pragma unroll
+      for (int j = s; j < s + h; ++j) {
+        const float u = v[j], w = v[j + h];
+        v[j] = u + w;
+        v[j + h] = u - w;
+      }
+    }
+  }
+  const float cb = (BS == 16) ? 0.25f : __uint_as_float(0x3E3504F3u);  // fp32(1/sqrt(32))
+#pragma unroll
+  for (int j = 0; j < BS; ++j) v[j] = v[j] * cb;
+}
+
+template <int BS>
+__device__ __forceinline__ float amax_block(const float v[BS]) {
+  float a = 0.0f;
+#pragma unroll
+  for (int j = 0; j < BS; j += 2) a = fmaxf(a, fmaxf(fabsf(v[j]), fabsf(v[j + 1])));
+  return a;
+}
+
+// One block to its BS/8 code dwords and scale byte (arithmetic as in
+// quantize_chunk).
+template <int FMT, int BS>
+__device__ __forceinline__ void quantize_block(const float v[BS], float s_t, float d,
+                                               uint32_t w[BS / 8], uint32_t& sbyte) {
+  const float a = amax_block<BS>(v);
+  float r;
+  if (FMT == kFmtNV) {
+    const float u = a / d;
+    sbyte = e4m3_encode_pos(u);
+    const float S = e4m3_decode_pos(sbyte) * s_t;
+    r = 1.0f / S;
+    // S == 0 (zero block) or an overflowing reciprocal: sign bits only.
+    if (!(S != 0.0f && r < __builtin_inff())) r = 0.0f;
+  } else {
+    const int kx = mx_block_exponent(a);
+    sbyte = (uint32_t)(kx + 127);
+    r = as_f((uint32_t)(127 - kx) << 23);  // 2^-k, a normal float for k in [-127, 126]
+  }
+#pragma unroll
+  for (int i = 0; i < BS / 8; ++i) {
+    const float* q = v + 8 * i;
+    uint32_t t = e2m1_pack2<0>(0u, q[0] * r, q[1] * r);
+    t = e2m1_pack2<1>(t, q[2] * r, q[3] * r);
+    t = e2m1_pack2<2>(t, q[4] * r, q[5] * r);
+    w[i] = e2m1_pack2<3>(t, q[6] * r, q[7] * r);
+  }
+}
+
+template <int FMT>
+constexpr int blocks_per_thread() { return FMT == kFmtNV ? 4 : 2; }
+
+// Pass 1 of dynamic NVFP4 scaling: per-workgroup max |x| (of the rotated
+// values when HAD > 0) into partials[blockIdx.x].  The same block -> thread
+// mapping as blocks_kernel, and ordinary (cached) loads, so that the second
+// pass finds much of x in the caches of the same XCD.
+template <int DT, int HAD>
+__global__ __launch_bounds__(kThreads) void amax_blocks_kernel(const void* __restrict__ x,
+                                                               int64_t nblocks,
+                                                               float* __restrict__ partials) {
+  constexpr int BS = 16, U = blocks_per_thread<kFmtNV>();
+  float m = 0.0f;
+  // one trip per workgroup unless the tensor needs more than kMaxPartials
+  for (int64_t base = (int64_t)blockIdx.x * (U * kThreads) + threadIdx.x; base < nblocks + threadIdx.x;
+       base += (int64_t)gridDim.x * (U * kThreads)) {
+    float v[U][BS];
+#pragma unroll
+    for (int j = 0; j < U; ++j) load_block<DT, BS, false>(x, base + j * kThreads, base + j * kThreads < nblocks, v[j]);
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+      if (HAD) fwht_block<BS>(v[j]);
+      m = fmaxf(m, amax_block<BS>(v[j]));
     }
   }
   m = block_max(m);
   if (threadIdx.x == 0) partials[blockIdx.x] = m;
 }
 
-// Quantize.  FMT: kFmtNV / kFmtMX.  HAD: 0, 16 or 32.  COMPUTE (NVFP4):
-// reduce the amax partials to s_t here (every workgroup, redundantly: at
-// most 4 KiB from L2) and let workgroup 0 publish it; otherwise read s_t.
+// Quantize, one block per lane, U blocks per thread.  COMPUTE (NVFP4):
+// reduce the npartials maxima of amax_blocks_kernel to s_t (every workgroup,
+// redundantly) and let workgroup 0 publish it; otherwise read s_t.
 template <int FMT, int DT, int HAD, bool COMPUTE>
-__global__ __launch_bounds__(kThreads) void quantize_kernel(
-    const void* __restrict__ x, int64_t nchunks, uint32_t* __restrict__ codes,
-    uint8_t* __restrict__ scales, float* __restrict__ tscale,
-    const float* __restrict__ partials, int npartials) {
-  const int lane = threadIdx.x & 63;
+__global__ __launch_bounds__(kThreads) void blocks_kernel(
+    const void* __restrict__ x, int64_t nblocks, uint8_t* __restrict__ codes,
+    uint8_t* __restrict__ scales, float* __restrict__ tscale, const float* __restrict__ partials,
+    int npartials) {
+  constexpr int BS = FMT == kFmtNV ? 16 : 32, U = blocks_per_thread<FMT>();
+  const int64_t base = (int64_t)blockIdx.x * (U * kThreads) + threadIdx.x;
+  float v[U][BS];
+#pragma unroll
+  for (int j = 0; j < U; ++j) load_block<DT, BS, true>(x, base + j * kThreads, base + j * kThreads < nblocks, v[j]);
   float s_t = 1.0f, d = 6.0f;
   if (FMT == kFmtNV) {
     if (COMPUTE) {
@@ -213,20 +324,21 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
     }
     d = 6.0f * s_t;
   }
-
-  for (int64_t base = (int64_t)blockIdx.x * kChunksPerTrip; base < nchunks;
-       base += (int64_t)gridDim.x * kChunksPerTrip) {
-    float v[kUnroll][8];
 #pragma unroll
-    for (int j = 0; j < kUnroll; ++j) {
-      const int64_t c = base + j * kThreads + threadIdx.x;
-      load_chunk<DT>(x, c, c < nchunks, v[j]);
-    }
-#pragma unroll
-    for (int j = 0; j < kUnroll; ++j) {
-      const int64_t c = base + j * kThreads + threadIdx.x;
-      if (HAD) fwht_chunk<HAD>(v[j], lane);
-      quantize_chunk<FMT>(v[j], lane, s_t, d, c, c < nchunks, codes, scales);
+  for (int j = 0; j < U; ++j) {
+    const int64_t b = base + j * kThreads;
+    if (HAD) fwht_block<BS>(v[j]);
+    uint32_t w[BS / 8], sbyte;
+    quantize_block<FMT, BS>(v[j], s_t, d, w, sbyte);
+    if (b < nblocks) {
+      if (BS == 16) {
+        __builtin_nontemporal_store(((u32x2e){w[0], w[1 % (BS / 8)]}),
+                                    reinterpret_cast<u32x2e*>(codes) + b);
+      } else {
+        __builtin_nontemporal_store(((u32x4e){w[0], w[1 % (BS / 8)], w[2 % (BS / 8)], w[3 % (BS / 8)]}),
+                                    reinterpret_cast<u32x4e*>(codes) + b);
+      }
+      scales[b] = (uint8_t)sbyte;
     }
   }
 }
@@ -416,11 +528,11 @@ hipError_t launch_mse_typed(const void* x, int64_t nblocks, uint8_t* codes, uint
   const int grid = (int)((nblocks + kMseThreads - 1) / kMseThreads);
   uint2* codes64 = reinterpret_cast<uint2*>(codes);
   if (compute) {
-    const int64_t nchunks = 2 * nblocks;
-    const int64_t trips = (nchunks + kChunksPerTrip - 1) / kChunksPerTrip;
+    const int64_t per_wg = (int64_t)blocks_per_thread<kFmtNV>() * kThreads;
+    const int64_t trips = (nblocks + per_wg - 1) / per_wg;
     const int g = (int)(trips < kMaxPartials ? trips : kMaxPartials);
     float* partials = reinterpret_cast<float*>(workspace);
-    hipLaunchKernelGGL((amax_partial_kernel<DT, 0>), dim3(g), dim3(kThreads), 0, stream, x, nchunks,
+    hipLaunchKernelGGL((amax_blocks_kernel<DT, 0>), dim3(g), dim3(kThreads), 0, stream, x, nblocks,
                        partials);
     hipLaunchKernelGGL((quantize_mse_kernel<DT, true>), dim3(grid), dim3(kMseThreads), 0, stream, x,
                        nblocks, codes64, scales, tscale, (const float*)partials, g);
@@ -435,26 +547,23 @@ template <int FMT, int DT, int HAD>
 hipError_t launch_typed(const void* x, int64_t nchunks, uint8_t* codes,
                         uint8_t* scales, float* tscale, bool compute,
                         void* workspace, hipStream_t stream) {
-  // one trip per workgroup: a grid-stride cap (a few thousand workgroups)
-  // cost 10 % of the bandwidth on long tensors; at most 2^26 workgroups here
-  int64_t trips = (nchunks + kChunksPerTrip - 1) / kChunksPerTrip;
-  const int grid = (int)trips;
-  uint32_t* codes32 = reinterpret_cast<uint32_t*>(codes);
+  constexpr int BS = FMT == kFmtNV ? 16 : 32;
+  const int64_t nblocks = nchunks / (BS / 8);
+  const int64_t per_wg = (int64_t)blocks_per_thread<FMT>() * kThreads;
+  const int64_t grid = (nblocks + per_wg - 1) / per_wg;      // at most 2^30 / 4 workgroups
   if (FMT == kFmtNV && compute && nchunks <= kSmallChunks) {
     hipLaunchKernelGGL((quantize_small_kernel<DT, HAD>), dim3(1), dim3(kSmallThreads), 0, stream,
-                       x, nchunks, codes32, scales, tscale);
+                       x, nchunks, reinterpret_cast<uint32_t*>(codes), scales, tscale);
   } else if (FMT == kFmtNV && compute) {
     float* partials = reinterpret_cast<float*>(workspace);
-    const int g = (int)(trips < kMaxPartials ? trips : kMaxPartials);
-    hipLaunchKernelGGL((amax_partial_kernel<DT, HAD>), dim3(g), dim3(kThreads), 0,
-                       stream, x, nchunks, partials);
-    hipLaunchKernelGGL((quantize_kernel<FMT, DT, HAD, true>), dim3(grid), dim3(kThreads),
-                       0, stream, x, nchunks, codes32, scales, tscale,
-                       (const float*)partials, g);
+    const int g = (int)(grid < kMaxPartials ? grid : kMaxPartials);
+    hipLaunchKernelGGL((amax_blocks_kernel<DT, HAD>), dim3(g), dim3(kThreads), 0, stream, x, nblocks,
+                       partials);
+    hipLaunchKernelGGL((blocks_kernel<FMT, DT, HAD, true>), dim3((unsigned)grid), dim3(kThreads), 0,
+                       stream, x, nblocks, codes, scales, tscale, (const float*)partials, g);
   } else {
-    hipLaunchKernelGGL((quantize_kernel<FMT, DT, HAD, false>), dim3(grid),
-                       dim3(kThreads), 0, stream, x, nchunks, codes32, scales,
-                       tscale, (const float*)nullptr, 0);
+    hipLaunchKernelGGL((blocks_kernel<FMT, DT, HAD, false>), dim3((unsigned)grid), dim3(kThreads), 0,
+                       stream, x, nblocks, codes, scales, tscale, (const float*)nullptr, 0);
   }
   return hipGetLastError();
 }
@@ -476,6 +585,7 @@ hipError_t launch_dtype(int dtype, const void* x, int64_t nchunks, uint8_t* code
 }  // namespace
 
 size_t quantize_workspace_bytes(int fmt, bool compute) {
+  // the partial maxima of the tensor amax pass
   return (fmt == kFmtNV && compute) ? kMaxPartials * sizeof(float) : 0;
 }
 

@@ -149,3 +149,24 @@ def test_rotated_weight_full_size(fmt):
             t = oracle.nvfp4_tensor_scale_from_amax(np.float32(run.amax(b)))
             assert ts.item() == float(t)
         assert run.check(fmt, t, b) is None
+
+
+# --- compute mode: a workspace reused across calls ----------------------------
+
+def test_compute_workspace_reused_across_calls():
+    # One workspace (uninitialized) for a run of calls of different sizes,
+    # dtypes and rotations, including tensors that need more than one pass
+    # of the max kernel per workgroup: every result bit-exact.
+    need = fq.lib().fp4_quantize_workspace_size(fq.fp4.NVFP4, fq.fp4.TSCALE_COMPUTE, 1, 16)
+    ws = torch.full((need,), 0x7F, dtype=torch.uint8, device=DEV)
+    cases = [((2048, 8192), torch.bfloat16, True, 21), ((300, 2048), torch.float32, False, 22),
+             ((4096, 4096), torch.bfloat16, False, 23), ((77, 1024), torch.float16, True, 24),
+             ((8192, 4160), torch.bfloat16, True, 26), ((2048, 8192), torch.bfloat16, True, 25)]
+    for (rows, k), dtype, had, seed in cases:
+        x = randn((rows, k), dtype, seed, 2.0)
+        note("compute-mode quantize with a shared workspace %s %s had=%s" % ((rows, k), dtype, had))
+        codes, scales, ts = fq.quantize(x.to(DEV), "nvfp4", hadamard=had, workspace=ws)
+        torch.cuda.synchronize()
+        p, s, t = oracle_quant("nvfp4", host_f32(x), had)
+        assert ts.item() == float(t)
+        assert np.array_equal(np_u8(scales), s) and np.array_equal(np_u8(codes), p)
