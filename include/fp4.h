@@ -120,6 +120,28 @@ fp4_status fp4_quantize(fp4_format fmt, const void* x, fp4_dtype x_dtype,
                         size_t workspace_bytes, void* stream);
 
 /*
+ * fp4_quantize_noalloc -- fp4_quantize without a workspace argument, for
+ * callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation.  It allocates
+ * nothing (no hipMalloc / hipFree, no allocating library routine): the
+ * partial maxima of FP4_TSCALE_COMPUTE mode go to a 4 KiB scratch array the
+ * library holds in device memory, one copy per GPU, kept until the process
+ * ends.  The max pass never needs more than that, whatever rows * k, so no
+ * size is refused for lack of scratch (sizes are limited as in fp4_quantize);
+ * nothing in the scratch has to start at zero.
+ *   Arguments, results, alignment and errors as fp4_quantize (without
+ *   workspace / workspace_bytes); FP4_EHIP also when the scratch cannot be
+ *   located on the current device.
+ *   Every call on one GPU shares that GPU's scratch: calls that overlap in
+ *   time on one GPU (several streams, several host threads) race and must
+ *   be serialized by the caller.
+ */
+fp4_status fp4_quantize_noalloc(fp4_format fmt, const void* x, fp4_dtype x_dtype,
+                                int64_t rows, int64_t k, uint8_t* codes,
+                                uint8_t* scales, float* tensor_scale,
+                                fp4_tscale_mode mode, void* stream);
+
+/*
  * fp4_hadamard_quantize -- rotate each block of x by H_b / sqrt(b), then
  * quantize exactly as fp4_quantize does (the tensor amax of COMPUTE mode is
  * taken over the rotated values).

@@ -26,11 +26,13 @@ fp4_status from_hip(hipError_t e) {
 }
 
 // Shared checks of fp4_quantize / fp4_hadamard_quantize.
+// check_workspace = false: the caller brings no workspace (the library's
+// own scratch is used).
 fp4_status check_quantize(fp4_format fmt, const void* x, fp4_dtype x_dtype,
                           int64_t rows, int64_t k, const uint8_t* codes,
                           const uint8_t* scales, const float* tensor_scale,
                           fp4_tscale_mode mode, const void* workspace,
-                          size_t workspace_bytes) {
+                          size_t workspace_bytes, bool check_workspace = true) {
   if (!valid_format(fmt)) return FP4_EINVAL;
   if (x_dtype != FP4_F32 && x_dtype != FP4_BF16 && x_dtype != FP4_F16) return FP4_EINVAL;
   if (fmt == FP4_NVFP4 && mode != FP4_TSCALE_COMPUTE && mode != FP4_TSCALE_GIVEN) return FP4_EINVAL;
@@ -42,7 +44,8 @@ fp4_status check_quantize(fp4_format fmt, const void* x, fp4_dtype x_dtype,
   if (fmt == FP4_NVFP4) {
     if (!tensor_scale || !aligned(tensor_scale, 4)) return FP4_EINVAL;
     const size_t need = fp4_quantize_workspace_size(fmt, mode, rows, k);
-    if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 16))) return FP4_EINVAL;
+    if (check_workspace && need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 16)))
+      return FP4_EINVAL;
   } else if (tensor_scale) {
     return FP4_EINVAL;
   }
@@ -102,6 +105,25 @@ fp4_status fp4_hadamard_quantize(fp4_format fmt, const void* x,
                                  void* stream) {
   return quantize_common(true, fmt, x, x_dtype, rows, k, codes, scales,
                          tensor_scale, mode, workspace, workspace_bytes, stream);
+}
+
+fp4_status fp4_quantize_noalloc(fp4_format fmt, const void* x, fp4_dtype x_dtype, int64_t rows,
+                                int64_t k, uint8_t* codes, uint8_t* scales, float* tensor_scale,
+                                fp4_tscale_mode mode, void* stream) {
+  fp4_status s = check_quantize(fmt, x, x_dtype, rows, k, codes, scales, tensor_scale, mode,
+                                nullptr, 0, false);
+  if (s != FP4_OK || rows == 0) return s;
+  const bool compute = fmt == FP4_NVFP4 && mode == FP4_TSCALE_COMPUTE;
+  void* scratch = nullptr;
+  size_t scratch_bytes = 0;
+  if (compute) {
+    const hipError_t e = quantize_static_scratch(&scratch, &scratch_bytes);
+    if (e != hipSuccess) return from_hip(e);
+    // the compute-mode max pass writes at most this many bytes for any size
+    if (scratch_bytes < quantize_workspace_bytes((int)fmt, true)) return FP4_EUNSUPPORTED;
+  }
+  return from_hip(launch_quantize((int)fmt, false, x, (int)x_dtype, rows * k, codes, scales,
+                                  tensor_scale, compute, scratch, static_cast<hipStream_t>(stream)));
 }
 
 fp4_status fp4_quantize_mse(const void* x, fp4_dtype x_dtype, int64_t rows, int64_t k,

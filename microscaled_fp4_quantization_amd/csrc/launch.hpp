@@ -16,6 +16,10 @@ constexpr int kOutE4M3 = 3;
 
 size_t quantize_workspace_bytes(int fmt, bool compute);
 
+// The library's own scratch for launch_quantize's workspace on the current
+// device (its address and size); looked up once per device.
+hipError_t quantize_static_scratch(void** ptr, size_t* bytes);
+
 // n = rows * k elements (a multiple of 16 for NVFP4, 32 for MXFP4).
 hipError_t launch_quantize(int fmt, bool hadamard, const void* x, int dtype,
                            int64_t n, uint8_t* codes, uint8_t* scales,

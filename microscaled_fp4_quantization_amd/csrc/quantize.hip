@@ -20,6 +20,8 @@
 // lane quad, and the block max and the cross-lane butterfly stages use DPP
 // quad permutes.  Both orders of arithmetic are the same, so both give the
 // same bits.
+#include <mutex>
+
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -583,6 +585,39 @@ hipError_t launch_dtype(int dtype, const void* x, int64_t nchunks, uint8_t* code
 }
 
 }  // namespace
+
+// Scratch of fp4_quantize_noalloc: the partial maxima of the compute-mode
+// max pass (kMaxPartials floats; the pass never writes more, whatever the
+// tensor size), in device memory the library owns instead of a caller
+// workspace.  Each device holds its own copy at its own address, looked up
+// once per device; nothing in it needs to start at zero (every partial is
+// written before it is read).
+static __device__ __align__(256) float scratch[kMaxPartials];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices];
+}  // namespace
+
+hipError_t quantize_static_scratch(void** ptr, size_t* bytes) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    // the array's name is a host-side stand-in: only this address may be
+    // handed to kernels
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  *bytes = sizeof(scratch);
+  return hipSuccess;
+}
 
 size_t quantize_workspace_bytes(int fmt, bool compute) {
   // the partial maxima of the tensor amax pass

@@ -30,7 +30,7 @@ EXPORTS = ("fp4_status_string", "fp4_quantize_workspace_size", "fp4_quantize",
            "fp4_gemm", "fp4_quantize_gemm_workspace_size", "fp4_quantize_gemm",
            "fp4_quantize_mse", "fp4_gemm_w4a16", "fp4_kv_append",
            "fp4_attention_workspace_size", "fp4_attention_decode", "fp4_gptq_workspace_size",
-           "fp4_gptq_quantize")
+           "fp4_gptq_quantize", "fp4_quantize_noalloc")
 
 _lib = None
 
@@ -59,6 +59,8 @@ def lib():
         f = getattr(L, name)
         f.argtypes = [i32, vp, i32, i64, i64, vp, vp, vp, i32, vp, sz, vp]
         f.restype = i32
+    L.fp4_quantize_noalloc.argtypes = [i32, vp, i32, i64, i64, vp, vp, vp, i32, vp]
+    L.fp4_quantize_noalloc.restype = i32
     L.fp4_quantize_mse.argtypes = [vp, i32, i64, i64, vp, vp, vp, i32, vp, sz, vp]
     L.fp4_quantize_mse.restype = i32
     L.fp4_gemm_w4a16.argtypes = [i32, vp, i32, i64, i64, i64, vp, vp, vp, vp, i32, vp]

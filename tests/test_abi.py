@@ -77,6 +77,29 @@ def test_quantize_rejects_bad_arguments(name):
     assert _q(f, rows=0, x=None, codes=None, scales=None) == fp4.OK
 
 
+def test_quantize_noalloc_rejects_bad_arguments():
+    # as fp4_quantize, without the workspace arguments: every check runs on
+    # the host before any HIP call (compute mode included)
+    f = fp4.lib().fp4_quantize_noalloc
+
+    def q(fmt=NV, x=FAKE, dt=fp4.BF16, rows=4, k=64, codes=FAKE, scales=FAKE, ts=FAKE,
+          mode=fp4.TSCALE_COMPUTE):
+        return f(fmt, x, dt, rows, k, codes, scales, ts, mode, None)
+
+    E = fp4.EINVAL
+    assert q(fmt=7) == E
+    assert q(dt=fp4.E4M3) == E
+    assert q(k=40) == E
+    assert q(rows=-1) == E
+    assert q(rows=1 << 30, k=1 << 20) == E
+    assert q(x=None) == E
+    assert q(codes=FAKE_ODD) == E
+    assert q(ts=None) == E
+    assert q(fmt=MX) == E                                # MXFP4 takes no tensor scale
+    assert q(mode=5) == E
+    assert q(rows=0, x=None, codes=None, scales=None) == fp4.OK
+
+
 def test_quantize_mse_rejects_bad_arguments():
     f = fp4.lib().fp4_quantize_mse
 
