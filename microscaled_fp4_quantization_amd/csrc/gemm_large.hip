@@ -194,9 +194,10 @@ __device__ __forceinline__ void store_tile(const v16f (&acc)[TI][TJ], uint8_t* e
 
 // ---- NVFP4 helpers ---------------------------------------------------------
 // 16-byte chunk c of a 64-byte code row r is stored at position
-// c ^ ((r >> 1) & 3): the 16 rows a 16-lane phase of a 16-byte fragment read
-// touches then cover the 8 bank groups twice each.
-__device__ __forceinline__ int swz16(int row, int chunk) { return chunk ^ ((row >> 1) & 3); }
+// c ^ ((r >> 2) & 3): the LDS has 64 banks of 4 bytes (16 groups of 16
+// bytes), a 64-byte row spans 4 groups, and the 16 rows a 16-lane phase of a
+// 16-byte fragment read touches then fall on 16 different groups.
+__device__ __forceinline__ int swz16(int row, int chunk) { return chunk ^ ((row >> 2) & 3); }
 
 // 8 codes times half HI of the scale pair sp (the splat folds into the
 // packed multiply's operand select: no register for it)
@@ -339,7 +340,7 @@ __global__ __launch_bounds__(256, 1) void gemm_nv4w(
   const __amdgpu_buffer_rsrc_t rs_bs = __builtin_amdgcn_make_buffer_rsrc((void*)bs, (short)0, n * srow, 0x00020000);
   // Code block q = i NW + wave (16 rows x 64 bytes): lane p fills position
   // p, i.e. row 16 q + p / 4 at stored chunk p % 4, holding logical chunk
-  // (p % 4) ^ ((row >> 1) & 3), which does not depend on i.  The lane's
+  // (p % 4) ^ ((row >> 2) & 3), which does not depend on i.  The lane's
   // offset is that of block i = 0; the 64 i rows further on, the tile's first
   // row and the stage go into the uniform offset.  Rows past m or n read
   // past the buffer's end (the buffer load returns zeros) or into the next
