@@ -353,39 +353,41 @@ __global__ __launch_bounds__(256) void gemm_nv_decode(
 
 
 // ---- NVFP4 weight-stream kernel (m <= 8, k = 2048 or 4096, n <= 16384) -------
-// The weight rows are dealt out evenly: one workgroup per CU-share of R rows
-// (R = 8 ceil(n / 2048), at most 64, i.e. up to four 16-row MFMA tiles, the
-// last possibly partial), so every CU streams the same number of bytes.  A
-// workgroup's 16 waves split k: wave w takes the slice [w k / 16,
-// (w + 1) k / 16), one or two 128-value steps, for all its tiles, and issues
+// The weight rows are dealt out evenly: one workgroup of 16 waves per
+// CU-share of R = ceil(n / 256) rows (at most 64: up to four 16-row MFMA
+// tiles, the last possibly partial), so every CU streams the same number of
+// bytes.  The 16 waves split k: wave w takes the slice [w k / 16, (w + 1) k /
+// 16), NSTEP = k / 2048 steps of 128 values, for all its tiles, and issues
 // all its loads at once.  Requests are not served in issue order (a wave's
 // data tends to arrive in one burst at any time during the stream), so each
-// wave depends only on its own loads: it dequantizes its activation slice
-// and stores its scale slices in LDS regions of its own, and the 16 partial
-// tiles meet only at the end.  Lane (r, g) = (lane % 16, lane / 16) reads,
-// per step t, the 16 bytes at 64 t + 16 g of weight row r of each tile: a
-// load instruction covers 64 contiguous bytes of 16 rows.  Rows past the
+// wave depends only on its own loads: it dequantizes its activation slice and
+// stores its scale slices in LDS regions of its own, and the 16 partial tiles
+// meet only at the end.  Lane (r, g) = (lane % 16, lane / 16) reads, per step
+// t, the 16 bytes at 64 t + 16 g of weight row r of each tile: a load
+// instruction covers 64 contiguous bytes of 16 rows.  Rows past the
 // workgroup's share re-read its last row, in the same instruction, so they
 // cost no extra traffic.
 constexpr int kStrWaves = 16;
 constexpr int kStrTiles = 4;                          // 64 rows at most per workgroup
-constexpr int kStrSeg = 4096 / kStrWaves / 16;        // scale bytes per row and slice, at most (16)
-constexpr int kStrPitch = kStrSeg + 4;                // padded: the 16 rows of a read hit distinct banks
-constexpr int kStrXSlice = 4096 / kStrWaves + 8;      // fp16 per activation row and slice (padded)
+constexpr int kStrGroups = 256;                       // one workgroup per CU
 
+template <int NSTEP>
 struct StreamLds {
-  _Float16 x[kStrWaves][8][kStrXSlice];               // dequantized activation slices
-  uint8_t w[kStrWaves][16 * kStrTiles][kStrPitch];    // weight scale slices
+  // dequantized activation slices, rows padded so that the 8 rows of a read
+  // fall on distinct banks
+  _Float16 x[kStrWaves][8][128 * NSTEP + 8];
+  // weight scale slices, rows padded: the 16 rows of a read hit distinct banks
+  uint8_t w[kStrWaves][16 * kStrTiles][8 * NSTEP + 4];
 };
 
 // The activations (XM):
 //   kXCodes  NVFP4 codes, scales and tensor scale (`a`, `as`, `at`).
 //   kXQuant  bf16 X [m, k] (`a`), quantized here to NVFP4 with the tensor
-//            scale computed from the data, exactly as quantize_chunk does it:
-//            every workgroup reduces max |X| over the whole tensor (16
-//            slices, one per wave) and quantizes its own slices; workgroup 0
-//            also writes the codes, scales and tensor scale out (qcodes,
-//            qscales, qtscale).
+//            scale computed from the data, with the arithmetic of the
+//            quantize kernels: every workgroup reduces max |X| over the whole
+//            tensor (16 slices, one per wave) and quantizes its own slices;
+//            workgroup 0 also writes the codes, scales and tensor scale out
+//            (qcodes, qscales, qtscale).
 //   kXRaw    bf16 X [m, k] (`a`) used as it is: W4A16 (pimento.cloud "FP8,
 //            NVFP4 czy AWQ?", section "Dlaczego W8A8 i W4A16 to nie to
 //            samo?": only the weights are 4-bit, the products stay 16-bit).
@@ -394,6 +396,11 @@ struct StreamLds {
 //            every value above 2^-15 max |X| (bf16 has 8 significant bits, fp16
 //            11), the rest within 2^-25 max |X|; C is scaled back by 2^E.
 // `as` and `at` are unused but for kXCodes.
+//
+// With bf16 X, max |X| is needed before any weight can be used.  While the
+// weight stream is in flight, a load queued behind it waits for most of it,
+// so the activation loads go first and only the first tile's weights with
+// them; the rest goes out once every wave's part of max |X| is in.
 constexpr int kXCodes = 0, kXQuant = 1, kXRaw = 2;
 
 template <int NSTEP, int XM>
@@ -403,32 +410,51 @@ __global__ __launch_bounds__(64 * kStrWaves) void gemm_nv_stream(
     const uint8_t* __restrict__ b, const uint8_t* __restrict__ bs,
     const float* __restrict__ bt, void* __restrict__ c, int c_dtype,
     uint8_t* __restrict__ qcodes, uint8_t* __restrict__ qscales, float* __restrict__ qtscale) {
-  __shared__ StreamLds L;
+  constexpr int NT = kStrTiles;
+  __shared__ union {
+    StreamLds<NSTEP> s;
+    v4f part[kStrWaves][NT][64];                      // the partial tiles, at the end
+  } LU;
   __shared__ float red[kStrWaves];
+  StreamLds<NSTEP>& L = LU.s;
   constexpr bool QX = XM != kXCodes;                  // bf16 X loaded here
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = lane & 15, g = lane >> 4;
   const int64_t nbase = (int64_t)blockIdx.x * rows_per_wg;
-  int64_t nlast = nbase + rows_per_wg - 1;              // last row of this share
+  int64_t nlast = nbase + rows_per_wg - 1;            // last row of this share
   if (nlast > n - 1) nlast = n - 1;
-  const int ks0 = wave * (128 * NSTEP);                 // first value of this wave's slice
+  const int ks0 = wave * (128 * NSTEP);               // first value of this wave's slice
   const int64_t kbytes = k / 2, kblocks = k / 16;
 
-  // ---- all loads of the wave -------------------------------------------------
-  // QX: this wave's slice of X first, lane -> row lane / 8, the 16 NSTEP
-  // values at ks0 + 16 NSTEP (lane % 8) (one or two whole blocks)
+  // ---- activation slice: lane -> row lane / 8, the 16 NSTEP values (NSTEP
+  // whole blocks) at ks0 + 16 NSTEP (lane % 8) --------------------------------------
   const int xrow = lane >> 3, xc = lane & 7;
-  const int64_t xsrc = xrow < m ? xrow : m - 1;
+  const bool live = xrow < m;
+  const int64_t xsrc = live ? xrow : m - 1;
   const int xv0 = ks0 + 16 * NSTEP * xc;
-  u32x4 xb[2 * NSTEP];
+  u32x4 xb[QX ? 2 * NSTEP : 1];                        // bf16 X, 8 values each
+  uint32_t xq[2 * NSTEP];                             // codes, 8 per dword (kXCodes)
+  uint32_t xs = 0;                                    // NSTEP scale bytes (kXCodes)
   if (QX) {
 #pragma unroll
     for (int i = 0; i < 2 * NSTEP; ++i)
       xb[i] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(a) + xsrc * k + xv0 + 8 * i);
+  } else {
+    const uint8_t* src = a + xsrc * kbytes + xv0 / 2;
+    if (NSTEP == 1) {
+      const u32x2 h = *reinterpret_cast<const u32x2*>(src);
+      xq[0] = h.x; xq[1] = h.y;
+    } else {
+      const u32x4 h = *reinterpret_cast<const u32x4*>(src);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) xq[j] = h[j];
+    }
+    const uint8_t* ss = as + xsrc * kblocks + xv0 / 16;
+    xs = NSTEP == 2 ? (uint32_t)*reinterpret_cast<const uint16_t*>(ss) : (uint32_t)*ss;
   }
-  // weight scale slices: lane p loads row p's 8 NSTEP bytes (QX: later,
-  // with the weight codes)
+
+  // ---- weights: scale slices (lane p loads row p's 8 NSTEP bytes) and codes ----
   const int64_t swr = (nbase + lane <= nlast) ? nbase + lane : nlast;
   u32x4 sv;
   auto load_ws = [&]() {
@@ -439,148 +465,135 @@ __global__ __launch_bounds__(64 * kStrWaves) void gemm_nv_stream(
       sv = (u32x4){h.x, h.y, 0u, 0u};
     }
   };
-  if (!QX) load_ws();
-  // activation slice (quantized input): lane -> row lane / 8, 16 NSTEP
-  // values at (lane % 8) 16 NSTEP of the slice
-  u32x4 xq = {0u, 0u, 0u, 0u};
-  uint32_t xs2 = 0;
-  if (QX) {
-  } else if (NSTEP == 2) {
-    xq = *reinterpret_cast<const u32x4*>(a + xsrc * kbytes + ks0 / 2 + 16 * xc);
-    xs2 = *reinterpret_cast<const uint16_t*>(as + xsrc * kblocks + ks0 / 16 + 2 * xc);
-  } else {
-    const u32x2 h = *reinterpret_cast<const u32x2*>(a + xsrc * kbytes + ks0 / 2 + 8 * xc);
-    xq = (u32x4){h.x, h.y, 0u, 0u};
-    xs2 = as[xsrc * kblocks + ks0 / 16 + xc];
-  }
-  // QX: this wave's part of max |X|; the workgroup reduces the 16 parts at a
-  // barrier and only then sends its weight loads (queued behind them, the
-  // activation loads of slower waves would wait for the whole stream).
-  float xv[16 * NSTEP], am[NSTEP];
-  if (QX) {
-    const bool live = xrow < m;
+  u32x4 w[NT][NSTEP];
+  auto load_w = [&](int t0, int t1) {
 #pragma unroll
-    for (int i = 0; i < 2 * NSTEP; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        xv[8 * i + 2 * j] = live ? bf16_lo(xb[i][j]) : 0.0f;
-        xv[8 * i + 2 * j + 1] = live ? bf16_hi(xb[i][j]) : 0.0f;
-      }
-#pragma unroll
-    for (int bl = 0; bl < NSTEP; ++bl) {
-      float mx = 0.0f;
-#pragma unroll
-      for (int j = 0; j < 16; ++j) mx = fmaxf(mx, fabsf(xv[16 * bl + j]));
-      am[bl] = mx;
-    }
-    float wm = NSTEP == 2 ? fmaxf(am[0], am[1]) : am[0];
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) wm = fmaxf(wm, __shfl_xor(wm, off));
-    if (lane == 0) red[wave] = wm;
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  // weight codes (QX: only once every wave's part of max |X| is in, so the
-  // activation loads of the workgroup do not queue behind its weight stream)
-  u32x4 w[kStrTiles][NSTEP];
-  auto load_w = [&]() {
-#pragma unroll
-    for (int tl = 0; tl < kStrTiles; ++tl) {
+    for (int tl = 0; tl < NT; ++tl) {
+      if (tl < t0 || tl >= t1) continue;
       const int64_t wr = (nbase + 16 * tl + r <= nlast) ? nbase + 16 * tl + r : nlast;
 #pragma unroll
       for (int t = 0; t < NSTEP; ++t)
         w[tl][t] = *reinterpret_cast<const u32x4*>(b + wr * kbytes + ks0 / 2 + 64 * t + 16 * g);
     }
   };
-  if (!QX) load_w();
+  if (QX) {
+    load_w(0, 1);
+  } else {
+    load_ws();
+    load_w(0, NT);
+  }
   __builtin_amdgcn_sched_barrier(0);
 
-  // ---- this wave's LDS regions (loads complete in issue order) ---------------
-  auto store_ws = [&]() {
-    u32_alias* dd = reinterpret_cast<u32_alias*>(&L.w[wave][lane][0]);
-    dd[0] = sv[0]; dd[1] = sv[1];
-    if (NSTEP == 2) { dd[2] = sv[2]; dd[3] = sv[3]; }
-  };
-  if (!QX) store_ws();
+  // ---- activations into this wave's LDS region --------------------------------------
+  _Float16* xdst = &L.x[wave][xrow][16 * NSTEP * xc];
   float xscale = 1.0f;                                // the activations' tensor scale
   if (QX) {
-    // max |x| over the whole tensor: every wave's part is in `red`
-    const bool live = xrow < m;
+    // this wave's part of max |X|
+    float am[NSTEP];
+#pragma unroll
+    for (int bl = 0; bl < NSTEP; ++bl) {
+      float mx = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          mx = fmaxf(mx, fmaxf(fabsf(bf16_lo(xb[2 * bl + i][j])), fabsf(bf16_hi(xb[2 * bl + i][j]))));
+      am[bl] = live ? mx : 0.0f;
+    }
+    float wm = NSTEP == 2 ? fmaxf(am[0], am[NSTEP - 1]) : am[0];
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) wm = fmaxf(wm, __shfl_xor(wm, off));
+    if (lane == 0) red[wave] = wm;
+    // max |X| over the whole tensor once every wave's part is in `red`; then
+    // the rest of the weights go out
     __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));   // lgkmcnt(0), loads stay in flight
     __asm__ volatile("s_barrier" ::: "memory");
     load_ws();
-    load_w();
+    load_w(1, NT);
     __builtin_amdgcn_sched_barrier(0);
     float A = red[0];
 #pragma unroll
     for (int i = 1; i < kStrWaves; ++i) A = fmaxf(A, red[i]);
-    float s_t = A / 2688.0f;                          // 6 * 448
-    if (s_t == 0.0f) s_t = 1.0f;
-    const float dd = 6.0f * s_t;
-    xscale = s_t;                                    // kXRaw: replaced below
-    const bool out = blockIdx.x == 0 && live;
     if (XM == kXRaw) {
       // 2^-E with max |X| in [2^E, 2^(E+1)); 1 for a zero tensor
       const int eb = (int)(as_u(A) >> 23);
       const int pe = A == 0.0f ? 127 : (254 - eb < 1 ? 1 : 254 - eb);
       const float p2 = as_f((uint32_t)pe << 23);
-      xscale = as_f((uint32_t)(254 - pe) << 23);        // 2^E, exact
+      xscale = as_f((uint32_t)(254 - pe) << 23);      // 2^E, exact
 #pragma unroll
       for (int i = 0; i < 2 * NSTEP; ++i) {
         v8h f;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) f[j] = live ? (_Float16)(xv[8 * i + j] * p2) : (_Float16)0.0f;
-        *reinterpret_cast<v8h*>(&L.x[wave][xrow][16 * NSTEP * xc + 8 * i]) = f;
+        for (int j = 0; j < 4; ++j) {
+          f[2 * j] = (_Float16)(bf16_lo(xb[i][j]) * p2);
+          f[2 * j + 1] = (_Float16)(bf16_hi(xb[i][j]) * p2);
+        }
+        if (!live) f = (v8h){0, 0, 0, 0, 0, 0, 0, 0};
+        *reinterpret_cast<v8h*>(xdst + 8 * i) = f;
       }
     } else {
+      float s_t = A / 2688.0f;                        // 6 * 448
+      if (s_t == 0.0f) s_t = 1.0f;
+      const float dd = 6.0f * s_t;
+      xscale = s_t;
+      const bool out = blockIdx.x == 0 && live;
 #pragma unroll
       for (int bl = 0; bl < NSTEP; ++bl) {
         const uint32_t sbyte = e4m3_encode_pos(am[bl] / dd);
         const float S = e4m3_decode_pos(sbyte) * s_t;
-        float r = 1.0f / S;
-        if (!(S != 0.0f && r < __builtin_inff())) r = 0.0f;   // zero block or overflowing reciprocal
+        float rs = 1.0f / S;
+        if (!(S != 0.0f && rs < __builtin_inff())) rs = 0.0f;   // zero block or overflowing reciprocal
         uint32_t wd[2];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-          const float* q = &xv[16 * bl + 8 * h];
-          uint32_t w = e2m1_pack2<0>(0u, q[0] * r, q[1] * r);
-          w = e2m1_pack2<1>(w, q[2] * r, q[3] * r);
-          w = e2m1_pack2<2>(w, q[4] * r, q[5] * r);
-          w = e2m1_pack2<3>(w, q[6] * r, q[7] * r);
-          wd[h] = w;
-          v8h f = dequant8(w, (_Float16)e4m3_decode_pos(sbyte));
+          const u32x4 v = xb[2 * bl + h];
+          uint32_t p = e2m1_pack2<0>(0u, bf16_lo(v[0]) * rs, bf16_hi(v[0]) * rs);
+          p = e2m1_pack2<1>(p, bf16_lo(v[1]) * rs, bf16_hi(v[1]) * rs);
+          p = e2m1_pack2<2>(p, bf16_lo(v[2]) * rs, bf16_hi(v[2]) * rs);
+          p = e2m1_pack2<3>(p, bf16_lo(v[3]) * rs, bf16_hi(v[3]) * rs);
+          wd[h] = p;
+          v8h f = dequant8(p, (_Float16)e4m3_decode_pos(sbyte));
           if (!live) f = (v8h){0, 0, 0, 0, 0, 0, 0, 0};
-          *reinterpret_cast<v8h*>(&L.x[wave][xrow][16 * NSTEP * xc + 16 * bl + 8 * h]) = f;
+          *reinterpret_cast<v8h*>(xdst + 16 * bl + 8 * h) = f;
         }
-        if (out) {
+        if (XM == kXQuant && out) {
           *reinterpret_cast<u32x2*>(qcodes + xsrc * kbytes + (xv0 + 16 * bl) / 2) = (u32x2){wd[0], wd[1]};
           qscales[xsrc * kblocks + (xv0 + 16 * bl) / 16] = (uint8_t)sbyte;
         }
       }
+      if (XM == kXQuant && blockIdx.x == 0 && tid == 0) *qtscale = s_t;
     }
-    if (XM == kXQuant && blockIdx.x == 0 && tid == 0) *qtscale = s_t;
-    store_ws();
   } else {
-    const bool live = xrow < m;
-    const v2h sc = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(xs2, 1.0f, false);
+    // the E4M3 bytes to f16 (sign and NaN included)
+    const v2h s01 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(xs, 1.0f, false);
 #pragma unroll
-    for (int d = 0; d < 2 * NSTEP; ++d) {             // 8 values per dword, 2 dwords per block
-      v8h f = dequant8(xq[d], (NSTEP == 2 && d >= 2) ? sc.y : sc.x);
-      if (!live) f = (v8h){0, 0, 0, 0, 0, 0, 0, 0};
-      *reinterpret_cast<v8h*>(&L.x[wave][xrow][16 * NSTEP * xc + 8 * d]) = f;
+    for (int bl = 0; bl < NSTEP; ++bl) {
+      const _Float16 s = bl == 0 ? s01.x : s01.y;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        v8h f = dequant8(xq[2 * bl + h], s);
+        if (!live) f = (v8h){0, 0, 0, 0, 0, 0, 0, 0};
+        *reinterpret_cast<v8h*>(xdst + 16 * bl + 8 * h) = f;
+      }
     }
+  }
+  {
+    u32_alias* dd = reinterpret_cast<u32_alias*>(&L.w[wave][lane][0]);
+    dd[0] = sv[0]; dd[1] = sv[1];
+    if (NSTEP == 2) { dd[2] = sv[2]; dd[3] = sv[3]; }
   }
   // Only this wave reads these regions: LDS accesses of one wave complete in
   // order, so no barrier is needed.
   const _Float16* xf = &L.x[wave][r & 7][32 * g];    // rows >= m are zero; r >= 8 repeats r - 8
 
-  v4f acc[kStrTiles];
+  v4f acc[NT];
 #pragma unroll
-  for (int tl = 0; tl < kStrTiles; ++tl) acc[tl] = (v4f){0.f, 0.f, 0.f, 0.f};
+  for (int tl = 0; tl < NT; ++tl) acc[tl] = (v4f){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int t = 0; t < NSTEP; ++t) {
-    v2h s[kStrTiles];
+    v2h s[NT];
 #pragma unroll
-    for (int tl = 0; tl < kStrTiles; ++tl) {
+    for (int tl = 0; tl < NT; ++tl) {
       const uint32_t p = *reinterpret_cast<const u16_alias*>(&L.w[wave][16 * tl + r][8 * t + 2 * g]);
       s[tl] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(p, 1.0f, false);
     }
@@ -588,7 +601,7 @@ __global__ __launch_bounds__(64 * kStrWaves) void gemm_nv_stream(
     for (int d = 0; d < 4; ++d) {                     // 8 values per dword; blocks 2g, 2g+1
       const v8h fx = *reinterpret_cast<const v8h*>(xf + 128 * t + 8 * d);
 #pragma unroll
-      for (int tl = 0; tl < kStrTiles; ++tl) {
+      for (int tl = 0; tl < NT; ++tl) {
         const v8h fw = dequant8(w[tl][t][d], d < 2 ? s[tl].x : s[tl].y);
         acc[tl] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fw, fx, acc[tl], 0, 0, 0);
       }
@@ -597,24 +610,29 @@ __global__ __launch_bounds__(64 * kStrWaves) void gemm_nv_stream(
 
   // ---- add the 16 slices, store ------------------------------------------------
   __syncthreads();                                    // LDS becomes the partial area
-  v4f* part = reinterpret_cast<v4f*>(&L);             // [16 waves][tiles][64 lanes]
 #pragma unroll
-  for (int tl = 0; tl < kStrTiles; ++tl) part[(wave * kStrTiles + tl) * 64 + lane] = acc[tl];
+  for (int tl = 0; tl < NT; ++tl) LU.part[wave][tl][lane] = acc[tl];
   __syncthreads();
-  if (tid < 64 * kStrTiles) {                         // thread -> (tile, lane)
+  if (tid < 64 * NT) {                                // thread -> (tile, lane)
     const int tl = tid >> 6, l = tid & 63;
-    v4f sum = part[tl * 64 + l];
+    v4f sum = LU.part[0][tl][l];
 #pragma unroll
-    for (int wv = 1; wv < kStrWaves; ++wv) sum += part[(wv * kStrTiles + tl) * 64 + l];
+    for (int wv = 1; wv < kStrWaves; ++wv) sum += LU.part[wv][tl][l];
     const float scale = (QX ? xscale : *at) * (*bt);
     // D layout: lane l holds weight rows 4 (l / 16) + e of the tile, activation row l % 16
-    const int xr = l & 15;
-    if (xr < m) {
-      const int64_t ni = nbase + 16 * tl + 4 * (l >> 4);
+    const int xr = l & 15, lr = 16 * tl + 4 * (l >> 4);   // first row within the share
+    const int64_t ni = nbase + lr;
+    if (xr < m && lr < rows_per_wg && ni <= nlast) {
+      const int64_t o = (int64_t)xr * n + ni;
+      if (c_dtype != kInF32 && lr + 3 < rows_per_wg && ni + 3 <= nlast && (o & 3) == 0) {
+        const __bf16 h[4] = {(__bf16)(sum[0] * scale), (__bf16)(sum[1] * scale), (__bf16)(sum[2] * scale),
+                             (__bf16)(sum[3] * scale)};
+        *reinterpret_cast<u32x2*>(reinterpret_cast<__bf16*>(c) + o) = *reinterpret_cast<const u32x2*>(h);
+      } else {
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (ni + e <= nlast && 16 * tl + 4 * (l >> 4) + e < rows_per_wg)
-          store_out(c, c_dtype, (int64_t)xr * n + ni + e, sum[e] * scale);
+        for (int e = 0; e < 4; ++e)
+          if (lr + e < rows_per_wg && ni + e <= nlast) store_out(c, c_dtype, o + e, sum[e] * scale);
+      }
     }
   }
 }
@@ -660,6 +678,27 @@ __global__ __launch_bounds__(256) void gemm_w4a16_simple(
   for (int i = 0; i < rows; ++i) store_out(c, c_dtype, (int64_t)(i0 + i) * n + j, acc[i] * ts);
 }
 
+// The stream kernel's shapes: m <= 8, k = 2048 or 4096, n <= 16384.
+bool stream_shape(int64_t m, int64_t n, int64_t k) {
+  return m >= 1 && m <= 8 && (k == 2048 || k == 4096) && n >= 1 && n <= 16 * kStrTiles * kStrGroups;
+}
+
+// An equal share of ceil(n / 256) weight rows per workgroup.
+template <int XM>
+hipError_t launch_stream(int m, int64_t n, int k, const uint8_t* a, const uint8_t* as, const float* at,
+                         const uint8_t* b, const uint8_t* bs, const float* bt, void* c, int c_dtype,
+                         uint8_t* qcodes, uint8_t* qscales, float* qtscale, hipStream_t stream) {
+  const int rows = (int)((n + kStrGroups - 1) / kStrGroups);
+  const dim3 grid((unsigned)((n + rows - 1) / rows));
+  if (k == 4096)
+    hipLaunchKernelGGL((gemm_nv_stream<2, XM>), grid, dim3(64 * kStrWaves), 0, stream, m, n, k, rows, a, as,
+                       at, b, bs, bt, c, c_dtype, qcodes, qscales, qtscale);
+  else
+    hipLaunchKernelGGL((gemm_nv_stream<1, XM>), grid, dim3(64 * kStrWaves), 0, stream, m, n, k, rows, a, as,
+                       at, b, bs, bt, c, c_dtype, qcodes, qscales, qtscale);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_gemm_skinny(int fmt, int64_t m, int64_t n, int64_t k,
@@ -670,20 +709,9 @@ hipError_t launch_gemm_skinny(int fmt, int64_t m, int64_t n, int64_t k,
   const bool aligned16 = ((reinterpret_cast<uintptr_t>(b_scales) | reinterpret_cast<uintptr_t>(b_codes) |
                            reinterpret_cast<uintptr_t>(a_codes)) & 15) == 0 &&
                          (reinterpret_cast<uintptr_t>(a_scales) & 1) == 0;
-  if (fmt == kFmtNV && m <= 8 && (k == 2048 || k == 4096) && n <= 16 * kStrTiles * 256 && aligned16) {
-    // an equal share of rows per workgroup, one workgroup per CU (256 CUs)
-    const int rows = (int)(8 * ((n + 2047) / 2048));
-    const dim3 grid((unsigned)((n + rows - 1) / rows));
-    if (k == 4096)
-      hipLaunchKernelGGL((gemm_nv_stream<2, kXCodes>), grid, dim3(64 * kStrWaves), 0, stream, (int)m, n,
-                         (int)k, rows, a_codes, a_scales, a_tscale, b_codes, b_scales, b_tscale, c,
-                         c_dtype, nullptr, nullptr, nullptr);
-    else
-      hipLaunchKernelGGL((gemm_nv_stream<1, kXCodes>), grid, dim3(64 * kStrWaves), 0, stream, (int)m, n,
-                         (int)k, rows, a_codes, a_scales, a_tscale, b_codes, b_scales, b_tscale, c,
-                         c_dtype, nullptr, nullptr, nullptr);
-    return hipGetLastError();
-  }
+  if (fmt == kFmtNV && stream_shape(m, n, k) && aligned16)
+    return launch_stream<kXCodes>((int)m, n, (int)k, a_codes, a_scales, a_tscale, b_codes, b_scales,
+                                  b_tscale, c, c_dtype, nullptr, nullptr, nullptr, stream);
   if (fmt == kFmtNV && m <= 8 && k % kDecKC == 0 && aligned16) {
     hipLaunchKernelGGL((gemm_nv_decode<kDecKC, 4>), dim3((unsigned)((n + kDecRows - 1) / kDecRows)),
                        dim3(256), 0, stream, (int)m, n, (int)k, a_codes, a_scales, a_tscale, b_codes,
@@ -712,19 +740,9 @@ bool launch_quantize_gemm_decode(int64_t m, int64_t n, int64_t k, const void* x,
   const bool aligned = ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(b_codes) |
                          reinterpret_cast<uintptr_t>(b_scales) | reinterpret_cast<uintptr_t>(a_codes)) &
                         15) == 0;
-  if (!(m >= 1 && m <= 8 && (k == 2048 || k == 4096) && n <= 16 * kStrTiles * 256 && aligned))
-    return false;
-  const int rows = (int)(8 * ((n + 2047) / 2048));
-  const dim3 grid((unsigned)((n + rows - 1) / rows));
-  if (k == 4096)
-    hipLaunchKernelGGL((gemm_nv_stream<2, kXQuant>), grid, dim3(64 * kStrWaves), 0, stream, (int)m, n,
-                       (int)k, rows, reinterpret_cast<const uint8_t*>(x), nullptr, nullptr, b_codes,
-                       b_scales, b_tscale, c, c_dtype, a_codes, a_scales, a_tscale);
-  else
-    hipLaunchKernelGGL((gemm_nv_stream<1, kXQuant>), grid, dim3(64 * kStrWaves), 0, stream, (int)m, n,
-                       (int)k, rows, reinterpret_cast<const uint8_t*>(x), nullptr, nullptr, b_codes,
-                       b_scales, b_tscale, c, c_dtype, a_codes, a_scales, a_tscale);
-  *err = hipGetLastError();
+  if (!(stream_shape(m, n, k) && aligned)) return false;
+  *err = launch_stream<kXQuant>((int)m, n, (int)k, reinterpret_cast<const uint8_t*>(x), nullptr, nullptr,
+                                b_codes, b_scales, b_tscale, c, c_dtype, a_codes, a_scales, a_tscale, stream);
   return true;
 }
 
@@ -733,25 +751,15 @@ hipError_t launch_gemm_w4a16(int fmt, int64_t m, int64_t n, int64_t k, const voi
                              const float* b_tscale, void* c, int c_dtype, hipStream_t stream) {
   const bool aligned = ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(b_codes) |
                          reinterpret_cast<uintptr_t>(b_scales)) & 15) == 0;
-  if (fmt == kFmtNV && x_dtype == kInBF16 && (k == 2048 || k == 4096) &&
-      n <= 16 * kStrTiles * 256 && aligned) {
+  if (fmt == kFmtNV && x_dtype == kInBF16 && stream_shape(1, n, k) && aligned) {
     // streaming kernel, 8 activation rows per launch
-    const int rows = (int)(8 * ((n + 2047) / 2048));
-    const dim3 grid((unsigned)((n + rows - 1) / rows));
     const int64_t osz = c_dtype == kInF32 ? 4 : 2;
     for (int64_t i0 = 0; i0 < m; i0 += 8) {
       const int mc = (int)(m - i0 < 8 ? m - i0 : 8);
       const uint8_t* xa = reinterpret_cast<const uint8_t*>(x) + i0 * k * 2;
       void* ca = reinterpret_cast<char*>(c) + i0 * n * osz;
-      if (k == 4096)
-        hipLaunchKernelGGL((gemm_nv_stream<2, kXRaw>), grid, dim3(64 * kStrWaves), 0, stream, mc, n,
-                           (int)k, rows, xa, nullptr, nullptr, b_codes, b_scales, b_tscale, ca, c_dtype,
-                           nullptr, nullptr, nullptr);
-      else
-        hipLaunchKernelGGL((gemm_nv_stream<1, kXRaw>), grid, dim3(64 * kStrWaves), 0, stream, mc, n,
-                           (int)k, rows, xa, nullptr, nullptr, b_codes, b_scales, b_tscale, ca, c_dtype,
-                           nullptr, nullptr, nullptr);
-      hipError_t e = hipGetLastError();
+      const hipError_t e = launch_stream<kXRaw>(mc, n, (int)k, xa, nullptr, nullptr, b_codes, b_scales,
+                                                b_tscale, ca, c_dtype, nullptr, nullptr, nullptr, stream);
       if (e != hipSuccess) return e;
     }
     return hipSuccess;

@@ -94,7 +94,7 @@ def test_nv_integer_special_case_bit_exact():
 def test_random_shapes(fmt, out_dtype):
     g = torch.Generator().manual_seed(2)
     for m, n, k in [(1, 1, 32), (7, 9, 64), (16, 100, 4128), (3, 1000, 800), (16, 17, 160), (17, 33, 96),
-                    (8, 100, 4096), (1, 33, 2048), (5, 64, 6144), (4, 47, 8192),
+                    (8, 100, 4096), (1, 33, 2048), (5, 64, 6144), (4, 47, 8192), (6, 16000, 4096), (8, 517, 2048),
                     (37, 50, 96), (64, 64, 128), (130, 257, 544), (256, 512, 2048),
                     (300, 600, 1024), (1000, 129, 512), (128, 2048, 256), (513, 700, 2304)]:
         x = torch.randn((m, k), generator=g).to(torch.bfloat16)
@@ -196,6 +196,7 @@ def test_rotated_full_size():
     ("nvfp4", 1, 100, 4096, torch.bfloat16),     # partial share of rows
     ("nvfp4", 5, 333, 2048, torch.bfloat16),
     ("nvfp4", 8, 16384, 4096, torch.bfloat16),   # largest n of the one-launch path
+    ("nvfp4", 7, 1025, 2048, torch.bfloat16),    # 3 rows per share, last share partial
     ("nvfp4", 16, 64, 256, torch.bfloat16),      # m > 8: quantize + GEMM calls
     ("nvfp4", 3, 50, 96, torch.bfloat16),
     ("nvfp4", 8, 200, 4096, torch.float32),      # not bf16: two calls
