@@ -248,10 +248,12 @@ fp4_status fp4_gemm(fp4_format fmt, int64_t m, int64_t n, int64_t k,
  *                 FP4_EUNSUPPORTED).
  *   Numerics: the weights are widened exactly (v * E4M3 scale in fp16 or
  *   fp32, v * 2^e); NVFP4 with bf16 X, k in {2048, 4096} and 16-byte aligned
- *   x / codes / scales takes the streaming path: X is scaled by the power of
- *   two that brings max |X| into [1, 2) and rounded to fp16 (exact for every
- *   value above 2^-15 max |X|), the products accumulate in fp32 on the matrix
- *   cores and C is scaled back; other shapes sum fp32 products.  Tolerance
+ *   x / codes / scales takes the streaming path: each row of X is cut into
+ *   16 pieces of k / 16 values, each piece scaled by the power of two that
+ *   brings its max |x| into [1, 2) and rounded to fp16 (exact for every value
+ *   above 2^-15 of that max), the products accumulate in fp32 on the matrix
+ *   cores and each piece's partial sums are scaled back before they are
+ *   added; other shapes sum fp32 products.  Tolerance
  *   against the float64 reference: relative Frobenius error <= 1e-3.
  *   m = 0 or n = 0 enqueues nothing.  Returns FP4_OK, FP4_EINVAL,
  *   FP4_EUNSUPPORTED or FP4_EHIP.

@@ -391,16 +391,19 @@ struct StreamLds {
 //   kXRaw    bf16 X [m, k] (`a`) used as it is: W4A16 (pimento.cloud "FP8,
 //            NVFP4 czy AWQ?", section "Dlaczego W8A8 i W4A16 to nie to
 //            samo?": only the weights are 4-bit, the products stay 16-bit).
-//            X is scaled by the power of two 2^-E that brings max |X| into
-//            [1, 2) (reduced as for kXQuant) and rounded to fp16: exact for
-//            every value above 2^-15 max |X| (bf16 has 8 significant bits, fp16
-//            11), the rest within 2^-25 max |X|; C is scaled back by 2^E.
+//            Each wave scales each row of its slice by the power of two 2^-E
+//            that brings the slice row's max |x| into [1, 2) and rounds to
+//            fp16: exact for every value above 2^-15 of that max (bf16 has 8
+//            significant bits, fp16 11), the rest within 2^-25 of it; the
+//            wave's partial sums are scaled back by 2^E (exact) before the
+//            slices are added.
 // `as` and `at` are unused but for kXCodes.
 //
-// With bf16 X, max |X| is needed before any weight can be used.  While the
-// weight stream is in flight, a load queued behind it waits for most of it,
-// so the activation loads go first and only the first tile's weights with
-// them; the rest goes out once every wave's part of max |X| is in.
+// kXQuant needs max |X| over the whole tensor before any weight can be used.
+// While the weight stream is in flight, a load queued behind it waits for
+// most of it, so the activation loads go first and only the first tile's
+// weights with them; the rest goes out once every wave's part of max |X| is
+// in.
 constexpr int kXCodes = 0, kXQuant = 1, kXRaw = 2;
 
 template <int NSTEP, int XM>
@@ -418,6 +421,7 @@ __global__ __launch_bounds__(64 * kStrWaves) void gemm_nv_stream(
   __shared__ float red[kStrWaves];
   StreamLds<NSTEP>& L = LU.s;
   constexpr bool QX = XM != kXCodes;                  // bf16 X loaded here
+  constexpr bool GMAX = XM == kXQuant;                // max |X| over the tensor first
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = lane & 15, g = lane >> 4;
@@ -476,7 +480,7 @@ __global__ __launch_bounds__(64 * kStrWaves) void gemm_nv_stream(
         w[tl][t] = *reinterpret_cast<const u32x4*>(b + wr * kbytes + ks0 / 2 + 64 * t + 16 * g);
     }
   };
-  if (QX) {
+  if (GMAX) {
     load_w(0, 1);
   } else {
     load_ws();
@@ -501,25 +505,33 @@ __global__ __launch_bounds__(64 * kStrWaves) void gemm_nv_stream(
       am[bl] = live ? mx : 0.0f;
     }
     float wm = NSTEP == 2 ? fmaxf(am[0], am[NSTEP - 1]) : am[0];
+    float A = 0.0f;
+    if (GMAX) {
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) wm = fmaxf(wm, __shfl_xor(wm, off));
-    if (lane == 0) red[wave] = wm;
-    // max |X| over the whole tensor once every wave's part is in `red`; then
-    // the rest of the weights go out
-    __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));   // lgkmcnt(0), loads stay in flight
-    __asm__ volatile("s_barrier" ::: "memory");
-    load_ws();
-    load_w(1, NT);
-    __builtin_amdgcn_sched_barrier(0);
-    float A = red[0];
+      for (int off = 32; off >= 1; off >>= 1) wm = fmaxf(wm, __shfl_xor(wm, off));
+      if (lane == 0) red[wave] = wm;
+      // max |X| over the whole tensor once every wave's part is in `red`;
+      // then the rest of the weights go out
+      __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));   // lgkmcnt(0), loads stay in flight
+      __asm__ volatile("s_barrier" ::: "memory");
+      load_ws();
+      load_w(1, NT);
+      __builtin_amdgcn_sched_barrier(0);
+      A = red[0];
 #pragma unroll
-    for (int i = 1; i < kStrWaves; ++i) A = fmaxf(A, red[i]);
+      for (int i = 1; i < kStrWaves; ++i) A = fmaxf(A, red[i]);
+    } else {
+      // max |x| of this slice row: the 8 lanes of row lane / 8
+#pragma unroll
+      for (int off = 4; off >= 1; off >>= 1) wm = fmaxf(wm, __shfl_xor(wm, off));
+      A = wm;
+    }
     if (XM == kXRaw) {
-      // 2^-E with max |X| in [2^E, 2^(E+1)); 1 for a zero tensor
+      // 2^-E with the slice row's max |x| in [2^E, 2^(E+1)); 1 for a zero row
       const int eb = (int)(as_u(A) >> 23);
       const int pe = A == 0.0f ? 127 : (254 - eb < 1 ? 1 : 254 - eb);
       const float p2 = as_f((uint32_t)pe << 23);
-      xscale = as_f((uint32_t)(254 - pe) << 23);      // 2^E, exact
+      xscale = as_f((uint32_t)(254 - pe) << 23);      // 2^E of row lane / 8, exact
 #pragma unroll
       for (int i = 0; i < 2 * NSTEP; ++i) {
         v8h f;
@@ -608,6 +620,14 @@ __global__ __launch_bounds__(64 * kStrWaves) void gemm_nv_stream(
     }
   }
 
+  if (XM == kXRaw) {
+    // back to the scale of X: acc column lane % 16 is activation row
+    // lane % 16, whose 2^E lane 8 (lane % 8) holds (rows >= 8 are zero)
+    const float e = __shfl(xscale, 8 * (lane & 7));
+#pragma unroll
+    for (int tl = 0; tl < NT; ++tl) acc[tl] *= e;
+  }
+
   // ---- add the 16 slices, store ------------------------------------------------
   __syncthreads();                                    // LDS becomes the partial area
 #pragma unroll
@@ -618,7 +638,7 @@ __global__ __launch_bounds__(64 * kStrWaves) void gemm_nv_stream(
     v4f sum = LU.part[0][tl][l];
 #pragma unroll
     for (int wv = 1; wv < kStrWaves; ++wv) sum += LU.part[wv][tl][l];
-    const float scale = (QX ? xscale : *at) * (*bt);
+    const float scale = (XM == kXQuant ? xscale : XM == kXRaw ? 1.0f : *at) * (*bt);
     // D layout: lane l holds weight rows 4 (l / 16) + e of the tile, activation row l % 16
     const int xr = l & 15, lr = 16 * tl + 4 * (l >> 4);   // first row within the share
     const int64_t ni = nbase + lr;
