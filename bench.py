@@ -97,10 +97,10 @@ def parse():
 # while these files are unchanged.
 DOMINANT = {
     "decode": ("gemm_nv_stream<2, 1>", ["gemm_skinny.hip"]),
-    "prefill": ("gemm_large<0", ["gemm_large.hip"]),
-    "rotated_nv": ("gemm_large<0", ["gemm_large.hip"]),
+    "prefill": ("gemm_nv4w<", ["gemm_large.hip"]),
+    "rotated_nv": ("gemm_nv4w<", ["gemm_large.hip"]),
     "rotated_mx": ("gemm_large_mx<", ["gemm_large.hip"]),
-    "kv": ("quantize_kernel<0, 1, 0, false>", ["quantize.hip", "device_common.hpp"]),
+    "kv": ("blocks_kernel<0, 1, 0, false>", ["quantize.hip", "device_common.hpp"]),
     "mse": ("quantize_mse_kernel<1, true>", ["quantize.hip", "device_common.hpp"]),
     "w4a16": ("gemm_nv_stream<2, 2>", ["gemm_skinny.hip"]),
     "attention": ("attn_decode_kernel<0, 1>", ["attention.hip", "device_common.hpp"]),

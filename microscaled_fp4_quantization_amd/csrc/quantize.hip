@@ -310,8 +310,11 @@ __global__ __launch_bounds__(kThreads) void blocks_kernel(
   constexpr int BS = FMT == kFmtNV ? 16 : 32, U = blocks_per_thread<FMT>();
   const int64_t base = (int64_t)blockIdx.x * (U * kThreads) + threadIdx.x;
   float v[U][BS];
+  // nontemporal loads after the max pass (x is read a second time); cached
+  // loads otherwise: a lane's two 16-byte pieces share lines with its
+  // neighbours' and are requested by two instructions
 #pragma unroll
-  for (int j = 0; j < U; ++j) load_block<DT, BS, true>(x, base + j * kThreads, base + j * kThreads < nblocks, v[j]);
+  for (int j = 0; j < U; ++j) load_block<DT, BS, COMPUTE>(x, base + j * kThreads, base + j * kThreads < nblocks, v[j]);
   float s_t = 1.0f, d = 6.0f;
   if (FMT == kFmtNV) {
     if (COMPUTE) {
