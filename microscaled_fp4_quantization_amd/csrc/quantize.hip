@@ -31,6 +31,7 @@ namespace {
 
 constexpr int kThreads = 256;        // 4 waves of 64
 constexpr int kMaxPartials = 1024;   // amax partials (workspace floats)
+static_assert(kMaxPartials % kThreads == 0, "partials per thread");
 
 typedef uint32_t u32x4e __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2e __attribute__((ext_vector_type(2)));
@@ -123,11 +124,14 @@ __device__ __forceinline__ float block_max(float m) {
   __shared__ float red[NT / 64];
   m = wave_max(m);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
-  __syncthreads();
+  // LDS only: barriers that leave the wave's global loads in flight
+  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));   // lgkmcnt(0)
+  __asm__ volatile("s_barrier" ::: "memory");
   float r = red[0];
 #pragma unroll
   for (int i = 1; i < NT / 64; ++i) r = fmaxf(r, red[i]);
-  __syncthreads();
+  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));
+  __asm__ volatile("s_barrier" ::: "memory");
   return r;
 }
 
@@ -179,17 +183,27 @@ __device__ __forceinline__ void quantize_chunk(const float v[8], int lane, float
 // scale arithmetic (two IEEE divisions for NVFP4) runs once per block.  The
 // arithmetic, and its order, is that of quantize_chunk / fwht_chunk.
 
+// 16-byte pieces of one block of BS values of type DT
+template <int DT, int BS>
+constexpr int block_pieces() { return BS * (DT == kInF32 ? 4 : 2) / 16; }
+
+// The raw pieces of block b.  A block past the end loads block 0 instead (it
+// exists whenever the kernel runs): counted once more in a maximum it changes
+// nothing, and it is never stored.  No branch and no select around the
+// loads, so a wait for an earlier load does not wait for these.
 template <int DT, int BS, bool NT>
 __device__ __forceinline__ void load_block(const void* __restrict__ x, int64_t b, bool valid,
-                                           float v[BS]) {
-  constexpr int L = BS * (DT == kInF32 ? 4 : 2) / 16;     // 16-byte pieces
-  const u32x4e* p = reinterpret_cast<const u32x4e*>(x) + b * L;
-  u32x4e w[L];
+                                           u32x4e (&w)[block_pieces<DT, BS>()]) {
+  constexpr int L = block_pieces<DT, BS>();
+  const u32x4e* p = reinterpret_cast<const u32x4e*>(x) + (valid ? b : 0) * L;
 #pragma unroll
-  for (int i = 0; i < L; ++i) {
-    w[i] = (u32x4e){0u, 0u, 0u, 0u};
-    if (valid) w[i] = NT ? __builtin_nontemporal_load(p + i) : p[i];
-  }
+  for (int i = 0; i < L; ++i) w[i] = NT ? __builtin_nontemporal_load(p + i) : p[i];
+}
+
+// The pieces widened exactly to fp32.
+template <int DT, int BS>
+__device__ __forceinline__ void widen_block(const u32x4e (&w)[block_pieces<DT, BS>()], float v[BS]) {
+  constexpr int L = block_pieces<DT, BS>();
 #pragma unroll
   for (int i = 0; i < L; ++i) {
 #pragma unroll
@@ -209,6 +223,22 @@ __device__ __forceinline__ void load_block(const void* __restrict__ x, int64_t b
       }
     }
   }
+}
+
+// Block b widened, zeros past the end (the given-scale path: nothing waits
+// between its loads, and this form streams faster there).
+template <int DT, int BS>
+__device__ __forceinline__ void load_widen_block(const void* __restrict__ x, int64_t b, bool valid,
+                                                 float v[BS]) {
+  constexpr int L = block_pieces<DT, BS>();
+  const u32x4e* p = reinterpret_cast<const u32x4e*>(x) + b * L;
+  u32x4e w[L];
+#pragma unroll
+  for (int i = 0; i < L; ++i) {
+    w[i] = (u32x4e){0u, 0u, 0u, 0u};
+    if (valid) w[i] = p[i];
+  }
+  widen_block<DT, BS>(w, v);
 }
 
 // Blockwise Hadamard of one whole block in the lane: stages h = 1, 2, 4, ...,
@@ -286,11 +316,14 @@ __global__ __launch_bounds__(kThreads) void amax_blocks_kernel(const void* __res
   // one trip per workgroup unless the tensor needs more than kMaxPartials
   for (int64_t base = (int64_t)blockIdx.x * (U * kThreads) + threadIdx.x; base < nblocks + threadIdx.x;
        base += (int64_t)gridDim.x * (U * kThreads)) {
+    u32x4e w[U][block_pieces<DT, BS>()];
+#pragma unroll
+    for (int j = 0; j < U; ++j) load_block<DT, BS, false>(x, base + j * kThreads, base + j * kThreads < nblocks, w[j]);
+    __builtin_amdgcn_sched_barrier(0);        // every load issued before the first wait
     float v[U][BS];
 #pragma unroll
-    for (int j = 0; j < U; ++j) load_block<DT, BS, false>(x, base + j * kThreads, base + j * kThreads < nblocks, v[j]);
-#pragma unroll
     for (int j = 0; j < U; ++j) {
+      widen_block<DT, BS>(w[j], v[j]);
       if (HAD) fwht_block<BS>(v[j]);
       m = fmaxf(m, amax_block<BS>(v[j]));
     }
@@ -309,17 +342,35 @@ __global__ __launch_bounds__(kThreads) void blocks_kernel(
     int npartials) {
   constexpr int BS = FMT == kFmtNV ? 16 : 32, U = blocks_per_thread<FMT>();
   const int64_t base = (int64_t)blockIdx.x * (U * kThreads) + threadIdx.x;
-  float v[U][BS];
-  // nontemporal loads after the max pass (x is read a second time); cached
-  // loads otherwise: a lane's two 16-byte pieces share lines with its
-  // neighbours' and are requested by two instructions
+  // the partial maxima first, all in flight at once: loads return in order,
+  // and queued behind the block loads they would hold the whole workgroup up
+  // for one more trip
+  constexpr int PP = (FMT == kFmtNV && COMPUTE) ? kMaxPartials / kThreads : 1;
+  float pv[PP];
 #pragma unroll
-  for (int j = 0; j < U; ++j) load_block<DT, BS, COMPUTE>(x, base + j * kThreads, base + j * kThreads < nblocks, v[j]);
+  for (int i = 0; i < PP; ++i) {
+    const int idx = threadIdx.x + i * kThreads;
+    pv[i] = (FMT == kFmtNV && COMPUTE && idx < npartials) ? partials[idx] : 0.0f;
+  }
+  // given scale: cached loads (a lane's two 16-byte pieces share lines with
+  // its neighbours' and are requested by two instructions)
+  // COMPUTE: nontemporal loads (x is read a second time), every one issued
+  // before the first wait (the partial maxima come first); widened later
+  u32x4e raw[U][COMPUTE ? block_pieces<DT, BS>() : 1];
+  float vg[U][COMPUTE ? 1 : BS];
+#pragma unroll
+  for (int j = 0; j < U; ++j) {
+    const int64_t b = base + j * kThreads;
+    if constexpr (COMPUTE) load_block<DT, BS, true>(x, b, b < nblocks, raw[j]);
+    else load_widen_block<DT, BS>(x, b, b < nblocks, vg[j]);
+  }
+  if (COMPUTE) __builtin_amdgcn_sched_barrier(0);
   float s_t = 1.0f, d = 6.0f;
   if (FMT == kFmtNV) {
     if (COMPUTE) {
-      float m = 0.0f;
-      for (int i = threadIdx.x; i < npartials; i += kThreads) m = fmaxf(m, partials[i]);
+      float m = pv[0];
+#pragma unroll
+      for (int i = 1; i < PP; ++i) m = fmaxf(m, pv[i]);
       const float A = block_max(m);
       s_t = A / 2688.0f;                       // 6 * 448
       if (s_t == 0.0f) s_t = 1.0f;
@@ -332,9 +383,16 @@ __global__ __launch_bounds__(kThreads) void blocks_kernel(
 #pragma unroll
   for (int j = 0; j < U; ++j) {
     const int64_t b = base + j * kThreads;
-    if (HAD) fwht_block<BS>(v[j]);
+    float v[BS];
+    if constexpr (COMPUTE) {
+      widen_block<DT, BS>(raw[j], v);
+    } else {
+#pragma unroll
+      for (int e = 0; e < BS; ++e) v[e] = vg[j][e];
+    }
+    if (HAD) fwht_block<BS>(v);
     uint32_t w[BS / 8], sbyte;
-    quantize_block<FMT, BS>(v[j], s_t, d, w, sbyte);
+    quantize_block<FMT, BS>(v, s_t, d, w, sbyte);
     if (b < nblocks) {
       if (BS == 16) {
         __builtin_nontemporal_store(((u32x2e){w[0], w[1 % (BS / 8)]}),
