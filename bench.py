@@ -83,6 +83,9 @@ def parse():
     p.add_argument("--stat-ms", type=float, default=200.0,
                    help="least GPU time of each sampling phase (median / p10 / p90)")
     p.add_argument("--no-stats", action="store_true", help="skip the sampling phases")
+    p.add_argument("--tp", type=int, default=1,
+                   help="one GPU's share of a column-parallel split of the weights over TP GPUs: "
+                        "n / TP weight rows (decode, prefill, rotated_nv, rotated_mx, w4a16)")
     p.add_argument("--copy-bytes", type=int, default=0,
                    help="after the timed region, copy this many bytes device to device three "
                         "times: the plain copy that scales rocprofv3 FETCH_SIZE / WRITE_SIZE")
@@ -276,7 +279,7 @@ def quant_bytes(rows, k, fmt, in_bytes):
     return rows * k * in_bytes + rows * k // 2 + rows * k // bs + (4 if fmt == "nvfp4" else 0)
 
 
-def setup(workload, torch, fq, lib):
+def setup(workload, torch, fq, lib, tp=1):
     """Returns dict with: steps (list of per-step callables split into
     pre/dominant/post), flops, bytes, dominant info, oracle sample fn."""
     from microscaled_fp4_quantization_amd import fp4, workloads
@@ -285,7 +288,8 @@ def setup(workload, torch, fq, lib):
     W = {}
     if workload in ("decode", "prefill"):
         m = 8 if workload == "decode" else 4096
-        d = workloads.decode(device=dev) if workload == "decode" else workloads.prefill(device=dev)
+        d = (workloads.decode(device=dev, n=14336 // tp) if workload == "decode"
+             else workloads.prefill(device=dev, n=14336 // tp))
         x, w = d["x"], d["w"]
         n, k = w.shape
         wq = fq.quantize(w, "nvfp4")
@@ -325,7 +329,7 @@ def setup(workload, torch, fq, lib):
     elif workload in ("rotated_nv", "rotated_mx"):
         fmt = "nvfp4" if workload == "rotated_nv" else "mxfp4"
         f = NV if fmt == "nvfp4" else MX
-        d = workloads.rotated(device=dev)
+        d = workloads.rotated(device=dev, n=28672 // tp)
         x, w = d["x"], d["w"]
         m, k = x.shape
         n = w.shape[0]
@@ -354,7 +358,7 @@ def setup(workload, torch, fq, lib):
                  host=dict(x=x.float().cpu().numpy(), w=w.float().cpu().numpy(), fmt=fmt,
                            hadamard=True))
     elif workload == "w4a16":
-        d = workloads.decode(device=dev)
+        d = workloads.decode(device=dev, n=14336 // tp)
         x, w = d["x"], d["w"]
         m, k = x.shape
         n = w.shape[0]
@@ -669,7 +673,12 @@ def main():
     import microscaled_fp4_quantization_amd as fq
     torch.cuda.set_device(0)
     lib = Lib(torch, fq)
-    W = setup(args.workload, torch, fq, lib)
+    if args.tp != 1 and args.workload not in ("decode", "prefill", "rotated_nv", "rotated_mx", "w4a16"):
+        print("bench.py: --tp applies to the GEMM workloads only", file=sys.stderr)
+        sys.exit(2)
+    W = setup(args.workload, torch, fq, lib, tp=args.tp)
+    if args.tp != 1:
+        W["config"]["tp_share"] = "1/%d of the weight rows (one GPU of a column-parallel split)" % args.tp
     pre, dom, post = W["pre"], W["dominant"], W["post"]
     ndom = len(dom)
 
