@@ -195,8 +195,10 @@ class Lib:
     def gemm_call(self, fmt, a, b, c, c_dtype):
         (ac, asc, at), (bc, bsc, bt) = a, b
         m, n, k = ac.shape[0], bc.shape[0], ac.shape[1] * 2
+        need = self.L.fp4_gemm_workspace_size(fmt, m, n, k)
+        ws = self.torch.empty(need, dtype=self.torch.uint8, device=c.device) if need else None
         args = (fmt, m, n, k, self.p(ac), self.p(asc), self.p(at), self.p(bc), self.p(bsc),
-                self.p(bt), self.p(c), c_dtype, None, 0, self.stream)
+                self.p(bt), self.p(c), c_dtype, self.p(ws), need, self.stream)
         fn = self.L.fp4_gemm
         return lambda: self.check(fn(*args), "gemm")
 

@@ -205,7 +205,10 @@ fp4_status fp4_dequantize(fp4_format fmt, const uint8_t* codes,
                           int64_t rows, int64_t k, void* out,
                           fp4_dtype out_dtype, void* stream);
 
-/* Bytes of device workspace fp4_gemm needs for these sizes (0 today). */
+/* Bytes of device workspace fp4_gemm needs for these sizes: nonzero only
+ * where few output tiles would leave most of the GPU idle and the large-m
+ * kernels split k over several workgroups per tile (the slices' fp32 partial
+ * sums, added in a fixed order by a second pass). */
 size_t fp4_gemm_workspace_size(fp4_format fmt, int64_t m, int64_t n, int64_t k);
 
 /*
@@ -222,7 +225,10 @@ size_t fp4_gemm_workspace_size(fp4_format fmt, int64_t m, int64_t n, int64_t k);
  *   the end.
  *   c, c_dtype      out, row-major [m, n], FP4_F32 or FP4_BF16 (nearest even).
  *   a_tscale, b_tscale  NVFP4: device floats; MXFP4: must be NULL.
- *   workspace       may be NULL when fp4_gemm_workspace_size() is 0.
+ *   workspace       at least fp4_gemm_workspace_size() bytes, 16-byte
+ *                   aligned (may be NULL when that size is 0); its contents
+ *                   on entry do not matter; calls that overlap must not
+ *                   share one.
  *   m, n >= 0 (0 enqueues nothing), k > 0 with k % 32 == 0 (NVFP4 too).
  * Pointer alignment: codes 16 bytes, scales 4 bytes, c 16 bytes.
  * Returns FP4_OK, FP4_EINVAL, FP4_EUNSUPPORTED or FP4_EHIP.

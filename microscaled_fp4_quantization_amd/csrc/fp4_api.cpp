@@ -190,7 +190,7 @@ fp4_status fp4_gemm(fp4_format fmt, int64_t m, int64_t n, int64_t k,
     return FP4_EINVAL;
   }
   const size_t need = gemm_workspace_bytes((int)fmt, m, n, k);
-  if (need > 0 && (!workspace || workspace_bytes < need)) return FP4_EINVAL;
+  if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 16))) return FP4_EINVAL;
   return from_hip(launch_gemm((int)fmt, m, n, k, a_codes, a_scales, a_tscale,
                               b_codes, b_scales, b_tscale, c, (int)c_dtype,
                               workspace, static_cast<hipStream_t>(stream)));
@@ -253,7 +253,7 @@ fp4_status fp4_quantize_gemm(fp4_format fmt, const void* x, fp4_dtype x_dtype,
       return FP4_EINVAL;
     }
     const size_t need = gemm_workspace_bytes((int)fmt, m, n, k);
-    if (need > 0 && (!workspace || workspace_bytes < need)) return FP4_EINVAL;
+    if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 16))) return FP4_EINVAL;
   }
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (fmt == FP4_NVFP4 && x_dtype == FP4_BF16 && n > 0) {

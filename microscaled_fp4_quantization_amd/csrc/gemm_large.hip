@@ -52,6 +52,9 @@ constexpr int NSTAGE = 4;             // LDS ring depth
 constexpr int NXCD = 8;
 // waves per workgroup along m and n
 constexpr int kMXWM = 2, kMXWN = 2;
+// Elements between two split-k slices of fp32 partial sums in the GEMM
+// workspace: m n rounded up to a multiple of 4 (16-byte aligned slices).
+__host__ __device__ __forceinline__ int64_t split_stride(int64_t m, int64_t n) { return (m * n + 3) / 4 * 4; }
 
 constexpr int NSGRP = 3;              // scale-group ring depth
 
@@ -308,7 +311,8 @@ template <int BNT>
 __global__ __launch_bounds__(256, 1) void gemm_nv4w(
     int m, int n, int k, const uint8_t* __restrict__ a, const uint8_t* __restrict__ as,
     const float* __restrict__ at, const uint8_t* __restrict__ b, const uint8_t* __restrict__ bs,
-    const float* __restrict__ bt, void* __restrict__ c, int c_dtype, int tiles_m, int tiles_n) {
+    const float* __restrict__ bt, void* __restrict__ c, int c_dtype, int tiles_m, int tiles_n,
+    int ksplit, float* __restrict__ part) {
   using Stage = LargeStage;
   constexpr int WMW = 2, WNW = 2, NW = 4;
   constexpr int G = 2;                         // NVFP4 stages per 16-byte scale group
@@ -331,7 +335,9 @@ __global__ __launch_bounds__(256, 1) void gemm_nv4w(
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int kbytes = k / 2, srow = k / 16;
-  const int nstages = k / BK;
+  // split k: workgroup row blockIdx.y takes values [ksplit y, ksplit (y + 1))
+  const int kofs = (int)blockIdx.y * ksplit;
+  const int nstages = ksplit / BK;
   const int ngroups = nstages / G;
 
   const __amdgpu_buffer_rsrc_t rs_a = __builtin_amdgcn_make_buffer_rsrc((void*)a, (short)0, m * kbytes, 0x00020000);
@@ -352,7 +358,7 @@ __global__ __launch_bounds__(256, 1) void gemm_nv4w(
   const int voff_s = lane * srow;
   auto issue_stage = [&](int t) {
     Stage& S = st[t % NSTAGE];
-    const int kb = (t < nstages ? t : nstages - 1) * ROWB;
+    const int kb = (t < nstages ? t : nstages - 1) * ROWB + kofs / 2;
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
       const int q = i * NW + wave;
@@ -362,7 +368,7 @@ __global__ __launch_bounds__(256, 1) void gemm_nv4w(
   };
   auto issue_group = [&](int g) {
     ScaleGroup& SG = sgr[g % NSGRP];
-    const int gb = 16 * (g < ngroups ? g : ngroups - 1);
+    const int gb = 16 * (g < ngroups ? g : ngroups - 1) + kofs / 16;
 #pragma unroll
     for (int j = 0; j < NSG; ++j) {
       const int gw = j * NW + wave;
@@ -486,8 +492,11 @@ __global__ __launch_bounds__(256, 1) void gemm_nv4w(
   }
 
   wait_vm<0>();                 // no load may land in LDS after the workgroup ends
-  const float ts = (*at) * (*bt);
-  store_tile16<WMW, WNW, TI, TJ, BNT>(acc, reinterpret_cast<uint8_t*>(&smem), ts, c, c_dtype, m, n, m0, n0);
+  // split k: this slice's unscaled fp32 sums into the workspace
+  void* dst = part ? static_cast<void*>(part + (int64_t)blockIdx.y * split_stride(m, n)) : c;
+  const float ts = part ? 1.0f : (*at) * (*bt);
+  store_tile16<WMW, WNW, TI, TJ, BNT>(acc, reinterpret_cast<uint8_t*>(&smem), ts, dst,
+                                      part ? kInF32 : c_dtype, m, n, m0, n0);
 }
 
 // ---- MXFP4: 256-value stages ----------------------------------------------
@@ -529,7 +538,7 @@ template <int WMW, int WNW>
 __global__ __launch_bounds__(64 * WMW * WNW, 1) void gemm_large_mx(
     int m, int n, int k, const uint8_t* __restrict__ a, const uint8_t* __restrict__ as,
     const uint8_t* __restrict__ b, const uint8_t* __restrict__ bs, void* __restrict__ c,
-    int c_dtype, int tiles_m, int tiles_n) {
+    int c_dtype, int tiles_m, int tiles_n, int ksplit, float* __restrict__ part) {
   constexpr int NW = WMW * WNW;
   constexpr int NL = BM * MXROWB / 1024 / NW;        // code loads per operand per wave per stage
   constexpr int NSG = 2 * BM * MXSGB / 1024 / NW;    // scale loads per wave per group
@@ -554,7 +563,9 @@ __global__ __launch_bounds__(64 * WMW * WNW, 1) void gemm_large_mx(
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int kbytes = k / 2, srow = k / 32;
-  const int nst = k / MXBK;                          // even: k is a multiple of 512
+  // split k: workgroup row blockIdx.y takes values [ksplit y, ksplit (y + 1))
+  const int kofs = (int)blockIdx.y * ksplit;
+  const int nst = ksplit / MXBK;                     // even: ksplit is a multiple of 512
   const int ngr = (nst + MXG - 1) / MXG;
 
   const __amdgpu_buffer_rsrc_t rs_a = __builtin_amdgcn_make_buffer_rsrc((void*)a, (short)0, m * kbytes, 0x00020000);
@@ -579,7 +590,7 @@ __global__ __launch_bounds__(64 * WMW * WNW, 1) void gemm_large_mx(
   // stage t (clamped to the last; a repeat is never read) into slot t % 2
   auto issue_stage = [&](int t) {
     MxStage& S = smem.st[t & 1];
-    const int kb = (t < nst ? t : nst - 1) * MXROWB;
+    const int kb = (t < nst ? t : nst - 1) * MXROWB + kofs / 2;
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
       const int q = i * NW + wave;
@@ -594,14 +605,14 @@ __global__ __launch_bounds__(64 * WMW * WNW, 1) void gemm_large_mx(
     MxScaleGroup& SG = smem.sg[g & 1];
     const int gc = g < ngr ? g : ngr - 1;
     const int gb = MXSGB * gc;
-    const bool whole = gb + MXSGB <= srow;
+    const bool whole = gb + MXSGB <= ksplit / 32;
     const int vo = voff_s + (whole ? hoff_s : 0);
 #pragma unroll
     for (int j = 0; j < NSG; ++j) {
       const int gw = j * NW + wave;
       const bool isb = j >= 2;
       load_lds16(isb ? rs_bs : rs_as, (isb ? SG.b : SG.a) + 1024 * (gw % 8), vo,
-                 ((isb ? n0 : m0) + 128 * (j & 1)) * srow + gb);
+                 ((isb ? n0 : m0) + 128 * (j & 1)) * srow + gb + kofs / 32);
     }
   };
 
@@ -752,7 +763,39 @@ __global__ __launch_bounds__(64 * WMW * WNW, 1) void gemm_large_mx(
   }
 
   wait_vm<0>();                 // no load may land in LDS after the workgroup ends
-  store_tile<WMW, WNW>(acc, reinterpret_cast<uint8_t*>(&smem), 1.0f, c, c_dtype, m, n, m0, n0, m_lo, n_lo);
+  // split k: this slice's fp32 sums into the workspace
+  void* dst = part ? static_cast<void*>(part + (int64_t)blockIdx.y * split_stride(m, n)) : c;
+  store_tile<WMW, WNW>(acc, reinterpret_cast<uint8_t*>(&smem), 1.0f, dst, part ? kInF32 : c_dtype, m, n,
+                       m0, n0, m_lo, n_lo);
+}
+
+// Split k: C = ts (sum over slices of the fp32 partial sums), the slices
+// added in order.  Thread -> 4 consecutive elements.
+__global__ __launch_bounds__(256) void split_reduce_kernel(const float* __restrict__ part, int nsplit,
+                                                           int64_t mn, int64_t stride,
+                                                           const float* __restrict__ at,
+                                                           const float* __restrict__ bt,
+                                                           void* __restrict__ c, int c_dtype) {
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i >= mn) return;
+  float4 s = *reinterpret_cast<const float4*>(part + i);
+  for (int z = 1; z < nsplit; ++z) {
+    const float4 v = *reinterpret_cast<const float4*>(part + z * stride + i);
+    s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+  }
+  const float ts = at ? (*at) * (*bt) : 1.0f;
+  const float o[4] = {s.x * ts, s.y * ts, s.z * ts, s.w * ts};
+  if (i + 4 <= mn && c_dtype != kInF32) {
+    const __bf16 h[4] = {(__bf16)o[0], (__bf16)o[1], (__bf16)o[2], (__bf16)o[3]};
+    *reinterpret_cast<uint2*>(reinterpret_cast<__bf16*>(c) + i) = *reinterpret_cast<const uint2*>(h);
+  } else if (i + 4 <= mn) {
+    *reinterpret_cast<float4*>(reinterpret_cast<float*>(c) + i) = make_float4(o[0], o[1], o[2], o[3]);
+  } else {
+    for (int e = 0; i + e < mn; ++e) {
+      if (c_dtype == kInF32) reinterpret_cast<float*>(c)[i + e] = o[e];
+      else reinterpret_cast<__bf16*>(c)[i + e] = (__bf16)o[e];
+    }
+  }
 }
 
 }  // namespace
@@ -766,31 +809,80 @@ bool gemm_large_supported(int fmt, int64_t m, int64_t n, int64_t k) {
   return m >= mn && n >= mn && k % kq == 0 && m * (k / 2) < lim && n * (k / 2) < lim;
 }
 
+namespace {
+
+constexpr int64_t kCUs = 256;
+
+// NVFP4 tile width: 224 or 256 columns, whichever needs fewer tile-column
+// rounds of the 256 CUs (time ~ rounds x width).
+int nv_tile_width(int64_t m, int64_t n) {
+  const int64_t tiles_m = (m + BM - 1) / BM;
+  auto cost = [&](int64_t bn) { return (tiles_m * ((n + bn - 1) / bn) + kCUs - 1) / kCUs * bn; };
+  return cost(224) < cost(256) ? 224 : 256;
+}
+
+// Slices of k per tile: while the tiles (times the slices) fill at most half
+// the CUs, split k in two again (at most 4 slices, each a whole number of the
+// kernel's k-unit: 256 values NVFP4, 512 MXFP4) if that saves at least twice
+// what it costs.  Saved: half of a slice's time, for a tile alone on its CU
+// ~24 ns (NVFP4) or ~6.8 ns (MXFP4) per k-value as measured; cost: the fp32
+// partial sums written and read back, 8 bytes per output and slice, at
+// ~5 TB/s.  (MXFP4's 2048 x 3584 x 8192 in two slices: 28 us saved against
+// 23 us of traffic, slower in practice; NVFP4's: 98 us against 23.)
+int large_split(int fmt, int64_t m, int64_t n, int64_t k) {
+  const int64_t bn = fmt == kFmtNV ? nv_tile_width(m, n) : BN;
+  const int64_t tiles = ((m + BM - 1) / BM) * ((n + bn - 1) / bn);
+  const int64_t unit = fmt == kFmtNV ? 256 : 512;
+  const double ns_per_k = fmt == kFmtNV ? 24.0 : 6.8;
+  int s = 1;
+  while (s < 4 && 2 * s * tiles <= kCUs && k % (2 * s * unit) == 0) {
+    const double saved_ns = ns_per_k * (double)k / (2.0 * s);
+    const double cost_ns = 8.0 * (2 * s - (s > 1 ? s : 0)) * (double)(m * n) / 5000.0;  // B / (B/ns)
+    if (saved_ns < 2.0 * cost_ns) break;
+    s *= 2;
+  }
+  return s;
+}
+
+}  // namespace
+
+size_t gemm_large_workspace_bytes(int fmt, int64_t m, int64_t n, int64_t k) {
+  const int s = large_split(fmt, m, n, k);
+  return s > 1 ? (size_t)s * (size_t)split_stride(m, n) * sizeof(float) : 0;
+}
+
 hipError_t launch_gemm_large(int fmt, int64_t m, int64_t n, int64_t k,
                              const uint8_t* a_codes, const uint8_t* a_scales,
                              const float* a_tscale, const uint8_t* b_codes,
                              const uint8_t* b_scales, const float* b_tscale,
-                             void* c, int c_dtype, hipStream_t stream) {
-  const int tiles_m = (int)((m + BM - 1) / BM), tiles_n = (int)((n + BN - 1) / BN);
-  const dim3 grid((unsigned)(tiles_m * tiles_n));
+                             void* c, int c_dtype, void* workspace, hipStream_t stream) {
+  const int nsplit = large_split(fmt, m, n, k);
+  const int ksplit = (int)(k / nsplit);
+  float* part = nsplit > 1 ? reinterpret_cast<float*>(workspace) : nullptr;
+  const int tiles_m = (int)((m + BM - 1) / BM);
   if (fmt == kFmtMX) {
-    hipLaunchKernelGGL((gemm_large_mx<kMXWM, kMXWN>), grid, dim3(64 * kMXWM * kMXWN), 0, stream,
-                       (int)m, (int)n, (int)k, a_codes, a_scales, b_codes, b_scales, c, c_dtype,
-                       tiles_m, tiles_n);
+    const int tiles_n = (int)((n + BN - 1) / BN);
+    hipLaunchKernelGGL((gemm_large_mx<kMXWM, kMXWN>), dim3((unsigned)(tiles_m * tiles_n), (unsigned)nsplit),
+                       dim3(64 * kMXWM * kMXWN), 0, stream, (int)m, (int)n, (int)k, a_codes, a_scales,
+                       b_codes, b_scales, c, c_dtype, tiles_m, tiles_n, ksplit, part);
+  } else if (nv_tile_width(m, n) == 224) {
+    const int tn = (int)((n + 223) / 224);
+    hipLaunchKernelGGL((gemm_nv4w<224>), dim3((unsigned)(tiles_m * tn), (unsigned)nsplit), dim3(256), 0,
+                       stream, (int)m, (int)n, (int)k, a_codes, a_scales, a_tscale, b_codes, b_scales,
+                       b_tscale, c, c_dtype, tiles_m, tn, ksplit, part);
   } else {
-    // NVFP4 tile width: 224 or 256 columns, whichever needs fewer tile-column
-    // rounds of the 256 CUs (time ~ rounds x width)
-    constexpr int64_t kCUs = 256;
-    auto cost = [&](int64_t bn) { return (tiles_m * ((n + bn - 1) / bn) + kCUs - 1) / kCUs * bn; };
-    if (cost(224) < cost(256)) {
-      const int tn224 = (int)((n + 223) / 224);
-      hipLaunchKernelGGL((gemm_nv4w<224>), dim3((unsigned)(tiles_m * tn224)), dim3(256), 0, stream,
-                         (int)m, (int)n, (int)k, a_codes, a_scales, a_tscale, b_codes, b_scales,
-                         b_tscale, c, c_dtype, tiles_m, tn224);
-    } else {
-      hipLaunchKernelGGL((gemm_nv4w<256>), grid, dim3(256), 0, stream, (int)m, (int)n, (int)k, a_codes,
-                         a_scales, a_tscale, b_codes, b_scales, b_tscale, c, c_dtype, tiles_m, tiles_n);
-    }
+    const int tn = (int)((n + 255) / 256);
+    hipLaunchKernelGGL((gemm_nv4w<256>), dim3((unsigned)(tiles_m * tn), (unsigned)nsplit), dim3(256), 0,
+                       stream, (int)m, (int)n, (int)k, a_codes, a_scales, a_tscale, b_codes, b_scales,
+                       b_tscale, c, c_dtype, tiles_m, tn, ksplit, part);
+  }
+  if (nsplit > 1) {
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t mn = m * n;
+    hipLaunchKernelGGL(split_reduce_kernel, dim3((unsigned)((mn + 1023) / 1024)), dim3(256), 0, stream,
+                       part, nsplit, mn, split_stride(m, n), fmt == kFmtNV ? a_tscale : nullptr,
+                       fmt == kFmtNV ? b_tscale : nullptr, c, c_dtype);
   }
   return hipGetLastError();
 }

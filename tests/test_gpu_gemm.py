@@ -118,6 +118,46 @@ def test_mxfp4_many_tiles(m, n, k, out_dtype):
     check_full("mxfp4", qx, qw, out_dtype)
 
 
+@pytest.mark.parametrize("fmt,m,n,k,out_dtype", [
+    ("nvfp4", 512, 1024, 4096, "bf16"),   # 10 tiles: k in four slices of 1024
+    ("nvfp4", 300, 700, 2048, "f32"),     # ragged, four slices of 512
+    ("mxfp4", 512, 512, 4096, "f32"),     # 4 tiles: four slices of 1024
+    ("mxfp4", 300, 700, 2048, "bf16"),    # ragged, four slices of 512 (two stages each)
+])
+def test_split_k(fmt, m, n, k, out_dtype):
+    # few output tiles: the large kernels split k over several workgroups per
+    # tile, fp32 partial sums in the workspace, added by a second pass
+    from microscaled_fp4_quantization_amd import fp4
+    assert fp4.lib().fp4_gemm_workspace_size(fp4.NVFP4 if fmt == "nvfp4" else fp4.MXFP4, m, n, k) > 0
+    g = torch.Generator().manual_seed(m + n + k)
+    x = torch.randn((m, k), generator=g).to(torch.bfloat16)
+    w = (torch.randn((n, k), generator=g) * 0.02).to(torch.bfloat16)
+    qx, qw = quant_pair(fmt, x, w)
+    check_full(fmt, qx, qw, out_dtype)
+
+
+def test_split_k_sampled_tp8_share():
+    # one GPU's share of a column-parallel split of the rotated weight over 8
+    # GPUs: 2048 x 3584 x 8192, 128 tiles; NVFP4 splits k in two slices,
+    # MXFP4 (a quarter of the time per tile) does not
+    from microscaled_fp4_quantization_amd import fp4
+    m, n, k = 2048, 3584, 8192
+    g = torch.Generator(device=DEV).manual_seed(5)
+    x = torch.randn((m, k), generator=g, device=DEV).to(torch.bfloat16)
+    w = (torch.randn((n, k), generator=g, device=DEV) * 0.015).to(torch.bfloat16)
+    assert fp4.lib().fp4_gemm_workspace_size(fp4.NVFP4, m, n, k) == 2 * m * n * 4
+    assert fp4.lib().fp4_gemm_workspace_size(fp4.MXFP4, m, n, k) == 0
+    for fmt in ("nvfp4", "mxfp4"):
+        qx = fq.quantize(x, fmt, hadamard=True)
+        qw = fq.quantize(w, fmt, hadamard=True)
+        note("gemm split-k %s m=%d n=%d k=%d" % (fmt, m, n, k))
+        c = fq.gemm(qx, qw, fmt, out_dtype="bf16")
+        torch.cuda.synchronize()
+        got, ref = _sampled(fmt, qx, qw, c)
+        assert rel_fro(got, bf16_round_f64(ref)) <= TOL
+        assert torch.isfinite(c).all()
+
+
 def test_tiny_workload():
     d = workloads.tiny()
     qx, qw = quant_pair("nvfp4", d["x"], d["w"])
