@@ -34,8 +34,10 @@ every input already resident in HBM:
   gptq     MR-GPTQ of the decode workload's weight W [14336, 4096] to NVFP4
            (blockwise Hadamard, 2048 calibration rows, fp4_gptq_quantize):
            the offline weight path; fp64 arithmetic (roofline "alu").
-Prints one JSON line.  The timed region is K steps back to back between one
-pair of HIP events (value, ms_per_step).  The dominant kernel is then timed
+Prints one JSON line.  The step first runs untimed for --preheat-s seconds
+(the GPU's clocks settle after a second or so of load), then W warm-up steps;
+the timed region is K steps back to back between one pair of HIP events
+(value, ms_per_step).  The dominant kernel is then timed
 the same way over the K steps' launches of it alone; its algorithmic bytes
 (or flops) per launch over that duration give the roofline figure.  A
 separate sampling phase (at least 100 launches or 200 ms, in 10 windows of
@@ -83,6 +85,8 @@ def parse():
     p.add_argument("--stat-ms", type=float, default=200.0,
                    help="least GPU time of each sampling phase (median / p10 / p90)")
     p.add_argument("--no-stats", action="store_true", help="skip the sampling phases")
+    p.add_argument("--preheat-s", type=float, default=1.0,
+                   help="seconds of untimed steps before the warm-up steps (the clocks settle)")
     p.add_argument("--tp", type=int, default=1,
                    help="one GPU's share of a column-parallel split of the weights over TP GPUs: "
                         "n / TP weight rows (decode, prefill, rotated_nv, rotated_mx, w4a16)")
@@ -648,7 +652,10 @@ def sample(torch, fn, per_call, min_ms, cycles_per_ms, windows=10):
     per = n // windows
     evs = [ev() for _ in range(windows + 1)]
     torch.cuda.synchronize()
-    torch.cuda._sleep(int((2.0 * host_ms * n + 2.0) * cycles_per_ms))
+    n_hot = int(min(10000, max(4, 40.0 / est)))
+    torch.cuda._sleep(int((2.0 * host_ms * (n + n_hot) + 2.0) * cycles_per_ms))
+    for i in range(n_hot):              # the GPU at full clock before the first window
+        fn(i)
     evs[0].record()
     for w in range(windows):
         for i in range(w * per, (w + 1) * per):
@@ -704,9 +711,28 @@ def main():
             dom[i % ndom]()
     launches_per_step = len(dom) if args.workload == "kv" else 1
 
+    # Pre-heat: the GPU's clocks settle only after a second or so of load
+    # (the first steps of a process run up to ~10 % slower), so the step runs
+    # untimed for --preheat-s seconds before the W warm-up steps.
+    t_end = time.perf_counter() + args.preheat_s
+    i = 0
+    while time.perf_counter() < t_end:
+        for _ in range(64):
+            step(i)
+            i += 1
+        torch.cuda.synchronize()
+    w0, w1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    w0.record()
     for i in range(args.warmup):
         step(i)
+    w1.record()
     torch.cuda.synchronize()
+    est_step_ms = max(w0.elapsed_time(w1) / max(1, args.warmup), 1e-3)
+    # Steps run untimed right before each timed region, after its GPU spin:
+    # ~40 ms of the step's own work.  After any idle stretch (the spin, a host
+    # pause) the GPU runs the next ~20 ms of load up to 25 % slower before its
+    # clocks settle; the timed steps start after that.
+    n_hot = int(min(10000, max(4, 40.0 / est_step_ms)))
     # Host cost of enqueuing one step (the GPU may be faster than the host).
     t0 = time.perf_counter()
     for i in range(min(args.warmup, 20)):
@@ -721,12 +747,14 @@ def main():
     c1.record()
     torch.cuda.synchronize()
     ms_per_cycle = c0.elapsed_time(c1) / float(1 << 20)
-    spin_ms = 2.0 * host_step * 1e3 * (args.steps + 4) + 2.0
-    spin_cycles = int(1.0 / ms_per_cycle)
+    spin_ms = 2.0 * host_step * 1e3 * (args.steps + n_hot + 4) + 2.0
+    spin_cycles = int(spin_ms / ms_per_cycle)
     # Timed region: K whole steps back to back, one event pair around them.
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     torch.cuda._sleep(spin_cycles)
+    for i in range(n_hot):
+        step(i)
     start.record()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -742,6 +770,8 @@ def main():
     d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     torch.cuda._sleep(spin_cycles)
+    for i in range(n_hot):
+        step(i)
     d0.record()
     for i in range(args.steps):
         dominant(i)
@@ -799,7 +829,8 @@ def main():
         vunit = "TFLOP/s"
     out = {
         "metric": METRIC, "value": round(value, 3), "unit": vunit, "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
+        "steps": args.steps, "warmup": args.warmup, "preheat_s": args.preheat_s,
+        "ms_per_step": round(ms_step, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": W["dtype"], "data": "synthetic (seeded, see workloads.py)",
         "config": W["config"],
