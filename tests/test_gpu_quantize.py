@@ -170,3 +170,54 @@ def test_compute_workspace_reused_across_calls():
         p, s, t = oracle_quant("nvfp4", host_f32(x), had)
         assert ts.item() == float(t)
         assert np.array_equal(np_u8(scales), s) and np.array_equal(np_u8(codes), p)
+
+
+# --- compute mode: calls queued back to back, and graph capture ---------------
+
+def test_compute_back_to_back():
+    # Calls queued on one stream with no wait between them, one workspace
+    # (uninitialized), inputs whose tensor scales differ by 10^4: a launch
+    # must never take an earlier launch's maxima for its own.
+    need = fq.lib().fp4_quantize_workspace_size(fq.fp4.NVFP4, fq.fp4.TSCALE_COMPUTE, 1, 16)
+    ws = torch.empty(need, dtype=torch.uint8, device=DEV)
+    xs = [randn((2048, 8192), torch.bfloat16, 70 + i, sc) for i, sc in enumerate((1.0, 100.0, 0.01, 1.0))]
+    xd = [x.to(DEV) for x in xs]
+    torch.cuda.synchronize()
+    note("four compute-mode calls back to back")
+    outs = [fq.quantize(x, "nvfp4", hadamard=True, workspace=ws) for x in xd]
+    torch.cuda.synchronize()
+    for x, (codes, scales, ts) in zip(xs, outs):
+        p, s, t = oracle_quant("nvfp4", host_f32(x), True)
+        assert ts.item() == float(t)
+        assert np.array_equal(np_u8(scales), s) and np.array_equal(np_u8(codes), p)
+
+
+def test_compute_under_graph_capture():
+    # Captured into a HIP graph, replayed with new data in the captured
+    # input, with eager calls on the same workspace between the replays:
+    # every replay and every eager call bit-exact.
+    need = fq.lib().fp4_quantize_workspace_size(fq.fp4.NVFP4, fq.fp4.TSCALE_COMPUTE, 1, 16)
+    ws = torch.zeros(need, dtype=torch.uint8, device=DEV)
+    x_static = randn((1024, 4096), torch.bfloat16, 80).to(DEV)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fq.quantize(x_static, "nvfp4", hadamard=True, workspace=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    note("compute-mode quantize captured into a graph")
+    with torch.cuda.graph(g):
+        codes, scales, ts = fq.quantize(x_static, "nvfp4", hadamard=True, workspace=ws)
+    for i, sc in enumerate((1.0, 1000.0, 0.001)):
+        x = randn((1024, 4096), torch.bfloat16, 81 + i, sc)
+        x_static.copy_(x.to(DEV))
+        note("graph replay %d" % i)
+        g.replay()
+        torch.cuda.synchronize()
+        p, s, t = oracle_quant("nvfp4", host_f32(x), True)
+        assert ts.item() == float(t)
+        assert np.array_equal(np_u8(scales), s) and np.array_equal(np_u8(codes), p)
+        e_codes, e_scales, e_ts = fq.quantize(x_static, "nvfp4", hadamard=True, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(e_codes, codes) and torch.equal(e_scales, scales) and torch.equal(e_ts, ts)
