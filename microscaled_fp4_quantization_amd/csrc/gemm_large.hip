@@ -111,7 +111,7 @@ struct Frags {
   uint32_t sb[TJ];
 };
 
-// Writes a workgroup's 256 x 256 tile of C = ts * acc.  The MFMAs take B as
+// Writes a workgroup's 256 x BNT tile of C = ts * acc.  The MFMAs take B as
 // the first operand, so in each 32x32 block a lane holds output row
 // r = lane % 32 and, in registers 4g .. 4g + 3, the four consecutive columns
 // 8g + 4h .. + 3.  The tile goes through LDS (ep: the workgroup's operand
@@ -122,11 +122,11 @@ struct Frags {
 // The tile starts at row m0 and column n0; only rows >= m_lo and columns >=
 // n_lo are this workgroup's (a last tile that was moved back so that all of
 // its rows exist leaves the overlap to its neighbour).
-template <int WMW, int WNW, int TI, int TJ>
+template <int WMW, int WNW, int TI, int TJ, int BNT = BN>
 __device__ __forceinline__ void store_tile(const v16f (&acc)[TI][TJ], uint8_t* ep, float ts,
                                            void* __restrict__ c, int c_dtype, int m, int n,
                                            int m0, int n0, int m_lo, int n_lo) {
-  constexpr int NW = WMW * WNW, TM = BM / WMW, TN = BN / WNW;
+  constexpr int NW = WMW * WNW, TM = BM / WMW, TN = BNT / WNW;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WNW, wn = wave % WNW;
@@ -167,8 +167,8 @@ __device__ __forceinline__ void store_tile(const v16f (&acc)[TI][TJ], uint8_t* e
         }
     }
     __syncthreads();
-    // 16-byte chunks: 32 (bf16) or 64 (f32) per row
-    const int cpr = f32 ? 64 : 32, epc = f32 ? 4 : 8;
+    // 16-byte chunks: BNT / 8 (bf16) or BNT / 4 (f32) per row
+    const int cpr = f32 ? BNT / 4 : BNT / 8, epc = f32 ? 4 : 8;
     const int row0 = m0 + band * band_rows;
     for (int idx = tid; idx < band_rows * cpr; idx += 64 * NW) {
       const int lr = idx / cpr, ch = idx % cpr;
@@ -542,31 +542,34 @@ __device__ __forceinline__ int swz_mx(int r, int c) { return c ^ ((r >> 1) & 7);
 // Stored position of 16-byte half hh of the 32-byte scale row r.
 __device__ __forceinline__ int swz_mxs(int r, int hh) { return hh ^ ((r >> 3) & 1); }
 
-template <int WMW, int WNW>
-__global__ __launch_bounds__(64 * WMW * WNW, 1) void gemm_large_mx(
-    int m, int n, int k, const uint8_t* __restrict__ a, const uint8_t* __restrict__ as,
-    const uint8_t* __restrict__ b, const uint8_t* __restrict__ bs, void* __restrict__ c,
-    int c_dtype, int tiles_m, int tiles_n, int ksplit, float* __restrict__ part) {
+// One 256 x BNT tile (BNT = 256, or 128 for the half-width tiles that finish
+// a grid whose last round of full tiles would leave CUs idle): tile `tile`
+// of the tiles_m-row grid of such tiles over the columns n_begin .. n - 1.
+template <int WMW, int WNW, int BNT>
+__device__ __forceinline__ void mx_tile(
+    MxSmem& smem, int tile, int m, int n, int k, const uint8_t* __restrict__ a,
+    const uint8_t* __restrict__ as, const uint8_t* __restrict__ b, const uint8_t* __restrict__ bs,
+    void* __restrict__ c, int c_dtype, int tiles_m, int n_begin, int ksplit, float* __restrict__ part) {
   constexpr int NW = WMW * WNW;
-  constexpr int NL = BM * MXROWB / 1024 / NW;        // code loads per operand per wave per stage
-  constexpr int NSG = 2 * BM * MXSGB / 1024 / NW;    // scale loads per wave per group
-  constexpr int TM = BM / WMW, TN = BN / WNW;
+  constexpr int NL = BM * MXROWB / 1024 / NW;        // A code loads per wave per stage
+  constexpr int NLB = BNT * MXROWB / 1024 / NW;      // B code loads per wave per stage
+  // scale loads per wave per group: two of A's 128-row halves, one or two of B's
+  constexpr int NSG = 2 + BNT / 128;
+  constexpr int NLD = NL + NLB;                      // code loads per wave per stage
+  constexpr int TM = BM / WMW, TN = BNT / WNW;
   constexpr int TI = TM / 32, TJ = TN / 32;
-  static_assert(BM == BN && NL * NW * 1024 == BM * MXROWB && NSG * NW * 1024 == 2 * BM * MXSGB, "tile shape");
-  static_assert(2 * NL + NSG < 64, "vmcnt range");
-  __shared__ __attribute__((aligned(16))) MxSmem smem;
+  static_assert(BNT <= BN && BNT % 128 == 0 && NL * NW * 1024 == BM * MXROWB && NLB * NW * 1024 == BNT * MXROWB &&
+                2 * BM * MXSGB == 4 * NW * 1024, "tile shape");
+  static_assert(NLD + NSG < 64, "vmcnt range");
 
-  const int ntiles = tiles_m * tiles_n;
-  const int wg = blockIdx.x;
-  int tile = wg;
-  if (ntiles % NXCD == 0) tile = (wg % NXCD) * (ntiles / NXCD) + wg / NXCD;
   const int tm = tile % tiles_m, tn = tile / tiles_m;
   // A last tile that would run past m or n is moved back to end at the last
-  // row or column (m, n >= 256): every row it loads exists, and the rows and
-  // columns it shares with its neighbour are left to the neighbour.
-  const int m_lo = tm * BM, n_lo = tn * BN;
+  // row or column (m >= 256, n - n_begin >= BNT): every row it loads exists,
+  // and the rows and columns it shares with its neighbour are left to the
+  // neighbour.
+  const int m_lo = tm * BM, n_lo = n_begin + tn * BNT;
   const int m0 = m_lo + BM <= m ? m_lo : m - BM;
-  const int n0 = n_lo + BN <= n ? n_lo : n - BN;
+  const int n0 = n_lo + BNT <= n ? n_lo : n - BNT;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -591,7 +594,7 @@ __global__ __launch_bounds__(64 * WMW * WNW, 1) void gemm_large_mx(
   // slot: operand g / 8, rows 32 (g % 8) .. + 31, i.e. rows 32 wave + 128
   // (j % 2) of operand j / 2; lane p writes row 32 (g % 8) + p / 2 at stored
   // half p % 2, i.e. fetches half (p % 2) ^ ((row >> 3) & 1).
-  static_assert(NW == 4 && NSG == 4, "scale-load mapping");
+  static_assert(NW == 4, "scale-load mapping");
   const int srw = 32 * wave + (lane >> 1);
   const int voff_s = srw * srow;
   const int hoff_s = 16 * swz_mxs(srw, lane & 1);
@@ -603,12 +606,13 @@ __global__ __launch_bounds__(64 * WMW * WNW, 1) void gemm_large_mx(
     for (int i = 0; i < NL; ++i) {
       const int q = i * NW + wave;
       load_lds16(rs_a, &S.a[q * 1024], voff_c, (m0 + 32 * i) * kbytes + kb);
-      load_lds16(rs_b, &S.b[q * 1024], voff_c, (n0 + 32 * i) * kbytes + kb);
+      if (i < NLB) load_lds16(rs_b, &S.b[q * 1024], voff_c, (n0 + 32 * i) * kbytes + kb);
     }
   };
   // scale group g (clamped to the last) into group slot g % 2.  A last group
   // of two stages has only its first half inside the row: the second half
-  // then repeats the first and is never read.
+  // then repeats the first and is never read.  Load j < 2 covers A's rows
+  // 128 j .. + 127, load j >= 2 B's rows 128 (j - 2) .. + 127.
   auto issue_group = [&](int g) {
     MxScaleGroup& SG = smem.sg[g & 1];
     const int gc = g < ngr ? g : ngr - 1;
@@ -686,8 +690,13 @@ __global__ __launch_bounds__(64 * WMW * WNW, 1) void gemm_large_mx(
     }
   };
   using C0 = std::integral_constant<int, 0>;
-  using CE = std::integral_constant<int, 8>;                 // MFMAs ahead of a barrier
+  using CE = std::integral_constant<int, BNT == BN ? 8 : 4>; // MFMAs ahead of a barrier
   using CN = std::integral_constant<int, 2 * TI * TJ>;       // MFMAs per half-stage
+  // the MFMAs after the barrier, in NIG groups of MPG between groups of
+  // direct loads (even half-steps) or fragment reads (odd half-steps)
+  constexpr int NIG = BNT == BN ? 8 : 6;
+  constexpr int MPG = (CN::value - CE::value) / NIG;
+  static_assert(MPG * NIG == CN::value - CE::value, "interleave");
 
   // ---- software pipeline ----------------------------------------------------
   // Half-step u multiplies half-stage u from registers while the fragments
@@ -708,7 +717,7 @@ __global__ __launch_bounds__(64 * WMW * WNW, 1) void gemm_large_mx(
   issue_stage(0);
   issue_stage(1);
   issue_group(1);
-  wait_vm<2 * NL + NSG>();                   // stage 0 and group 0
+  wait_vm<NLD + NSG>();                      // stage 0 and group 0
   __asm__ volatile("s_barrier" ::: "memory");
   Frags<TI, TJ> F0, F1;
   read_frags(0, F0);
@@ -728,24 +737,24 @@ __global__ __launch_bounds__(64 * WMW * WNW, 1) void gemm_large_mx(
       if constexpr (j == 6) issue_group((t + 2) / MXG + 1);
       compute(Fc, CE{}, CN{});
 #pragma unroll
-      for (int g = 0; g < 8; ++g) {
+      for (int g = 0; g < NIG; ++g) {
         __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);                        // global loads
-        __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);                        // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x008, MPG, 0);                      // MFMA
       }
       __builtin_amdgcn_sched_barrier(0);
     } else {
       compute(Fc, C0{}, CE{});
       __builtin_amdgcn_sched_barrier(0);
       // stage t + 1; issued after it: stage t + 2 and, at j == 7, a group
-      if constexpr (j == 7) wait_vm<2 * NL + NSG>();
-      else wait_vm<2 * NL>();
+      if constexpr (j == 7) wait_vm<NLD + NSG>();
+      else wait_vm<NLD>();
       __asm__ volatile("s_barrier" ::: "memory");
       read_frags(u + 1, Fn);                   // past the end: a repeated stage, unused
       compute(Fc, CE{}, CN{});
 #pragma unroll
-      for (int g = 0; g < 8; ++g) {
+      for (int g = 0; g < NIG; ++g) {
         __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);                        // LDS reads
-        __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);                        // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x008, MPG, 0);                      // MFMA
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -773,8 +782,34 @@ __global__ __launch_bounds__(64 * WMW * WNW, 1) void gemm_large_mx(
   wait_vm<0>();                 // no load may land in LDS after the workgroup ends
   // split k: this slice's fp32 sums into the workspace
   void* dst = part ? static_cast<void*>(part + (int64_t)blockIdx.y * split_stride(m, n)) : c;
-  store_tile<WMW, WNW>(acc, reinterpret_cast<uint8_t*>(&smem), 1.0f, dst, part ? kInF32 : c_dtype, m, n,
-                       m0, n0, m_lo, n_lo);
+  store_tile<WMW, WNW, TI, TJ, BNT>(acc, reinterpret_cast<uint8_t*>(&smem), 1.0f, dst,
+                                    part ? kInF32 : c_dtype, m, n, m0, n0, m_lo, n_lo);
+}
+
+// Tile order within a class of cnt tiles: each XCD (workgroup w runs on XCD
+// w % 8) takes a contiguous run of tiles, m fastest, so that the tiles in
+// flight on an XCD share weight rows in its L2.
+__device__ __forceinline__ int xcd_tile(int local, int cnt) {
+  return cnt % NXCD == 0 ? (local % NXCD) * (cnt / NXCD) + local / NXCD : local;
+}
+
+// Workgroups [0, full) take the 256 x 256 tiles of columns 0 .. n_half - 1
+// (n_half = n when there are no half-width tiles), the rest the 256 x 128
+// tiles of columns n_half .. n - 1; full is a multiple of 8, so both classes
+// keep the XCD order.
+template <int WMW, int WNW>
+__global__ __launch_bounds__(64 * WMW * WNW, 1) void gemm_large_mx(
+    int m, int n, int k, const uint8_t* __restrict__ a, const uint8_t* __restrict__ as,
+    const uint8_t* __restrict__ b, const uint8_t* __restrict__ bs, void* __restrict__ c,
+    int c_dtype, int tiles_m, int full, int half, int n_half, int ksplit, float* __restrict__ part) {
+  __shared__ __attribute__((aligned(16))) MxSmem smem;
+  const int wg = blockIdx.x;
+  if (wg < full)
+    mx_tile<WMW, WNW, BN>(smem, xcd_tile(wg, full), m, n, k, a, as, b, bs, c, c_dtype, tiles_m, 0,
+                          ksplit, part);
+  else
+    mx_tile<WMW, WNW, BN / 2>(smem, xcd_tile(wg - full, half), m, n, k, a, as, b, bs, c, c_dtype,
+                              tiles_m, n_half, ksplit, part);
 }
 
 // Split k: C = ts (sum over slices of the fp32 partial sums), the slices
@@ -852,6 +887,32 @@ int large_split(int fmt, int64_t m, int64_t n, int64_t k) {
   return s;
 }
 
+// MXFP4 tile classes: when the 256 x 256 tiles fill some whole rounds of the
+// CUs and then at most half of one more, the tile columns that fit in the
+// whole rounds stay 256 wide and the rest of the columns go to 256 x 128
+// tiles, which take ~0.6 of a full tile's time (measured on 2048 x 28672 x
+// 8192: 896 tiles, 3.5 rounds, become 768 + 256 half-width tiles).  full and
+// half are the counts, n_half the first column of the half-width tiles.
+void mx_tile_classes(int64_t m, int64_t n, int* full, int* half, int64_t* n_half) {
+  const int64_t tiles_m = (m + BM - 1) / BM, ntiles = tiles_m * ((n + BN - 1) / BN);
+  *full = (int)ntiles;
+  *half = 0;
+  *n_half = n;
+  const int64_t rem = ntiles % kCUs;
+  if (ntiles <= kCUs || rem == 0 || rem > kCUs / 2) return;
+  int64_t cols = (ntiles - rem) / tiles_m;           // full-width tile columns
+  while (cols > 0 && (tiles_m * cols) % NXCD != 0) --cols;
+  const int64_t nh = cols * BN;
+  if (cols == 0 || n - nh < BN / 2) return;
+  const int64_t h = tiles_m * ((n - nh + BN / 2 - 1) / (BN / 2));
+  const double before = (double)((ntiles + kCUs - 1) / kCUs);
+  const double after = (double)((tiles_m * cols + kCUs - 1) / kCUs) + 0.6 * (double)((h + kCUs - 1) / kCUs);
+  if (after + 0.1 > before) return;
+  *full = (int)(tiles_m * cols);
+  *half = (int)h;
+  *n_half = nh;
+}
+
 }  // namespace
 
 size_t gemm_large_workspace_bytes(int fmt, int64_t m, int64_t n, int64_t k) {
@@ -869,10 +930,12 @@ hipError_t launch_gemm_large(int fmt, int64_t m, int64_t n, int64_t k,
   float* part = nsplit > 1 ? reinterpret_cast<float*>(workspace) : nullptr;
   const int tiles_m = (int)((m + BM - 1) / BM);
   if (fmt == kFmtMX) {
-    const int tiles_n = (int)((n + BN - 1) / BN);
-    hipLaunchKernelGGL((gemm_large_mx<kMXWM, kMXWN>), dim3((unsigned)(tiles_m * tiles_n), (unsigned)nsplit),
+    int full = (int)(tiles_m * ((n + BN - 1) / BN)), half = 0;
+    int64_t n_half = n;
+    if (nsplit == 1) mx_tile_classes(m, n, &full, &half, &n_half);
+    hipLaunchKernelGGL((gemm_large_mx<kMXWM, kMXWN>), dim3((unsigned)(full + half), (unsigned)nsplit),
                        dim3(64 * kMXWM * kMXWN), 0, stream, (int)m, (int)n, (int)k, a_codes, a_scales,
-                       b_codes, b_scales, c, c_dtype, tiles_m, tiles_n, ksplit, part);
+                       b_codes, b_scales, c, c_dtype, tiles_m, full, half, (int)n_half, ksplit, part);
   } else if (nv_tile_width(m, n) == 224) {
     const int tn = (int)((n + 223) / 224);
     hipLaunchKernelGGL((gemm_nv4w<224>), dim3((unsigned)(tiles_m * tn), (unsigned)nsplit), dim3(256), 0,
