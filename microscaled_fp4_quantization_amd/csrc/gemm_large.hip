@@ -795,8 +795,8 @@ __device__ __forceinline__ int xcd_tile(int local, int cnt) {
 
 // Workgroups [0, full) take the 256 x 256 tiles of columns 0 .. n_half - 1
 // (n_half = n when there are no half-width tiles), the rest the 256 x 128
-// tiles of columns n_half .. n - 1; full is a multiple of 8, so both classes
-// keep the XCD order.
+// tiles of columns n_half .. n - 1.  When both classes are there, full is a
+// multiple of 8, so both keep the XCD order.
 template <int WMW, int WNW>
 __global__ __launch_bounds__(64 * WMW * WNW, 1) void gemm_large_mx(
     int m, int n, int k, const uint8_t* __restrict__ a, const uint8_t* __restrict__ as,
@@ -887,17 +887,31 @@ int large_split(int fmt, int64_t m, int64_t n, int64_t k) {
   return s;
 }
 
-// MXFP4 tile classes: when the 256 x 256 tiles fill some whole rounds of the
-// CUs and then at most half of one more, the tile columns that fit in the
-// whole rounds stay 256 wide and the rest of the columns go to 256 x 128
-// tiles, which take ~0.6 of a full tile's time (measured on 2048 x 28672 x
-// 8192: 896 tiles, 3.5 rounds, become 768 + 256 half-width tiles).  full and
-// half are the counts, n_half the first column of the half-width tiles.
+// MXFP4 tile classes.  A 256 x 128 tile takes ~0.6 of a 256 x 256 tile's
+// time, so half-width tiles pay where full ones would leave CUs idle:
+// - the 256 x 256 tiles fill some whole rounds of the CUs and then at most
+//   half of one more: the tile columns that fit in the whole rounds stay 256
+//   wide and the rest of the columns go to 256 x 128 tiles (2048 x 28672 x
+//   8192: 896 tiles, 3.5 rounds, become 768 + 256 half-width tiles);
+// - the 256 x 256 tiles fill at most half the CUs: every tile is half-width
+//   (2048 x 3584 x 8192: 112 tiles become 224).
+// The time model counts rounds (a round of half-width tiles as 0.6) and keeps
+// the full tiles unless it saves a tenth of a round.  full and half are the
+// counts, n_half the first column of the half-width tiles.
 void mx_tile_classes(int64_t m, int64_t n, int* full, int* half, int64_t* n_half) {
   const int64_t tiles_m = (m + BM - 1) / BM, ntiles = tiles_m * ((n + BN - 1) / BN);
+  auto rounds = [](int64_t t) { return (double)((t + kCUs - 1) / kCUs); };
   *full = (int)ntiles;
   *half = 0;
   *n_half = n;
+  double best = rounds(ntiles) - 0.1;
+  const int64_t all_half = tiles_m * ((n + BN / 2 - 1) / (BN / 2));
+  if (0.6 * rounds(all_half) < best) {
+    best = 0.6 * rounds(all_half);
+    *full = 0;
+    *half = (int)all_half;
+    *n_half = 0;
+  }
   const int64_t rem = ntiles % kCUs;
   if (ntiles <= kCUs || rem == 0 || rem > kCUs / 2) return;
   int64_t cols = (ntiles - rem) / tiles_m;           // full-width tile columns
@@ -905,12 +919,12 @@ void mx_tile_classes(int64_t m, int64_t n, int* full, int* half, int64_t* n_half
   const int64_t nh = cols * BN;
   if (cols == 0 || n - nh < BN / 2) return;
   const int64_t h = tiles_m * ((n - nh + BN / 2 - 1) / (BN / 2));
-  const double before = (double)((ntiles + kCUs - 1) / kCUs);
-  const double after = (double)((tiles_m * cols + kCUs - 1) / kCUs) + 0.6 * (double)((h + kCUs - 1) / kCUs);
-  if (after + 0.1 > before) return;
-  *full = (int)(tiles_m * cols);
-  *half = (int)h;
-  *n_half = nh;
+  const double split = rounds(tiles_m * cols) + 0.6 * rounds(h);
+  if (split < best) {
+    *full = (int)(tiles_m * cols);
+    *half = (int)h;
+    *n_half = nh;
+  }
 }
 
 }  // namespace

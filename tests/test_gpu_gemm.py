@@ -107,10 +107,14 @@ def test_random_shapes(fmt, out_dtype):
     (1100, 16000, 512, "bf16"),    # more tiles than CUs, k = 512 mod 1024
     (2048, 9000, 1024, "f32"),     # tile count a multiple of 8: XCD-ordered tiles
     (520, 30001, 1536, "bf16"),    # n not a multiple of 8
+    (500, 3000, 1024, "f32"),      # few tiles: every tile half-width
+    (600, 2100, 2560, "bf16"),     # few tiles, half-width, k = 512 mod 1024
 ])
 def test_mxfp4_many_tiles(m, n, k, out_dtype):
-    # the MXFP4 large-m kernel over more tiles than CUs, with tiles moved back
-    # at the edges and a half scale group at the end of k (k = 512 mod 1024)
+    # the MXFP4 large-m kernel over more tiles than CUs (256-wide tiles for
+    # the whole rounds, 128-wide ones after them) or so few that every tile
+    # is 128 wide, with tiles moved back at the edges and a half scale group
+    # at the end of k (k = 512 mod 1024)
     g = torch.Generator().manual_seed(11)
     x = torch.randn((m, k), generator=g).to(torch.bfloat16)
     w = (torch.randn((n, k), generator=g) * 0.02).to(torch.bfloat16)
