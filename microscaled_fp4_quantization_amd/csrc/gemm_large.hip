@@ -280,6 +280,56 @@ __device__ __forceinline__ void store_tile16(const v4f (&acc)[TI][TJ], uint8_t* 
   }
 }
 
+// Where the NVFP4 kernel's conversions go in a k-step.  Row i of the TI x TJ
+// MFMAs (q = TJ i .. TJ i + TJ - 1) is followed, spread evenly after its
+// MFMAs, by its pieces: kind 0 = A row idx of this k-step (row i + 1: its
+// register is free once row i - 1 is issued and must be ready for row
+// i + 1), 1 = B fragment idx of the next k-step, 2 = A row 0 of the next
+// k-step (last row), 3 / 4 = the next stage's B / A scale pair idx (last
+// k-step of a stage).  u = piece (values 2u, 2u + 1) of a conversion.  In a
+// stage's last k-step the next stage's words are read first, so its B
+// conversions start at row 3, after its scale pairs (rows 1 and 2).
+struct ConvPiece {
+  int kind, idx, u;
+};
+template <int TI, int TJ>
+struct ConvRows {
+  ConvPiece p[TI][32];
+  int n[TI];
+};
+template <int TI, int TJ>
+constexpr ConvRows<TI, TJ> conv_rows(bool last) {
+  ConvRows<TI, TJ> r{};
+  for (int i = 0; i < TI; ++i) r.n[i] = 0;
+  for (int i = 0; i + 1 < TI; ++i)
+    for (int u = 0; u < 4; ++u) r.p[i][r.n[i]++] = ConvPiece{0, i + 1, u};
+  if (last) {
+    for (int j = 0; j < TJ; ++j) r.p[1][r.n[1]++] = ConvPiece{3, j, 0};
+    for (int i = 0; i < TI; ++i) r.p[2][r.n[2]++] = ConvPiece{4, i, 0};
+  }
+  const int b0 = last ? 3 : 0, nb = TI - b0;
+  for (int k = 0; k < 4 * TJ; ++k) {
+    const int row = b0 + k * nb / (4 * TJ);
+    r.p[row][r.n[row]++] = ConvPiece{1, k / 4, k % 4};
+  }
+  for (int u = 0; u < 4; ++u) r.p[TI - 1][r.n[TI - 1]++] = ConvPiece{2, 0, u};
+  return r;
+}
+template <int TI, int TJ>
+constexpr bool conv_rows_ok() {
+  for (int l = 0; l < 2; ++l) {
+    const ConvRows<TI, TJ> r = conv_rows<TI, TJ>(l == 1);
+    for (int i = 0; i < TI; ++i) {
+      if (r.n[i] > 32 || r.n[i] < 1) return false;
+      // an A row's pieces come before the row's other pieces, so they land
+      // among its MFMAs; the rest is checked by construction
+      for (int k = 0; k < r.n[i]; ++k)
+        if (r.p[i][k].kind == 0 && r.p[i][k].idx != i + 1) return false;
+    }
+  }
+  return true;
+}
+
 // ---- NVFP4: 16x16x32 f16 MFMAs, one wave per SIMD --------------------------
 // Measured alternatives on 2048 x 28672 x 8192: eight waves of 128 x 64 run
 // the multiply-and-convert work alone at 1.9 PFLOP/s but read the fragments
@@ -366,6 +416,23 @@ __global__ __launch_bounds__(256, 1) void gemm_nv4w(
       load_lds16(rs_b, &S.b[q * 1024], voff_c, (n0 + 64 * i) * kbytes + kb);
     }
   };
+  // load q of issue_stage(t) (A block q / 2 for even q, B for odd) and
+  // load j of issue_group(g)
+  auto issue_load = [&](int t, int q) {
+    Stage& S = st[t % NSTAGE];
+    const int kb = (t < nstages ? t : nstages - 1) * ROWB + kofs / 2;
+    const int i = q >> 1, blk = i * NW + wave;
+    if ((q & 1) == 0) load_lds16(rs_a, &S.a[blk * 1024], voff_c, (m0 + 64 * i) * kbytes + kb);
+    else load_lds16(rs_b, &S.b[blk * 1024], voff_c, (n0 + 64 * i) * kbytes + kb);
+  };
+  auto issue_group_load = [&](int g, int j) {
+    ScaleGroup& SG = sgr[g % NSGRP];
+    const int gb = 16 * (g < ngroups ? g : ngroups - 1) + kofs / 16;
+    const int gw = j * NW + wave;
+    const bool isb = gw >= 4;
+    load_lds16(isb ? rs_bs : rs_as, &SG.w[isb][256 * (gw % 4)], voff_s,
+               ((isb ? n0 : m0) + 64 * (gw % 4)) * srow + gb);
+  };
   auto issue_group = [&](int g) {
     ScaleGroup& SG = sgr[g % NSGRP];
     const int gb = 16 * (g < ngroups ? g : ngroups - 1) + kofs / 16;
@@ -414,33 +481,42 @@ __global__ __launch_bounds__(256, 1) void gemm_nv4w(
     for (int j = 0; j < TJ; ++j) acc[i][j] = (v4f){0.f, 0.f, 0.f, 0.f};
 
   const int sh = 16 * (g4 & 1);
-  // k-steps S0 .. S1 - 1 of a stage's fragments
-  auto compute = [&](const Frags16<TI, TJ>& F, auto S0, auto S1) {
-    constexpr int s0 = decltype(S0)::value, s1 = decltype(S1)::value;
-    v2h sap[TI], sbp[TJ];
-#pragma unroll
-    for (int i = 0; i < TI; ++i) sap[i] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(F.sa[i] >> sh, 1.0f, false);
-#pragma unroll
-    for (int j = 0; j < TJ; ++j) sbp[j] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(F.sb[j] >> sh, 1.0f, false);
-#pragma unroll
-    for (int s = s0; s < s1; ++s) {
-      v8h hb[TJ];
-#pragma unroll
-      for (int j = 0; j < TJ; ++j) hb[j] = s < 2 ? dequant8_sel<0>(F.b[j][s], sbp[j]) : dequant8_sel<1>(F.b[j][s], sbp[j]);
-#pragma unroll
-      for (int i = 0; i < TI; ++i) {
-        const v8h ha = s < 2 ? dequant8_sel<0>(F.a[i][s], sap[i]) : dequant8_sel<1>(F.a[i][s], sap[i]);
-#pragma unroll
-        for (int j = 0; j < TJ; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(hb[j], ha, acc[i][j], 0, 0, 0);
-      }
-      // one k-step's converted operands at a time
-      if (s + 1 < s1) __builtin_amdgcn_sched_barrier(0);
+
+  // ---- the conversions, spread between the MFMAs ---------------------------
+  // A k-step issues its TI x TJ MFMAs (q = 0 .. NQ - 1: row q / TJ, column
+  // q % TJ) from converted operands: hb[s & 1][j] for the B fragments and
+  // ha[i & 1] for A row i.  The conversions the later MFMAs need run between
+  // them, about two VALU instructions after each MFMA: the next row's A
+  // fragment during each row, the next k-step's B fragments and first A
+  // fragment during the whole k-step.  A wave keeps the matrix core busy
+  // with that many independent VALU instructions between MFMAs, while
+  // converted in clusters the conversions and the MFMAs ran one after the
+  // other.  A scheduling fence after every MFMA keeps this order.  In k-step
+  // 3 the next stage's fragment words are read from LDS as their registers
+  // free up (its B and scale words first, A row i once row i's last word is
+  // converted), and its scale pairs are converted.
+  //
+  // piece t (values 2t, 2t + 1) of the conversion of word w under half HI of
+  // the scale pair sp, into the v8h x
+  auto conv_piece = [&](v8h& x, uint32_t w, v2h sp, int hi, int t) {
+    const _Float16 sv = hi ? sp.y : sp.x;
+    const v2h s2 = {sv, sv};
+    v2h pc;
+    switch (t) {
+      case 0: pc = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * s2; break;
+      case 1: pc = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * s2; break;
+      case 2: pc = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * s2; break;
+      default: pc = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * s2; break;
     }
+    x[2 * t] = pc.x;
+    x[2 * t + 1] = pc.y;
   };
-  using K0 = std::integral_constant<int, 0>;
-  using K3 = std::integral_constant<int, 3>;
-  using K4 = std::integral_constant<int, 4>;
+  auto scale_pair = [&](uint32_t word) { return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(word >> sh, 1.0f, false); };
+
+  static_assert(conv_rows_ok<TI, TJ>(), "conversion plan");
+  constexpr int NQ = TI * TJ;
+  v8h hb[2][TJ], ha[2];
+  v2h sap[TI], sbp[TJ], sapn[TI], sbpn[TJ];
 
   // Software pipeline: iteration s waits for stage s + 1 (this wave's loads
   // by count, everyone's at the barrier, which also ends every wave's LDS
@@ -462,65 +538,97 @@ __global__ __launch_bounds__(256, 1) void gemm_nv4w(
   issue_group(2);                              // -1
   wait_vm<6 * NL + 2 * NSG>();                 // stage 0, group 0
   __asm__ volatile("s_barrier" ::: "memory");
-  Frags16<TI, TJ> F0;
-  read_frags(0, F0);
+  Frags16<TI, TJ> F;
+  read_frags(0, F);
+  // the first k-step's operands
+#pragma unroll
+  for (int i = 0; i < TI; ++i) sap[i] = scale_pair(F.sa[i]);
+#pragma unroll
+  for (int j = 0; j < TJ; ++j) sbp[j] = scale_pair(F.sb[j]);
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) conv_piece(hb[0][j], F.b[j][0], sbp[j], 0, t);
+    conv_piece(ha[0], F.a[0][0], sap[0], 0, t);
+  }
 
-  // k-step 3 of stage s from F, the fragments of stage s + 1 read into each
-  // fragment's registers as soon as its last dword is converted
-  auto compute_last = [&](Frags16<TI, TJ>& F, int tn) {
-    v2h sap[TI], sbp[TJ];
-#pragma unroll
-    for (int i = 0; i < TI; ++i) sap[i] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(F.sa[i] >> sh, 1.0f, false);
-#pragma unroll
-    for (int j = 0; j < TJ; ++j) sbp[j] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(F.sb[j] >> sh, 1.0f, false);
+  // k-step S of stage s (the fragments in F); in k-step 3 the words of stage
+  // s + 1 replace them
+  auto kstep = [&](auto SS, int s) {
+    constexpr int S = decltype(SS)::value;
+    constexpr bool LAST = S == 3;
+    constexpr ConvRows<TI, TJ> R = conv_rows<TI, TJ>(LAST);
+    constexpr int HI = S < 2 ? 0 : 1;                      // scale half of this k-step
+    constexpr int HN = LAST ? 0 : (S + 1 < 2 ? 0 : 1);     // of the next one
+    const int tn = s + 1;
     int ao = (tn % NSTAGE) * (int)sizeof(Stage) + a_lane;
     int bo = (tn % NSTAGE) * (int)sizeof(Stage) + b_lane;
     const int sgo = ((tn / G) % NSGRP) * (int)sizeof(ScaleGroup) + (tn % G) * 8;
     int sao = sgo + sa_lane, sbo = sgo + sb_lane;
-    __asm__ volatile("" : "+v"(ao), "+v"(bo), "+v"(sao), "+v"(sbo));
-    v8h hb[TJ];
+    if constexpr (LAST) {
+      __asm__ volatile("" : "+v"(ao), "+v"(bo), "+v"(sao), "+v"(sbo));
+      // stage s + 1's B words, scale words and A row 0 (row 0's last word of
+      // this stage was converted in k-step 2)
 #pragma unroll
-    for (int j = 0; j < TJ; ++j) {
-      hb[j] = dequant8_sel<1>(F.b[j][3], sbp[j]);
-      F.b[j] = *reinterpret_cast<const u32x4*>(sm + bo + 1024 * j);
-      F.sb[j] = *reinterpret_cast<const uint32_t*>(sm + sbo + 256 * j);
+      for (int j = 0; j < TJ; ++j) {
+        F.b[j] = *reinterpret_cast<const u32x4*>(sm + bo + 1024 * j);
+        F.sb[j] = *reinterpret_cast<const uint32_t*>(sm + sbo + 256 * j);
+      }
+#pragma unroll
+      for (int i = 0; i < TI; ++i) F.sa[i] = *reinterpret_cast<const uint32_t*>(sm + sao + 256 * i);
+      F.a[0] = *reinterpret_cast<const u32x4*>(sm + ao);
     }
 #pragma unroll
-    for (int i = 0; i < TI; ++i) {
-      const v8h ha = dequant8_sel<1>(F.a[i][3], sap[i]);
-      F.a[i] = *reinterpret_cast<const u32x4*>(sm + ao + 1024 * i);
-      F.sa[i] = *reinterpret_cast<const uint32_t*>(sm + sao + 256 * i);
+    for (int q = 0; q < NQ; ++q) {
+      const int i = q / TJ, j = q % TJ;
+      acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(hb[S & 1][j], ha[i & 1], acc[i][j], 0, 0, 0);
+      if constexpr (S == 0) {
+        // this stage's loads: stage s + 4, then after odd stages a scale group
+        if (q < 2 * NL) issue_load(s + NSTAGE, q);
+        if (q >= 2 * NL && q < 2 * NL + NSG && (s & 1) == 1) issue_group_load((s + 1) / G + 2, q - 2 * NL);
+      }
 #pragma unroll
-      for (int j = 0; j < TJ; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(hb[j], ha, acc[i][j], 0, 0, 0);
+      for (int k = 0; k < R.n[i]; ++k) {
+        if (TJ * i + k * TJ / R.n[i] != q) continue;
+        const int kind = R.p[i][k].kind, idx = R.p[i][k].idx, u = R.p[i][k].u;
+        if (kind == 0) {
+          conv_piece(ha[idx & 1], F.a[idx][S], sap[idx], HI, u);
+          if (LAST && u == 3) F.a[idx] = *reinterpret_cast<const u32x4*>(sm + ao + 1024 * idx);
+        } else if (kind == 1) {
+          if (LAST) conv_piece(hb[(S + 1) & 1][idx], F.b[idx][0], sbpn[idx], HN, u);
+          else conv_piece(hb[(S + 1) & 1][idx], F.b[idx][(S + 1) & 3], sbp[idx], HN, u);
+        } else if (kind == 2) {
+          if (LAST) conv_piece(ha[0], F.a[0][0], sapn[0], HN, u);
+          else conv_piece(ha[0], F.a[0][(S + 1) & 3], sap[0], HN, u);
+        } else if (kind == 3) {
+          sbpn[idx] = scale_pair(F.sb[idx]);
+        } else {
+          sapn[idx] = scale_pair(F.sa[idx]);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if constexpr (LAST) {
+#pragma unroll
+      for (int i = 0; i < TI; ++i) sap[i] = sapn[i];
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) sbp[j] = sbpn[j];
     }
   };
-  // One stage per loop iteration, the scale-group parity a uniform branch:
-  // with two stages per iteration the compiler kept the accumulators in
-  // different AGPRs in the two halves and moved them between (176 AGPR/VGPR
-  // moves per 448 MFMAs; none this way, 2.5 % faster).
-  auto step = [&](int s, Frags16<TI, TJ>& F) {
+
+  for (int s = 0; s < nstages; ++s) {
+    // stage s + 1 (this wave's loads by count, everyone's at the barrier,
+    // which also ends every wave's LDS reads of stage s - 1's slot)
     if ((s & 1) == 0) wait_vm<4 * NL + 2 * NSG>();
     else wait_vm<4 * NL + NSG>();
     wait_lgkm0();
     __asm__ volatile("s_barrier" ::: "memory");
-    issue_stage(s + NSTAGE);
-    if ((s & 1) == 1) issue_group((s + 1) / G + 2);
-    compute(F, K0{}, K3{});
-    // spread the direct loads over the multiplies: a load can stall issue
-    // while the memory pipeline drains
-#pragma unroll
-    for (int q = 0; q < 2 * NL + NSG; ++q) {
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // global load
-      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);   // MFMA
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    // at s = nstages - 1 this reads the repeated last stage: valid, unused
-    compute_last(F, s + 1);
-    __builtin_amdgcn_sched_barrier(0);
-  };
+    kstep(std::integral_constant<int, 0>{}, s);
+    kstep(std::integral_constant<int, 1>{}, s);
+    kstep(std::integral_constant<int, 2>{}, s);
+    kstep(std::integral_constant<int, 3>{}, s);    // at s = nstages - 1: the repeated last stage, unused
+  }
   static_assert(G == 2, "scale-group parity");
-  for (int s = 0; s < nstages; ++s) step(s, F0);
 
   wait_vm<0>();                 // no load may land in LDS after the workgroup ends
   // split k: this slice's unscaled fp32 sums into the workspace
