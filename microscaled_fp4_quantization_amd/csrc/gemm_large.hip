@@ -202,18 +202,6 @@ __device__ __forceinline__ void store_tile(const v16f (&acc)[TI][TJ], uint8_t* e
 // 16-byte fragment read touches then fall on 16 different groups.
 __device__ __forceinline__ int swz16(int row, int chunk) { return chunk ^ ((row >> 2) & 3); }
 
-// 8 codes times half HI of the scale pair sp (the splat folds into the
-// packed multiply's operand select: no register for it)
-template <int HI>
-__device__ __forceinline__ v8h dequant8_sel(uint32_t w, v2h sp) {
-  const v2h sv = __builtin_shufflevector(sp, sp, HI, HI);
-  const v2h p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * sv;
-  const v2h p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * sv;
-  const v2h p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * sv;
-  const v2h p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * sv;
-  return (v8h){p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
-}
-
 template <int WMW, int WNW, int TI, int TJ, int BNT = BN>
 __device__ __forceinline__ void store_tile16(const v4f (&acc)[TI][TJ], uint8_t* ep, float ts,
                                              void* __restrict__ c, int c_dtype, int m, int n,
@@ -491,12 +479,13 @@ __global__ __launch_bounds__(256, 1) void gemm_nv4w(
   // fragment during the whole k-step.  A wave keeps the matrix core busy
   // with that many independent VALU instructions between MFMAs, while
   // converted in clusters the conversions and the MFMAs ran one after the
-  // other.  A scheduling fence after every MFMA keeps this order.  In k-step
-  // 3 the next stage's fragment words are read from LDS as their registers
-  // free up (its B and scale words first, A row i once row i's last word is
-  // converted), and its scale pairs are converted.
-  //
-  // piece t (values 2t, 2t + 1) of the conversion of word w under half HI of
+  // other.  A scheduling fence after every MFMA keeps this order (the rows'
+  // pieces: conv_rows).  In k-step 3 the next stage's fragment words are
+  // read from LDS as their registers free up (its B and scale words first,
+  // A row i once row i's last word is converted), and its scale pairs are
+  // converted.
+
+  // piece t (values 2t, 2t + 1) of the conversion of word w under half hi of
   // the scale pair sp, into the v8h x
   auto conv_piece = [&](v8h& x, uint32_t w, v2h sp, int hi, int t) {
     const _Float16 sv = hi ? sp.y : sp.x;
@@ -520,15 +509,14 @@ __global__ __launch_bounds__(256, 1) void gemm_nv4w(
 
   // Software pipeline: iteration s waits for stage s + 1 (this wave's loads
   // by count, everyone's at the barrier, which also ends every wave's LDS
-  // reads of stage s), loads stage s + 4 into the slot stage s vacated and,
-  // at the end of a scale group, group (s + 1) / 2 + 2 into the slot of the
-  // group just finished, then multiplies stage s from registers: k-steps
-  // 0..2, then k-step 3, in which each fragment's registers take its stage
-  // s + 1 read as soon as the fragment's last dword is converted (one set of
-  // fragment registers instead of two: 1.5 % faster on 2048 x 28672 x 8192
-  // and 4096 x 14336 x 4096, with fewer AGPR <-> VGPR moves).  Issued after
-  // stage s + 1 in the steady state: stages s + 2, s + 3 and the groups of
-  // iterations s - 3 .. s - 1.
+  // reads of stage s), then multiplies stage s from registers in four
+  // k-steps.  Between the first MFMAs of k-step 0 it loads stage s + 4 into
+  // the slot stage s vacated and, at the end of a scale group, group
+  // (s + 1) / 2 + 2 into the slot of the group just finished; in k-step 3
+  // each fragment's registers take its stage s + 1 words once its last word
+  // is converted (one set of fragment registers instead of two, with fewer
+  // AGPR <-> VGPR moves).  Issued after stage s + 1 in the steady state:
+  // stages s + 2, s + 3 and the groups of iterations s - 3 .. s - 1.
   issue_group(0);                              // -5
   issue_stage(0);                              // -4
   issue_stage(1);                              // -3
