@@ -122,6 +122,20 @@ def test_mxfp4_many_tiles(m, n, k, out_dtype):
     check_full("mxfp4", qx, qw, out_dtype)
 
 
+@pytest.mark.parametrize("m,n,k,out_dtype", [
+    (256, 60000, 512, "bf16"),     # 235 tiles of 256 columns: one round (224 would need two)
+    (300, 30000, 1024, "f32"),     # ragged m and n, 236 tiles of 256 columns
+])
+def test_nvfp4_wide_tiles(m, n, k, out_dtype):
+    # the NVFP4 large-m kernel with 256-column tiles (8 B fragments per wave
+    # and k-step), chosen where 224-column tiles would need another round
+    g = torch.Generator().manual_seed(12)
+    x = torch.randn((m, k), generator=g).to(torch.bfloat16)
+    w = (torch.randn((n, k), generator=g) * 0.02).to(torch.bfloat16)
+    qx, qw = quant_pair("nvfp4", x, w)
+    check_full("nvfp4", qx, qw, out_dtype)
+
+
 @pytest.mark.parametrize("fmt,m,n,k,out_dtype", [
     ("nvfp4", 512, 1024, 4096, "bf16"),   # 10 tiles: k in four slices of 1024
     ("nvfp4", 300, 700, 2048, "f32"),     # ragged, four slices of 512
