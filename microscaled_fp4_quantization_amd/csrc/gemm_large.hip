@@ -32,6 +32,8 @@
 // sharing a weight slab run on the same L2.
 #include <type_traits>
 
+#include <utility>
+
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -303,6 +305,17 @@ constexpr ConvRows<TI, TJ> conv_rows(bool last) {
   for (int u = 0; u < 4; ++u) r.p[TI - 1][r.n[TI - 1]++] = ConvPiece{2, 0, u};
   return r;
 }
+// f(std::integral_constant<int, 0>{}) .. f(std::integral_constant<int, N - 1>{}),
+// expanded at compile time whatever the loop unroller decides.
+template <class F, int... Is>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, Is...>) {
+  (f(std::integral_constant<int, Is>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
 template <int TI, int TJ>
 constexpr bool conv_rows_ok() {
   for (int l = 0; l < 2; ++l) {
@@ -545,7 +558,6 @@ __global__ __launch_bounds__(256, 1) void gemm_nv4w(
   auto kstep = [&](auto SS, int s) {
     constexpr int S = decltype(SS)::value;
     constexpr bool LAST = S == 3;
-    constexpr ConvRows<TI, TJ> R = conv_rows<TI, TJ>(LAST);
     constexpr int HI = S < 2 ? 0 : 1;                      // scale half of this k-step
     constexpr int HN = LAST ? 0 : (S + 1 < 2 ? 0 : 1);     // of the next one
     const int tn = s + 1;
@@ -566,8 +578,12 @@ __global__ __launch_bounds__(256, 1) void gemm_nv4w(
       for (int i = 0; i < TI; ++i) F.sa[i] = *reinterpret_cast<const uint32_t*>(sm + sao + 256 * i);
       F.a[0] = *reinterpret_cast<const u32x4*>(sm + ao);
     }
-#pragma unroll
-    for (int q = 0; q < NQ; ++q) {
+    constexpr ConvRows<TI, TJ> R = conv_rows<TI, TJ>(LAST);
+    // MFMA q and the conversion pieces placed after it; q is a constant once
+    // the slots are expanded: by the loop unroller for 8 x 7 blocks, by
+    // static_for for 8 x 8 (the unroller leaves those rolled, and the
+    // fragment registers then spill)
+    auto slot = [&](int q) {
       const int i = q / TJ, j = q % TJ;
       acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(hb[S & 1][j], ha[i & 1], acc[i][j], 0, 0, 0);
       if constexpr (S == 0) {
@@ -595,6 +611,12 @@ __global__ __launch_bounds__(256, 1) void gemm_nv4w(
         }
       }
       __builtin_amdgcn_sched_barrier(0);
+    };
+    if constexpr (TJ == 7) {
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) slot(q);
+    } else {
+      static_for<NQ>([&](auto Q) { slot(decltype(Q)::value); });
     }
     if constexpr (LAST) {
 #pragma unroll
