@@ -38,16 +38,42 @@ FLAGS = [
 ]
 
 
+# Scratch (bytes per lane) the main-loop kernels may use, from the compiler's
+# resource report.  The large GEMMs keep their operands in registers; when a
+# code change makes the compiler leave a k-step rolled, their fragment arrays
+# go to scratch (1.5-1.7 KiB per lane) and the kernel runs ~70x slower with
+# correct results, so the build refuses it.  (The MXFP4 kernel spills ~116
+# bytes in its epilogue only.)
+SCRATCH_LIMITS = {"gemm_nv4w": 32, "gemm_large_mx": 128}
+
+
 def hipcc():
     return os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "bin", "hipcc")
+
+
+def _check_scratch(src, report):
+    name = None
+    for line in report.splitlines():
+        if "Function Name:" in line:
+            name = line.split("Function Name:")[1].strip().split()[0]
+        elif "ScratchSize [bytes/lane]:" in line and name:
+            size = int(line.split("ScratchSize [bytes/lane]:")[1].split()[0])
+            for kernel, limit in SCRATCH_LIMITS.items():
+                if kernel in name and size > limit:
+                    raise RuntimeError("%s: %s uses %d bytes of scratch per lane (limit %d): "
+                                       "its main loop no longer stays in registers" % (src, name, size, limit))
 
 
 def _compile(src):
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
     cmd = [hipcc()] + FLAGS + ["-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    if src == "gemm_large.hip":
+        cmd.append("-Rpass-analysis=kernel-resource-usage")
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("hipcc failed on %s:\n%s\n%s" % (src, " ".join(cmd), r.stderr))
+    if src == "gemm_large.hip":
+        _check_scratch(src, r.stderr)
     return obj
 
 
