@@ -567,7 +567,10 @@ __global__ __launch_bounds__(kMseThreads) void quantize_mse_kernel(
         const float dv[8] = {p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          const double d = (double)v[8 * h + i] - (double)dv[i] * Sd;
+          // v - dv S rounded once: dv S is exact in fp64 (at most 2 + 24
+          // significant bits), so the fused form gives the same bits as the
+          // product followed by the subtraction
+          const double d = __builtin_fma(-(double)dv[i], Sd, (double)v[8 * h + i]);
           err = err + d * d;
         }
       }
