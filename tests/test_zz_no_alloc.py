@@ -83,3 +83,23 @@ def test_noalloc_matches_quantize():
     x = torch.randn((256, 1024), generator=g).to(torch.bfloat16).to(DEV)
     ts = torch.tensor([0.002], dtype=torch.float32, device=DEV)
     same(noalloc(x, fp4.NVFP4, fp4.TSCALE_GIVEN, ts), reference(x, fp4.NVFP4, fp4.TSCALE_GIVEN, ts))
+
+
+def test_noalloc_under_graph_capture():
+    # The caller it is for: fp4_quantize_noalloc captured into a HIP graph
+    # (compute mode, so the kernels use the library's scratch), replayed
+    # with new data in the captured input, fp4_quantize with a workspace run
+    # eagerly between the replays: every replay bit-identical to it.
+    g = torch.Generator(device="cpu").manual_seed(41)
+    x_static = torch.randn((1024, 4096), generator=g).to(torch.bfloat16).to(DEV)
+    noalloc(x_static, fp4.NVFP4, fp4.TSCALE_COMPUTE)   # scratch located before capture
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    note("fp4_quantize_noalloc captured into a graph")
+    with torch.cuda.graph(graph):
+        out = noalloc(x_static, fp4.NVFP4, fp4.TSCALE_COMPUTE)
+    for i, scale in enumerate((1.0, 500.0, 0.002)):
+        x_static.copy_((torch.randn((1024, 4096), generator=g) * scale).to(torch.bfloat16).to(DEV))
+        note("graph replay %d" % i)
+        graph.replay()
+        same(out, reference(x_static, fp4.NVFP4, fp4.TSCALE_COMPUTE))
