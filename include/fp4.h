@@ -206,9 +206,11 @@ fp4_status fp4_dequantize(fp4_format fmt, const uint8_t* codes,
                           fp4_dtype out_dtype, void* stream);
 
 /* Bytes of device workspace fp4_gemm needs for these sizes: nonzero only
- * where few output tiles would leave most of the GPU idle and the large-m
- * kernels split k over several workgroups per tile (the slices' fp32 partial
- * sums, added in a fixed order by a second pass). */
+ * where k is split over several workgroups per output tile (the slices'
+ * fp32 partial sums, added in a fixed order by a second pass): large m with
+ * few output tiles, which would leave most of the GPU idle, and NVFP4 with
+ * m <= 8 and a long k (k > 4096, a multiple of 2048) over few enough weight
+ * rows. */
 size_t fp4_gemm_workspace_size(fp4_format fmt, int64_t m, int64_t n, int64_t k);
 
 /*

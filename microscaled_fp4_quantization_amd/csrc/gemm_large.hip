@@ -984,6 +984,16 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(const float* __restri
 
 }  // namespace
 
+int64_t gemm_split_stride(int64_t m, int64_t n) { return split_stride(m, n); }
+
+hipError_t launch_split_reduce(const float* part, int nsplit, int64_t m, int64_t n, const float* at,
+                               const float* bt, void* c, int c_dtype, hipStream_t stream) {
+  const int64_t mn = m * n;
+  hipLaunchKernelGGL(split_reduce_kernel, dim3((unsigned)((mn + 1023) / 1024)), dim3(256), 0, stream, part,
+                     nsplit, mn, split_stride(m, n), at, bt, c, c_dtype);
+  return hipGetLastError();
+}
+
 bool gemm_large_supported(int fmt, int64_t m, int64_t n, int64_t k) {
   const int64_t lim = int64_t(1) << 31;     // 32-bit buffer offsets
   // 16-byte scale rows: k a multiple of 512 (MXFP4) or 256 (NVFP4)

@@ -412,7 +412,8 @@ __global__ __launch_bounds__(64 * kStrWaves) void gemm_nv_stream(
     const uint8_t* __restrict__ as, const float* __restrict__ at,
     const uint8_t* __restrict__ b, const uint8_t* __restrict__ bs,
     const float* __restrict__ bt, void* __restrict__ c, int c_dtype,
-    uint8_t* __restrict__ qcodes, uint8_t* __restrict__ qscales, float* __restrict__ qtscale) {
+    uint8_t* __restrict__ qcodes, uint8_t* __restrict__ qscales, float* __restrict__ qtscale,
+    float* __restrict__ part, int64_t pstride) {
   constexpr int NT = kStrTiles;
   __shared__ union {
     StreamLds<NSTEP> s;
@@ -428,7 +429,10 @@ __global__ __launch_bounds__(64 * kStrWaves) void gemm_nv_stream(
   const int64_t nbase = (int64_t)blockIdx.x * rows_per_wg;
   int64_t nlast = nbase + rows_per_wg - 1;            // last row of this share
   if (nlast > n - 1) nlast = n - 1;
-  const int ks0 = wave * (128 * NSTEP);               // first value of this wave's slice
+  // split k (part != nullptr, codes in): workgroup row blockIdx.y takes the
+  // 2048 NSTEP values from kc0 on, and its unscaled fp32 sums go to part
+  const int kc0 = (int)blockIdx.y * (kStrWaves * 128 * NSTEP);
+  const int ks0 = kc0 + wave * (128 * NSTEP);         // first value of this wave's slice
   const int64_t kbytes = k / 2, kblocks = k / 16;
 
   // ---- activation slice: lane -> row lane / 8, the 16 NSTEP values (NSTEP
@@ -644,7 +648,12 @@ __global__ __launch_bounds__(64 * kStrWaves) void gemm_nv_stream(
     const int64_t ni = nbase + lr;
     if (xr < m && lr < rows_per_wg && ni <= nlast) {
       const int64_t o = (int64_t)xr * n + ni;
-      if (c_dtype != kInF32 && lr + 3 < rows_per_wg && ni + 3 <= nlast && (o & 3) == 0) {
+      if (XM == kXCodes && part) {
+        float* pp = part + (int64_t)blockIdx.y * pstride + o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (lr + e < rows_per_wg && ni + e <= nlast) pp[e] = sum[e];
+      } else if (c_dtype != kInF32 && lr + 3 < rows_per_wg && ni + 3 <= nlast && (o & 3) == 0) {
         const __bf16 h[4] = {(__bf16)(sum[0] * scale), (__bf16)(sum[1] * scale), (__bf16)(sum[2] * scale),
                              (__bf16)(sum[3] * scale)};
         *reinterpret_cast<u32x2*>(reinterpret_cast<__bf16*>(c) + o) = *reinterpret_cast<const u32x2*>(h);
@@ -704,34 +713,80 @@ bool stream_shape(int64_t m, int64_t n, int64_t k) {
 }
 
 // An equal share of ceil(n / 256) weight rows per workgroup.
+// nsplit > 1 (codes in): k in nsplit chunks of 2048 NSTEP values, NSTEP = 2
+// when k is a multiple of 4096, the chunks' fp32 sums in part.
 template <int XM>
 hipError_t launch_stream(int m, int64_t n, int k, const uint8_t* a, const uint8_t* as, const float* at,
                          const uint8_t* b, const uint8_t* bs, const float* bt, void* c, int c_dtype,
-                         uint8_t* qcodes, uint8_t* qscales, float* qtscale, hipStream_t stream) {
-  const int rows = (int)((n + kStrGroups - 1) / kStrGroups);
-  const dim3 grid((unsigned)((n + rows - 1) / rows));
-  if (k == 4096)
+                         uint8_t* qcodes, uint8_t* qscales, float* qtscale, hipStream_t stream,
+                         int nsplit = 1, float* part = nullptr) {
+  // Split k: as many rows per workgroup (at most 64) as fill whole rounds of
+  // co-resident workgroups (two per CU with the 64 KiB of LDS of NSTEP = 1,
+  // one with the 88 KiB of NSTEP = 2); short-lived workgroups of a few rows
+  // would spend their time on the activation slice and the reduction, and a
+  // round begun by a few workgroups costs a whole workgroup lifetime.
+  const bool nstep2 = nsplit > 1 ? k % 4096 == 0 : k == 4096;
+  const int64_t slots = nstep2 ? kStrGroups : 2 * kStrGroups;
+  int rows = (int)((n + kStrGroups - 1) / kStrGroups);
+  if (nsplit > 1) {
+    const int64_t rmax = 16 * kStrTiles;
+    const int64_t rounds = (((n + rmax - 1) / rmax) * nsplit + slots - 1) / slots;
+    const int64_t per_chunk = rounds * slots / nsplit;     // >= ceil(n / rmax)
+    rows = (int)((n + per_chunk - 1) / per_chunk);
+  }
+  const dim3 grid((unsigned)((n + rows - 1) / rows), (unsigned)nsplit);
+  const int64_t pstride = nsplit > 1 ? gemm_split_stride(m, n) : 0;
+  if (nstep2)
     hipLaunchKernelGGL((gemm_nv_stream<2, XM>), grid, dim3(64 * kStrWaves), 0, stream, m, n, k, rows, a, as,
-                       at, b, bs, bt, c, c_dtype, qcodes, qscales, qtscale);
+                       at, b, bs, bt, c, c_dtype, qcodes, qscales, qtscale, part, pstride);
   else
     hipLaunchKernelGGL((gemm_nv_stream<1, XM>), grid, dim3(64 * kStrWaves), 0, stream, m, n, k, rows, a, as,
-                       at, b, bs, bt, c, c_dtype, qcodes, qscales, qtscale);
+                       at, b, bs, bt, c, c_dtype, qcodes, qscales, qtscale, part, pstride);
   return hipGetLastError();
 }
 
+// Chunks of the split-k stream kernel for NVFP4 codes with m <= 8 and k >
+// 4096 a multiple of 2048: chunks of 4096 values when k allows, else 2048,
+// as long as workgroups of at most 64 rows cover every chunk in one round of
+// co-resident workgroups (two per CU for chunks of 2048, one for 4096); 0
+// for any other shape.  Without the split, a long k and few rows (a down
+// projection, say) leave few workgroups, each walking all of k; with more
+// than one round, the unsplit kernels measured faster.
+int stream_split(int fmt, int64_t m, int64_t n, int64_t k) {
+  if (fmt != kFmtNV || m < 1 || m > 8 || n < 1 || k <= 4096 || k % 2048 != 0) return 0;
+  const bool nstep2 = k % 4096 == 0;
+  const int64_t s = nstep2 ? k / 4096 : k / 2048;
+  const int64_t slots = nstep2 ? kStrGroups : 2 * kStrGroups;
+  return (n + 16 * kStrTiles - 1) / (16 * kStrTiles) * s <= slots ? (int)s : 0;
+}
+
 }  // namespace
+
+size_t gemm_skinny_workspace_bytes(int fmt, int64_t m, int64_t n, int64_t k) {
+  const int s = stream_split(fmt, m, n, k);
+  return s > 1 ? (size_t)s * (size_t)gemm_split_stride(m, n) * sizeof(float) : 0;
+}
 
 hipError_t launch_gemm_skinny(int fmt, int64_t m, int64_t n, int64_t k,
                               const uint8_t* a_codes, const uint8_t* a_scales,
                               const float* a_tscale, const uint8_t* b_codes,
                               const uint8_t* b_scales, const float* b_tscale,
-                              void* c, int c_dtype, hipStream_t stream) {
+                              void* c, int c_dtype, void* workspace, hipStream_t stream) {
   const bool aligned16 = ((reinterpret_cast<uintptr_t>(b_scales) | reinterpret_cast<uintptr_t>(b_codes) |
                            reinterpret_cast<uintptr_t>(a_codes)) & 15) == 0 &&
                          (reinterpret_cast<uintptr_t>(a_scales) & 1) == 0;
   if (fmt == kFmtNV && stream_shape(m, n, k) && aligned16)
     return launch_stream<kXCodes>((int)m, n, (int)k, a_codes, a_scales, a_tscale, b_codes, b_scales,
                                   b_tscale, c, c_dtype, nullptr, nullptr, nullptr, stream);
+  const int nsplit = stream_split(fmt, m, n, k);
+  if (nsplit > 1 && aligned16) {
+    float* part = reinterpret_cast<float*>(workspace);
+    const hipError_t e = launch_stream<kXCodes>((int)m, n, (int)k, a_codes, a_scales, a_tscale, b_codes,
+                                                b_scales, b_tscale, c, c_dtype, nullptr, nullptr, nullptr,
+                                                stream, nsplit, part);
+    if (e != hipSuccess) return e;
+    return launch_split_reduce(part, nsplit, m, n, a_tscale, b_tscale, c, c_dtype, stream);
+  }
   if (fmt == kFmtNV && m <= 8 && k % kDecKC == 0 && aligned16) {
     hipLaunchKernelGGL((gemm_nv_decode<kDecKC, 4>), dim3((unsigned)((n + kDecRows - 1) / kDecRows)),
                        dim3(256), 0, stream, (int)m, n, (int)k, a_codes, a_scales, a_tscale, b_codes,

@@ -38,6 +38,12 @@ hipError_t launch_dequantize(int fmt, const uint8_t* codes,
                              hipStream_t stream);
 
 size_t gemm_workspace_bytes(int fmt, int64_t m, int64_t n, int64_t k);
+// Split-k GEMMs: elements between two slices of fp32 partial sums (m n
+// rounded up to a multiple of 4), and the pass that adds the nsplit slices
+// in order, applies at * bt (NVFP4; at == nullptr: 1) and stores C.
+int64_t gemm_split_stride(int64_t m, int64_t n);
+hipError_t launch_split_reduce(const float* part, int nsplit, int64_t m, int64_t n, const float* at,
+                               const float* bt, void* c, int c_dtype, hipStream_t stream);
 
 hipError_t launch_gemm(int fmt, int64_t m, int64_t n, int64_t k,
                        const uint8_t* a_codes, const uint8_t* a_scales,

@@ -44,6 +44,18 @@ def test_workspace_sizes():
     assert L.fp4_quantize_workspace_size(NV, fp4.TSCALE_GIVEN, 4096, 4096) == 0
     assert L.fp4_quantize_workspace_size(MX, fp4.TSCALE_COMPUTE, 4096, 4096) == 0
     assert L.fp4_gemm_workspace_size(NV, 16, 16, 256) >= 0
+    # NVFP4 decode shapes with k > 4096 split k into chunks of 4096 (k a
+    # multiple of 4096) or 2048, each chunk's fp32 sums m n (rounded up to a
+    # multiple of 4) floats, when one round of workgroups covers the chunks
+    assert L.fp4_gemm_workspace_size(NV, 8, 4096, 14336) == 7 * 8 * 4096 * 4
+    assert L.fp4_gemm_workspace_size(NV, 3, 777, 12288) == 3 * 2332 * 4
+    assert L.fp4_gemm_workspace_size(NV, 8, 8192, 6144) == 3 * 8 * 8192 * 4   # 384 of 512 slots
+    assert L.fp4_gemm_workspace_size(NV, 8, 14336, 4096) == 0      # one chunk: no split
+    assert L.fp4_gemm_workspace_size(NV, 8, 14336, 8192) == 0      # 448 workgroups for 256 slots
+    assert L.fp4_gemm_workspace_size(NV, 8, 16384, 6144) == 0      # 768 for 512
+    assert L.fp4_gemm_workspace_size(NV, 9, 4096, 14336) == 0      # m > 8
+    assert L.fp4_gemm_workspace_size(NV, 8, 4096, 5120) == 0       # k not a multiple of 2048
+    assert L.fp4_gemm_workspace_size(MX, 8, 4096, 14336) == 0
 
 
 def _q(fn, fmt=NV, x=FAKE, dt=fp4.BF16, rows=4, k=64, codes=FAKE, scales=FAKE,

@@ -123,6 +123,23 @@ def test_mxfp4_many_tiles(m, n, k, out_dtype):
 
 
 @pytest.mark.parametrize("m,n,k,out_dtype", [
+    (8, 4096, 14336, "bf16"),      # a down projection: 7 chunks of 2048
+    (1, 2000, 8192, "f32"),        # 2 chunks of 4096
+    (6, 8192, 6144, "bf16"),       # 3 chunks of 2048, 384 workgroups
+    (3, 777, 12288, "f32"),        # 3 chunks of 4096, ragged n
+])
+def test_nvfp4_decode_split_k(m, n, k, out_dtype):
+    # the NVFP4 decode kernel with k split over workgroup rows (fp32 partial
+    # sums in the workspace, added by the reduction pass)
+    assert fq.fp4.lib().fp4_gemm_workspace_size(fq.fp4.NVFP4, m, n, k) > 0
+    g = torch.Generator().manual_seed(12)
+    x = torch.randn((m, k), generator=g).to(torch.bfloat16)
+    w = (torch.randn((n, k), generator=g) * 0.02).to(torch.bfloat16)
+    qx, qw = quant_pair("nvfp4", x, w)
+    check_full("nvfp4", qx, qw, out_dtype)
+
+
+@pytest.mark.parametrize("m,n,k,out_dtype", [
     (256, 60000, 512, "bf16"),     # 235 tiles of 256 columns: one round (224 would need two)
     (300, 30000, 1024, "f32"),     # ragged m and n, 236 tiles of 256 columns
 ])
@@ -256,6 +273,7 @@ def test_rotated_full_size():
     ("nvfp4", 8, 16384, 4096, torch.bfloat16),   # largest n of the one-launch path
     ("nvfp4", 7, 1025, 2048, torch.bfloat16),    # 3 rows per share, last share partial
     ("nvfp4", 16, 64, 256, torch.bfloat16),      # m > 8: quantize + GEMM calls
+    ("nvfp4", 8, 4096, 14336, torch.bfloat16),   # long k: quantize + split-k GEMM
     ("nvfp4", 3, 50, 96, torch.bfloat16),
     ("nvfp4", 8, 200, 4096, torch.float32),      # not bf16: two calls
     ("mxfp4", 8, 100, 4096, torch.bfloat16),
