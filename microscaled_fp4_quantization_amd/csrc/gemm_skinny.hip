@@ -371,11 +371,11 @@ constexpr int kStrWaves = 16;
 constexpr int kStrTiles = 4;                          // 64 rows at most per workgroup
 constexpr int kStrGroups = 256;                       // one workgroup per CU
 
-template <int NSTEP>
+template <int NSTEP, int XH>
 struct StreamLds {
-  // dequantized activation slices, rows padded so that the 8 rows of a read
-  // fall on distinct banks
-  _Float16 x[kStrWaves][8][128 * NSTEP + 8];
+  // dequantized activation slices (8 XH rows), rows padded so that the 8
+  // rows of a read fall on distinct banks
+  _Float16 x[kStrWaves][8 * XH][128 * NSTEP + 8];
   // weight scale slices, rows padded: the 16 rows of a read hit distinct banks
   uint8_t w[kStrWaves][16 * kStrTiles][8 * NSTEP + 4];
 };
@@ -406,7 +406,9 @@ struct StreamLds {
 // in.
 constexpr int kXCodes = 0, kXQuant = 1, kXRaw = 2;
 
-template <int NSTEP, int XM>
+// XH = 2 (codes in only): up to 16 activation rows, all 16 columns of the
+// MFMA tile (XH = 1: 8 rows, the other 8 columns repeat them).
+template <int NSTEP, int XM, int XH>
 __global__ __launch_bounds__(64 * kStrWaves) void gemm_nv_stream(
     int m, int64_t n, int k, int rows_per_wg, const uint8_t* __restrict__ a,
     const uint8_t* __restrict__ as, const float* __restrict__ at,
@@ -416,11 +418,12 @@ __global__ __launch_bounds__(64 * kStrWaves) void gemm_nv_stream(
     float* __restrict__ part, int64_t pstride) {
   constexpr int NT = kStrTiles;
   __shared__ union {
-    StreamLds<NSTEP> s;
+    StreamLds<NSTEP, XH> s;
     v4f part[kStrWaves][NT][64];                      // the partial tiles, at the end
   } LU;
   __shared__ float red[kStrWaves];
-  StreamLds<NSTEP>& L = LU.s;
+  StreamLds<NSTEP, XH>& L = LU.s;
+  static_assert(XH == 1 || XM == kXCodes, "16 activation rows: codes in only");
   constexpr bool QX = XM != kXCodes;                  // bf16 X loaded here
   constexpr bool GMAX = XM == kXQuant;                // max |X| over the tensor first
   const int tid = threadIdx.x, lane = tid & 63;
@@ -442,24 +445,29 @@ __global__ __launch_bounds__(64 * kStrWaves) void gemm_nv_stream(
   const int64_t xsrc = live ? xrow : m - 1;
   const int xv0 = ks0 + 16 * NSTEP * xc;
   u32x4 xb[QX ? 2 * NSTEP : 1];                        // bf16 X, 8 values each
-  uint32_t xq[2 * NSTEP];                             // codes, 8 per dword (kXCodes)
-  uint32_t xs = 0;                                    // NSTEP scale bytes (kXCodes)
+  uint32_t xq[XH][2 * NSTEP];                         // codes, 8 per dword (kXCodes)
+  uint32_t xs[XH];                                    // NSTEP scale bytes (kXCodes)
   if (QX) {
 #pragma unroll
     for (int i = 0; i < 2 * NSTEP; ++i)
       xb[i] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(a) + xsrc * k + xv0 + 8 * i);
   } else {
-    const uint8_t* src = a + xsrc * kbytes + xv0 / 2;
-    if (NSTEP == 1) {
-      const u32x2 h = *reinterpret_cast<const u32x2*>(src);
-      xq[0] = h.x; xq[1] = h.y;
-    } else {
-      const u32x4 h = *reinterpret_cast<const u32x4*>(src);
+    // row 8 hf + lane / 8 of each group of 8 rows
 #pragma unroll
-      for (int j = 0; j < 4; ++j) xq[j] = h[j];
+    for (int hf = 0; hf < XH; ++hf) {
+      const int64_t xsh = 8 * hf + xrow < m ? 8 * hf + xrow : m - 1;
+      const uint8_t* src = a + xsh * kbytes + xv0 / 2;
+      if (NSTEP == 1) {
+        const u32x2 h = *reinterpret_cast<const u32x2*>(src);
+        xq[hf][0] = h.x; xq[hf][1] = h.y;
+      } else {
+        const u32x4 h = *reinterpret_cast<const u32x4*>(src);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) xq[hf][j] = h[j];
+      }
+      const uint8_t* ss = as + xsh * kblocks + xv0 / 16;
+      xs[hf] = NSTEP == 2 ? (uint32_t)*reinterpret_cast<const uint16_t*>(ss) : (uint32_t)*ss;
     }
-    const uint8_t* ss = as + xsrc * kblocks + xv0 / 16;
-    xs = NSTEP == 2 ? (uint32_t)*reinterpret_cast<const uint16_t*>(ss) : (uint32_t)*ss;
   }
 
   // ---- weights: scale slices (lane p loads row p's 8 NSTEP bytes) and codes ----
@@ -580,16 +588,21 @@ __global__ __launch_bounds__(64 * kStrWaves) void gemm_nv_stream(
       if (XM == kXQuant && blockIdx.x == 0 && tid == 0) *qtscale = s_t;
     }
   } else {
-    // the E4M3 bytes to f16 (sign and NaN included)
-    const v2h s01 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(xs, 1.0f, false);
 #pragma unroll
-    for (int bl = 0; bl < NSTEP; ++bl) {
-      const _Float16 s = bl == 0 ? s01.x : s01.y;
+    for (int hf = 0; hf < XH; ++hf) {
+      _Float16* xd = &L.x[wave][8 * hf + xrow][16 * NSTEP * xc];
+      const bool lv = 8 * hf + xrow < m;
+      // the E4M3 bytes to f16 (sign and NaN included)
+      const v2h s01 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(xs[hf], 1.0f, false);
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        v8h f = dequant8(xq[2 * bl + h], s);
-        if (!live) f = (v8h){0, 0, 0, 0, 0, 0, 0, 0};
-        *reinterpret_cast<v8h*>(xdst + 16 * bl + 8 * h) = f;
+      for (int bl = 0; bl < NSTEP; ++bl) {
+        const _Float16 s = bl == 0 ? s01.x : s01.y;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          v8h f = dequant8(xq[hf][2 * bl + h], s);
+          if (!lv) f = (v8h){0, 0, 0, 0, 0, 0, 0, 0};
+          *reinterpret_cast<v8h*>(xd + 16 * bl + 8 * h) = f;
+        }
       }
     }
   }
@@ -600,7 +613,8 @@ __global__ __launch_bounds__(64 * kStrWaves) void gemm_nv_stream(
   }
   // Only this wave reads these regions: LDS accesses of one wave complete in
   // order, so no barrier is needed.
-  const _Float16* xf = &L.x[wave][r & 7][32 * g];    // rows >= m are zero; r >= 8 repeats r - 8
+  // rows >= m are zero; with XH = 1, r >= 8 repeats r - 8
+  const _Float16* xf = &L.x[wave][XH == 2 ? r : (r & 7)][32 * g];
 
   v4f acc[NT];
 #pragma unroll
@@ -715,7 +729,7 @@ bool stream_shape(int64_t m, int64_t n, int64_t k) {
 // An equal share of ceil(n / 256) weight rows per workgroup.
 // nsplit > 1 (codes in): k in nsplit chunks of 2048 NSTEP values, NSTEP = 2
 // when k is a multiple of 4096, the chunks' fp32 sums in part.
-template <int XM>
+template <int XM, int XH = 1>
 hipError_t launch_stream(int m, int64_t n, int k, const uint8_t* a, const uint8_t* as, const float* at,
                          const uint8_t* b, const uint8_t* bs, const float* bt, void* c, int c_dtype,
                          uint8_t* qcodes, uint8_t* qscales, float* qtscale, hipStream_t stream,
@@ -737,10 +751,10 @@ hipError_t launch_stream(int m, int64_t n, int k, const uint8_t* a, const uint8_
   const dim3 grid((unsigned)((n + rows - 1) / rows), (unsigned)nsplit);
   const int64_t pstride = nsplit > 1 ? gemm_split_stride(m, n) : 0;
   if (nstep2)
-    hipLaunchKernelGGL((gemm_nv_stream<2, XM>), grid, dim3(64 * kStrWaves), 0, stream, m, n, k, rows, a, as,
+    hipLaunchKernelGGL((gemm_nv_stream<2, XM, XH>), grid, dim3(64 * kStrWaves), 0, stream, m, n, k, rows, a, as,
                        at, b, bs, bt, c, c_dtype, qcodes, qscales, qtscale, part, pstride);
   else
-    hipLaunchKernelGGL((gemm_nv_stream<1, XM>), grid, dim3(64 * kStrWaves), 0, stream, m, n, k, rows, a, as,
+    hipLaunchKernelGGL((gemm_nv_stream<1, XM, XH>), grid, dim3(64 * kStrWaves), 0, stream, m, n, k, rows, a, as,
                        at, b, bs, bt, c, c_dtype, qcodes, qscales, qtscale, part, pstride);
   return hipGetLastError();
 }
@@ -778,6 +792,9 @@ hipError_t launch_gemm_skinny(int fmt, int64_t m, int64_t n, int64_t k,
   if (fmt == kFmtNV && stream_shape(m, n, k) && aligned16)
     return launch_stream<kXCodes>((int)m, n, (int)k, a_codes, a_scales, a_tscale, b_codes, b_scales,
                                   b_tscale, c, c_dtype, nullptr, nullptr, nullptr, stream);
+  if (fmt == kFmtNV && m > 8 && m <= 16 && stream_shape(8, n, k) && aligned16)
+    return launch_stream<kXCodes, 2>((int)m, n, (int)k, a_codes, a_scales, a_tscale, b_codes, b_scales,
+                                     b_tscale, c, c_dtype, nullptr, nullptr, nullptr, stream);
   const int nsplit = stream_split(fmt, m, n, k);
   if (nsplit > 1 && aligned16) {
     float* part = reinterpret_cast<float*>(workspace);

@@ -123,6 +123,22 @@ def test_mxfp4_many_tiles(m, n, k, out_dtype):
 
 
 @pytest.mark.parametrize("m,n,k,out_dtype", [
+    (16, 14336, 4096, "bf16"),     # all 16 columns of the MFMA tile
+    (9, 1000, 2048, "f32"),        # one row past 8
+    (12, 16384, 2048, "bf16"),     # the largest n
+    (16, 333, 4096, "f32"),        # ragged shares
+])
+def test_nvfp4_decode_16_rows(m, n, k, out_dtype):
+    # the NVFP4 decode stream kernel with 9 to 16 activation rows
+    g = torch.Generator().manual_seed(13)
+    x = torch.randn((m, k), generator=g).to(torch.bfloat16)
+    x[m - 1] *= 100.0                                # the last row on its own scale
+    w = (torch.randn((n, k), generator=g) * 0.02).to(torch.bfloat16)
+    qx, qw = quant_pair("nvfp4", x, w)
+    check_full("nvfp4", qx, qw, out_dtype)
+
+
+@pytest.mark.parametrize("m,n,k,out_dtype", [
     (8, 4096, 14336, "bf16"),      # a down projection: 7 chunks of 2048
     (1, 2000, 8192, "f32"),        # 2 chunks of 4096
     (6, 8192, 6144, "bf16"),       # 3 chunks of 2048, 384 workgroups
@@ -274,6 +290,7 @@ def test_rotated_full_size():
     ("nvfp4", 7, 1025, 2048, torch.bfloat16),    # 3 rows per share, last share partial
     ("nvfp4", 16, 64, 256, torch.bfloat16),      # m > 8: quantize + GEMM calls
     ("nvfp4", 8, 4096, 14336, torch.bfloat16),   # long k: quantize + split-k GEMM
+    ("nvfp4", 16, 2000, 4096, torch.bfloat16),   # 16 rows: quantize + stream GEMM
     ("nvfp4", 3, 50, 96, torch.bfloat16),
     ("nvfp4", 8, 200, 4096, torch.float32),      # not bf16: two calls
     ("mxfp4", 8, 100, 4096, torch.bfloat16),
