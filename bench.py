@@ -107,13 +107,13 @@ def parse():
 # sources its code comes from: a recorded HBM traffic figure is used only
 # while these files are unchanged.
 DOMINANT = {
-    "decode": ("gemm_nv_stream<2, 1>", ["gemm_skinny.hip"]),
+    "decode": ("gemm_nv_stream<2, 1, 1>", ["gemm_skinny.hip"]),
     "prefill": ("gemm_nv4w<", ["gemm_large.hip"]),
     "rotated_nv": ("gemm_nv4w<", ["gemm_large.hip"]),
     "rotated_mx": ("gemm_large_mx<", ["gemm_large.hip"]),
     "kv": ("blocks_kernel<0, 1, 0, false>", ["quantize.hip", "device_common.hpp"]),
     "mse": ("quantize_mse_kernel<1, true>", ["quantize.hip", "device_common.hpp"]),
-    "w4a16": ("gemm_nv_stream<2, 2>", ["gemm_skinny.hip"]),
+    "w4a16": ("gemm_nv_stream<2, 2, 1>", ["gemm_skinny.hip"]),
     "attention": ("attn_decode_kernel<0, 1>", ["attention.hip", "device_common.hpp"]),
     "gptq": ("gemm_f64_kernel", ["gptq.hip", "quantize.hip", "device_common.hpp"]),
 }
