@@ -176,7 +176,10 @@ def summarize_pmc(workload, fetch_dir, write_dir, copy_bytes):
 
 
 class Lib:
-    """Direct ctypes calls with pre-built arguments (low host overhead)."""
+    """Direct ctypes calls with pre-built arguments (low host overhead).  Each
+    call holds the tensors its pointers come from (the `keep` default), so
+    that none is freed and its memory handed out again while the call is
+    still in use."""
 
     def __init__(self, torch, fq):
         self.torch = torch
@@ -198,7 +201,7 @@ class Lib:
         need = self.L.fp4_quantize_workspace_size(fmt, mode, x.shape[0], x.shape[1])
         args = (fmt, self.p(x), dt, x.shape[0], x.shape[1], self.p(codes), self.p(scales),
                 self.p(ts), mode, self.p(ws) if need else None, need, self.stream)
-        return lambda: self.check(fn(*args), "quantize")
+        return lambda keep=(x, codes, scales, ts, ws): self.check(fn(*args), "quantize")
 
     def gemm_call(self, fmt, a, b, c, c_dtype):
         (ac, asc, at), (bc, bsc, bt) = a, b
@@ -208,7 +211,7 @@ class Lib:
         args = (fmt, m, n, k, self.p(ac), self.p(asc), self.p(at), self.p(bc), self.p(bsc),
                 self.p(bt), self.p(c), c_dtype, self.p(ws), need, self.stream)
         fn = self.L.fp4_gemm
-        return lambda: self.check(fn(*args), "gemm")
+        return lambda keep=(a, b, c, ws): self.check(fn(*args), "gemm")
 
     def quantize_gemm_call(self, fmt, x, a, b, c, c_dtype, ws):
         from microscaled_fp4_quantization_amd import fp4
@@ -220,7 +223,7 @@ class Lib:
                 self.p(bsc), self.p(bt), self.p(c), c_dtype, self.p(ws) if need else None, need,
                 self.stream)
         fn = self.L.fp4_quantize_gemm
-        return lambda: self.check(fn(*args), "quantize_gemm")
+        return lambda keep=(x, a, b, c, ws): self.check(fn(*args), "quantize_gemm")
 
     def quantize_mse_call(self, x, codes, scales, ts, mode, ws):
         from microscaled_fp4_quantization_amd import fp4
@@ -229,17 +232,19 @@ class Lib:
         args = (self.p(x), dt, x.shape[0], x.shape[1], self.p(codes), self.p(scales), self.p(ts), mode,
                 self.p(ws) if need else None, need, self.stream)
         fn = self.L.fp4_quantize_mse
-        return lambda: self.check(fn(*args), "quantize_mse")
+        return lambda keep=(x, codes, scales, ts, ws): self.check(fn(*args), "quantize_mse")
 
     def w4a16_call(self, fmt, x, b, c, c_dtype):
         from microscaled_fp4_quantization_amd import fp4
         bc, bsc, bt = b
         m, k, n = x.shape[0], x.shape[1], bc.shape[0]
         dt = {self.torch.bfloat16: fp4.BF16, self.torch.float32: fp4.F32, self.torch.float16: fp4.F16}[x.dtype]
+        need = self.L.fp4_gemm_w4a16_workspace_size(fmt, m, n, k)
+        ws = self.torch.empty(need, dtype=self.torch.uint8, device=x.device) if need else None
         args = (fmt, self.p(x), dt, m, n, k, self.p(bc), self.p(bsc), self.p(bt), self.p(c), c_dtype,
-                self.stream)
+                self.p(ws), need, self.stream)
         fn = self.L.fp4_gemm_w4a16
-        return lambda: self.check(fn(*args), "gemm_w4a16")
+        return lambda keep=(x, b, c, ws): self.check(fn(*args), "gemm_w4a16")
 
     def kv_append_call(self, fmt, x, cache, positions, ts):
         from microscaled_fp4_quantization_amd import fp4
@@ -249,7 +254,7 @@ class Lib:
         args = (fmt, self.p(x), dt, B, H, tn, d, self.p(positions), self.p(codes), self.p(scales),
                 self.p(ts), codes.shape[2], self.stream)
         fn = self.L.fp4_kv_append
-        return lambda: self.check(fn(*args), "kv_append")
+        return lambda keep=(x, cache, positions, ts): self.check(fn(*args), "kv_append")
 
     def attention_call(self, fmt, q, kcache, kts, vcache, vts, lens, scale, out, out_dtype, ws):
         from microscaled_fp4_quantization_amd import fp4
@@ -260,7 +265,7 @@ class Lib:
                 self.p(vc), self.p(vs), self.p(vts), kc.shape[2], self.p(lens), ctypes.c_float(scale),
                 self.p(out), out_dtype, self.p(ws), ws.numel(), self.stream)
         fn = self.L.fp4_attention_decode
-        return lambda: self.check(fn(*args), "attention_decode")
+        return lambda keep=(q, kcache, kts, vcache, vts, lens, out, ws): self.check(fn(*args), "attention_decode")
 
     def gptq_call(self, fmt, w, x, codes, scales, ts, ws):
         from microscaled_fp4_quantization_amd import fp4
@@ -270,13 +275,13 @@ class Lib:
                 ctypes.c_double(0.01), 1, self.p(codes), self.p(scales), self.p(ts), self.p(ws),
                 ws.numel(), self.stream)
         fn = self.L.fp4_gptq_quantize
-        return lambda: self.check(fn(*args), "gptq_quantize")
+        return lambda keep=(w, x, codes, scales, ts, ws): self.check(fn(*args), "gptq_quantize")
 
     def dequant_call(self, fmt, codes, scales, ts, out, out_dtype):
         rows, k = codes.shape[0], codes.shape[1] * 2
         args = (fmt, self.p(codes), self.p(scales), self.p(ts), rows, k, self.p(out), out_dtype, self.stream)
         fn = self.L.fp4_dequantize
-        return lambda: self.check(fn(*args), "dequantize")
+        return lambda keep=(codes, scales, ts, out): self.check(fn(*args), "dequantize")
 
 
 def gemm_bytes(m, n, k, fmt, out_bytes):

@@ -254,15 +254,20 @@ fp4_status fp4_gemm(fp4_format fmt, int64_t m, int64_t n, int64_t k,
  *   b_*           weights [n, k] as fp4_gemm's B; b_tscale NVFP4 only.
  *   c, c_dtype    out [m, n], FP4_F32 or FP4_BF16 (FP4_F16 / FP4_E4M3:
  *                 FP4_EUNSUPPORTED).
+ *   workspace     at least fp4_gemm_w4a16_workspace_size() bytes, 16-byte
+ *                 aligned (may be NULL when that size is 0); contents on
+ *                 entry do not matter; calls that overlap must not share one.
  *   Numerics: the weights are widened exactly (v * E4M3 scale in fp16 or
- *   fp32, v * 2^e); NVFP4 with bf16 X, k in {2048, 4096} and 16-byte aligned
- *   x / codes / scales takes the streaming path: each row of X is cut into
- *   16 pieces of k / 16 values, each piece scaled by the power of two that
- *   brings its max |x| into [1, 2) and rounded to fp16 (exact for every value
- *   above 2^-15 of that max), the products accumulate in fp32 on the matrix
- *   cores and each piece's partial sums are scaled back before they are
- *   added; other shapes sum fp32 products.  Tolerance
- *   against the float64 reference: relative Frobenius error <= 1e-3.
+ *   fp32, v * 2^e); NVFP4 with bf16 X, k = 2048, 4096 or a larger multiple
+ *   of 2048 and 16-byte aligned x / codes / scales takes the streaming path:
+ *   each row of X is cut into pieces of 128 or 256 values, each piece scaled
+ *   by the power of two that brings its max |x| into [1, 2) and rounded to
+ *   fp16 (exact for every value above 2^-15 of that max), the products
+ *   accumulate in fp32 on the matrix cores and each piece's partial sums
+ *   are scaled back before they are added (for k > 4096 the sums of each
+ *   chunk of 2048 or 4096 values go through the workspace); other shapes
+ *   sum fp32 products.  Tolerance against the float64 reference: relative
+ *   Frobenius error <= 1e-3.
  *   m = 0 or n = 0 enqueues nothing.  Returns FP4_OK, FP4_EINVAL,
  *   FP4_EUNSUPPORTED or FP4_EHIP.
  */
@@ -270,7 +275,12 @@ fp4_status fp4_gemm_w4a16(fp4_format fmt, const void* x, fp4_dtype x_dtype,
                           int64_t m, int64_t n, int64_t k,
                           const uint8_t* b_codes, const uint8_t* b_scales,
                           const float* b_tscale, void* c, fp4_dtype c_dtype,
-                          void* stream);
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of device workspace fp4_gemm_w4a16 needs for these sizes: nonzero
+ * only for NVFP4 with k > 4096 a multiple of 2048 (the fp32 sums of each
+ * chunk of k for up to 8 rows of X at a time). */
+size_t fp4_gemm_w4a16_workspace_size(fp4_format fmt, int64_t m, int64_t n, int64_t k);
 
 /* Bytes of device workspace fp4_quantize_gemm needs for these sizes. */
 size_t fp4_quantize_gemm_workspace_size(fp4_format fmt, int64_t m, int64_t n,

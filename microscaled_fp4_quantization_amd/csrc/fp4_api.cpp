@@ -196,9 +196,15 @@ fp4_status fp4_gemm(fp4_format fmt, int64_t m, int64_t n, int64_t k,
                               workspace, static_cast<hipStream_t>(stream)));
 }
 
+size_t fp4_gemm_w4a16_workspace_size(fp4_format fmt, int64_t m, int64_t n, int64_t k) {
+  if (!valid_format(fmt)) return 0;
+  return gemm_w4a16_workspace_bytes((int)fmt, m, n, k);
+}
+
 fp4_status fp4_gemm_w4a16(fp4_format fmt, const void* x, fp4_dtype x_dtype, int64_t m, int64_t n,
                           int64_t k, const uint8_t* b_codes, const uint8_t* b_scales,
-                          const float* b_tscale, void* c, fp4_dtype c_dtype, void* stream) {
+                          const float* b_tscale, void* c, fp4_dtype c_dtype, void* workspace,
+                          size_t workspace_bytes, void* stream) {
   if (!valid_format(fmt)) return FP4_EINVAL;
   if (x_dtype != FP4_F32 && x_dtype != FP4_BF16 && x_dtype != FP4_F16) return FP4_EINVAL;
   if (c_dtype != FP4_F32 && c_dtype != FP4_BF16) {
@@ -216,8 +222,11 @@ fp4_status fp4_gemm_w4a16(fp4_format fmt, const void* x, fp4_dtype x_dtype, int6
   } else if (b_tscale) {
     return FP4_EINVAL;
   }
+  const size_t need = gemm_w4a16_workspace_bytes((int)fmt, m, n, k);
+  if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 16))) return FP4_EINVAL;
   return from_hip(launch_gemm_w4a16((int)fmt, m, n, k, x, (int)x_dtype, b_codes, b_scales,
-                                    b_tscale, c, (int)c_dtype, static_cast<hipStream_t>(stream)));
+                                    b_tscale, c, (int)c_dtype, workspace,
+                                    static_cast<hipStream_t>(stream)));
 }
 
 size_t fp4_quantize_gemm_workspace_size(fp4_format fmt, int64_t m, int64_t n, int64_t k) {

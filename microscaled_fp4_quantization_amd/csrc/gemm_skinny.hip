@@ -432,8 +432,8 @@ __global__ __launch_bounds__(64 * kStrWaves) void gemm_nv_stream(
   const int64_t nbase = (int64_t)blockIdx.x * rows_per_wg;
   int64_t nlast = nbase + rows_per_wg - 1;            // last row of this share
   if (nlast > n - 1) nlast = n - 1;
-  // split k (part != nullptr, codes in): workgroup row blockIdx.y takes the
-  // 2048 NSTEP values from kc0 on, and its unscaled fp32 sums go to part
+  // split k (part != nullptr; codes in or W4A16): workgroup row blockIdx.y
+  // takes the 2048 NSTEP values from kc0 on, and its fp32 sums go to part
   const int kc0 = (int)blockIdx.y * (kStrWaves * 128 * NSTEP);
   const int ks0 = kc0 + wave * (128 * NSTEP);         // first value of this wave's slice
   const int64_t kbytes = k / 2, kblocks = k / 16;
@@ -662,11 +662,13 @@ __global__ __launch_bounds__(64 * kStrWaves) void gemm_nv_stream(
     const int64_t ni = nbase + lr;
     if (xr < m && lr < rows_per_wg && ni <= nlast) {
       const int64_t o = (int64_t)xr * n + ni;
-      if (XM == kXCodes && part) {
+      if (part) {
+        // codes in: unscaled (the reduction applies the tensor scales);
+        // W4A16: times the weights' tensor scale
         float* pp = part + (int64_t)blockIdx.y * pstride + o;
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          if (lr + e < rows_per_wg && ni + e <= nlast) pp[e] = sum[e];
+          if (lr + e < rows_per_wg && ni + e <= nlast) pp[e] = XM == kXRaw ? sum[e] * scale : sum[e];
       } else if (c_dtype != kInF32 && lr + 3 < rows_per_wg && ni + 3 <= nlast && (o & 3) == 0) {
         const __bf16 h[4] = {(__bf16)(sum[0] * scale), (__bf16)(sum[1] * scale), (__bf16)(sum[2] * scale),
                              (__bf16)(sum[3] * scale)};
@@ -742,7 +744,7 @@ hipError_t launch_stream(int m, int64_t n, int k, const uint8_t* a, const uint8_
   const bool nstep2 = nsplit > 1 ? k % 4096 == 0 : k == 4096;
   const int64_t slots = nstep2 ? kStrGroups : 2 * kStrGroups;
   int rows = (int)((n + kStrGroups - 1) / kStrGroups);
-  if (nsplit > 1) {
+  if (nsplit > 1 || n > 16 * kStrTiles * kStrGroups) {
     const int64_t rmax = 16 * kStrTiles;
     const int64_t rounds = (((n + rmax - 1) / rmax) * nsplit + slots - 1) / slots;
     const int64_t per_chunk = rounds * slots / nsplit;     // >= ceil(n / rmax)
@@ -838,20 +840,48 @@ bool launch_quantize_gemm_decode(int64_t m, int64_t n, int64_t k, const void* x,
   return true;
 }
 
+namespace {
+
+// W4A16 chunks of k on the stream kernel for NVFP4 weights: 1 for k = 2048
+// or 4096, the chunks of 4096 (k a multiple of 4096) or 2048 for a longer k
+// (at most 64), 0 for any other k.  Any n: past 16384 rows the workgroups
+// take up to 64 rows in whole rounds.
+int w4a16_chunks(int fmt, int64_t n, int64_t k) {
+  if (fmt != kFmtNV || n < 1 || k % 2048 != 0) return 0;
+  if (k <= 4096) return 1;
+  const int64_t s = k % 4096 == 0 ? k / 4096 : k / 2048;
+  return s <= 64 ? (int)s : 0;
+}
+
+}  // namespace
+
+size_t gemm_w4a16_workspace_bytes(int fmt, int64_t m, int64_t n, int64_t k) {
+  const int s = w4a16_chunks(fmt, n, k);
+  const int64_t mc = m < 8 ? m : 8;
+  return s > 1 && mc > 0 ? (size_t)s * (size_t)gemm_split_stride(mc, n) * sizeof(float) : 0;
+}
+
 hipError_t launch_gemm_w4a16(int fmt, int64_t m, int64_t n, int64_t k, const void* x, int x_dtype,
                              const uint8_t* b_codes, const uint8_t* b_scales,
-                             const float* b_tscale, void* c, int c_dtype, hipStream_t stream) {
+                             const float* b_tscale, void* c, int c_dtype, void* workspace,
+                             hipStream_t stream) {
   const bool aligned = ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(b_codes) |
                          reinterpret_cast<uintptr_t>(b_scales)) & 15) == 0;
-  if (fmt == kFmtNV && x_dtype == kInBF16 && stream_shape(1, n, k) && aligned) {
-    // streaming kernel, 8 activation rows per launch
+  const int nsplit = x_dtype == kInBF16 ? w4a16_chunks(fmt, n, k) : 0;
+  if (nsplit > 0 && aligned) {
+    // streaming kernel, 8 activation rows per launch; a split k's chunk sums
+    // (times the tensor scale) added by the reduction pass, which reuses
+    // the workspace for the next 8 rows in stream order
+    float* part = nsplit > 1 ? reinterpret_cast<float*>(workspace) : nullptr;
     const int64_t osz = c_dtype == kInF32 ? 4 : 2;
     for (int64_t i0 = 0; i0 < m; i0 += 8) {
       const int mc = (int)(m - i0 < 8 ? m - i0 : 8);
       const uint8_t* xa = reinterpret_cast<const uint8_t*>(x) + i0 * k * 2;
       void* ca = reinterpret_cast<char*>(c) + i0 * n * osz;
-      const hipError_t e = launch_stream<kXRaw>(mc, n, (int)k, xa, nullptr, nullptr, b_codes, b_scales,
-                                                b_tscale, ca, c_dtype, nullptr, nullptr, nullptr, stream);
+      hipError_t e = launch_stream<kXRaw>(mc, n, (int)k, xa, nullptr, nullptr, b_codes, b_scales, b_tscale, ca,
+                                          c_dtype, nullptr, nullptr, nullptr, stream, nsplit, part);
+      if (e == hipSuccess && nsplit > 1)
+        e = launch_split_reduce(part, nsplit, mc, n, nullptr, nullptr, ca, c_dtype, stream);
       if (e != hipSuccess) return e;
     }
     return hipSuccess;

@@ -61,9 +61,11 @@ bool launch_quantize_gemm_decode(int64_t m, int64_t n, int64_t k, const void* x,
 
 // W4A16: C [m, n] = X [m, k] (16-bit or fp32 activations, as they are) times
 // the dequantized 4-bit weights B [n, k].
+size_t gemm_w4a16_workspace_bytes(int fmt, int64_t m, int64_t n, int64_t k);
 hipError_t launch_gemm_w4a16(int fmt, int64_t m, int64_t n, int64_t k, const void* x, int x_dtype,
                              const uint8_t* b_codes, const uint8_t* b_scales,
-                             const float* b_tscale, void* c, int c_dtype, hipStream_t stream);
+                             const float* b_tscale, void* c, int c_dtype, void* workspace,
+                             hipStream_t stream);
 
 // KV cache append: rows of x [batch, heads, t_new, k] quantized (NVFP4 with
 // the given tensor scale) into a [batch, heads, t_max, ...] cache at

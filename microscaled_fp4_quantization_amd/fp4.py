@@ -30,7 +30,7 @@ EXPORTS = ("fp4_status_string", "fp4_quantize_workspace_size", "fp4_quantize",
            "fp4_gemm", "fp4_quantize_gemm_workspace_size", "fp4_quantize_gemm",
            "fp4_quantize_mse", "fp4_gemm_w4a16", "fp4_kv_append",
            "fp4_attention_workspace_size", "fp4_attention_decode", "fp4_gptq_workspace_size",
-           "fp4_gptq_quantize", "fp4_quantize_noalloc")
+           "fp4_gptq_quantize", "fp4_quantize_noalloc", "fp4_gemm_w4a16_workspace_size")
 
 _lib = None
 
@@ -63,8 +63,10 @@ def lib():
     L.fp4_quantize_noalloc.restype = i32
     L.fp4_quantize_mse.argtypes = [vp, i32, i64, i64, vp, vp, vp, i32, vp, sz, vp]
     L.fp4_quantize_mse.restype = i32
-    L.fp4_gemm_w4a16.argtypes = [i32, vp, i32, i64, i64, i64, vp, vp, vp, vp, i32, vp]
+    L.fp4_gemm_w4a16.argtypes = [i32, vp, i32, i64, i64, i64, vp, vp, vp, vp, i32, vp, sz, vp]
     L.fp4_gemm_w4a16.restype = i32
+    L.fp4_gemm_w4a16_workspace_size.argtypes = [i32, i64, i64, i64]
+    L.fp4_gemm_w4a16_workspace_size.restype = sz
     L.fp4_dequantize.argtypes = [i32, vp, vp, vp, i64, i64, vp, i32, vp]
     L.fp4_dequantize.restype = i32
     L.fp4_gemm_workspace_size.argtypes = [i32, i64, i64, i64]
@@ -213,8 +215,11 @@ def gemm_w4a16(x, b, fmt="nvfp4", out_dtype="bf16", out=None):
     code, tdt = _OUT_DTYPES[out_dtype]
     if out is None:
         out = torch.empty((m, n), dtype=tdt, device=x.device)
-    st = lib().fp4_gemm_w4a16(f, _ptr(x), _IN_DTYPES[x.dtype], m, n, k, _ptr(bc), _ptr(bsc),
-                              _ptr(bt), _ptr(out), code, _stream(x))
+    L = lib()
+    need = L.fp4_gemm_w4a16_workspace_size(f, m, n, k)
+    ws = torch.empty(need, dtype=torch.uint8, device=x.device) if need else None
+    st = L.fp4_gemm_w4a16(f, _ptr(x), _IN_DTYPES[x.dtype], m, n, k, _ptr(bc), _ptr(bsc),
+                          _ptr(bt), _ptr(out), code, _ptr(ws), need, _stream(x))
     _check(st, "fp4_gemm_w4a16")
     return out
 

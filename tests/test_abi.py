@@ -137,8 +137,8 @@ def test_gemm_w4a16_rejects_bad_arguments():
     f = fp4.lib().fp4_gemm_w4a16
 
     def g(fmt=NV, x=FAKE, dt=fp4.BF16, m=8, n=64, k=256, bc=FAKE, bs=FAKE, bt=FAKE, c=FAKE,
-          cdt=fp4.BF16):
-        return f(fmt, x, dt, m, n, k, bc, bs, bt, c, cdt, None)
+          cdt=fp4.BF16, ws=None, wsb=0):
+        return f(fmt, x, dt, m, n, k, bc, bs, bt, c, cdt, ws, wsb, None)
 
     E = fp4.EINVAL
     assert g(fmt=9) == E
@@ -154,6 +154,15 @@ def test_gemm_w4a16_rejects_bad_arguments():
     assert g(fmt=MX) == E                                # MXFP4 takes none
     assert g(x=FAKE_ODD) == E
     assert g(m=0, x=None, c=None) == fp4.OK
+    # NVFP4 with k > 4096 (a multiple of 2048): chunk sums of up to 8 rows
+    ws = fp4.lib().fp4_gemm_w4a16_workspace_size
+    assert ws(NV, 8, 64, 8192) == 2 * 8 * 64 * 4
+    assert ws(NV, 20, 64, 14336) == 7 * 8 * 64 * 4
+    assert ws(NV, 3, 5, 6144) == 3 * 16 * 4
+    assert ws(NV, 8, 64, 4096) == 0 and ws(NV, 8, 64, 5120) == 0 and ws(MX, 8, 64, 8192) == 0
+    assert g(k=8192) == E                                # workspace missing
+    assert g(k=8192, ws=FAKE, wsb=2 * 8 * 64 * 4 - 1) == E
+    assert g(k=8192, ws=FAKE_ODD, wsb=2 * 8 * 64 * 4) == E
 
 
 def test_dequantize_rejects_bad_arguments():

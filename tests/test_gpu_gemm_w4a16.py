@@ -53,11 +53,18 @@ def test_decode_shape():
     (1, 100, 4096),          # one row, a partial share of weight rows
     (5, 333, 2048),          # k = 2048
     (16, 4096, 4096),        # two launches of 8 rows
-    (13, 16384, 4096),       # ragged second launch, the largest n of the streaming path
-    (3, 20000, 4096),        # beyond it: the fallback kernel
+    (13, 16384, 4096),       # ragged second launch, one round of 64-row workgroups
+    (3, 20000, 4096),        # beyond it: workgroups of up to 64 rows in whole rounds
+    (8, 28672, 2048),        # the same with k = 2048 (two workgroups per CU)
+    (8, 4096, 14336),        # a down projection: k split in 7 chunks of 2048
+    (20, 1000, 8192),        # 2 chunks of 4096; three launches reuse the workspace
+    (6, 17000, 6144),        # 3 chunks of 2048 over more than one round
     (4, 200, 96),            # k outside the streaming path
+    (4, 200, 5120),          # k > 4096 but not a multiple of 2048: the fallback kernel
 ])
 def test_shapes(m, n, k):
+    if k > 4096 and k % 2048 == 0:
+        assert fq.fp4.lib().fp4_gemm_w4a16_workspace_size(fq.fp4.NVFP4, m, n, k) > 0
     x = randn((m, k), torch.bfloat16, m + n)
     w = randn((n, k), torch.bfloat16, k, 0.02)
     check("nvfp4", x, w)
