@@ -279,7 +279,7 @@ fp4_status fp4_gemm_w4a16(fp4_format fmt, const void* x, fp4_dtype x_dtype,
 
 /* Bytes of device workspace fp4_gemm_w4a16 needs for these sizes: nonzero
  * only for NVFP4 with k > 4096 a multiple of 2048 (the fp32 sums of each
- * chunk of k for up to 8 rows of X at a time). */
+ * chunk of k for up to 16 rows of X at a time). */
 size_t fp4_gemm_w4a16_workspace_size(fp4_format fmt, int64_t m, int64_t n, int64_t k);
 
 /* Bytes of device workspace fp4_quantize_gemm needs for these sizes. */

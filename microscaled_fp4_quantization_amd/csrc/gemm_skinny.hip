@@ -406,8 +406,8 @@ struct StreamLds {
 // in.
 constexpr int kXCodes = 0, kXQuant = 1, kXRaw = 2;
 
-// XH = 2 (codes in only): up to 16 activation rows, all 16 columns of the
-// MFMA tile (XH = 1: 8 rows, the other 8 columns repeat them).
+// XH = 2 (codes in or W4A16): up to 16 activation rows, all 16 columns of
+// the MFMA tile (XH = 1: 8 rows, the other 8 columns repeat them).
 template <int NSTEP, int XM, int XH>
 __global__ __launch_bounds__(64 * kStrWaves) void gemm_nv_stream(
     int m, int64_t n, int k, int rows_per_wg, const uint8_t* __restrict__ a,
@@ -423,7 +423,7 @@ __global__ __launch_bounds__(64 * kStrWaves) void gemm_nv_stream(
   } LU;
   __shared__ float red[kStrWaves];
   StreamLds<NSTEP, XH>& L = LU.s;
-  static_assert(XH == 1 || XM == kXCodes, "16 activation rows: codes in only");
+  static_assert(XH == 1 || XM != kXQuant, "16 activation rows: codes in or W4A16");
   constexpr bool QX = XM != kXCodes;                  // bf16 X loaded here
   constexpr bool GMAX = XM == kXQuant;                // max |X| over the tensor first
   const int tid = threadIdx.x, lane = tid & 63;
@@ -447,10 +447,20 @@ __global__ __launch_bounds__(64 * kStrWaves) void gemm_nv_stream(
   u32x4 xb[QX ? 2 * NSTEP : 1];                        // bf16 X, 8 values each
   uint32_t xq[XH][2 * NSTEP];                         // codes, 8 per dword (kXCodes)
   uint32_t xs[XH];                                    // NSTEP scale bytes (kXCodes)
+  // W4A16 with 16 rows: row 8 + lane / 8 as well
+  constexpr bool RAW2 = XM == kXRaw && XH == 2;
+  u32x4 xb2[RAW2 ? 2 * NSTEP : 1];
+  const bool live2 = 8 + xrow < m;
   if (QX) {
 #pragma unroll
     for (int i = 0; i < 2 * NSTEP; ++i)
       xb[i] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(a) + xsrc * k + xv0 + 8 * i);
+    if constexpr (RAW2) {
+      const int64_t xsrc2 = live2 ? 8 + xrow : m - 1;
+#pragma unroll
+      for (int i = 0; i < 2 * NSTEP; ++i)
+        xb2[i] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(a) + xsrc2 * k + xv0 + 8 * i);
+    }
   } else {
     // row 8 hf + lane / 8 of each group of 8 rows
 #pragma unroll
@@ -503,6 +513,7 @@ __global__ __launch_bounds__(64 * kStrWaves) void gemm_nv_stream(
   // ---- activations into this wave's LDS region --------------------------------------
   _Float16* xdst = &L.x[wave][xrow][16 * NSTEP * xc];
   float xscale = 1.0f;                                // the activations' tensor scale
+  float xscale2 = 1.0f;                               // W4A16, 16 rows: 2^E of row 8 + lane / 8
   if (QX) {
     // this wave's part of max |X|
     float am[NSTEP];
@@ -554,6 +565,34 @@ __global__ __launch_bounds__(64 * kStrWaves) void gemm_nv_stream(
         }
         if (!live) f = (v8h){0, 0, 0, 0, 0, 0, 0, 0};
         *reinterpret_cast<v8h*>(xdst + 8 * i) = f;
+      }
+      if constexpr (RAW2) {
+        // the second group of 8 rows, scaled the same way (2^E in xscale2)
+        float m2 = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 2 * NSTEP; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            m2 = fmaxf(m2, fmaxf(fabsf(bf16_lo(xb2[i][j])), fabsf(bf16_hi(xb2[i][j]))));
+        m2 = live2 ? m2 : 0.0f;
+#pragma unroll
+        for (int off = 4; off >= 1; off >>= 1) m2 = fmaxf(m2, __shfl_xor(m2, off));
+        const int eb2 = (int)(as_u(m2) >> 23);
+        const int pe2 = m2 == 0.0f ? 127 : (254 - eb2 < 1 ? 1 : 254 - eb2);
+        const float q2 = as_f((uint32_t)pe2 << 23);
+        xscale2 = as_f((uint32_t)(254 - pe2) << 23);
+        _Float16* xd2 = &L.x[wave][8 + xrow][16 * NSTEP * xc];
+#pragma unroll
+        for (int i = 0; i < 2 * NSTEP; ++i) {
+          v8h f;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            f[2 * j] = (_Float16)(bf16_lo(xb2[i][j]) * q2);
+            f[2 * j + 1] = (_Float16)(bf16_hi(xb2[i][j]) * q2);
+          }
+          if (!live2) f = (v8h){0, 0, 0, 0, 0, 0, 0, 0};
+          *reinterpret_cast<v8h*>(xd2 + 8 * i) = f;
+        }
       }
     } else {
       float s_t = A / 2688.0f;                        // 6 * 448
@@ -641,7 +680,11 @@ __global__ __launch_bounds__(64 * kStrWaves) void gemm_nv_stream(
   if (XM == kXRaw) {
     // back to the scale of X: acc column lane % 16 is activation row
     // lane % 16, whose 2^E lane 8 (lane % 8) holds (rows >= 8 are zero)
-    const float e = __shfl(xscale, 8 * (lane & 7));
+    float e = __shfl(xscale, 8 * (lane & 7));
+    if constexpr (RAW2) {
+      const float e2 = __shfl(xscale2, 8 * (lane & 7));
+      if ((lane & 15) >= 8) e = e2;
+    }
 #pragma unroll
     for (int tl = 0; tl < NT; ++tl) acc[tl] *= e;
   }
@@ -742,7 +785,7 @@ hipError_t launch_stream(int m, int64_t n, int k, const uint8_t* a, const uint8_
   // would spend their time on the activation slice and the reduction, and a
   // round begun by a few workgroups costs a whole workgroup lifetime.
   const bool nstep2 = nsplit > 1 ? k % 4096 == 0 : k == 4096;
-  const int64_t slots = nstep2 ? kStrGroups : 2 * kStrGroups;
+  const int64_t slots = nstep2 || XH == 2 ? kStrGroups : 2 * kStrGroups;
   int rows = (int)((n + kStrGroups - 1) / kStrGroups);
   if (nsplit > 1 || n > 16 * kStrTiles * kStrGroups) {
     const int64_t rmax = 16 * kStrTiles;
@@ -857,7 +900,7 @@ int w4a16_chunks(int fmt, int64_t n, int64_t k) {
 
 size_t gemm_w4a16_workspace_bytes(int fmt, int64_t m, int64_t n, int64_t k) {
   const int s = w4a16_chunks(fmt, n, k);
-  const int64_t mc = m < 8 ? m : 8;
+  const int64_t mc = m < 16 ? m : 16;
   return s > 1 && mc > 0 ? (size_t)s * (size_t)gemm_split_stride(mc, n) * sizeof(float) : 0;
 }
 
@@ -869,17 +912,20 @@ hipError_t launch_gemm_w4a16(int fmt, int64_t m, int64_t n, int64_t k, const voi
                          reinterpret_cast<uintptr_t>(b_scales)) & 15) == 0;
   const int nsplit = x_dtype == kInBF16 ? w4a16_chunks(fmt, n, k) : 0;
   if (nsplit > 0 && aligned) {
-    // streaming kernel, 8 activation rows per launch; a split k's chunk sums
-    // (times the tensor scale) added by the reduction pass, which reuses
-    // the workspace for the next 8 rows in stream order
+    // streaming kernel, 16 activation rows per launch; a split k's chunk
+    // sums (times the tensor scale) added by the reduction pass, which
+    // reuses the workspace for the next 16 rows in stream order
     float* part = nsplit > 1 ? reinterpret_cast<float*>(workspace) : nullptr;
     const int64_t osz = c_dtype == kInF32 ? 4 : 2;
-    for (int64_t i0 = 0; i0 < m; i0 += 8) {
-      const int mc = (int)(m - i0 < 8 ? m - i0 : 8);
+    for (int64_t i0 = 0; i0 < m; i0 += 16) {
+      const int mc = (int)(m - i0 < 16 ? m - i0 : 16);
       const uint8_t* xa = reinterpret_cast<const uint8_t*>(x) + i0 * k * 2;
       void* ca = reinterpret_cast<char*>(c) + i0 * n * osz;
-      hipError_t e = launch_stream<kXRaw>(mc, n, (int)k, xa, nullptr, nullptr, b_codes, b_scales, b_tscale, ca,
-                                          c_dtype, nullptr, nullptr, nullptr, stream, nsplit, part);
+      hipError_t e =
+          mc > 8 ? launch_stream<kXRaw, 2>(mc, n, (int)k, xa, nullptr, nullptr, b_codes, b_scales, b_tscale, ca,
+                                           c_dtype, nullptr, nullptr, nullptr, stream, nsplit, part)
+                 : launch_stream<kXRaw>(mc, n, (int)k, xa, nullptr, nullptr, b_codes, b_scales, b_tscale, ca,
+                                        c_dtype, nullptr, nullptr, nullptr, stream, nsplit, part);
       if (e == hipSuccess && nsplit > 1)
         e = launch_split_reduce(part, nsplit, mc, n, nullptr, nullptr, ca, c_dtype, stream);
       if (e != hipSuccess) return e;

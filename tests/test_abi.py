@@ -154,10 +154,11 @@ def test_gemm_w4a16_rejects_bad_arguments():
     assert g(fmt=MX) == E                                # MXFP4 takes none
     assert g(x=FAKE_ODD) == E
     assert g(m=0, x=None, c=None) == fp4.OK
-    # NVFP4 with k > 4096 (a multiple of 2048): chunk sums of up to 8 rows
+    # NVFP4 with k > 4096 (a multiple of 2048): chunk sums of up to 16 rows
     ws = fp4.lib().fp4_gemm_w4a16_workspace_size
     assert ws(NV, 8, 64, 8192) == 2 * 8 * 64 * 4
-    assert ws(NV, 20, 64, 14336) == 7 * 8 * 64 * 4
+    assert ws(NV, 20, 64, 14336) == 7 * 16 * 64 * 4
+    assert ws(NV, 12, 5, 14336) == 7 * 60 * 4
     assert ws(NV, 3, 5, 6144) == 3 * 16 * 4
     assert ws(NV, 8, 64, 4096) == 0 and ws(NV, 8, 64, 5120) == 0 and ws(MX, 8, 64, 8192) == 0
     assert g(k=8192) == E                                # workspace missing

@@ -52,12 +52,13 @@ def test_decode_shape():
 @pytest.mark.parametrize("m,n,k", [
     (1, 100, 4096),          # one row, a partial share of weight rows
     (5, 333, 2048),          # k = 2048
-    (16, 4096, 4096),        # two launches of 8 rows
-    (13, 16384, 4096),       # ragged second launch, one round of 64-row workgroups
+    (16, 4096, 4096),        # 16 rows in one launch
+    (13, 16384, 4096),       # 13 rows, one round of 64-row workgroups
     (3, 20000, 4096),        # beyond it: workgroups of up to 64 rows in whole rounds
     (8, 28672, 2048),        # the same with k = 2048 (two workgroups per CU)
     (8, 4096, 14336),        # a down projection: k split in 7 chunks of 2048
-    (20, 1000, 8192),        # 2 chunks of 4096; three launches reuse the workspace
+    (16, 4096, 14336),       # the same for 16 rows (one workgroup per CU)
+    (20, 1000, 8192),        # 2 chunks of 4096; launches of 16 and 4 rows reuse the workspace
     (6, 17000, 6144),        # 3 chunks of 2048 over more than one round
     (4, 200, 96),            # k outside the streaming path
     (4, 200, 5120),          # k > 4096 but not a multiple of 2048: the fallback kernel
@@ -90,6 +91,14 @@ def test_activation_range():
     check("nvfp4", torch.zeros((8, 4096), dtype=torch.bfloat16), w, "f32")
     big = randn((2, 2048), torch.float32, 5) * 1.0e30      # far beyond fp16 range
     check("nvfp4", big.to(torch.bfloat16), randn((512, 2048), torch.bfloat16, 6, 0.02), "f32")
+    # 16 rows in one launch: each row of the second group of 8 on its own scale
+    x16 = randn((16, 4096), torch.float32, 9)
+    for i in range(8, 16):
+        x16[i] *= 10.0 ** (i - 11)
+    x16[13, ::3] = 0.0
+    x16[15] = 0.0
+    check("nvfp4", x16.to(torch.bfloat16), w, "f32")
+    check("nvfp4", x16[:11].to(torch.bfloat16), w, "f32")
 
 
 def test_agrees_with_w4a4_on_nvfp4_activations():
