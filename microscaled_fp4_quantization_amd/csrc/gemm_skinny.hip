@@ -352,7 +352,7 @@ __global__ __launch_bounds__(256) void gemm_nv_decode(
 }
 
 
-// ---- NVFP4 weight-stream kernel (m <= 8, k = 2048 or 4096, n <= 16384) -------
+// ---- NVFP4 weight-stream kernel (m <= 16, k = 2048 or 4096 or split) ---------
 // The weight rows are dealt out evenly: one workgroup of 16 waves per
 // CU-share of R = ceil(n / 256) rows (at most 64: up to four 16-row MFMA
 // tiles, the last possibly partial), so every CU streams the same number of
@@ -766,7 +766,9 @@ __global__ __launch_bounds__(256) void gemm_w4a16_simple(
   for (int i = 0; i < rows; ++i) store_out(c, c_dtype, (int64_t)(i0 + i) * n + j, acc[i] * ts);
 }
 
-// The stream kernel's shapes: m <= 8, k = 2048 or 4096, n <= 16384.
+// The stream kernel's one-round shapes with 8 activation rows: m <= 8, k =
+// 2048 or 4096, n <= 16384 (16 rows, a split k and, for W4A16, any n are
+// taken by the launchers below).
 bool stream_shape(int64_t m, int64_t n, int64_t k) {
   return m >= 1 && m <= 8 && (k == 2048 || k == 4096) && n >= 1 && n <= 16 * kStrTiles * kStrGroups;
 }
