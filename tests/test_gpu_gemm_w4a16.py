@@ -60,6 +60,8 @@ def test_decode_shape():
     (16, 4096, 14336),       # the same for 16 rows (one workgroup per CU)
     (20, 1000, 8192),        # 2 chunks of 4096; launches of 16 and 4 rows reuse the workspace
     (6, 17000, 6144),        # 3 chunks of 2048 over more than one round
+    (16, 20000, 2048),       # 16 rows past 16384 weight rows (one workgroup per CU)
+    (11, 3000, 12288),       # 11 rows, 3 chunks of 4096
     (4, 200, 96),            # k outside the streaming path
     (4, 200, 5120),          # k > 4096 but not a multiple of 2048: the fallback kernel
 ])
@@ -68,7 +70,7 @@ def test_shapes(m, n, k):
         assert fq.fp4.lib().fp4_gemm_w4a16_workspace_size(fq.fp4.NVFP4, m, n, k) > 0
     x = randn((m, k), torch.bfloat16, m + n)
     w = randn((n, k), torch.bfloat16, k, 0.02)
-    check("nvfp4", x, w)
+    check("nvfp4", x, w, "f32" if m % 2 else "bf16")
 
 
 def test_mxfp4_and_other_activation_types():
