@@ -271,6 +271,12 @@ fp4_status fp4_quantize_gemm(fp4_format fmt, const void* x, fp4_dtype x_dtype,
                                     b_tscale, c, (int)c_dtype, st, &e))
       return from_hip(e);
   }
+  if (fmt == FP4_MXFP4 && x_dtype == FP4_BF16 && n > 0) {
+    hipError_t e = hipSuccess;
+    if (launch_quantize_gemm_mx_decode(m, n, k, x, a_codes, a_scales, b_codes, b_scales, c, (int)c_dtype, st,
+                                       &e))
+      return from_hip(e);
+  }
   s = quantize_common(false, fmt, x, x_dtype, m, k, a_codes, a_scales, a_tscale,
                       FP4_TSCALE_COMPUTE, workspace, workspace_bytes, stream);
   if (s != FP4_OK || n == 0) return s;

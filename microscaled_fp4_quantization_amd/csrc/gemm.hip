@@ -37,6 +37,10 @@ hipError_t launch_gemm(int fmt, int64_t m, int64_t n, int64_t k,
                        const uint8_t* b_scales, const float* b_tscale, void* c,
                        int c_dtype, void* workspace, hipStream_t stream) {
   if (m <= 16) {
+    hipError_t e = hipSuccess;
+    if (fmt == kFmtMX && launch_gemm_mx_decode(m, n, k, a_codes, a_scales, b_codes, b_scales, c, c_dtype,
+                                               stream, &e))
+      return e;
     return launch_gemm_skinny(fmt, m, n, k, a_codes, a_scales, a_tscale, b_codes,
                               b_scales, b_tscale, c, c_dtype, workspace, stream);
   }

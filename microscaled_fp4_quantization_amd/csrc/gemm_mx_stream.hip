@@ -1,0 +1,237 @@
+// MXFP4 W4A4 decode GEMM (m <= 16, k = 2048 or 4096, n <= 16384): a weight
+// stream on the block-scaled FP4 matrix instruction.  C[m, n] = sum_k
+// deq(X)[m, k] deq(W)[n, k], with or without the activation quantize in the
+// same launch.
+//
+// pimento.cloud "FP8, NVFP4 czy AWQ?", section "Dlaczego W8A8 i W4A16 to nie
+// to samo?": token-by-token generation is bound by reading the weights, so W
+// is streamed once.  The layout is that of the NVFP4 stream kernel: one
+// workgroup of 16 waves per CU-share of ceil(n / 256) weight rows (at most 64,
+// four 16-row tiles), the waves splitting k into slices of 128 NSTEP values
+// and issuing all their loads at once, the 16 partial tiles added through LDS
+// at the end.  Lane (r, g) = (lane % 16, lane / 16) holds, per step t, the 16
+// bytes at 64 t + 16 g of weight row r of each tile: 32 values, exactly one
+// MXFP4 block, which is one lane's share of a v_mfma_scale_f32_16x16x128
+// operand with its E8M0 scale byte.  Nothing is dequantized: the matrix core
+// applies both operands' block scales, so the products are exact and the sums
+// are fp32.  The same lane holds the same 32 positions of activation row r
+// (a zero operand for r >= m).
+//
+// MXFP4 has no tensor scale, so the activation quantize (QX) needs no
+// tensor-wide maximum: each lane quantizes its own block of X (amax, the
+// smallest 2^k with amax <= 6 2^k, E2M1 codes of x 2^-k) with the arithmetic
+// of the quantize kernels, and feeds the codes to the matrix core directly;
+// workgroup 0 also writes them out.
+#include <cstddef>
+
+#include "device_common.hpp"
+#include "launch.hpp"
+
+using namespace fp4dev;
+
+namespace {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kMxWaves = 16;
+constexpr int kMxTiles = 4;                           // 64 rows at most per workgroup
+constexpr int kMxGroups = 256;                        // one workgroup per CU
+
+// 4 NSTEP scale bytes of one row's slice (blocks ks0 / 32 ..), as dwords.
+template <int NSTEP>
+__device__ __forceinline__ void load_scale_slice(const uint8_t* p, uint32_t (&s)[NSTEP]) {
+  if (NSTEP == 2) {
+    const u32x2 h = *reinterpret_cast<const u32x2*>(p);
+    s[0] = h.x;
+    s[NSTEP - 1] = h.y;
+  } else {
+    s[0] = *reinterpret_cast<const uint32_t*>(p);
+  }
+}
+
+template <int NSTEP, bool QX>
+__global__ __launch_bounds__(64 * kMxWaves) void gemm_mx_stream(
+    int m, int64_t n, int k, int rows_per_wg, const void* __restrict__ a, const uint8_t* __restrict__ as,
+    const uint8_t* __restrict__ b, const uint8_t* __restrict__ bs, void* __restrict__ c, int c_dtype,
+    uint8_t* __restrict__ qcodes, uint8_t* __restrict__ qscales) {
+  constexpr int NT = kMxTiles;
+  __shared__ v4f part[kMxWaves][NT][64];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r = lane & 15, g = lane >> 4;
+  const int64_t nbase = (int64_t)blockIdx.x * rows_per_wg;
+  int64_t nlast = nbase + rows_per_wg - 1;            // last row of this share
+  if (nlast > n - 1) nlast = n - 1;
+  const int ks0 = wave * (128 * NSTEP);               // first value of this wave's slice
+  const int64_t kbytes = k / 2, kblocks = k / 32;
+
+  // ---- activations: row r, block ks0 / 32 + 4 t + g of step t ----------------
+  const bool alive = r < m;
+  const int64_t arow = alive ? r : m - 1;
+  u32x4 xr[QX ? NSTEP : 1][QX ? 4 : 1];               // bf16 X, 8 values each (QX)
+  u32x4 av[NSTEP];                                    // codes (kept as loaded without QX)
+  uint32_t asl[NSTEP];                                // the row's 4 NSTEP scale bytes (without QX)
+  if (QX) {
+#pragma unroll
+    for (int t = 0; t < NSTEP; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        xr[t][i] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(a) + arow * k + ks0 +
+                                                   128 * t + 32 * g + 8 * i);
+  } else {
+#pragma unroll
+    for (int t = 0; t < NSTEP; ++t)
+      av[t] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint8_t*>(a) + arow * kbytes + ks0 / 2 +
+                                              64 * t + 16 * g);
+    load_scale_slice<NSTEP>(as + arow * kblocks + ks0 / 32, asl);
+  }
+
+  // ---- weights: lane p loads row p's scale slice; codes per tile and step ------
+  const int64_t swr = (nbase + lane <= nlast) ? nbase + lane : nlast;
+  uint32_t wsl[NSTEP];
+  load_scale_slice<NSTEP>(bs + swr * kblocks + ks0 / 32, wsl);
+  u32x4 w[NT][NSTEP];
+#pragma unroll
+  for (int tl = 0; tl < NT; ++tl) {
+    const int64_t wr = (nbase + 16 * tl + r <= nlast) ? nbase + 16 * tl + r : nlast;
+#pragma unroll
+    for (int t = 0; t < NSTEP; ++t)
+      w[tl][t] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(b + wr * kbytes + ks0 / 2 + 64 * t + 16 * g));
+  }
+
+  // ---- activation operands and scale bytes -----------------------------------
+  uint32_t asb[NSTEP];
+  if (QX) {
+#pragma unroll
+    for (int t = 0; t < NSTEP; ++t) {
+      float v[32];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          v[8 * i + 2 * j] = bf16_lo(xr[t][i][j]);
+          v[8 * i + 2 * j + 1] = bf16_hi(xr[t][i][j]);
+        }
+      float amax = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 32; j += 2) amax = fmaxf(amax, fmaxf(fabsf(v[j]), fabsf(v[j + 1])));
+      const int kx = mx_block_exponent(amax);
+      const float rs = as_f((uint32_t)(127 - kx) << 23);   // 2^-k, a normal float for k in [-127, 126]
+      uint32_t q[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float* p = v + 8 * i;
+        uint32_t u = e2m1_pack2<0>(0u, p[0] * rs, p[1] * rs);
+        u = e2m1_pack2<1>(u, p[2] * rs, p[3] * rs);
+        u = e2m1_pack2<2>(u, p[4] * rs, p[5] * rs);
+        q[i] = e2m1_pack2<3>(u, p[6] * rs, p[7] * rs);
+      }
+      asb[t] = (uint32_t)(kx + 127);
+      av[t] = (u32x4){q[0], q[1], q[2], q[3]};
+      if (blockIdx.x == 0 && alive) {
+        *reinterpret_cast<u32x4*>(qcodes + arow * kbytes + ks0 / 2 + 64 * t + 16 * g) = av[t];
+        qscales[arow * kblocks + ks0 / 32 + 4 * t + g] = (uint8_t)asb[t];
+      }
+    }
+  } else {
+#pragma unroll
+    for (int t = 0; t < NSTEP; ++t) asb[t] = (asl[t] >> (8 * g)) & 0xFFu;
+  }
+#pragma unroll
+  for (int t = 0; t < NSTEP; ++t)
+    if (!alive) av[t] = (u32x4){0u, 0u, 0u, 0u};
+
+  // ---- products: one block-scaled MFMA per tile and step -----------------------
+  v4f acc[NT];
+#pragma unroll
+  for (int tl = 0; tl < NT; ++tl) acc[tl] = (v4f){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int t = 0; t < NSTEP; ++t) {
+    const v8i fa = {(int)av[t][0], (int)av[t][1], (int)av[t][2], (int)av[t][3], 0, 0, 0, 0};
+#pragma unroll
+    for (int tl = 0; tl < NT; ++tl) {
+      // the weight row's scale byte, from the lane that loaded its slice
+      const uint32_t sw = ((uint32_t)__shfl((int)wsl[t], 16 * tl + r) >> (8 * g)) & 0xFFu;
+      const v8i fw = {(int)w[tl][t][0], (int)w[tl][t][1], (int)w[tl][t][2], (int)w[tl][t][3], 0, 0, 0, 0};
+      acc[tl] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fw, fa, acc[tl], 4, 4, 0, (int)sw, 0,
+                                                                  (int)asb[t]);
+    }
+  }
+
+  // ---- add the 16 slices, store ------------------------------------------------
+#pragma unroll
+  for (int tl = 0; tl < NT; ++tl) part[wave][tl][lane] = acc[tl];
+  __syncthreads();
+  if (tid < 64 * NT) {                                // thread -> (tile, lane)
+    const int tl = tid >> 6, l = tid & 63;
+    v4f sum = part[0][tl][l];
+#pragma unroll
+    for (int wv = 1; wv < kMxWaves; ++wv) sum += part[wv][tl][l];
+    // D layout: lane l holds weight rows 4 (l / 16) + e of the tile, activation row l % 16
+    const int xrw = l & 15, lr = 16 * tl + 4 * (l >> 4);
+    const int64_t ni = nbase + lr;
+    if (xrw < m && lr < rows_per_wg && ni <= nlast) {
+      const int64_t o = (int64_t)xrw * n + ni;
+      if (c_dtype != kInF32 && lr + 3 < rows_per_wg && ni + 3 <= nlast && (o & 3) == 0) {
+        const __bf16 h[4] = {(__bf16)sum[0], (__bf16)sum[1], (__bf16)sum[2], (__bf16)sum[3]};
+        *reinterpret_cast<u32x2*>(reinterpret_cast<__bf16*>(c) + o) = *reinterpret_cast<const u32x2*>(h);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if (lr + e < rows_per_wg && ni + e <= nlast) {
+            if (c_dtype == kInF32) reinterpret_cast<float*>(c)[o + e] = sum[e];
+            else reinterpret_cast<__bf16*>(c)[o + e] = (__bf16)sum[e];
+          }
+        }
+      }
+    }
+  }
+}
+
+bool mx_stream_shape(int64_t m, int64_t n, int64_t k) {
+  return m >= 1 && m <= 16 && (k == 2048 || k == 4096) && n >= 1 && n <= 16 * kMxTiles * kMxGroups;
+}
+
+template <bool QX>
+hipError_t launch_mx_stream(int m, int64_t n, int k, const void* a, const uint8_t* as, const uint8_t* b,
+                            const uint8_t* bs, void* c, int c_dtype, uint8_t* qcodes, uint8_t* qscales,
+                            hipStream_t stream) {
+  const int rows = (int)((n + kMxGroups - 1) / kMxGroups);
+  const dim3 grid((unsigned)((n + rows - 1) / rows));
+  if (k == 4096)
+    hipLaunchKernelGGL((gemm_mx_stream<2, QX>), grid, dim3(64 * kMxWaves), 0, stream, m, n, k, rows, a, as, b,
+                       bs, c, c_dtype, qcodes, qscales);
+  else
+    hipLaunchKernelGGL((gemm_mx_stream<1, QX>), grid, dim3(64 * kMxWaves), 0, stream, m, n, k, rows, a, as, b,
+                       bs, c, c_dtype, qcodes, qscales);
+  return hipGetLastError();
+}
+
+bool aligned_to(const void* p, uintptr_t al) { return (reinterpret_cast<uintptr_t>(p) & (al - 1)) == 0; }
+
+}  // namespace
+
+bool launch_gemm_mx_decode(int64_t m, int64_t n, int64_t k, const uint8_t* a_codes,
+                           const uint8_t* a_scales, const uint8_t* b_codes, const uint8_t* b_scales,
+                           void* c, int c_dtype, hipStream_t stream, hipError_t* err) {
+  if (!(mx_stream_shape(m, n, k) && aligned_to(a_codes, 16) && aligned_to(b_codes, 16) &&
+        aligned_to(a_scales, 8) && aligned_to(b_scales, 8)))
+    return false;
+  *err = launch_mx_stream<false>((int)m, n, (int)k, a_codes, a_scales, b_codes, b_scales, c, c_dtype, nullptr,
+                                 nullptr, stream);
+  return true;
+}
+
+bool launch_quantize_gemm_mx_decode(int64_t m, int64_t n, int64_t k, const void* x, uint8_t* a_codes,
+                                    uint8_t* a_scales, const uint8_t* b_codes, const uint8_t* b_scales,
+                                    void* c, int c_dtype, hipStream_t stream, hipError_t* err) {
+  if (!(mx_stream_shape(m, n, k) && aligned_to(x, 16) && aligned_to(a_codes, 16) && aligned_to(b_codes, 16) &&
+        aligned_to(b_scales, 8)))
+    return false;
+  *err = launch_mx_stream<true>((int)m, n, (int)k, x, nullptr, b_codes, b_scales, c, c_dtype, a_codes, a_scales,
+                                stream);
+  return true;
+}

@@ -123,6 +123,22 @@ def test_mxfp4_many_tiles(m, n, k, out_dtype):
 
 
 @pytest.mark.parametrize("m,n,k,out_dtype", [
+    (8, 14336, 4096, "bf16"),      # the decode shape
+    (16, 16384, 2048, "f32"),      # 16 rows, the largest n
+    (1, 333, 4096, "bf16"),        # ragged shares
+    (11, 70, 2048, "f32"),
+])
+def test_mxfp4_decode_stream(m, n, k, out_dtype):
+    # the MXFP4 decode kernel on the block-scaled FP4 matrix instruction
+    g = torch.Generator().manual_seed(14)
+    x = torch.randn((m, k), generator=g).to(torch.bfloat16)
+    x[m - 1] *= 1.0e4                                # a row far from the others
+    w = (torch.randn((n, k), generator=g) * 0.02).to(torch.bfloat16)
+    qx, qw = quant_pair("mxfp4", x, w)
+    check_full("mxfp4", qx, qw, out_dtype)
+
+
+@pytest.mark.parametrize("m,n,k,out_dtype", [
     (16, 14336, 4096, "bf16"),     # all 16 columns of the MFMA tile
     (9, 1000, 2048, "f32"),        # one row past 8
     (12, 16384, 2048, "bf16"),     # the largest n
@@ -294,6 +310,9 @@ def test_rotated_full_size():
     ("nvfp4", 3, 50, 96, torch.bfloat16),
     ("nvfp4", 8, 200, 4096, torch.float32),      # not bf16: two calls
     ("mxfp4", 8, 100, 4096, torch.bfloat16),
+    ("mxfp4", 16, 2000, 2048, torch.bfloat16),   # one launch, 16 rows
+    ("mxfp4", 3, 16384, 4096, torch.bfloat16),
+    ("mxfp4", 5, 64, 1024, torch.bfloat16),      # k outside the one-launch path: two calls
 ])
 def test_quantize_gemm(fmt, m, n, k, xdt):
     g = torch.Generator().manual_seed(4)
