@@ -224,6 +224,11 @@ fp4_status fp4_gemm_w4a16(fp4_format fmt, const void* x, fp4_dtype x_dtype, int6
   }
   const size_t need = gemm_w4a16_workspace_bytes((int)fmt, m, n, k);
   if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 16))) return FP4_EINVAL;
+  if (fmt == FP4_MXFP4 && x_dtype == FP4_BF16) {
+    hipError_t e = hipSuccess;
+    if (launch_gemm_w4a16_mx(m, n, k, x, b_codes, b_scales, c, (int)c_dtype, static_cast<hipStream_t>(stream), &e))
+      return from_hip(e);
+  }
   return from_hip(launch_gemm_w4a16((int)fmt, m, n, k, x, (int)x_dtype, b_codes, b_scales,
                                     b_tscale, c, (int)c_dtype, workspace,
                                     static_cast<hipStream_t>(stream)));

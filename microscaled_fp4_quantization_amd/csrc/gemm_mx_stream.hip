@@ -17,11 +17,20 @@
 // are fp32.  The same lane holds the same 32 positions of activation row r
 // (a zero operand for r >= m).
 //
-// MXFP4 has no tensor scale, so the activation quantize (QX) needs no
-// tensor-wide maximum: each lane quantizes its own block of X (amax, the
-// smallest 2^k with amax <= 6 2^k, E2M1 codes of x 2^-k) with the arithmetic
-// of the quantize kernels, and feeds the codes to the matrix core directly;
-// workgroup 0 also writes them out.
+// The activations (XM):
+//   kMxCodes  MXFP4 codes and scales.
+//   kMxQuant  bf16 X quantized here.  MXFP4 has no tensor scale, so this
+//             needs no tensor-wide maximum: each lane quantizes its own block
+//             of X (amax, the smallest 2^k with amax <= 6 2^k, E2M1 codes of
+//             x 2^-k) with the arithmetic of the quantize kernels and feeds
+//             the codes to the matrix core directly; workgroup 0 also writes
+//             them out.
+//   kMxRaw    bf16 X as it is (W4A16: pimento.cloud, section "Dlaczego W8A8
+//             i W4A16 to nie to samo?", only the weights are 4-bit): the
+//             weights widened to bf16, v 2^e, which is exact (at most two
+//             significant bits, bf16 has fp32's exponent range), and
+//             v_mfma_f32_16x16x32_bf16 on the lane's 8 values per
+//             instruction, the same 8 positions of the activation row.
 #include <cstddef>
 
 #include "device_common.hpp"
@@ -35,6 +44,10 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+
+constexpr int kMxCodes = 0, kMxQuant = 1, kMxRaw = 2;
 
 constexpr int kMxWaves = 16;
 constexpr int kMxTiles = 4;                           // 64 rows at most per workgroup
@@ -52,12 +65,37 @@ __device__ __forceinline__ void load_scale_slice(const uint8_t* p, uint32_t (&s)
   }
 }
 
-template <int NSTEP, bool QX>
+// 8 E2M1 values (one dword, low nibble first) times the E8M0 scale byte sb,
+// as bf16.  Exact: v 2^(sb - 127) has at most two significant bits and lies
+// in bf16's range but for sb = 254 with |v| >= 4.  The byte 0 (2^-127, an fp32
+// subnormal) goes through fp32, 0xFF is NaN.
+__device__ __forceinline__ v8bf mx_widen8_bf16(uint32_t w, uint32_t sb) {
+  v8bf f;
+  if (sb - 1u < 254u) {
+    const float s = as_f(sb << 23);
+    const v2bf p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 0);
+    const v2bf p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 1);
+    const v2bf p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 2);
+    const v2bf p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 3);
+    f = (v8bf){p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
+  } else {
+    const float s = sb ? __builtin_nanf("") : as_f(0x00400000u);
+    const v2f q0 = e2m1_unpack2<0>(w), q1 = e2m1_unpack2<1>(w);
+    const v2f q2 = e2m1_unpack2<2>(w), q3 = e2m1_unpack2<3>(w);
+    f = (v8bf){(__bf16)(q0.x * s), (__bf16)(q0.y * s), (__bf16)(q1.x * s), (__bf16)(q1.y * s),
+               (__bf16)(q2.x * s), (__bf16)(q2.y * s), (__bf16)(q3.x * s), (__bf16)(q3.y * s)};
+  }
+  return f;
+}
+
+template <int NSTEP, int XM>
 __global__ __launch_bounds__(64 * kMxWaves) void gemm_mx_stream(
     int m, int64_t n, int k, int rows_per_wg, const void* __restrict__ a, const uint8_t* __restrict__ as,
     const uint8_t* __restrict__ b, const uint8_t* __restrict__ bs, void* __restrict__ c, int c_dtype,
     uint8_t* __restrict__ qcodes, uint8_t* __restrict__ qscales) {
   constexpr int NT = kMxTiles;
+  constexpr bool QX = XM == kMxQuant;
+  constexpr bool XB = XM != kMxCodes;                 // bf16 X loaded here
   __shared__ v4f part[kMxWaves][NT][64];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -71,10 +109,10 @@ __global__ __launch_bounds__(64 * kMxWaves) void gemm_mx_stream(
   // ---- activations: row r, block ks0 / 32 + 4 t + g of step t ----------------
   const bool alive = r < m;
   const int64_t arow = alive ? r : m - 1;
-  u32x4 xr[QX ? NSTEP : 1][QX ? 4 : 1];               // bf16 X, 8 values each (QX)
-  u32x4 av[NSTEP];                                    // codes (kept as loaded without QX)
-  uint32_t asl[NSTEP];                                // the row's 4 NSTEP scale bytes (without QX)
-  if (QX) {
+  u32x4 xr[XB ? NSTEP : 1][XB ? 4 : 1];               // bf16 X, 8 values each
+  u32x4 av[NSTEP];                                    // codes (kept as loaded for kMxCodes)
+  uint32_t asl[NSTEP];                                // the row's 4 NSTEP scale bytes (kMxCodes)
+  if (XB) {
 #pragma unroll
     for (int t = 0; t < NSTEP; ++t)
 #pragma unroll
@@ -104,7 +142,16 @@ __global__ __launch_bounds__(64 * kMxWaves) void gemm_mx_stream(
 
   // ---- activation operands and scale bytes -----------------------------------
   uint32_t asb[NSTEP];
-  if (QX) {
+  if (XM == kMxRaw) {
+#pragma unroll
+    for (int t = 0; t < NSTEP; ++t) {
+      asb[t] = 0u;
+      av[t] = (u32x4){0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (!alive) xr[t][i] = (u32x4){0u, 0u, 0u, 0u};
+    }
+  } else if (QX) {
 #pragma unroll
     for (int t = 0; t < NSTEP; ++t) {
       float v[32];
@@ -144,10 +191,25 @@ __global__ __launch_bounds__(64 * kMxWaves) void gemm_mx_stream(
   for (int t = 0; t < NSTEP; ++t)
     if (!alive) av[t] = (u32x4){0u, 0u, 0u, 0u};
 
-  // ---- products: one block-scaled MFMA per tile and step -----------------------
+  // ---- products: one block-scaled MFMA per tile and step (W4A16: four bf16) ----
   v4f acc[NT];
 #pragma unroll
   for (int tl = 0; tl < NT; ++tl) acc[tl] = (v4f){0.f, 0.f, 0.f, 0.f};
+  if (XM == kMxRaw) {
+#pragma unroll
+    for (int t = 0; t < NSTEP; ++t) {
+#pragma unroll
+      for (int tl = 0; tl < NT; ++tl) {
+        const uint32_t sw = ((uint32_t)__shfl((int)wsl[t], 16 * tl + r) >> (8 * g)) & 0xFFu;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          const v8bf fw = mx_widen8_bf16(w[tl][t][d], sw);
+          acc[tl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fw, __builtin_bit_cast(v8bf, xr[t][d]), acc[tl], 0, 0,
+                                                            0);
+        }
+      }
+    }
+  } else
 #pragma unroll
   for (int t = 0; t < NSTEP; ++t) {
     const v8i fa = {(int)av[t][0], (int)av[t][1], (int)av[t][2], (int)av[t][3], 0, 0, 0, 0};
@@ -195,17 +257,17 @@ bool mx_stream_shape(int64_t m, int64_t n, int64_t k) {
   return m >= 1 && m <= 16 && (k == 2048 || k == 4096) && n >= 1 && n <= 16 * kMxTiles * kMxGroups;
 }
 
-template <bool QX>
+template <int XM>
 hipError_t launch_mx_stream(int m, int64_t n, int k, const void* a, const uint8_t* as, const uint8_t* b,
                             const uint8_t* bs, void* c, int c_dtype, uint8_t* qcodes, uint8_t* qscales,
                             hipStream_t stream) {
   const int rows = (int)((n + kMxGroups - 1) / kMxGroups);
   const dim3 grid((unsigned)((n + rows - 1) / rows));
   if (k == 4096)
-    hipLaunchKernelGGL((gemm_mx_stream<2, QX>), grid, dim3(64 * kMxWaves), 0, stream, m, n, k, rows, a, as, b,
+    hipLaunchKernelGGL((gemm_mx_stream<2, XM>), grid, dim3(64 * kMxWaves), 0, stream, m, n, k, rows, a, as, b,
                        bs, c, c_dtype, qcodes, qscales);
   else
-    hipLaunchKernelGGL((gemm_mx_stream<1, QX>), grid, dim3(64 * kMxWaves), 0, stream, m, n, k, rows, a, as, b,
+    hipLaunchKernelGGL((gemm_mx_stream<1, XM>), grid, dim3(64 * kMxWaves), 0, stream, m, n, k, rows, a, as, b,
                        bs, c, c_dtype, qcodes, qscales);
   return hipGetLastError();
 }
@@ -220,7 +282,7 @@ bool launch_gemm_mx_decode(int64_t m, int64_t n, int64_t k, const uint8_t* a_cod
   if (!(mx_stream_shape(m, n, k) && aligned_to(a_codes, 16) && aligned_to(b_codes, 16) &&
         aligned_to(a_scales, 8) && aligned_to(b_scales, 8)))
     return false;
-  *err = launch_mx_stream<false>((int)m, n, (int)k, a_codes, a_scales, b_codes, b_scales, c, c_dtype, nullptr,
+  *err = launch_mx_stream<kMxCodes>((int)m, n, (int)k, a_codes, a_scales, b_codes, b_scales, c, c_dtype, nullptr,
                                  nullptr, stream);
   return true;
 }
@@ -231,7 +293,24 @@ bool launch_quantize_gemm_mx_decode(int64_t m, int64_t n, int64_t k, const void*
   if (!(mx_stream_shape(m, n, k) && aligned_to(x, 16) && aligned_to(a_codes, 16) && aligned_to(b_codes, 16) &&
         aligned_to(b_scales, 8)))
     return false;
-  *err = launch_mx_stream<true>((int)m, n, (int)k, x, nullptr, b_codes, b_scales, c, c_dtype, a_codes, a_scales,
+  *err = launch_mx_stream<kMxQuant>((int)m, n, (int)k, x, nullptr, b_codes, b_scales, c, c_dtype, a_codes, a_scales,
                                 stream);
+  return true;
+}
+
+bool launch_gemm_w4a16_mx(int64_t m, int64_t n, int64_t k, const void* x, const uint8_t* b_codes,
+                          const uint8_t* b_scales, void* c, int c_dtype, hipStream_t stream, hipError_t* err) {
+  if (!(mx_stream_shape(1, n, k) && aligned_to(x, 16) && aligned_to(b_codes, 16) && aligned_to(b_scales, 8)))
+    return false;
+  // 16 activation rows per launch
+  const int64_t osz = c_dtype == kInF32 ? 4 : 2;
+  *err = hipSuccess;
+  for (int64_t i0 = 0; i0 < m && *err == hipSuccess; i0 += 16) {
+    const int mc = (int)(m - i0 < 16 ? m - i0 : 16);
+    const uint16_t* xa = reinterpret_cast<const uint16_t*>(x) + i0 * k;
+    void* ca = reinterpret_cast<char*>(c) + i0 * n * osz;
+    *err = launch_mx_stream<kMxRaw>(mc, n, (int)k, xa, nullptr, b_codes, b_scales, ca, c_dtype, nullptr, nullptr,
+                                    stream);
+  }
   return true;
 }

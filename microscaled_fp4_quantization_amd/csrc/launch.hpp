@@ -61,6 +61,10 @@ bool launch_gemm_mx_decode(int64_t m, int64_t n, int64_t k, const uint8_t* a_cod
 bool launch_quantize_gemm_mx_decode(int64_t m, int64_t n, int64_t k, const void* x, uint8_t* a_codes,
                                     uint8_t* a_scales, const uint8_t* b_codes, const uint8_t* b_scales,
                                     void* c, int c_dtype, hipStream_t stream, hipError_t* err);
+// W4A16 with MXFP4 weights and bf16 X on the same kernel (any m, 16 rows per
+// launch; k = 2048 or 4096, n <= 16384); false (nothing launched) otherwise.
+bool launch_gemm_w4a16_mx(int64_t m, int64_t n, int64_t k, const void* x, const uint8_t* b_codes,
+                          const uint8_t* b_scales, void* c, int c_dtype, hipStream_t stream, hipError_t* err);
 // One-launch NVFP4 activation quantize (tensor scale from the data) + GEMM
 // for the decode shapes; false (nothing launched) for any other shape.
 bool launch_quantize_gemm_decode(int64_t m, int64_t n, int64_t k, const void* x,

@@ -73,6 +73,25 @@ def test_shapes(m, n, k):
     check("nvfp4", x, w, "f32" if m % 2 else "bf16")
 
 
+@pytest.mark.parametrize("m,n,k", [
+    (8, 14336, 4096),        # the decode shape with MXFP4 weights
+    (16, 333, 2048),         # 16 rows, ragged shares
+    (20, 1000, 4096),        # launches of 16 and 4 rows
+])
+def test_mxfp4_stream(m, n, k):
+    # W4A16 with MXFP4 weights on the decode stream kernel (bf16 products of
+    # the exactly widened weights); scale bytes at both ends of E8M0 in some
+    # blocks: 0 (2^-127), 1, 2 and 200 (2^73)
+    x = randn((m, k), torch.bfloat16, m + n + 1)
+    w = randn((n, k), torch.bfloat16, k + 1, 0.02)
+    codes, scales, _ = fq.quantize(w.to(DEV), "mxfp4")
+    sc = scales.cpu()
+    for i, byte in enumerate((0, 1, 2, 200)):
+        sc[(7 * i + 3) % n, (5 * i) % (k // 32)] = byte
+    wq = (codes, sc.to(DEV), None)
+    check("mxfp4", x, w, "f32" if m % 2 else "bf16", wq=wq)
+
+
 def test_mxfp4_and_other_activation_types():
     w = randn((300, 1024), torch.bfloat16, 1, 0.02)
     for dt in (torch.bfloat16, torch.float16, torch.float32):
