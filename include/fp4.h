@@ -208,9 +208,9 @@ fp4_status fp4_dequantize(fp4_format fmt, const uint8_t* codes,
 /* Bytes of device workspace fp4_gemm needs for these sizes: nonzero only
  * where k is split over several workgroups per output tile (the slices'
  * fp32 partial sums, added in a fixed order by a second pass): large m with
- * few output tiles, which would leave most of the GPU idle, and NVFP4 with
- * m <= 8 and a long k (k > 4096, a multiple of 2048) over few enough weight
- * rows. */
+ * few output tiles, which would leave most of the GPU idle, and a long k
+ * (k > 4096, a multiple of 2048) with few activation rows (NVFP4: m <= 8
+ * over few enough weight rows; MXFP4: m <= 16). */
 size_t fp4_gemm_workspace_size(fp4_format fmt, int64_t m, int64_t n, int64_t k);
 
 /*
@@ -278,8 +278,8 @@ fp4_status fp4_gemm_w4a16(fp4_format fmt, const void* x, fp4_dtype x_dtype,
                           void* workspace, size_t workspace_bytes, void* stream);
 
 /* Bytes of device workspace fp4_gemm_w4a16 needs for these sizes: nonzero
- * only for NVFP4 with k > 4096 a multiple of 2048 (the fp32 sums of each
- * chunk of k for up to 16 rows of X at a time). */
+ * only for k > 4096 a multiple of 2048 (the fp32 sums of each chunk of k for
+ * up to 16 rows of X at a time). */
 size_t fp4_gemm_w4a16_workspace_size(fp4_format fmt, int64_t m, int64_t n, int64_t k);
 
 /* Bytes of device workspace fp4_quantize_gemm needs for these sizes. */

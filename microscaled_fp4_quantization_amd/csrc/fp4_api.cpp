@@ -198,7 +198,7 @@ fp4_status fp4_gemm(fp4_format fmt, int64_t m, int64_t n, int64_t k,
 
 size_t fp4_gemm_w4a16_workspace_size(fp4_format fmt, int64_t m, int64_t n, int64_t k) {
   if (!valid_format(fmt)) return 0;
-  return gemm_w4a16_workspace_bytes((int)fmt, m, n, k);
+  return fmt == FP4_MXFP4 ? gemm_mx_stream_workspace_bytes(m, n, k) : gemm_w4a16_workspace_bytes((int)fmt, m, n, k);
 }
 
 fp4_status fp4_gemm_w4a16(fp4_format fmt, const void* x, fp4_dtype x_dtype, int64_t m, int64_t n,
@@ -222,11 +222,12 @@ fp4_status fp4_gemm_w4a16(fp4_format fmt, const void* x, fp4_dtype x_dtype, int6
   } else if (b_tscale) {
     return FP4_EINVAL;
   }
-  const size_t need = gemm_w4a16_workspace_bytes((int)fmt, m, n, k);
+  const size_t need = fp4_gemm_w4a16_workspace_size(fmt, m, n, k);
   if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 16))) return FP4_EINVAL;
   if (fmt == FP4_MXFP4 && x_dtype == FP4_BF16) {
     hipError_t e = hipSuccess;
-    if (launch_gemm_w4a16_mx(m, n, k, x, b_codes, b_scales, c, (int)c_dtype, static_cast<hipStream_t>(stream), &e))
+    if (launch_gemm_w4a16_mx(m, n, k, x, b_codes, b_scales, c, (int)c_dtype, workspace,
+                             static_cast<hipStream_t>(stream), &e))
       return from_hip(e);
   }
   return from_hip(launch_gemm_w4a16((int)fmt, m, n, k, x, (int)x_dtype, b_codes, b_scales,
@@ -278,8 +279,8 @@ fp4_status fp4_quantize_gemm(fp4_format fmt, const void* x, fp4_dtype x_dtype,
   }
   if (fmt == FP4_MXFP4 && x_dtype == FP4_BF16 && n > 0) {
     hipError_t e = hipSuccess;
-    if (launch_quantize_gemm_mx_decode(m, n, k, x, a_codes, a_scales, b_codes, b_scales, c, (int)c_dtype, st,
-                                       &e))
+    if (launch_quantize_gemm_mx_decode(m, n, k, x, a_codes, a_scales, b_codes, b_scales, c, (int)c_dtype,
+                                       workspace, st, &e))
       return from_hip(e);
   }
   s = quantize_common(false, fmt, x, x_dtype, m, k, a_codes, a_scales, a_tscale,

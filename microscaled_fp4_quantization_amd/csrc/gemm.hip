@@ -23,10 +23,10 @@ hipError_t launch_gemm_large(int fmt, int64_t m, int64_t n, int64_t k,
                              void* c, int c_dtype, void* workspace, hipStream_t stream);
 
 // The large kernels split k over several workgroups per tile when the tiles
-// alone would leave most CUs idle, and the NVFP4 decode kernel splits a long
-// k over workgroup rows; the slices' fp32 sums go to the workspace.
+// alone would leave most CUs idle, and the decode kernels split a long k over
+// workgroup rows; the slices' fp32 sums go to the workspace.
 size_t gemm_workspace_bytes(int fmt, int64_t m, int64_t n, int64_t k) {
-  if (m <= 16) return gemm_skinny_workspace_bytes(fmt, m, n, k);
+  if (m <= 16) return fmt == kFmtMX ? gemm_mx_stream_workspace_bytes(m, n, k) : gemm_skinny_workspace_bytes(fmt, m, n, k);
   if (gemm_large_supported(fmt, m, n, k)) return gemm_large_workspace_bytes(fmt, m, n, k);
   return 0;
 }
@@ -39,7 +39,7 @@ hipError_t launch_gemm(int fmt, int64_t m, int64_t n, int64_t k,
   if (m <= 16) {
     hipError_t e = hipSuccess;
     if (fmt == kFmtMX && launch_gemm_mx_decode(m, n, k, a_codes, a_scales, b_codes, b_scales, c, c_dtype,
-                                               stream, &e))
+                                               workspace, stream, &e))
       return e;
     return launch_gemm_skinny(fmt, m, n, k, a_codes, a_scales, a_tscale, b_codes,
                               b_scales, b_tscale, c, c_dtype, workspace, stream);

@@ -1,4 +1,4 @@
-// MXFP4 W4A4 decode GEMM (m <= 16, k = 2048 or 4096, n <= 16384): a weight
+// MXFP4 W4A4 decode GEMM (m <= 16, k a multiple of 2048, any n): a weight
 // stream on the block-scaled FP4 matrix instruction.  C[m, n] = sum_k
 // deq(X)[m, k] deq(W)[n, k], with or without the activation quantize in the
 // same launch.
@@ -15,7 +15,9 @@
 // operand with its E8M0 scale byte.  Nothing is dequantized: the matrix core
 // applies both operands' block scales, so the products are exact and the sums
 // are fp32.  The same lane holds the same 32 positions of activation row r
-// (a zero operand for r >= m).
+// (a zero operand for r >= m).  A k longer than 4096 is split over rows of
+// workgroups, each row's fp32 sums added by a second pass in order; past
+// 16384 weight rows the workgroups take up to 64 rows in whole rounds.
 //
 // The activations (XM):
 //   kMxCodes  MXFP4 codes and scales.
@@ -92,18 +94,21 @@ template <int NSTEP, int XM>
 __global__ __launch_bounds__(64 * kMxWaves) void gemm_mx_stream(
     int m, int64_t n, int k, int rows_per_wg, const void* __restrict__ a, const uint8_t* __restrict__ as,
     const uint8_t* __restrict__ b, const uint8_t* __restrict__ bs, void* __restrict__ c, int c_dtype,
-    uint8_t* __restrict__ qcodes, uint8_t* __restrict__ qscales) {
+    uint8_t* __restrict__ qcodes, uint8_t* __restrict__ qscales, float* __restrict__ part, int64_t pstride) {
   constexpr int NT = kMxTiles;
   constexpr bool QX = XM == kMxQuant;
   constexpr bool XB = XM != kMxCodes;                 // bf16 X loaded here
-  __shared__ v4f part[kMxWaves][NT][64];
+  __shared__ v4f tiles[kMxWaves][NT][64];          // the waves' partial tiles
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = lane & 15, g = lane >> 4;
   const int64_t nbase = (int64_t)blockIdx.x * rows_per_wg;
   int64_t nlast = nbase + rows_per_wg - 1;            // last row of this share
   if (nlast > n - 1) nlast = n - 1;
-  const int ks0 = wave * (128 * NSTEP);               // first value of this wave's slice
+  // split k (part != nullptr): workgroup row blockIdx.y takes the 2048 NSTEP
+  // values from kc0 on, and its fp32 sums go to part
+  const int kc0 = (int)blockIdx.y * (kMxWaves * 128 * NSTEP);
+  const int ks0 = kc0 + wave * (128 * NSTEP);         // first value of this wave's slice
   const int64_t kbytes = k / 2, kblocks = k / 32;
 
   // ---- activations: row r, block ks0 / 32 + 4 t + g of step t ----------------
@@ -225,19 +230,24 @@ __global__ __launch_bounds__(64 * kMxWaves) void gemm_mx_stream(
 
   // ---- add the 16 slices, store ------------------------------------------------
 #pragma unroll
-  for (int tl = 0; tl < NT; ++tl) part[wave][tl][lane] = acc[tl];
+  for (int tl = 0; tl < NT; ++tl) tiles[wave][tl][lane] = acc[tl];
   __syncthreads();
   if (tid < 64 * NT) {                                // thread -> (tile, lane)
     const int tl = tid >> 6, l = tid & 63;
-    v4f sum = part[0][tl][l];
+    v4f sum = tiles[0][tl][l];
 #pragma unroll
-    for (int wv = 1; wv < kMxWaves; ++wv) sum += part[wv][tl][l];
+    for (int wv = 1; wv < kMxWaves; ++wv) sum += tiles[wv][tl][l];
     // D layout: lane l holds weight rows 4 (l / 16) + e of the tile, activation row l % 16
     const int xrw = l & 15, lr = 16 * tl + 4 * (l >> 4);
     const int64_t ni = nbase + lr;
     if (xrw < m && lr < rows_per_wg && ni <= nlast) {
       const int64_t o = (int64_t)xrw * n + ni;
-      if (c_dtype != kInF32 && lr + 3 < rows_per_wg && ni + 3 <= nlast && (o & 3) == 0) {
+      if (part) {
+        float* pp = part + (int64_t)blockIdx.y * pstride + o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (lr + e < rows_per_wg && ni + e <= nlast) pp[e] = sum[e];
+      } else if (c_dtype != kInF32 && lr + 3 < rows_per_wg && ni + 3 <= nlast && (o & 3) == 0) {
         const __bf16 h[4] = {(__bf16)sum[0], (__bf16)sum[1], (__bf16)sum[2], (__bf16)sum[3]};
         *reinterpret_cast<u32x2*>(reinterpret_cast<__bf16*>(c) + o) = *reinterpret_cast<const u32x2*>(h);
       } else {
@@ -253,64 +263,96 @@ __global__ __launch_bounds__(64 * kMxWaves) void gemm_mx_stream(
   }
 }
 
-bool mx_stream_shape(int64_t m, int64_t n, int64_t k) {
-  return m >= 1 && m <= 16 && (k == 2048 || k == 4096) && n >= 1 && n <= 16 * kMxTiles * kMxGroups;
+// Chunks of k for up to 16 activation rows: 1 for k = 2048 or 4096, and for
+// a longer k that is a multiple of 2048 the chunks of 4096 (k a multiple of
+// 4096) or 2048, at most 64; 0 for any other shape.  Any n.
+int mx_chunks(int64_t m, int64_t n, int64_t k) {
+  if (m < 1 || m > 16 || n < 1 || k % 2048 != 0) return 0;
+  if (k <= 4096) return 1;
+  const int64_t s = k % 4096 == 0 ? k / 4096 : k / 2048;
+  return s <= 64 ? (int)s : 0;
 }
 
+// One launch for up to 16 activation rows; nsplit > 1: k in nsplit chunks
+// (NSTEP = 2 when k is a multiple of 4096), the chunks' fp32 sums in part,
+// added by the reduction pass.
 template <int XM>
 hipError_t launch_mx_stream(int m, int64_t n, int k, const void* a, const uint8_t* as, const uint8_t* b,
                             const uint8_t* bs, void* c, int c_dtype, uint8_t* qcodes, uint8_t* qscales,
-                            hipStream_t stream) {
-  const int rows = (int)((n + kMxGroups - 1) / kMxGroups);
-  const dim3 grid((unsigned)((n + rows - 1) / rows));
-  if (k == 4096)
+                            int nsplit, float* part, hipStream_t stream) {
+  const bool nstep2 = nsplit > 1 ? k % 4096 == 0 : k == 4096;
+  // one workgroup per CU-share of rows; with a split or past 16384 rows, as
+  // many rows (at most 64) as fill whole rounds of co-resident workgroups
+  // (two per CU with NSTEP = 1, one with NSTEP = 2)
+  int rows = (int)((n + kMxGroups - 1) / kMxGroups);
+  if (nsplit > 1 || n > 16 * kMxTiles * kMxGroups) {
+    const int64_t slots = nstep2 ? kMxGroups : 2 * kMxGroups, rmax = 16 * kMxTiles;
+    const int64_t rounds = (((n + rmax - 1) / rmax) * nsplit + slots - 1) / slots;
+    const int64_t per_chunk = rounds * slots / nsplit;
+    rows = (int)((n + per_chunk - 1) / per_chunk);
+  }
+  const dim3 grid((unsigned)((n + rows - 1) / rows), (unsigned)nsplit);
+  const int64_t pstride = nsplit > 1 ? gemm_split_stride(m, n) : 0;
+  if (nstep2)
     hipLaunchKernelGGL((gemm_mx_stream<2, XM>), grid, dim3(64 * kMxWaves), 0, stream, m, n, k, rows, a, as, b,
-                       bs, c, c_dtype, qcodes, qscales);
+                       bs, c, c_dtype, qcodes, qscales, part, pstride);
   else
     hipLaunchKernelGGL((gemm_mx_stream<1, XM>), grid, dim3(64 * kMxWaves), 0, stream, m, n, k, rows, a, as, b,
-                       bs, c, c_dtype, qcodes, qscales);
-  return hipGetLastError();
+                       bs, c, c_dtype, qcodes, qscales, part, pstride);
+  hipError_t e = hipGetLastError();
+  if (e == hipSuccess && nsplit > 1) e = launch_split_reduce(part, nsplit, m, n, nullptr, nullptr, c, c_dtype, stream);
+  return e;
 }
 
 bool aligned_to(const void* p, uintptr_t al) { return (reinterpret_cast<uintptr_t>(p) & (al - 1)) == 0; }
 
 }  // namespace
 
+size_t gemm_mx_stream_workspace_bytes(int64_t m, int64_t n, int64_t k) {
+  const int64_t mc = m < 16 ? m : 16;
+  const int s = mx_chunks(mc, n, k);
+  return s > 1 ? (size_t)s * (size_t)gemm_split_stride(mc, n) * sizeof(float) : 0;
+}
+
 bool launch_gemm_mx_decode(int64_t m, int64_t n, int64_t k, const uint8_t* a_codes,
                            const uint8_t* a_scales, const uint8_t* b_codes, const uint8_t* b_scales,
-                           void* c, int c_dtype, hipStream_t stream, hipError_t* err) {
-  if (!(mx_stream_shape(m, n, k) && aligned_to(a_codes, 16) && aligned_to(b_codes, 16) &&
-        aligned_to(a_scales, 8) && aligned_to(b_scales, 8)))
+                           void* c, int c_dtype, void* workspace, hipStream_t stream, hipError_t* err) {
+  const int s = mx_chunks(m, n, k);
+  if (!(s > 0 && aligned_to(a_codes, 16) && aligned_to(b_codes, 16) && aligned_to(a_scales, 8) &&
+        aligned_to(b_scales, 8)))
     return false;
   *err = launch_mx_stream<kMxCodes>((int)m, n, (int)k, a_codes, a_scales, b_codes, b_scales, c, c_dtype, nullptr,
-                                 nullptr, stream);
+                                    nullptr, s, reinterpret_cast<float*>(workspace), stream);
   return true;
 }
 
 bool launch_quantize_gemm_mx_decode(int64_t m, int64_t n, int64_t k, const void* x, uint8_t* a_codes,
                                     uint8_t* a_scales, const uint8_t* b_codes, const uint8_t* b_scales,
-                                    void* c, int c_dtype, hipStream_t stream, hipError_t* err) {
-  if (!(mx_stream_shape(m, n, k) && aligned_to(x, 16) && aligned_to(a_codes, 16) && aligned_to(b_codes, 16) &&
+                                    void* c, int c_dtype, void* workspace, hipStream_t stream, hipError_t* err) {
+  const int s = mx_chunks(m, n, k);
+  if (!(s > 0 && aligned_to(x, 16) && aligned_to(a_codes, 16) && aligned_to(b_codes, 16) &&
         aligned_to(b_scales, 8)))
     return false;
-  *err = launch_mx_stream<kMxQuant>((int)m, n, (int)k, x, nullptr, b_codes, b_scales, c, c_dtype, a_codes, a_scales,
-                                stream);
+  *err = launch_mx_stream<kMxQuant>((int)m, n, (int)k, x, nullptr, b_codes, b_scales, c, c_dtype, a_codes,
+                                    a_scales, s, reinterpret_cast<float*>(workspace), stream);
   return true;
 }
 
 bool launch_gemm_w4a16_mx(int64_t m, int64_t n, int64_t k, const void* x, const uint8_t* b_codes,
-                          const uint8_t* b_scales, void* c, int c_dtype, hipStream_t stream, hipError_t* err) {
-  if (!(mx_stream_shape(1, n, k) && aligned_to(x, 16) && aligned_to(b_codes, 16) && aligned_to(b_scales, 8)))
-    return false;
-  // 16 activation rows per launch
+                          const uint8_t* b_scales, void* c, int c_dtype, void* workspace, hipStream_t stream,
+                          hipError_t* err) {
+  const int s = mx_chunks(1, n, k);
+  if (!(s > 0 && aligned_to(x, 16) && aligned_to(b_codes, 16) && aligned_to(b_scales, 8))) return false;
+  // 16 activation rows per launch; a split k's partial sums reuse the
+  // workspace for the next 16 rows in stream order
   const int64_t osz = c_dtype == kInF32 ? 4 : 2;
   *err = hipSuccess;
   for (int64_t i0 = 0; i0 < m && *err == hipSuccess; i0 += 16) {
     const int mc = (int)(m - i0 < 16 ? m - i0 : 16);
     const uint16_t* xa = reinterpret_cast<const uint16_t*>(x) + i0 * k;
     void* ca = reinterpret_cast<char*>(c) + i0 * n * osz;
-    *err = launch_mx_stream<kMxRaw>(mc, n, (int)k, xa, nullptr, b_codes, b_scales, ca, c_dtype, nullptr, nullptr,
-                                    stream);
+    *err = launch_mx_stream<kMxRaw>(mc, n, (int)k, xa, nullptr, b_codes, b_scales, ca, c_dtype, nullptr, nullptr, s,
+                                    reinterpret_cast<float*>(workspace), stream);
   }
   return true;
 }

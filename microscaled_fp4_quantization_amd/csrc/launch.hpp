@@ -51,20 +51,23 @@ hipError_t launch_gemm(int fmt, int64_t m, int64_t n, int64_t k,
                        const uint8_t* b_scales, const float* b_tscale, void* c,
                        int c_dtype, void* workspace, hipStream_t stream);
 
-// MXFP4 decode GEMM on the block-scaled FP4 matrix instruction (m <= 16, k =
-// 2048 or 4096, n <= 16384, codes 16-byte and scales 8-byte aligned), with
+// MXFP4 decode GEMM on the block-scaled FP4 matrix instruction (m <= 16, k a
+// multiple of 2048, any n, codes 16-byte and scales 8-byte aligned), with
 // (quantize_gemm: bf16 X) or without the activation quantize in the launch;
-// false (nothing launched) for any other shape.
+// false (nothing launched) for any other shape.  k > 4096 splits over
+// workgroups: gemm_mx_stream_workspace_bytes of workspace.
+size_t gemm_mx_stream_workspace_bytes(int64_t m, int64_t n, int64_t k);
 bool launch_gemm_mx_decode(int64_t m, int64_t n, int64_t k, const uint8_t* a_codes,
                            const uint8_t* a_scales, const uint8_t* b_codes, const uint8_t* b_scales,
-                           void* c, int c_dtype, hipStream_t stream, hipError_t* err);
+                           void* c, int c_dtype, void* workspace, hipStream_t stream, hipError_t* err);
 bool launch_quantize_gemm_mx_decode(int64_t m, int64_t n, int64_t k, const void* x, uint8_t* a_codes,
                                     uint8_t* a_scales, const uint8_t* b_codes, const uint8_t* b_scales,
-                                    void* c, int c_dtype, hipStream_t stream, hipError_t* err);
+                                    void* c, int c_dtype, void* workspace, hipStream_t stream, hipError_t* err);
 // W4A16 with MXFP4 weights and bf16 X on the same kernel (any m, 16 rows per
-// launch; k = 2048 or 4096, n <= 16384); false (nothing launched) otherwise.
+// launch; k a multiple of 2048, any n); false (nothing launched) otherwise.
 bool launch_gemm_w4a16_mx(int64_t m, int64_t n, int64_t k, const void* x, const uint8_t* b_codes,
-                          const uint8_t* b_scales, void* c, int c_dtype, hipStream_t stream, hipError_t* err);
+                          const uint8_t* b_scales, void* c, int c_dtype, void* workspace, hipStream_t stream,
+                          hipError_t* err);
 // One-launch NVFP4 activation quantize (tensor scale from the data) + GEMM
 // for the decode shapes; false (nothing launched) for any other shape.
 bool launch_quantize_gemm_decode(int64_t m, int64_t n, int64_t k, const void* x,

@@ -55,7 +55,9 @@ def test_workspace_sizes():
     assert L.fp4_gemm_workspace_size(NV, 8, 16384, 6144) == 0      # 768 for 512
     assert L.fp4_gemm_workspace_size(NV, 9, 4096, 14336) == 0      # m > 8
     assert L.fp4_gemm_workspace_size(NV, 8, 4096, 5120) == 0       # k not a multiple of 2048
-    assert L.fp4_gemm_workspace_size(MX, 8, 4096, 14336) == 0
+    assert L.fp4_gemm_workspace_size(MX, 8, 4096, 14336) == 7 * 8 * 4096 * 4   # MXFP4: m <= 16, any n
+    assert L.fp4_gemm_workspace_size(MX, 16, 16384, 6144) == 3 * 16 * 16384 * 4
+    assert L.fp4_gemm_workspace_size(MX, 17, 4096, 14336) == 0
 
 
 def _q(fn, fmt=NV, x=FAKE, dt=fp4.BF16, rows=4, k=64, codes=FAKE, scales=FAKE,
@@ -160,7 +162,8 @@ def test_gemm_w4a16_rejects_bad_arguments():
     assert ws(NV, 20, 64, 14336) == 7 * 16 * 64 * 4
     assert ws(NV, 12, 5, 14336) == 7 * 60 * 4
     assert ws(NV, 3, 5, 6144) == 3 * 16 * 4
-    assert ws(NV, 8, 64, 4096) == 0 and ws(NV, 8, 64, 5120) == 0 and ws(MX, 8, 64, 8192) == 0
+    assert ws(NV, 8, 64, 4096) == 0 and ws(NV, 8, 64, 5120) == 0
+    assert ws(MX, 8, 64, 8192) == 2 * 8 * 64 * 4 and ws(MX, 20, 64, 14336) == 7 * 16 * 64 * 4
     assert g(k=8192) == E                                # workspace missing
     assert g(k=8192, ws=FAKE, wsb=2 * 8 * 64 * 4 - 1) == E
     assert g(k=8192, ws=FAKE_ODD, wsb=2 * 8 * 64 * 4) == E

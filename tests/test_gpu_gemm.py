@@ -127,6 +127,9 @@ def test_mxfp4_many_tiles(m, n, k, out_dtype):
     (16, 16384, 2048, "f32"),      # 16 rows, the largest n
     (1, 333, 4096, "bf16"),        # ragged shares
     (11, 70, 2048, "f32"),
+    (8, 4096, 14336, "bf16"),      # a down projection: k split in 7 chunks of 2048
+    (16, 20000, 2048, "f32"),      # past 16384 weight rows: whole rounds of workgroups
+    (3, 777, 12288, "bf16"),       # 3 chunks of 4096
 ])
 def test_mxfp4_decode_stream(m, n, k, out_dtype):
     # the MXFP4 decode kernel on the block-scaled FP4 matrix instruction
@@ -313,6 +316,7 @@ def test_rotated_full_size():
     ("mxfp4", 16, 2000, 2048, torch.bfloat16),   # one launch, 16 rows
     ("mxfp4", 3, 16384, 4096, torch.bfloat16),
     ("mxfp4", 5, 64, 1024, torch.bfloat16),      # k outside the one-launch path: two calls
+    ("mxfp4", 8, 4096, 14336, torch.bfloat16),   # one launch over 7 chunks of k + the reduction
 ])
 def test_quantize_gemm(fmt, m, n, k, xdt):
     g = torch.Generator().manual_seed(4)
