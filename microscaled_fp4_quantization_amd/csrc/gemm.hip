@@ -25,8 +25,22 @@ hipError_t launch_gemm_large(int fmt, int64_t m, int64_t n, int64_t k,
 // The large kernels split k over several workgroups per tile when the tiles
 // alone would leave most CUs idle, and the decode kernels split a long k over
 // workgroup rows; the slices' fp32 sums go to the workspace.
+// A small batch past 16 rows (NVFP4 below 128 rows with k = 2048 or 4096 and
+// n <= 16384, the shapes of the NVFP4 decode kernel; MXFP4 up to 48 rows):
+// the decode kernels over groups of 16 activation rows, W streamed once per
+// group (from the last-level cache after the first).  The generic kernel
+// took 105-207 us for 17..100 rows of an NVFP4 14336x4096 weight, the decode
+// kernel 10 us per 16 rows; for MXFP4 the generic kernel is faster from about
+// 64 rows on.
+bool small_batch_groups(int fmt, int64_t m, int64_t n, int64_t k) {
+  if (m <= 16) return false;
+  if (fmt == kFmtNV) return m < 128 && (k == 2048 || k == 4096) && n <= 16384;
+  return m <= 48 && k % 2048 == 0;
+}
+
 size_t gemm_workspace_bytes(int fmt, int64_t m, int64_t n, int64_t k) {
-  if (m <= 16) return fmt == kFmtMX ? gemm_mx_stream_workspace_bytes(m, n, k) : gemm_skinny_workspace_bytes(fmt, m, n, k);
+  if (m <= 16 || small_batch_groups(fmt, m, n, k))
+    return fmt == kFmtMX ? gemm_mx_stream_workspace_bytes(m, n, k) : gemm_skinny_workspace_bytes(fmt, m, n, k);
   if (gemm_large_supported(fmt, m, n, k)) return gemm_large_workspace_bytes(fmt, m, n, k);
   return 0;
 }
@@ -43,6 +57,17 @@ hipError_t launch_gemm(int fmt, int64_t m, int64_t n, int64_t k,
       return e;
     return launch_gemm_skinny(fmt, m, n, k, a_codes, a_scales, a_tscale, b_codes,
                               b_scales, b_tscale, c, c_dtype, workspace, stream);
+  }
+  if (small_batch_groups(fmt, m, n, k)) {
+    const int64_t osz = c_dtype == kInF32 ? 4 : 2, bs = fmt == kFmtNV ? 16 : 32;
+    for (int64_t i0 = 0; i0 < m; i0 += 16) {
+      const int64_t mc = m - i0 < 16 ? m - i0 : 16;
+      const hipError_t e = launch_gemm(fmt, mc, n, k, a_codes + i0 * (k / 2), a_scales + i0 * (k / bs), a_tscale,
+                                       b_codes, b_scales, b_tscale, reinterpret_cast<char*>(c) + i0 * n * osz,
+                                       c_dtype, workspace, stream);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
   }
   if (gemm_large_supported(fmt, m, n, k)) {
     return launch_gemm_large(fmt, m, n, k, a_codes, a_scales, a_tscale, b_codes, b_scales,

@@ -141,6 +141,23 @@ def test_mxfp4_decode_stream(m, n, k, out_dtype):
     check_full("mxfp4", qx, qw, out_dtype)
 
 
+@pytest.mark.parametrize("fmt,m,n,k,out_dtype", [
+    ("nvfp4", 17, 1000, 4096, "bf16"),    # 16 + 1 rows
+    ("nvfp4", 40, 14336, 2048, "f32"),
+    ("nvfp4", 127, 333, 4096, "bf16"),    # the last group of 15 rows, ragged shares
+    ("mxfp4", 33, 777, 4096, "f32"),
+    ("mxfp4", 48, 5000, 8192, "bf16"),    # three groups, each with k split in 2 chunks
+])
+def test_small_batch_groups(fmt, m, n, k, out_dtype):
+    # a small batch past 16 rows: the decode kernels over groups of 16 rows
+    g = torch.Generator().manual_seed(15)
+    x = torch.randn((m, k), generator=g).to(torch.bfloat16)
+    x[m // 2] *= 300.0
+    w = (torch.randn((n, k), generator=g) * 0.02).to(torch.bfloat16)
+    qx, qw = quant_pair(fmt, x, w)
+    check_full(fmt, qx, qw, out_dtype)
+
+
 @pytest.mark.parametrize("m,n,k,out_dtype", [
     (16, 14336, 4096, "bf16"),     # all 16 columns of the MFMA tile
     (9, 1000, 2048, "f32"),        # one row past 8
