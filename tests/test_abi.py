@@ -192,8 +192,8 @@ def test_gemm_rejects_bad_arguments():
     f = fp4.lib().fp4_gemm
 
     def g(fmt=NV, m=8, n=8, k=64, a=FAKE, asc=FAKE, at=FAKE, b=FAKE, bsc=FAKE, bt=FAKE,
-          c=FAKE, dt=fp4.BF16):
-        return f(fmt, m, n, k, a, asc, at, b, bsc, bt, c, dt, None, 0, None)
+          c=FAKE, dt=fp4.BF16, ws=None, wsb=0):
+        return f(fmt, m, n, k, a, asc, at, b, bsc, bt, c, dt, ws, wsb, None)
 
     E = fp4.EINVAL
     assert g(fmt=2) == E
@@ -208,6 +208,14 @@ def test_gemm_rejects_bad_arguments():
     assert g(dt=fp4.E4M3) == fp4.EUNSUPPORTED
     assert g(dt=11) == E
     assert g(m=0, a=None, c=None) == fp4.OK
+    # a split k needs its workspace (decode shapes with k > 4096)
+    need = fp4.lib().fp4_gemm_workspace_size(MX, 8, 64, 8192)
+    assert need == 2 * 8 * 64 * 4
+    assert g(fmt=MX, at=None, bt=None, n=64, k=8192) == E
+    assert g(fmt=MX, at=None, bt=None, n=64, k=8192, ws=FAKE, wsb=need - 1) == E
+    assert g(fmt=MX, at=None, bt=None, n=64, k=8192, ws=FAKE_ODD, wsb=need) == E
+    assert g(n=64, k=8192) == E                                            # NVFP4 likewise
+    assert g(n=64, k=8192, ws=FAKE, wsb=fp4.lib().fp4_gemm_workspace_size(NV, 8, 64, 8192) - 1) == E
 
 
 def test_quantize_gemm_rejects_bad_arguments():
