@@ -144,12 +144,16 @@ def test_mxfp4_decode_stream(m, n, k, out_dtype):
 @pytest.mark.parametrize("fmt,m,n,k,out_dtype", [
     ("nvfp4", 17, 1000, 4096, "bf16"),    # 16 + 1 rows
     ("nvfp4", 40, 14336, 2048, "f32"),
-    ("nvfp4", 127, 333, 4096, "bf16"),    # the last group of 15 rows, ragged shares
+    ("nvfp4", 95, 333, 4096, "bf16"),     # the last group of 15 rows, ragged shares
+    ("nvfp4", 96, 14336, 4096, "bf16"),   # 96..127 rows: the large kernel, one partly filled row of tiles
+    ("nvfp4", 127, 3000, 8192, "f32"),    # the same with k split over workgroups
+    ("nvfp4", 100, 60000, 512, "bf16"),   # the same with 256-column tiles
     ("mxfp4", 33, 777, 4096, "f32"),
     ("mxfp4", 48, 5000, 8192, "bf16"),    # three groups, each with k split in 2 chunks
 ])
 def test_small_batch_groups(fmt, m, n, k, out_dtype):
     # a small batch past 16 rows: the decode kernels over groups of 16 rows
+    # (NVFP4 96..127 rows: the large kernel)
     g = torch.Generator().manual_seed(15)
     x = torch.randn((m, k), generator=g).to(torch.bfloat16)
     x[m // 2] *= 300.0
