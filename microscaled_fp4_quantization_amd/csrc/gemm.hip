@@ -25,17 +25,17 @@ hipError_t launch_gemm_large(int fmt, int64_t m, int64_t n, int64_t k,
 // The large kernels split k over several workgroups per tile when the tiles
 // alone would leave most CUs idle, and the decode kernels split a long k over
 // workgroup rows; the slices' fp32 sums go to the workspace.
-// A small batch past 16 rows (NVFP4 below 128 rows with k = 2048 or 4096 and
-// n <= 16384, the shapes of the NVFP4 decode kernel; MXFP4 up to 48 rows):
+// A small batch past 16 rows (NVFP4 below 96 rows with k = 2048 or 4096 and
+// n <= 16384, the shapes of the NVFP4 decode kernel; MXFP4 up to 32 rows):
 // the decode kernels over groups of 16 activation rows, W streamed once per
 // group (from the last-level cache after the first).  The generic kernel
 // took 105-207 us for 17..100 rows of an NVFP4 14336x4096 weight, the decode
-// kernel 10 us per 16 rows; for MXFP4 the generic kernel is faster from about
-// 64 rows on.
+// kernel 10 us per 16 rows; from 33 MXFP4 rows the large kernel (one row of
+// tiles) is as fast as two groups.
 bool small_batch_groups(int fmt, int64_t m, int64_t n, int64_t k) {
   if (m <= 16) return false;
   if (fmt == kFmtNV) return m < 96 && (k == 2048 || k == 4096) && n <= 16384;
-  return m <= 48 && k % 2048 == 0;
+  return m <= 32 && k % 2048 == 0;
 }
 
 // NVFP4 with 96..127 rows: the large kernel with one partly filled row of

@@ -57,8 +57,8 @@ def test_workspace_sizes():
     assert L.fp4_gemm_workspace_size(NV, 8, 4096, 5120) == 0       # k not a multiple of 2048
     assert L.fp4_gemm_workspace_size(MX, 8, 4096, 14336) == 7 * 8 * 4096 * 4   # MXFP4: m <= 16, any n
     assert L.fp4_gemm_workspace_size(MX, 16, 16384, 6144) == 3 * 16 * 16384 * 4
-    assert L.fp4_gemm_workspace_size(MX, 48, 4096, 14336) == 7 * 16 * 4096 * 4   # groups of 16 rows
-    assert L.fp4_gemm_workspace_size(MX, 49, 4096, 14336) == 0
+    assert L.fp4_gemm_workspace_size(MX, 32, 4096, 14336) == 7 * 16 * 4096 * 4   # groups of 16 rows
+    assert L.fp4_gemm_workspace_size(MX, 33, 4096, 14336) == 0   # the large kernel, one row of tiles
 
 
 def _q(fn, fmt=NV, x=FAKE, dt=fp4.BF16, rows=4, k=64, codes=FAKE, scales=FAKE,

@@ -148,8 +148,13 @@ def test_mxfp4_decode_stream(m, n, k, out_dtype):
     ("nvfp4", 96, 14336, 4096, "bf16"),   # 96..127 rows: the large kernel, one partly filled row of tiles
     ("nvfp4", 127, 3000, 8192, "f32"),    # the same with k split over workgroups
     ("nvfp4", 100, 60000, 512, "bf16"),   # the same with 256-column tiles
-    ("mxfp4", 33, 777, 4096, "f32"),
-    ("mxfp4", 48, 5000, 8192, "bf16"),    # three groups, each with k split in 2 chunks
+    ("mxfp4", 17, 777, 4096, "f32"),
+    ("mxfp4", 32, 5000, 8192, "bf16"),    # two groups, each with k split in 2 chunks
+    ("mxfp4", 33, 14336, 4096, "f32"),    # 33..255 rows: the large kernel, one row of tiles at row 0
+    ("mxfp4", 48, 5000, 8192, "bf16"),
+    ("mxfp4", 128, 28672, 2048, "bf16"),  # the same, every tile half-width
+    ("mxfp4", 255, 3000, 1536, "bf16"),   # the same, k = 512 mod 1024, split k
+    ("mxfp4", 100, 300, 512, "f32"),      # the same, n just past one tile
 ])
 def test_small_batch_groups(fmt, m, n, k, out_dtype):
     # a small batch past 16 rows: the decode kernels over groups of 16 rows
