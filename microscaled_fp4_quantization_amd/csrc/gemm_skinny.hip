@@ -406,8 +406,8 @@ struct StreamLds {
 // in.
 constexpr int kXCodes = 0, kXQuant = 1, kXRaw = 2;
 
-// XH = 2 (codes in or W4A16): up to 16 activation rows, all 16 columns of
-// the MFMA tile (XH = 1: 8 rows, the other 8 columns repeat them).
+// XH = 2: up to 16 activation rows, all 16 columns of the MFMA tile (XH = 1:
+// 8 rows, the other 8 columns repeat them).
 template <int NSTEP, int XM, int XH>
 __global__ __launch_bounds__(64 * kStrWaves) void gemm_nv_stream(
     int m, int64_t n, int k, int rows_per_wg, const uint8_t* __restrict__ a,
@@ -423,7 +423,7 @@ __global__ __launch_bounds__(64 * kStrWaves) void gemm_nv_stream(
   } LU;
   __shared__ float red[kStrWaves];
   StreamLds<NSTEP, XH>& L = LU.s;
-  static_assert(XH == 1 || XM != kXQuant, "16 activation rows: codes in or W4A16");
+
   constexpr bool QX = XM != kXCodes;                  // bf16 X loaded here
   constexpr bool GMAX = XM == kXQuant;                // max |X| over the tensor first
   const int tid = threadIdx.x, lane = tid & 63;
@@ -447,16 +447,17 @@ __global__ __launch_bounds__(64 * kStrWaves) void gemm_nv_stream(
   u32x4 xb[QX ? 2 * NSTEP : 1];                        // bf16 X, 8 values each
   uint32_t xq[XH][2 * NSTEP];                         // codes, 8 per dword (kXCodes)
   uint32_t xs[XH];                                    // NSTEP scale bytes (kXCodes)
-  // W4A16 with 16 rows: row 8 + lane / 8 as well
+  // bf16 X with 16 rows: row 8 + lane / 8 as well
   constexpr bool RAW2 = XM == kXRaw && XH == 2;
-  u32x4 xb2[RAW2 ? 2 * NSTEP : 1];
+  constexpr bool Q2 = XM == kXQuant && XH == 2;
+  u32x4 xb2[(RAW2 || Q2) ? 2 * NSTEP : 1];
   const bool live2 = 8 + xrow < m;
+  const int64_t xsrc2 = live2 ? 8 + xrow : m - 1;
   if (QX) {
 #pragma unroll
     for (int i = 0; i < 2 * NSTEP; ++i)
       xb[i] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(a) + xsrc * k + xv0 + 8 * i);
-    if constexpr (RAW2) {
-      const int64_t xsrc2 = live2 ? 8 + xrow : m - 1;
+    if constexpr (RAW2 || Q2) {
 #pragma unroll
       for (int i = 0; i < 2 * NSTEP; ++i)
         xb2[i] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(a) + xsrc2 * k + xv0 + 8 * i);
@@ -528,6 +529,21 @@ __global__ __launch_bounds__(64 * kStrWaves) void gemm_nv_stream(
       am[bl] = live ? mx : 0.0f;
     }
     float wm = NSTEP == 2 ? fmaxf(am[0], am[NSTEP - 1]) : am[0];
+    // the second group of 8 rows (one-launch quantize of 16 rows)
+    float am2[NSTEP];
+    if constexpr (Q2) {
+#pragma unroll
+      for (int bl = 0; bl < NSTEP; ++bl) {
+        float mx = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            mx = fmaxf(mx, fmaxf(fabsf(bf16_lo(xb2[2 * bl + i][j])), fabsf(bf16_hi(xb2[2 * bl + i][j]))));
+        am2[bl] = live2 ? mx : 0.0f;
+        wm = fmaxf(wm, am2[bl]);
+      }
+    }
     float A = 0.0f;
     if (GMAX) {
 #pragma unroll
@@ -622,6 +638,35 @@ __global__ __launch_bounds__(64 * kStrWaves) void gemm_nv_stream(
         if (XM == kXQuant && out) {
           *reinterpret_cast<u32x2*>(qcodes + xsrc * kbytes + (xv0 + 16 * bl) / 2) = (u32x2){wd[0], wd[1]};
           qscales[xsrc * kblocks + (xv0 + 16 * bl) / 16] = (uint8_t)sbyte;
+        }
+      }
+      if constexpr (Q2) {
+        // the second group of 8 rows, the same arithmetic
+        _Float16* xd2 = &L.x[wave][8 + xrow][16 * NSTEP * xc];
+        const bool out2 = blockIdx.x == 0 && live2;
+#pragma unroll
+        for (int bl = 0; bl < NSTEP; ++bl) {
+          const uint32_t sbyte = e4m3_encode_pos(am2[bl] / dd);
+          const float S = e4m3_decode_pos(sbyte) * s_t;
+          float rs = 1.0f / S;
+          if (!(S != 0.0f && rs < __builtin_inff())) rs = 0.0f;
+          uint32_t wd[2];
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const u32x4 v = xb2[2 * bl + h];
+            uint32_t p = e2m1_pack2<0>(0u, bf16_lo(v[0]) * rs, bf16_hi(v[0]) * rs);
+            p = e2m1_pack2<1>(p, bf16_lo(v[1]) * rs, bf16_hi(v[1]) * rs);
+            p = e2m1_pack2<2>(p, bf16_lo(v[2]) * rs, bf16_hi(v[2]) * rs);
+            p = e2m1_pack2<3>(p, bf16_lo(v[3]) * rs, bf16_hi(v[3]) * rs);
+            wd[h] = p;
+            v8h f = dequant8(p, (_Float16)e4m3_decode_pos(sbyte));
+            if (!live2) f = (v8h){0, 0, 0, 0, 0, 0, 0, 0};
+            *reinterpret_cast<v8h*>(xd2 + 16 * bl + 8 * h) = f;
+          }
+          if (out2) {
+            *reinterpret_cast<u32x2*>(qcodes + xsrc2 * kbytes + (xv0 + 16 * bl) / 2) = (u32x2){wd[0], wd[1]};
+            qscales[xsrc2 * kblocks + (xv0 + 16 * bl) / 16] = (uint8_t)sbyte;
+          }
         }
       }
       if (XM == kXQuant && blockIdx.x == 0 && tid == 0) *qtscale = s_t;
@@ -879,9 +924,13 @@ bool launch_quantize_gemm_decode(int64_t m, int64_t n, int64_t k, const void* x,
   const bool aligned = ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(b_codes) |
                          reinterpret_cast<uintptr_t>(b_scales) | reinterpret_cast<uintptr_t>(a_codes)) &
                         15) == 0;
-  if (!(stream_shape(m, n, k) && aligned)) return false;
-  *err = launch_stream<kXQuant>((int)m, n, (int)k, reinterpret_cast<const uint8_t*>(x), nullptr, nullptr,
-                                b_codes, b_scales, b_tscale, c, c_dtype, a_codes, a_scales, a_tscale, stream);
+  if (!(m >= 1 && m <= 16 && stream_shape(8, n, k) && aligned)) return false;
+  if (m > 8)
+    *err = launch_stream<kXQuant, 2>((int)m, n, (int)k, reinterpret_cast<const uint8_t*>(x), nullptr, nullptr,
+                                     b_codes, b_scales, b_tscale, c, c_dtype, a_codes, a_scales, a_tscale, stream);
+  else
+    *err = launch_stream<kXQuant>((int)m, n, (int)k, reinterpret_cast<const uint8_t*>(x), nullptr, nullptr,
+                                  b_codes, b_scales, b_tscale, c, c_dtype, a_codes, a_scales, a_tscale, stream);
   return true;
 }
 

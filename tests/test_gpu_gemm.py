@@ -335,7 +335,9 @@ def test_rotated_full_size():
     ("nvfp4", 7, 1025, 2048, torch.bfloat16),    # 3 rows per share, last share partial
     ("nvfp4", 16, 64, 256, torch.bfloat16),      # m > 8: quantize + GEMM calls
     ("nvfp4", 8, 4096, 14336, torch.bfloat16),   # long k: quantize + split-k GEMM
-    ("nvfp4", 16, 2000, 4096, torch.bfloat16),   # 16 rows: quantize + stream GEMM
+    ("nvfp4", 16, 2000, 4096, torch.bfloat16),   # 16 rows in one launch
+    ("nvfp4", 9, 16384, 4096, torch.bfloat16),   # 9 rows in one launch, the largest n
+    ("nvfp4", 12, 1000, 2048, torch.bfloat16),
     ("nvfp4", 3, 50, 96, torch.bfloat16),
     ("nvfp4", 8, 200, 4096, torch.float32),      # not bf16: two calls
     ("mxfp4", 8, 100, 4096, torch.bfloat16),
