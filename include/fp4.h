@@ -296,10 +296,12 @@ size_t fp4_quantize_gemm_workspace_size(fp4_format fmt, int64_t m, int64_t n,
  * per call, the weights streamed once (cloudmagazin.com "FP8, FP4 und vLLM",
  * section "Rechnung": token-by-token decoding is bound by reading the
  * weights; hyper.ai, paper 2509.23202, Abstract: activations quantized
- * online).  For NVFP4 with bf16 x, 1 <= m <= 8, k = 2048 or 4096 and
- * n <= 16384 it runs as one launch (the activation quantization happens
- * inside the GEMM's workgroups, each reducing max |x| over the whole tensor
- * itself); otherwise as the two calls.
+ * online).  With bf16 x and 1 <= m <= 16 the activation quantization
+ * happens inside the GEMM's launch: NVFP4 for k = 2048 or 4096 and
+ * n <= 16384 (every workgroup reducing max |x| over the whole tensor
+ * itself), MXFP4 for k a multiple of 2048 and any n (no tensor-wide maximum;
+ * k > 4096 adds the reduction pass of the split k).  Otherwise it runs as
+ * the two calls.
  *   x            in, [m, k] of x_dtype, 16-byte aligned.
  *   a_codes, a_scales, a_tscale   out, as fp4_quantize (COMPUTE mode).
  *   b_*, c, c_dtype               as fp4_gemm.
