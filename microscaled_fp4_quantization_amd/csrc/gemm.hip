@@ -25,8 +25,8 @@ hipError_t launch_gemm_large(int fmt, int64_t m, int64_t n, int64_t k,
 // The large kernels split k over several workgroups per tile when the tiles
 // alone would leave most CUs idle, and the decode kernels split a long k over
 // workgroup rows; the slices' fp32 sums go to the workspace.
-// A small batch past 16 rows (NVFP4 below 96 rows with k = 2048 or 4096 and
-// n <= 16384, the shapes of the NVFP4 decode kernel; MXFP4 up to 32 rows):
+// A small batch past 16 rows (NVFP4 below 96 rows with k = 2048 or 4096, the
+// shapes of the NVFP4 decode kernel for 16 rows; MXFP4 up to 32 rows):
 // the decode kernels over groups of 16 activation rows, W streamed once per
 // group (from the last-level cache after the first).  The generic kernel
 // took 105-207 us for 17..100 rows of an NVFP4 14336x4096 weight, the decode
@@ -34,7 +34,7 @@ hipError_t launch_gemm_large(int fmt, int64_t m, int64_t n, int64_t k,
 // tiles) is as fast as two groups.
 bool small_batch_groups(int fmt, int64_t m, int64_t n, int64_t k) {
   if (m <= 16) return false;
-  if (fmt == kFmtNV) return m < 96 && (k == 2048 || k == 4096) && n <= 16384;
+  if (fmt == kFmtNV) return m < 96 && (k == 2048 || k == 4096);
   return m <= 32 && k % 2048 == 0;
 }
 

@@ -884,7 +884,9 @@ hipError_t launch_gemm_skinny(int fmt, int64_t m, int64_t n, int64_t k,
   if (fmt == kFmtNV && stream_shape(m, n, k) && aligned16)
     return launch_stream<kXCodes>((int)m, n, (int)k, a_codes, a_scales, a_tscale, b_codes, b_scales,
                                   b_tscale, c, c_dtype, nullptr, nullptr, nullptr, stream);
-  if (fmt == kFmtNV && m > 8 && m <= 16 && stream_shape(8, n, k) && aligned16)
+  // 9..16 rows: any n (past 16384 rows, whole rounds of up-to-64-row
+  // workgroups); 8 rows past 16384 keep the older decode kernel below, as fast
+  if (fmt == kFmtNV && m > 8 && m <= 16 && (k == 2048 || k == 4096) && n >= 1 && aligned16)
     return launch_stream<kXCodes, 2>((int)m, n, (int)k, a_codes, a_scales, a_tscale, b_codes, b_scales,
                                      b_tscale, c, c_dtype, nullptr, nullptr, nullptr, stream);
   const int nsplit = stream_split(fmt, m, n, k);

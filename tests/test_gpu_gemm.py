@@ -144,6 +144,7 @@ def test_mxfp4_decode_stream(m, n, k, out_dtype):
 @pytest.mark.parametrize("fmt,m,n,k,out_dtype", [
     ("nvfp4", 17, 1000, 4096, "bf16"),    # 16 + 1 rows
     ("nvfp4", 40, 14336, 2048, "f32"),
+    ("nvfp4", 33, 28672, 4096, "bf16"),   # groups past 16384 weight rows
     ("nvfp4", 95, 333, 4096, "bf16"),     # the last group of 15 rows, ragged shares
     ("nvfp4", 96, 14336, 4096, "bf16"),   # 96..127 rows: the large kernel, one partly filled row of tiles
     ("nvfp4", 127, 3000, 8192, "f32"),    # the same with k split over workgroups
@@ -170,7 +171,8 @@ def test_small_batch_groups(fmt, m, n, k, out_dtype):
 @pytest.mark.parametrize("m,n,k,out_dtype", [
     (16, 14336, 4096, "bf16"),     # all 16 columns of the MFMA tile
     (9, 1000, 2048, "f32"),        # one row past 8
-    (12, 16384, 2048, "bf16"),     # the largest n
+    (12, 16384, 2048, "bf16"),     # the largest n of one round
+    (16, 20000, 4096, "f32"),      # past it: whole rounds of workgroups
     (16, 333, 4096, "f32"),        # ragged shares
 ])
 def test_nvfp4_decode_16_rows(m, n, k, out_dtype):
