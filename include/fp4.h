@@ -258,16 +258,18 @@ fp4_status fp4_gemm(fp4_format fmt, int64_t m, int64_t n, int64_t k,
  *                 aligned (may be NULL when that size is 0); contents on
  *                 entry do not matter; calls that overlap must not share one.
  *   Numerics: the weights are widened exactly (v * E4M3 scale in fp16 or
- *   fp32, v * 2^e); NVFP4 with bf16 X, k = 2048, 4096 or a larger multiple
- *   of 2048 and 16-byte aligned x / codes / scales takes the streaming path:
- *   each row of X is cut into pieces of 128 or 256 values, each piece scaled
- *   by the power of two that brings its max |x| into [1, 2) and rounded to
- *   fp16 (exact for every value above 2^-15 of that max), the products
- *   accumulate in fp32 on the matrix cores and each piece's partial sums
- *   are scaled back before they are added (for k > 4096 the sums of each
- *   chunk of 2048 or 4096 values go through the workspace); other shapes
- *   sum fp32 products.  Tolerance against the float64 reference: relative
- *   Frobenius error <= 1e-3.
+ *   fp32, v * 2^e).  NVFP4 with bf16 or fp16 X, k = 2048, 4096 or a larger
+ *   multiple of 2048 and 16-byte aligned x / codes / scales takes the
+ *   streaming path: each row of X is cut into pieces of 128 or 256 values,
+ *   each piece scaled by the power of two that brings its max |x| into
+ *   [1, 2) and rounded to fp16 (exact for every value above 2^-15 of that
+ *   max), the products accumulate in fp32 on the matrix cores and each
+ *   piece's partial sums are scaled back before they are added (for
+ *   k > 4096 the sums of each chunk of 2048 or 4096 values go through the
+ *   workspace).  MXFP4 with bf16 X takes the same shapes with the weights
+ *   widened exactly to bf16 on the bf16 matrix cores.  Other shapes sum fp32
+ *   products.  Tolerance against the float64 reference: relative Frobenius
+ *   error <= 1e-3.
  *   m = 0 or n = 0 enqueues nothing.  Returns FP4_OK, FP4_EINVAL,
  *   FP4_EUNSUPPORTED or FP4_EHIP.
  */

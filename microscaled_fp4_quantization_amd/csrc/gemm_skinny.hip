@@ -404,7 +404,11 @@ struct StreamLds {
 // most of it, so the activation loads go first and only the first tile's
 // weights with them; the rest goes out once every wave's part of max |X| is
 // in.
-constexpr int kXCodes = 0, kXQuant = 1, kXRaw = 2;
+//   kXRawH   fp16 X, the same way as kXRaw.
+constexpr int kXCodes = 0, kXQuant = 1, kXRaw = 2, kXRawH = 3;
+
+__device__ __forceinline__ float f16_lo(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFFu)); }
+__device__ __forceinline__ float f16_hi(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16)); }
 
 // XH = 2: up to 16 activation rows, all 16 columns of the MFMA tile (XH = 1:
 // 8 rows, the other 8 columns repeat them).
@@ -424,7 +428,11 @@ __global__ __launch_bounds__(64 * kStrWaves) void gemm_nv_stream(
   __shared__ float red[kStrWaves];
   StreamLds<NSTEP, XH>& L = LU.s;
 
-  constexpr bool QX = XM != kXCodes;                  // bf16 X loaded here
+  constexpr bool QX = XM != kXCodes;                  // 16-bit X loaded here
+  constexpr bool RAW = XM == kXRaw || XM == kXRawH;   // W4A16
+  // the two 16-bit values of a dword of X, widened exactly
+  auto xlo = [](uint32_t w) { return XM == kXRawH ? f16_lo(w) : bf16_lo(w); };
+  auto xhi = [](uint32_t w) { return XM == kXRawH ? f16_hi(w) : bf16_hi(w); };
   constexpr bool GMAX = XM == kXQuant;                // max |X| over the tensor first
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -448,7 +456,7 @@ __global__ __launch_bounds__(64 * kStrWaves) void gemm_nv_stream(
   uint32_t xq[XH][2 * NSTEP];                         // codes, 8 per dword (kXCodes)
   uint32_t xs[XH];                                    // NSTEP scale bytes (kXCodes)
   // bf16 X with 16 rows: row 8 + lane / 8 as well
-  constexpr bool RAW2 = XM == kXRaw && XH == 2;
+  constexpr bool RAW2 = RAW && XH == 2;
   constexpr bool Q2 = XM == kXQuant && XH == 2;
   u32x4 xb2[(RAW2 || Q2) ? 2 * NSTEP : 1];
   const bool live2 = 8 + xrow < m;
@@ -525,7 +533,7 @@ __global__ __launch_bounds__(64 * kStrWaves) void gemm_nv_stream(
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          mx = fmaxf(mx, fmaxf(fabsf(bf16_lo(xb[2 * bl + i][j])), fabsf(bf16_hi(xb[2 * bl + i][j]))));
+          mx = fmaxf(mx, fmaxf(fabsf(xlo(xb[2 * bl + i][j])), fabsf(xhi(xb[2 * bl + i][j]))));
       am[bl] = live ? mx : 0.0f;
     }
     float wm = NSTEP == 2 ? fmaxf(am[0], am[NSTEP - 1]) : am[0];
@@ -539,7 +547,7 @@ __global__ __launch_bounds__(64 * kStrWaves) void gemm_nv_stream(
         for (int i = 0; i < 2; ++i)
 #pragma unroll
           for (int j = 0; j < 4; ++j)
-            mx = fmaxf(mx, fmaxf(fabsf(bf16_lo(xb2[2 * bl + i][j])), fabsf(bf16_hi(xb2[2 * bl + i][j]))));
+            mx = fmaxf(mx, fmaxf(fabsf(xlo(xb2[2 * bl + i][j])), fabsf(xhi(xb2[2 * bl + i][j]))));
         am2[bl] = live2 ? mx : 0.0f;
         wm = fmaxf(wm, am2[bl]);
       }
@@ -565,7 +573,7 @@ __global__ __launch_bounds__(64 * kStrWaves) void gemm_nv_stream(
       for (int off = 4; off >= 1; off >>= 1) wm = fmaxf(wm, __shfl_xor(wm, off));
       A = wm;
     }
-    if (XM == kXRaw) {
+    if (RAW) {
       // 2^-E with the slice row's max |x| in [2^E, 2^(E+1)); 1 for a zero row
       const int eb = (int)(as_u(A) >> 23);
       const int pe = A == 0.0f ? 127 : (254 - eb < 1 ? 1 : 254 - eb);
@@ -576,8 +584,8 @@ __global__ __launch_bounds__(64 * kStrWaves) void gemm_nv_stream(
         v8h f;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          f[2 * j] = (_Float16)(bf16_lo(xb[i][j]) * p2);
-          f[2 * j + 1] = (_Float16)(bf16_hi(xb[i][j]) * p2);
+          f[2 * j] = (_Float16)(xlo(xb[i][j]) * p2);
+          f[2 * j + 1] = (_Float16)(xhi(xb[i][j]) * p2);
         }
         if (!live) f = (v8h){0, 0, 0, 0, 0, 0, 0, 0};
         *reinterpret_cast<v8h*>(xdst + 8 * i) = f;
@@ -589,7 +597,7 @@ __global__ __launch_bounds__(64 * kStrWaves) void gemm_nv_stream(
         for (int i = 0; i < 2 * NSTEP; ++i)
 #pragma unroll
           for (int j = 0; j < 4; ++j)
-            m2 = fmaxf(m2, fmaxf(fabsf(bf16_lo(xb2[i][j])), fabsf(bf16_hi(xb2[i][j]))));
+            m2 = fmaxf(m2, fmaxf(fabsf(xlo(xb2[i][j])), fabsf(xhi(xb2[i][j]))));
         m2 = live2 ? m2 : 0.0f;
 #pragma unroll
         for (int off = 4; off >= 1; off >>= 1) m2 = fmaxf(m2, __shfl_xor(m2, off));
@@ -603,8 +611,8 @@ __global__ __launch_bounds__(64 * kStrWaves) void gemm_nv_stream(
           v8h f;
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            f[2 * j] = (_Float16)(bf16_lo(xb2[i][j]) * q2);
-            f[2 * j + 1] = (_Float16)(bf16_hi(xb2[i][j]) * q2);
+            f[2 * j] = (_Float16)(xlo(xb2[i][j]) * q2);
+            f[2 * j + 1] = (_Float16)(xhi(xb2[i][j]) * q2);
           }
           if (!live2) f = (v8h){0, 0, 0, 0, 0, 0, 0, 0};
           *reinterpret_cast<v8h*>(xd2 + 8 * i) = f;
@@ -722,7 +730,7 @@ __global__ __launch_bounds__(64 * kStrWaves) void gemm_nv_stream(
     }
   }
 
-  if (XM == kXRaw) {
+  if (RAW) {
     // back to the scale of X: acc column lane % 16 is activation row
     // lane % 16, whose 2^E lane 8 (lane % 8) holds (rows >= 8 are zero)
     float e = __shfl(xscale, 8 * (lane & 7));
@@ -744,7 +752,7 @@ __global__ __launch_bounds__(64 * kStrWaves) void gemm_nv_stream(
     v4f sum = LU.part[0][tl][l];
 #pragma unroll
     for (int wv = 1; wv < kStrWaves; ++wv) sum += LU.part[wv][tl][l];
-    const float scale = (XM == kXQuant ? xscale : XM == kXRaw ? 1.0f : *at) * (*bt);
+    const float scale = (XM == kXQuant ? xscale : RAW ? 1.0f : *at) * (*bt);
     // D layout: lane l holds weight rows 4 (l / 16) + e of the tile, activation row l % 16
     const int xr = l & 15, lr = 16 * tl + 4 * (l >> 4);   // first row within the share
     const int64_t ni = nbase + lr;
@@ -756,7 +764,7 @@ __global__ __launch_bounds__(64 * kStrWaves) void gemm_nv_stream(
         float* pp = part + (int64_t)blockIdx.y * pstride + o;
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          if (lr + e < rows_per_wg && ni + e <= nlast) pp[e] = XM == kXRaw ? sum[e] * scale : sum[e];
+          if (lr + e < rows_per_wg && ni + e <= nlast) pp[e] = RAW ? sum[e] * scale : sum[e];
       } else if (c_dtype != kInF32 && lr + 3 < rows_per_wg && ni + 3 <= nlast && (o & 3) == 0) {
         const __bf16 h[4] = {(__bf16)(sum[0] * scale), (__bf16)(sum[1] * scale), (__bf16)(sum[2] * scale),
                              (__bf16)(sum[3] * scale)};
@@ -963,7 +971,7 @@ hipError_t launch_gemm_w4a16(int fmt, int64_t m, int64_t n, int64_t k, const voi
                              hipStream_t stream) {
   const bool aligned = ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(b_codes) |
                          reinterpret_cast<uintptr_t>(b_scales)) & 15) == 0;
-  const int nsplit = x_dtype == kInBF16 ? w4a16_chunks(fmt, n, k) : 0;
+  const int nsplit = x_dtype == kInBF16 || x_dtype == kInF16 ? w4a16_chunks(fmt, n, k) : 0;
   if (nsplit > 0 && aligned) {
     // streaming kernel, 16 activation rows per launch; a split k's chunk
     // sums (times the tensor scale) added by the reduction pass, which
@@ -974,11 +982,17 @@ hipError_t launch_gemm_w4a16(int fmt, int64_t m, int64_t n, int64_t k, const voi
       const int mc = (int)(m - i0 < 16 ? m - i0 : 16);
       const uint8_t* xa = reinterpret_cast<const uint8_t*>(x) + i0 * k * 2;
       void* ca = reinterpret_cast<char*>(c) + i0 * n * osz;
-      hipError_t e =
-          mc > 8 ? launch_stream<kXRaw, 2>(mc, n, (int)k, xa, nullptr, nullptr, b_codes, b_scales, b_tscale, ca,
-                                           c_dtype, nullptr, nullptr, nullptr, stream, nsplit, part)
-                 : launch_stream<kXRaw>(mc, n, (int)k, xa, nullptr, nullptr, b_codes, b_scales, b_tscale, ca,
-                                        c_dtype, nullptr, nullptr, nullptr, stream, nsplit, part);
+      hipError_t e;
+      if (x_dtype == kInF16)
+        e = mc > 8 ? launch_stream<kXRawH, 2>(mc, n, (int)k, xa, nullptr, nullptr, b_codes, b_scales, b_tscale, ca,
+                                              c_dtype, nullptr, nullptr, nullptr, stream, nsplit, part)
+                   : launch_stream<kXRawH>(mc, n, (int)k, xa, nullptr, nullptr, b_codes, b_scales, b_tscale, ca,
+                                           c_dtype, nullptr, nullptr, nullptr, stream, nsplit, part);
+      else
+        e = mc > 8 ? launch_stream<kXRaw, 2>(mc, n, (int)k, xa, nullptr, nullptr, b_codes, b_scales, b_tscale, ca,
+                                             c_dtype, nullptr, nullptr, nullptr, stream, nsplit, part)
+                   : launch_stream<kXRaw>(mc, n, (int)k, xa, nullptr, nullptr, b_codes, b_scales, b_tscale, ca,
+                                          c_dtype, nullptr, nullptr, nullptr, stream, nsplit, part);
       if (e == hipSuccess && nsplit > 1)
         e = launch_split_reduce(part, nsplit, mc, n, nullptr, nullptr, ca, c_dtype, stream);
       if (e != hipSuccess) return e;

@@ -94,6 +94,22 @@ def test_mxfp4_stream(m, n, k):
     check("mxfp4", x, w, "f32" if m % 2 else "bf16", wq=wq)
 
 
+@pytest.mark.parametrize("m,n,k", [
+    (8, 14336, 4096),        # the decode shape with fp16 activations
+    (16, 333, 2048),         # 16 rows in one launch
+    (5, 4096, 14336),        # k split in 7 chunks of 2048
+])
+def test_fp16_activations_stream(m, n, k):
+    # NVFP4 weights and fp16 X on the decode stream kernel: X widened
+    # exactly from fp16, one row near fp16's largest value, one row tiny
+    x = randn((m, k), torch.float32, m + n + 2)
+    x[0] *= 5.0e3                            # up to ~2.5e4, below fp16's 65504
+    x[m - 1] *= 1.0e-5
+    x = x.to(torch.float16)
+    w = randn((n, k), torch.bfloat16, k + 2, 0.02)
+    check("nvfp4", x, w, "f32" if m % 2 else "bf16")
+
+
 def test_mxfp4_and_other_activation_types():
     w = randn((300, 1024), torch.bfloat16, 1, 0.02)
     for dt in (torch.bfloat16, torch.float16, torch.float32):

@@ -83,10 +83,11 @@ def test_gemm_special_scale_bytes(fmt, shape):
         compare(c.double().cpu().numpy(), ref, out_dtype)
 
 
-# fp4_gemm_w4a16: NVFP4 and MXFP4 with bf16 X and k 2048 (the streaming
-# kernels); fp32 X and k 256 (the generic kernel).
+# fp4_gemm_w4a16: NVFP4 with bf16 or fp16 X and MXFP4 with bf16 X, k 2048
+# (the streaming kernels); fp32 X and k 256 (the generic kernel).
 @pytest.mark.parametrize("fmt,x_dtype,k", [("nvfp4", torch.bfloat16, 2048), ("nvfp4", torch.float32, 256),
-                                           ("mxfp4", torch.bfloat16, 256), ("mxfp4", torch.bfloat16, 2048)])
+                                           ("mxfp4", torch.bfloat16, 256), ("mxfp4", torch.bfloat16, 2048),
+                                           ("nvfp4", torch.float16, 2048)])
 def test_w4a16_special_scale_bytes(fmt, x_dtype, k):
     m, n = 6, 80
     rng = np.random.default_rng(k + n)
