@@ -25,29 +25,44 @@ hipError_t launch_gemm_large(int fmt, int64_t m, int64_t n, int64_t k,
 // The large kernels split k over several workgroups per tile when the tiles
 // alone would leave most CUs idle, and the decode kernels split a long k over
 // workgroup rows; the slices' fp32 sums go to the workspace.
-// A small batch past 16 rows (NVFP4 below 96 rows with k = 2048 or 4096, the
-// shapes of the NVFP4 decode kernel for 16 rows; MXFP4 up to 32 rows):
-// the decode kernels over groups of 16 activation rows, W streamed once per
-// group (from the last-level cache after the first).  The generic kernel
-// took 105-207 us for 17..100 rows of an NVFP4 14336x4096 weight, the decode
-// kernel 10 us per 16 rows; from 33 MXFP4 rows the large kernel (one row of
-// tiles) is as fast as two groups.
+// A small batch past 16 rows on the decode kernels, in groups of 16
+// activation rows, W streamed once per group:
+// - NVFP4 with k = 2048 or 4096 below 96 rows.  The generic kernel took
+//   105-207 us for 17..100 rows of a 14336x4096 weight, the decode kernel
+//   10 us per 16 rows.
+// - NVFP4 with a longer k (a multiple of 2048, at most 64 chunks of the
+//   split-k decode kernel) up to 64 rows.  A group costs about what 16 rows
+//   alone do (13.6 us for a 4096x14336 weight, 38 us for 8192x28672, 9.5
+//   us for 4096x8192), the large kernel with one row of tiles a flat 84,
+//   146 and 55 us: four groups tie or win on all three, more lose on the
+//   largest.
+// - MXFP4 up to 32 rows; from 33 the large kernel (one row of tiles) is as
+//   fast as two groups.
+constexpr int64_t kNvLongGroupsBelow = 65;
+
+bool nv_long_k_chunks(int64_t k) {
+  return k > 4096 && k % 2048 == 0 && (k % 4096 == 0 ? k / 4096 : k / 2048) <= 64;
+}
+
 bool small_batch_groups(int fmt, int64_t m, int64_t n, int64_t k) {
   if (m <= 16) return false;
-  if (fmt == kFmtNV) return m < 96 && (k == 2048 || k == 4096);
+  if (fmt == kFmtNV) return (k == 2048 || k == 4096) ? m < 96 : nv_long_k_chunks(k) && m < kNvLongGroupsBelow;
   return m <= 32 && k % 2048 == 0;
 }
 
-// NVFP4 with 96..127 rows: the large kernel with one partly filled row of
-// tiles (rows past m load zeros and are not stored), 50 us for 100 rows of
-// a 14336x4096 weight against 58 us in 16-row groups.
+// NVFP4 below 128 rows past the groups (from 96 rows, or from 65 with a
+// long k): the large kernel with one partly filled row of tiles (rows past m
+// load zeros and are not stored), 50 us for 100 rows of a 14336x4096 weight
+// against 58 us in 16-row groups.
 bool large_nv_below_128(int fmt, int64_t m, int64_t n, int64_t k) {
-  return fmt == kFmtNV && m >= 96 && m < 128 && gemm_large_supported(fmt, 128, n, k);
+  if (fmt != kFmtNV || m >= 128 || m <= 16 || small_batch_groups(fmt, m, n, k)) return false;
+  return m >= (nv_long_k_chunks(k) ? kNvLongGroupsBelow : 96) && gemm_large_supported(fmt, 128, n, k);
 }
 
 size_t gemm_workspace_bytes(int fmt, int64_t m, int64_t n, int64_t k) {
-  if (m <= 16 || small_batch_groups(fmt, m, n, k))
-    return fmt == kFmtMX ? gemm_mx_stream_workspace_bytes(m, n, k) : gemm_skinny_workspace_bytes(fmt, m, n, k);
+  if (m <= 16 || small_batch_groups(fmt, m, n, k))   // one group's, reused by the next
+    return fmt == kFmtMX ? gemm_mx_stream_workspace_bytes(m, n, k)
+                         : gemm_skinny_workspace_bytes(fmt, m < 16 ? m : 16, n, k);
   if (large_nv_below_128(fmt, m, n, k)) return gemm_large_workspace_bytes(fmt, m, n, k);
   if (gemm_large_supported(fmt, m, n, k)) return gemm_large_workspace_bytes(fmt, m, n, k);
   return 0;

@@ -874,10 +874,21 @@ int stream_split(int fmt, int64_t m, int64_t n, int64_t k) {
   return (n + 16 * kStrTiles - 1) / (16 * kStrTiles) * s <= slots ? (int)s : 0;
 }
 
+// Chunks of the split-k stream kernel for NVFP4 codes with 9..16 rows and k >
+// 4096 a multiple of 2048 (chunks of 4096 when k allows, else 2048; at most
+// 64), in whole rounds of workgroups for any n; 0 for any other shape.  With
+// 16 activation rows per workgroup, the weights' dequantization is shared
+// by twice the columns, so more than one round still pays here.
+int stream_split16(int fmt, int64_t m, int64_t n, int64_t k) {
+  if (fmt != kFmtNV || m <= 8 || m > 16 || n < 1 || k <= 4096 || k % 2048 != 0) return 0;
+  const int64_t s = k % 4096 == 0 ? k / 4096 : k / 2048;
+  return s <= 64 ? (int)s : 0;
+}
+
 }  // namespace
 
 size_t gemm_skinny_workspace_bytes(int fmt, int64_t m, int64_t n, int64_t k) {
-  const int s = stream_split(fmt, m, n, k);
+  const int s = m > 8 ? stream_split16(fmt, m, n, k) : stream_split(fmt, m, n, k);
   return s > 1 ? (size_t)s * (size_t)gemm_split_stride(m, n) * sizeof(float) : 0;
 }
 
@@ -897,12 +908,15 @@ hipError_t launch_gemm_skinny(int fmt, int64_t m, int64_t n, int64_t k,
   if (fmt == kFmtNV && m > 8 && m <= 16 && (k == 2048 || k == 4096) && n >= 1 && aligned16)
     return launch_stream<kXCodes, 2>((int)m, n, (int)k, a_codes, a_scales, a_tscale, b_codes, b_scales,
                                      b_tscale, c, c_dtype, nullptr, nullptr, nullptr, stream);
-  const int nsplit = stream_split(fmt, m, n, k);
+  const int nsplit = m > 8 ? stream_split16(fmt, m, n, k) : stream_split(fmt, m, n, k);
   if (nsplit > 1 && aligned16) {
     float* part = reinterpret_cast<float*>(workspace);
-    const hipError_t e = launch_stream<kXCodes>((int)m, n, (int)k, a_codes, a_scales, a_tscale, b_codes,
-                                                b_scales, b_tscale, c, c_dtype, nullptr, nullptr, nullptr,
-                                                stream, nsplit, part);
+    const hipError_t e = m > 8 ? launch_stream<kXCodes, 2>((int)m, n, (int)k, a_codes, a_scales, a_tscale, b_codes,
+                                                           b_scales, b_tscale, c, c_dtype, nullptr, nullptr,
+                                                           nullptr, stream, nsplit, part)
+                               : launch_stream<kXCodes>((int)m, n, (int)k, a_codes, a_scales, a_tscale, b_codes,
+                                                        b_scales, b_tscale, c, c_dtype, nullptr, nullptr, nullptr,
+                                                        stream, nsplit, part);
     if (e != hipSuccess) return e;
     return launch_split_reduce(part, nsplit, m, n, a_tscale, b_tscale, c, c_dtype, stream);
   }

@@ -53,7 +53,11 @@ def test_workspace_sizes():
     assert L.fp4_gemm_workspace_size(NV, 8, 14336, 4096) == 0      # one chunk: no split
     assert L.fp4_gemm_workspace_size(NV, 8, 14336, 8192) == 0      # 448 workgroups for 256 slots
     assert L.fp4_gemm_workspace_size(NV, 8, 16384, 6144) == 0      # 768 for 512
-    assert L.fp4_gemm_workspace_size(NV, 9, 4096, 14336) == 0      # m > 8
+    # 9..16 rows: 16 activation rows per workgroup, any n (whole rounds)
+    assert L.fp4_gemm_workspace_size(NV, 9, 4096, 14336) == 7 * 9 * 4096 * 4
+    assert L.fp4_gemm_workspace_size(NV, 16, 14336, 8192) == 2 * 16 * 14336 * 4
+    assert L.fp4_gemm_workspace_size(NV, 32, 4096, 14336) == 7 * 16 * 4096 * 4   # groups of 16 rows
+    assert L.fp4_gemm_workspace_size(NV, 16, 4096, 4096) == 0      # one chunk: no split
     assert L.fp4_gemm_workspace_size(NV, 8, 4096, 5120) == 0       # k not a multiple of 2048
     assert L.fp4_gemm_workspace_size(MX, 8, 4096, 14336) == 7 * 8 * 4096 * 4   # MXFP4: m <= 16, any n
     assert L.fp4_gemm_workspace_size(MX, 16, 16384, 6144) == 3 * 16 * 16384 * 4

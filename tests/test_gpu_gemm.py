@@ -149,6 +149,12 @@ def test_mxfp4_decode_stream(m, n, k, out_dtype):
     ("nvfp4", 96, 14336, 4096, "bf16"),   # 96..127 rows: the large kernel, one partly filled row of tiles
     ("nvfp4", 127, 3000, 8192, "f32"),    # the same with k split over workgroups
     ("nvfp4", 100, 60000, 512, "bf16"),   # the same with 256-column tiles
+    ("nvfp4", 40, 4096, 14336, "bf16"),   # a long k: 16-row groups, k split in 7 chunks
+    ("nvfp4", 17, 777, 6144, "f32"),      # the last group of one row (8-row split)
+    ("nvfp4", 63, 1000, 8192, "f32"),     # the last group of 15 rows
+    ("nvfp4", 64, 4096, 14336, "bf16"),   # four groups
+    ("nvfp4", 65, 4096, 14336, "bf16"),   # a long k from 65 rows: the large kernel
+    ("nvfp4", 100, 2000, 12288, "f32"),
     ("mxfp4", 17, 777, 4096, "f32"),
     ("mxfp4", 32, 5000, 8192, "bf16"),    # two groups, each with k split in 2 chunks
     ("mxfp4", 33, 14336, 4096, "f32"),    # 33..255 rows: the large kernel, one row of tiles at row 0
@@ -190,6 +196,10 @@ def test_nvfp4_decode_16_rows(m, n, k, out_dtype):
     (1, 2000, 8192, "f32"),        # 2 chunks of 4096
     (6, 8192, 6144, "bf16"),       # 3 chunks of 2048, 384 workgroups
     (3, 777, 12288, "f32"),        # 3 chunks of 4096, ragged n
+    (16, 4096, 14336, "bf16"),     # 16 rows: 7 chunks of 2048
+    (9, 20000, 8192, "f32"),       # 9 rows, whole rounds of workgroups
+    (12, 777, 6144, "bf16"),       # ragged n
+    (13, 3000, 16384, "f32"),      # 4 chunks of 4096
 ])
 def test_nvfp4_decode_split_k(m, n, k, out_dtype):
     # the NVFP4 decode kernel with k split over workgroup rows (fp32 partial
