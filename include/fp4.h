@@ -208,9 +208,11 @@ fp4_status fp4_dequantize(fp4_format fmt, const uint8_t* codes,
 /* Bytes of device workspace fp4_gemm needs for these sizes: nonzero only
  * where k is split over several workgroups per output tile (the slices'
  * fp32 partial sums, added in a fixed order by a second pass): large m with
- * few output tiles, which would leave most of the GPU idle, and a long k
- * (k > 4096, a multiple of 2048) with few activation rows (NVFP4: m <= 8
- * over few enough weight rows; MXFP4: m <= 16). */
+ * few output tiles, which would leave most of the GPU idle, and a k of
+ * more than one chunk with few activation rows (NVFP4, up to 64 rows: k a
+ * multiple of 128 past 4096 values, or past 2048 where k is not a multiple
+ * of 4096; MXFP4, up to 32 rows: k > 4096 a multiple of 2048).  Rows past
+ * 16 go in groups of 16 that reuse one group's workspace. */
 size_t fp4_gemm_workspace_size(fp4_format fmt, int64_t m, int64_t n, int64_t k);
 
 /*
@@ -258,15 +260,17 @@ fp4_status fp4_gemm(fp4_format fmt, int64_t m, int64_t n, int64_t k,
  *                 aligned (may be NULL when that size is 0); contents on
  *                 entry do not matter; calls that overlap must not share one.
  *   Numerics: the weights are widened exactly (v * E4M3 scale in fp16 or
- *   fp32, v * 2^e).  NVFP4 with bf16 or fp16 X, k = 2048, 4096 or a larger
- *   multiple of 2048 and 16-byte aligned x / codes / scales takes the
+ *   fp32, v * 2^e).  NVFP4 with bf16 or fp16 X, k a multiple of 128 from
+ *   2048 on (at most 64 chunks of 2048 or 4096 values) and 16-byte aligned
+ *   x / codes / scales takes the
  *   streaming path: each row of X is cut into pieces of 128 or 256 values,
  *   each piece scaled by the power of two that brings its max |x| into
  *   [1, 2) and rounded to fp16 (exact for every value above 2^-15 of that
  *   max), the products accumulate in fp32 on the matrix cores and each
  *   piece's partial sums are scaled back before they are added (for
- *   k > 4096 the sums of each chunk of 2048 or 4096 values go through the
- *   workspace).  MXFP4 with bf16 X takes the same shapes with the weights
+ *   more than one chunk the sums of each chunk of 2048 or 4096 values go
+ *   through the workspace).  MXFP4 with bf16 X and k a multiple of 2048
+ *   takes the same path with the weights
  *   widened exactly to bf16 on the bf16 matrix cores.  Other shapes sum fp32
  *   products.  Tolerance against the float64 reference: relative Frobenius
  *   error <= 1e-3.
@@ -280,8 +284,10 @@ fp4_status fp4_gemm_w4a16(fp4_format fmt, const void* x, fp4_dtype x_dtype,
                           void* workspace, size_t workspace_bytes, void* stream);
 
 /* Bytes of device workspace fp4_gemm_w4a16 needs for these sizes: nonzero
- * only for k > 4096 a multiple of 2048 (the fp32 sums of each chunk of k for
- * up to 16 rows of X at a time). */
+ * only for a k of more than one chunk (NVFP4: a multiple of 128 past 4096
+ * values, or past 2048 where k is not a multiple of 4096; MXFP4: k > 4096 a
+ * multiple of 2048): the fp32 sums of each chunk of k for up to 16 rows of
+ * X at a time. */
 size_t fp4_gemm_w4a16_workspace_size(fp4_format fmt, int64_t m, int64_t n, int64_t k);
 
 /* Bytes of device workspace fp4_quantize_gemm needs for these sizes. */

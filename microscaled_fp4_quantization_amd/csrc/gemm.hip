@@ -8,6 +8,7 @@ hipError_t launch_gemm_simple(int fmt, int64_t m, int64_t n, int64_t k,
                               void* c, int c_dtype, hipStream_t stream);
 
 size_t gemm_skinny_workspace_bytes(int fmt, int64_t m, int64_t n, int64_t k);
+int64_t gemm_stream_chunks(int64_t k);
 hipError_t launch_gemm_skinny(int fmt, int64_t m, int64_t n, int64_t k,
                               const uint8_t* a_codes, const uint8_t* a_scales,
                               const float* a_tscale, const uint8_t* b_codes,
@@ -27,7 +28,7 @@ hipError_t launch_gemm_large(int fmt, int64_t m, int64_t n, int64_t k,
 // workgroup rows; the slices' fp32 sums go to the workspace.
 // A small batch past 16 rows on the decode kernels, in groups of 16
 // activation rows, W streamed once per group:
-// - NVFP4 with k = 2048 or 4096 below 96 rows.  The generic kernel took
+// - NVFP4 with one chunk of k (2048..4096 values) below 96 rows.  The generic kernel took
 //   105-207 us for 17..100 rows of a 14336x4096 weight, the decode kernel
 //   10 us per 16 rows.
 // - NVFP4 with a longer k (a multiple of 2048, at most 64 chunks of the
@@ -41,12 +42,13 @@ hipError_t launch_gemm_large(int fmt, int64_t m, int64_t n, int64_t k,
 constexpr int64_t kNvLongGroupsBelow = 65;
 
 bool nv_long_k_chunks(int64_t k) {
-  return k > 4096 && k % 2048 == 0 && (k % 4096 == 0 ? k / 4096 : k / 2048) <= 64;
+  const int64_t s = gemm_stream_chunks(k);
+  return s >= 2 && s <= 64;
 }
 
 bool small_batch_groups(int fmt, int64_t m, int64_t n, int64_t k) {
   if (m <= 16) return false;
-  if (fmt == kFmtNV) return (k == 2048 || k == 4096) ? m < 96 : nv_long_k_chunks(k) && m < kNvLongGroupsBelow;
+  if (fmt == kFmtNV) return gemm_stream_chunks(k) == 1 ? m < 96 : nv_long_k_chunks(k) && m < kNvLongGroupsBelow;
   return m <= 32 && k % 2048 == 0;
 }
 

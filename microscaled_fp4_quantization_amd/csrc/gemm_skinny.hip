@@ -352,12 +352,13 @@ __global__ __launch_bounds__(256) void gemm_nv_decode(
 }
 
 
-// ---- NVFP4 weight-stream kernel (m <= 16, k = 2048 or 4096 or split) ---------
+// ---- NVFP4 weight-stream kernel (m <= 16, k in chunks of 2048 or 4096) -------
 // The weight rows are dealt out evenly: one workgroup of 16 waves per
 // CU-share of R = ceil(n / 256) rows (at most 64: up to four 16-row MFMA
 // tiles, the last possibly partial), so every CU streams the same number of
-// bytes.  The 16 waves split k: wave w takes the slice [w k / 16, (w + 1) k /
-// 16), NSTEP = k / 2048 steps of 128 values, for all its tiles, and issues
+// bytes.  The 16 waves split a chunk of 2048 NSTEP values of k (NSTEP = 1 or
+// 2; k in one chunk, or split over workgroup rows): wave w takes the slice
+// of NSTEP steps of 128 values at 128 NSTEP w, for all its tiles, and issues
 // all its loads at once.  Requests are not served in issue order (a wave's
 // data tends to arrive in one burst at any time during the stream), so each
 // wave depends only on its own loads: it dequantizes its activation slice and
@@ -443,7 +444,10 @@ __global__ __launch_bounds__(64 * kStrWaves) void gemm_nv_stream(
   // split k (part != nullptr; codes in or W4A16): workgroup row blockIdx.y
   // takes the 2048 NSTEP values from kc0 on, and its fp32 sums go to part
   const int kc0 = (int)blockIdx.y * (kStrWaves * 128 * NSTEP);
-  const int ks0 = kc0 + wave * (128 * NSTEP);         // first value of this wave's slice
+  // k not a whole number of chunks (codes in, W4A16): a slice that starts
+  // past k loads the last slice again, in bounds, and adds nothing
+  const bool kdead = kc0 + wave * (128 * NSTEP) >= k;
+  const int ks0 = kdead ? k - 128 * NSTEP : kc0 + wave * (128 * NSTEP);   // first value of this wave's slice
   const int64_t kbytes = k / 2, kblocks = k / 16;
 
   // ---- activation slice: lane -> row lane / 8, the 16 NSTEP values (NSTEP
@@ -745,7 +749,7 @@ __global__ __launch_bounds__(64 * kStrWaves) void gemm_nv_stream(
   // ---- add the 16 slices, store ------------------------------------------------
   __syncthreads();                                    // LDS becomes the partial area
 #pragma unroll
-  for (int tl = 0; tl < NT; ++tl) LU.part[wave][tl][lane] = acc[tl];
+  for (int tl = 0; tl < NT; ++tl) LU.part[wave][tl][lane] = kdead ? (v4f){0.f, 0.f, 0.f, 0.f} : acc[tl];
   __syncthreads();
   if (tid < 64 * NT) {                                // thread -> (tile, lane)
     const int tl = tid >> 6, l = tid & 63;
@@ -819,16 +823,32 @@ __global__ __launch_bounds__(256) void gemm_w4a16_simple(
   for (int i = 0; i < rows; ++i) store_out(c, c_dtype, (int64_t)(i0 + i) * n + j, acc[i] * ts);
 }
 
-// The stream kernel's one-round shapes with 8 activation rows: m <= 8, k =
-// 2048 or 4096, n <= 16384 (16 rows, a split k and, for W4A16, any n are
-// taken by the launchers below).
+// The one-launch quantize's shapes with 8 activation rows: m <= 8, k = 2048
+// or 4096, n <= 16384 (one round of workgroups).
 bool stream_shape(int64_t m, int64_t n, int64_t k) {
   return m >= 1 && m <= 8 && (k == 2048 || k == 4096) && n >= 1 && n <= 16 * kStrTiles * kStrGroups;
 }
 
+// The stream kernel's k-step: NSTEP = 2 (chunks of 4096 values) when k is a
+// multiple of 4096 or a multiple of 256 in (2048, 4096], else NSTEP = 1
+// (chunks of 2048).
+bool stream_nstep2(int64_t k) { return k % 4096 == 0 || (k > 2048 && k <= 4096 && k % 256 == 0); }
+
+}  // namespace
+
+// Chunks of k for the stream kernel (codes in or W4A16): k from 2048 on, a
+// multiple of 128 (256 with NSTEP = 2); 0 for any other k.  A last chunk
+// that k does not fill leaves the slices past k idle.
+int64_t gemm_stream_chunks(int64_t k) {
+  if (k < 2048 || k % 128 != 0) return 0;
+  return stream_nstep2(k) ? (k + 4095) / 4096 : (k + 2047) / 2048;
+}
+
+namespace {
+
 // An equal share of ceil(n / 256) weight rows per workgroup.
-// nsplit > 1 (codes in): k in nsplit chunks of 2048 NSTEP values, NSTEP = 2
-// when k is a multiple of 4096, the chunks' fp32 sums in part.
+// nsplit > 1: k in nsplit chunks of 2048 NSTEP values (the last one
+// possibly short), the chunks' fp32 sums in part.
 template <int XM, int XH = 1>
 hipError_t launch_stream(int m, int64_t n, int k, const uint8_t* a, const uint8_t* as, const float* at,
                          const uint8_t* b, const uint8_t* bs, const float* bt, void* c, int c_dtype,
@@ -839,7 +859,7 @@ hipError_t launch_stream(int m, int64_t n, int k, const uint8_t* a, const uint8_
   // one with the 88 KiB of NSTEP = 2); short-lived workgroups of a few rows
   // would spend their time on the activation slice and the reduction, and a
   // round begun by a few workgroups costs a whole workgroup lifetime.
-  const bool nstep2 = nsplit > 1 ? k % 4096 == 0 : k == 4096;
+  const bool nstep2 = stream_nstep2(k);
   const int64_t slots = nstep2 || XH == 2 ? kStrGroups : 2 * kStrGroups;
   int rows = (int)((n + kStrGroups - 1) / kStrGroups);
   if (nsplit > 1 || n > 16 * kStrTiles * kStrGroups) {
@@ -859,30 +879,37 @@ hipError_t launch_stream(int m, int64_t n, int k, const uint8_t* a, const uint8_
   return hipGetLastError();
 }
 
-// Chunks of the split-k stream kernel for NVFP4 codes with m <= 8 and k >
-// 4096 a multiple of 2048: chunks of 4096 values when k allows, else 2048,
-// as long as workgroups of at most 64 rows cover every chunk in one round of
+// Chunks of the split-k stream kernel for NVFP4 codes with m <= 8 and more
+// than one chunk of k (gemm_stream_chunks): whole chunks, as long as
+// workgroups of at most 64 rows cover every chunk in one round of
 // co-resident workgroups (two per CU for chunks of 2048, one for 4096); 0
-// for any other shape.  Without the split, a long k and few rows (a down
-// projection, say) leave few workgroups, each walking all of k; with more
-// than one round, the unsplit kernels measured faster.
+// for any other shape.  Without
+// the split, a long k and few rows (a down projection, say) leave few
+// workgroups, each walking all of k; with more than one round, the unsplit
+// kernels measured faster.
 int stream_split(int fmt, int64_t m, int64_t n, int64_t k) {
-  if (fmt != kFmtNV || m < 1 || m > 8 || n < 1 || k <= 4096 || k % 2048 != 0) return 0;
-  const bool nstep2 = k % 4096 == 0;
-  const int64_t s = nstep2 ? k / 4096 : k / 2048;
-  const int64_t slots = nstep2 ? kStrGroups : 2 * kStrGroups;
+  if (fmt != kFmtNV || m < 1 || m > 8 || n < 1) return 0;
+  const int64_t s = gemm_stream_chunks(k);
+  if (s < 2) return 0;
+  // a k the older decode kernel cannot take (not a multiple of 1024): any
+  // round count, as the generic kernel would be slower still.  A short last
+  // chunk where that kernel can take k measured slower (8x5120x5120: 10.9
+  // us split, 10.1 on the older kernel).
+  if (k % kDecKC != 0) return s <= 64 ? (int)s : 0;
+  if (k % 2048 != 0) return 0;
+  const int64_t slots = stream_nstep2(k) ? kStrGroups : 2 * kStrGroups;
   return (n + 16 * kStrTiles - 1) / (16 * kStrTiles) * s <= slots ? (int)s : 0;
 }
 
-// Chunks of the split-k stream kernel for NVFP4 codes with 9..16 rows and k >
-// 4096 a multiple of 2048 (chunks of 4096 when k allows, else 2048; at most
-// 64), in whole rounds of workgroups for any n; 0 for any other shape.  With
-// 16 activation rows per workgroup, the weights' dequantization is shared
-// by twice the columns, so more than one round still pays here.
+// Chunks of the split-k stream kernel for NVFP4 codes with 9..16 rows and
+// 2 to 64 chunks of k, in whole rounds of workgroups for any n; 0 for any
+// other shape.  With 16 activation rows per workgroup, the weights'
+// dequantization is shared by twice the columns, so more than one round
+// still pays here.
 int stream_split16(int fmt, int64_t m, int64_t n, int64_t k) {
-  if (fmt != kFmtNV || m <= 8 || m > 16 || n < 1 || k <= 4096 || k % 2048 != 0) return 0;
-  const int64_t s = k % 4096 == 0 ? k / 4096 : k / 2048;
-  return s <= 64 ? (int)s : 0;
+  if (fmt != kFmtNV || m <= 8 || m > 16 || n < 1) return 0;
+  const int64_t s = gemm_stream_chunks(k);
+  return s >= 2 && s <= 64 ? (int)s : 0;
 }
 
 }  // namespace
@@ -900,12 +927,14 @@ hipError_t launch_gemm_skinny(int fmt, int64_t m, int64_t n, int64_t k,
   const bool aligned16 = ((reinterpret_cast<uintptr_t>(b_scales) | reinterpret_cast<uintptr_t>(b_codes) |
                            reinterpret_cast<uintptr_t>(a_codes)) & 15) == 0 &&
                          (reinterpret_cast<uintptr_t>(a_scales) & 1) == 0;
-  if (fmt == kFmtNV && stream_shape(m, n, k) && aligned16)
+  // one chunk of k (2048..4096 values), n within one round
+  if (fmt == kFmtNV && m >= 1 && m <= 8 && gemm_stream_chunks(k) == 1 && n >= 1 &&
+      n <= 16 * kStrTiles * kStrGroups && aligned16)
     return launch_stream<kXCodes>((int)m, n, (int)k, a_codes, a_scales, a_tscale, b_codes, b_scales,
                                   b_tscale, c, c_dtype, nullptr, nullptr, nullptr, stream);
   // 9..16 rows: any n (past 16384 rows, whole rounds of up-to-64-row
   // workgroups); 8 rows past 16384 keep the older decode kernel below, as fast
-  if (fmt == kFmtNV && m > 8 && m <= 16 && (k == 2048 || k == 4096) && n >= 1 && aligned16)
+  if (fmt == kFmtNV && m > 8 && m <= 16 && gemm_stream_chunks(k) == 1 && n >= 1 && aligned16)
     return launch_stream<kXCodes, 2>((int)m, n, (int)k, a_codes, a_scales, a_tscale, b_codes, b_scales,
                                      b_tscale, c, c_dtype, nullptr, nullptr, nullptr, stream);
   const int nsplit = m > 8 ? stream_split16(fmt, m, n, k) : stream_split(fmt, m, n, k);
@@ -960,14 +989,12 @@ bool launch_quantize_gemm_decode(int64_t m, int64_t n, int64_t k, const void* x,
 
 namespace {
 
-// W4A16 chunks of k on the stream kernel for NVFP4 weights: 1 for k = 2048
-// or 4096, the chunks of 4096 (k a multiple of 4096) or 2048 for a longer k
-// (at most 64), 0 for any other k.  Any n: past 16384 rows the workgroups
-// take up to 64 rows in whole rounds.
+// W4A16 chunks of k on the stream kernel for NVFP4 weights (at most 64 of
+// gemm_stream_chunks), 0 for any other k.  Any n: past 16384 rows the
+// workgroups take up to 64 rows in whole rounds.
 int w4a16_chunks(int fmt, int64_t n, int64_t k) {
-  if (fmt != kFmtNV || n < 1 || k % 2048 != 0) return 0;
-  if (k <= 4096) return 1;
-  const int64_t s = k % 4096 == 0 ? k / 4096 : k / 2048;
+  if (fmt != kFmtNV || n < 1) return 0;
+  const int64_t s = gemm_stream_chunks(k);
   return s <= 64 ? (int)s : 0;
 }
 

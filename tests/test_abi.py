@@ -58,7 +58,16 @@ def test_workspace_sizes():
     assert L.fp4_gemm_workspace_size(NV, 16, 14336, 8192) == 2 * 16 * 14336 * 4
     assert L.fp4_gemm_workspace_size(NV, 32, 4096, 14336) == 7 * 16 * 4096 * 4   # groups of 16 rows
     assert L.fp4_gemm_workspace_size(NV, 16, 4096, 4096) == 0      # one chunk: no split
-    assert L.fp4_gemm_workspace_size(NV, 8, 4096, 5120) == 0       # k not a multiple of 2048
+    # k not a multiple of 2048: chunks of 2048 (4096 when k is a multiple of
+    # 4096), the last one short; a k that is no multiple of 1024 in any round count
+    assert L.fp4_gemm_workspace_size(NV, 8, 5120, 5120) == 0       # the older kernel takes k = 5120
+    assert L.fp4_gemm_workspace_size(NV, 8, 5120, 4608) == 3 * 8 * 5120 * 4   # it does not take 4608
+    assert L.fp4_gemm_workspace_size(NV, 8, 5120, 13824) == 7 * 8 * 5120 * 4
+    assert L.fp4_gemm_workspace_size(NV, 8, 13824, 5120) == 0      # 648 workgroups: the older kernel
+    assert L.fp4_gemm_workspace_size(NV, 16, 2000, 5120) == 3 * 16 * 2000 * 4
+    assert L.fp4_gemm_workspace_size(NV, 4, 3000, 3072) == 0       # one chunk
+    assert L.fp4_gemm_workspace_size(NV, 8, 64, 4160) == 0         # k % 128 != 0: not the stream kernel
+    assert L.fp4_gemm_workspace_size(NV, 8, 4096, 5120) == 0       # a short last chunk: the older kernel
     assert L.fp4_gemm_workspace_size(MX, 8, 4096, 14336) == 7 * 8 * 4096 * 4   # MXFP4: m <= 16, any n
     assert L.fp4_gemm_workspace_size(MX, 16, 16384, 6144) == 3 * 16 * 16384 * 4
     assert L.fp4_gemm_workspace_size(MX, 32, 4096, 14336) == 7 * 16 * 4096 * 4   # groups of 16 rows
@@ -161,13 +170,15 @@ def test_gemm_w4a16_rejects_bad_arguments():
     assert g(fmt=MX) == E                                # MXFP4 takes none
     assert g(x=FAKE_ODD) == E
     assert g(m=0, x=None, c=None) == fp4.OK
-    # NVFP4 with k > 4096 (a multiple of 2048): chunk sums of up to 16 rows
+    # NVFP4 with more than one chunk of k: chunk sums of up to 16 rows
     ws = fp4.lib().fp4_gemm_w4a16_workspace_size
     assert ws(NV, 8, 64, 8192) == 2 * 8 * 64 * 4
     assert ws(NV, 20, 64, 14336) == 7 * 16 * 64 * 4
     assert ws(NV, 12, 5, 14336) == 7 * 60 * 4
     assert ws(NV, 3, 5, 6144) == 3 * 16 * 4
-    assert ws(NV, 8, 64, 4096) == 0 and ws(NV, 8, 64, 5120) == 0
+    assert ws(NV, 8, 64, 4096) == 0 and ws(NV, 8, 64, 3072) == 0
+    assert ws(NV, 8, 64, 5120) == 3 * 8 * 64 * 4                  # the last chunk half empty
+    assert ws(NV, 8, 64, 4160) == 0                               # k % 128 != 0: the fallback kernel
     assert ws(MX, 8, 64, 8192) == 2 * 8 * 64 * 4 and ws(MX, 20, 64, 14336) == 7 * 16 * 64 * 4
     assert g(k=8192) == E                                # workspace missing
     assert g(k=8192, ws=FAKE, wsb=2 * 8 * 64 * 4 - 1) == E
@@ -220,6 +231,13 @@ def test_gemm_rejects_bad_arguments():
     assert g(fmt=MX, at=None, bt=None, n=64, k=8192, ws=FAKE_ODD, wsb=need) == E
     assert g(n=64, k=8192) == E                                            # NVFP4 likewise
     assert g(n=64, k=8192, ws=FAKE, wsb=fp4.lib().fp4_gemm_workspace_size(NV, 8, 64, 8192) - 1) == E
+    # 9..16 NVFP4 rows with a long k, and the 16-row groups of a small batch
+    for m in (12, 40):
+        need = fp4.lib().fp4_gemm_workspace_size(NV, m, 64, 14336)
+        assert need == 7 * min(m, 16) * 64 * 4
+        assert g(m=m, n=64, k=14336) == E
+        assert g(m=m, n=64, k=14336, ws=FAKE, wsb=need - 1) == E
+        assert g(m=m, n=64, k=14336, ws=FAKE_ODD, wsb=need) == E
 
 
 def test_quantize_gemm_rejects_bad_arguments():

@@ -155,6 +155,8 @@ def test_mxfp4_decode_stream(m, n, k, out_dtype):
     ("nvfp4", 64, 4096, 14336, "bf16"),   # four groups
     ("nvfp4", 65, 4096, 14336, "bf16"),   # a long k from 65 rows: the large kernel
     ("nvfp4", 100, 2000, 12288, "f32"),
+    ("nvfp4", 40, 5120, 13824, "bf16"),   # a k that is no multiple of 2048: 16-row groups, 7 chunks
+    ("nvfp4", 33, 3000, 3072, "f32"),     # one short chunk per group
     ("mxfp4", 17, 777, 4096, "f32"),
     ("mxfp4", 32, 5000, 8192, "bf16"),    # two groups, each with k split in 2 chunks
     ("mxfp4", 33, 14336, 4096, "f32"),    # 33..255 rows: the large kernel, one row of tiles at row 0
@@ -180,6 +182,9 @@ def test_small_batch_groups(fmt, m, n, k, out_dtype):
     (12, 16384, 2048, "bf16"),     # the largest n of one round
     (16, 20000, 4096, "f32"),      # past it: whole rounds of workgroups
     (16, 333, 4096, "f32"),        # ragged shares
+    (4, 3000, 3072, "bf16"),       # one chunk of 4096, 12 of 16 slices
+    (11, 20000, 3072, "f32"),      # the same with 11 rows, whole rounds of workgroups
+    (3, 1000, 2304, "bf16"),       # 9 of 16 slices
 ])
 def test_nvfp4_decode_16_rows(m, n, k, out_dtype):
     # the NVFP4 decode stream kernel with 9 to 16 activation rows
@@ -200,6 +205,10 @@ def test_nvfp4_decode_16_rows(m, n, k, out_dtype):
     (9, 20000, 8192, "f32"),       # 9 rows, whole rounds of workgroups
     (12, 777, 6144, "bf16"),       # ragged n
     (13, 3000, 16384, "f32"),      # 4 chunks of 4096
+    (8, 5120, 4608, "bf16"),       # k no multiple of 1024: 3 chunks, the last a quarter full
+    (8, 5120, 13824, "f32"),       # 7 chunks over more than one round (k % 1024 != 0)
+    (16, 2000, 5120, "bf16"),      # 16 rows, 3 chunks
+    (12, 777, 2176, "f32"),        # 2 chunks, the second with one slice of 128 values
 ])
 def test_nvfp4_decode_split_k(m, n, k, out_dtype):
     # the NVFP4 decode kernel with k split over workgroup rows (fp32 partial
@@ -347,6 +356,8 @@ def test_rotated_full_size():
     ("nvfp4", 7, 1025, 2048, torch.bfloat16),    # 3 rows per share, last share partial
     ("nvfp4", 16, 64, 256, torch.bfloat16),      # m > 8: quantize + GEMM calls
     ("nvfp4", 8, 4096, 14336, torch.bfloat16),   # long k: quantize + split-k GEMM
+    ("nvfp4", 12, 4096, 14336, torch.bfloat16),  # the same with 16 activation rows per workgroup
+    ("nvfp4", 40, 1000, 8192, torch.bfloat16),   # quantize + 16-row groups of the split-k GEMM
     ("nvfp4", 16, 2000, 4096, torch.bfloat16),   # 16 rows in one launch
     ("nvfp4", 9, 16384, 4096, torch.bfloat16),   # 9 rows in one launch, the largest n
     ("nvfp4", 12, 1000, 2048, torch.bfloat16),

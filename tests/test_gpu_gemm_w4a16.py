@@ -63,7 +63,11 @@ def test_decode_shape():
     (16, 20000, 2048),       # 16 rows past 16384 weight rows (one workgroup per CU)
     (11, 3000, 12288),       # 11 rows, 3 chunks of 4096
     (4, 200, 96),            # k outside the streaming path
-    (4, 200, 5120),          # k > 4096 but not a multiple of 2048: the fallback kernel
+    (4, 200, 5120),          # 3 chunks of 2048, the last half empty
+    (8, 5120, 13824),        # 7 chunks, the last three quarters full
+    (12, 2000, 3072),        # one chunk of 4096, 12 of 16 slices
+    (40, 1000, 5120),        # three launches of up to 16 rows
+    (4, 200, 4160),          # k not a multiple of 128: the fallback kernel
 ])
 def test_shapes(m, n, k):
     if k > 4096 and k % 2048 == 0:
@@ -98,6 +102,7 @@ def test_mxfp4_stream(m, n, k):
     (8, 14336, 4096),        # the decode shape with fp16 activations
     (16, 333, 2048),         # 16 rows in one launch
     (5, 4096, 14336),        # k split in 7 chunks of 2048
+    (16, 2000, 2304),        # one chunk of 4096, 9 of 16 slices
 ])
 def test_fp16_activations_stream(m, n, k):
     # NVFP4 weights and fp16 X on the decode stream kernel: X widened
