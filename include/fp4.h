@@ -307,8 +307,10 @@ size_t fp4_quantize_gemm_workspace_size(fp4_format fmt, int64_t m, int64_t n,
  * online).  With bf16 x and 1 <= m <= 16 the activation quantization
  * happens inside the GEMM's launch: NVFP4 for k = 2048 or 4096 and
  * n <= 16384 (every workgroup reducing max |x| over the whole tensor
- * itself), MXFP4 for k a multiple of 2048 and any n (no tensor-wide maximum;
- * k > 4096 adds the reduction pass of the split k).  Otherwise it runs as
+ * itself), MXFP4 for k a multiple of 128 from 2048 on and any n (no
+ * tensor-wide maximum; a k of more than one chunk -- past 4096 values, or
+ * past 2048 where k is not a multiple of 4096 -- adds the reduction pass of
+ * the split k).  Otherwise it runs as
  * the two calls.
  *   x            in, [m, k] of x_dtype, 16-byte aligned.
  *   a_codes, a_scales, a_tscale   out, as fp4_quantize (COMPUTE mode).

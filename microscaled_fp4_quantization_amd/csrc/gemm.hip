@@ -8,7 +8,6 @@ hipError_t launch_gemm_simple(int fmt, int64_t m, int64_t n, int64_t k,
                               void* c, int c_dtype, hipStream_t stream);
 
 size_t gemm_skinny_workspace_bytes(int fmt, int64_t m, int64_t n, int64_t k);
-int64_t gemm_stream_chunks(int64_t k);
 hipError_t launch_gemm_skinny(int fmt, int64_t m, int64_t n, int64_t k,
                               const uint8_t* a_codes, const uint8_t* a_scales,
                               const float* a_tscale, const uint8_t* b_codes,
@@ -31,14 +30,14 @@ hipError_t launch_gemm_large(int fmt, int64_t m, int64_t n, int64_t k,
 // - NVFP4 with one chunk of k (2048..4096 values) below 96 rows.  The generic kernel took
 //   105-207 us for 17..100 rows of a 14336x4096 weight, the decode kernel
 //   10 us per 16 rows.
-// - NVFP4 with a longer k (a multiple of 2048, at most 64 chunks of the
-//   split-k decode kernel) up to 64 rows.  A group costs about what 16 rows
+// - NVFP4 with a longer k (2 to 64 chunks of the split-k decode kernel) up
+//   to 64 rows.  A group costs about what 16 rows
 //   alone do (13.6 us for a 4096x14336 weight, 38 us for 8192x28672, 9.5
 //   us for 4096x8192), the large kernel with one row of tiles a flat 84,
 //   146 and 55 us: four groups tie or win on all three, more lose on the
 //   largest.
-// - MXFP4 up to 32 rows; from 33 the large kernel (one row of tiles) is as
-//   fast as two groups.
+// - MXFP4 up to 32 rows (k as below); from 33 the large kernel (one row of
+//   tiles) is as fast as two groups.
 constexpr int64_t kNvLongGroupsBelow = 65;
 
 bool nv_long_k_chunks(int64_t k) {
@@ -49,7 +48,11 @@ bool nv_long_k_chunks(int64_t k) {
 bool small_batch_groups(int fmt, int64_t m, int64_t n, int64_t k) {
   if (m <= 16) return false;
   if (fmt == kFmtNV) return gemm_stream_chunks(k) == 1 ? m < 96 : nv_long_k_chunks(k) && m < kNvLongGroupsBelow;
-  return m <= 32 && k % 2048 == 0;
+  // MXFP4: k a multiple of 2048, or a longer k than 8192 with a short last
+  // chunk (32x5120x13824: 39.5 us in groups, 75 on the generic kernel;
+  // 32x13824x5120: 41.5 in groups, 35 generic)
+  const int64_t s = gemm_stream_chunks(k);
+  return m <= 32 && s >= 1 && s <= 64 && (k % 2048 == 0 || k > 8192);
 }
 
 // NVFP4 below 128 rows past the groups (from 96 rows, or from 65 with a

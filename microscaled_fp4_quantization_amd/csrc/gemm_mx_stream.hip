@@ -1,4 +1,4 @@
-// MXFP4 W4A4 decode GEMM (m <= 16, k a multiple of 2048, any n): a weight
+// MXFP4 W4A4 decode GEMM (m <= 16, k a multiple of 128 from 2048 on, any n): a weight
 // stream on the block-scaled FP4 matrix instruction.  C[m, n] = sum_k
 // deq(X)[m, k] deq(W)[n, k], with or without the activation quantize in the
 // same launch.
@@ -15,9 +15,11 @@
 // operand with its E8M0 scale byte.  Nothing is dequantized: the matrix core
 // applies both operands' block scales, so the products are exact and the sums
 // are fp32.  The same lane holds the same 32 positions of activation row r
-// (a zero operand for r >= m).  A k longer than 4096 is split over rows of
-// workgroups, each row's fp32 sums added by a second pass in order; past
-// 16384 weight rows the workgroups take up to 64 rows in whole rounds.
+// (a zero operand for r >= m).  A k of more than one chunk (2048 values, or
+// 4096) is split over rows of workgroups, each row's fp32 sums added by a
+// second pass in order; in a short last chunk the slices past k add
+// nothing.  Past 16384 weight rows the workgroups take up to 64 rows in
+// whole rounds.
 //
 // The activations (XM):
 //   kMxCodes  MXFP4 codes and scales.
@@ -108,7 +110,10 @@ __global__ __launch_bounds__(64 * kMxWaves) void gemm_mx_stream(
   // split k (part != nullptr): workgroup row blockIdx.y takes the 2048 NSTEP
   // values from kc0 on, and its fp32 sums go to part
   const int kc0 = (int)blockIdx.y * (kMxWaves * 128 * NSTEP);
-  const int ks0 = kc0 + wave * (128 * NSTEP);         // first value of this wave's slice
+  // k not a whole number of chunks: a slice that starts past k loads the
+  // last slice again, in bounds, and adds (and writes) nothing
+  const bool kdead = kc0 + wave * (128 * NSTEP) >= k;
+  const int ks0 = kdead ? k - 128 * NSTEP : kc0 + wave * (128 * NSTEP);   // first value of this wave's slice
   const int64_t kbytes = k / 2, kblocks = k / 32;
 
   // ---- activations: row r, block ks0 / 32 + 4 t + g of step t ----------------
@@ -183,7 +188,7 @@ __global__ __launch_bounds__(64 * kMxWaves) void gemm_mx_stream(
       }
       asb[t] = (uint32_t)(kx + 127);
       av[t] = (u32x4){q[0], q[1], q[2], q[3]};
-      if (blockIdx.x == 0 && alive) {
+      if (blockIdx.x == 0 && alive && !kdead) {
         *reinterpret_cast<u32x4*>(qcodes + arow * kbytes + ks0 / 2 + 64 * t + 16 * g) = av[t];
         qscales[arow * kblocks + ks0 / 32 + 4 * t + g] = (uint8_t)asb[t];
       }
@@ -230,7 +235,7 @@ __global__ __launch_bounds__(64 * kMxWaves) void gemm_mx_stream(
 
   // ---- add the 16 slices, store ------------------------------------------------
 #pragma unroll
-  for (int tl = 0; tl < NT; ++tl) tiles[wave][tl][lane] = acc[tl];
+  for (int tl = 0; tl < NT; ++tl) tiles[wave][tl][lane] = kdead ? (v4f){0.f, 0.f, 0.f, 0.f} : acc[tl];
   __syncthreads();
   if (tid < 64 * NT) {                                // thread -> (tile, lane)
     const int tl = tid >> 6, l = tid & 63;
@@ -263,24 +268,23 @@ __global__ __launch_bounds__(64 * kMxWaves) void gemm_mx_stream(
   }
 }
 
-// Chunks of k for up to 16 activation rows: 1 for k = 2048 or 4096, and for
-// a longer k that is a multiple of 2048 the chunks of 4096 (k a multiple of
-// 4096) or 2048, at most 64; 0 for any other shape.  Any n.
+// Chunks of k for up to 16 activation rows (gemm_stream_chunks: chunks of
+// 2048 values, of 4096 for a multiple of 4096 or a k up to 4096 that is a
+// multiple of 256; the last one possibly short), at most 64; 0 for any
+// other shape.  Any n.
 int mx_chunks(int64_t m, int64_t n, int64_t k) {
-  if (m < 1 || m > 16 || n < 1 || k % 2048 != 0) return 0;
-  if (k <= 4096) return 1;
-  const int64_t s = k % 4096 == 0 ? k / 4096 : k / 2048;
+  if (m < 1 || m > 16 || n < 1) return 0;
+  const int64_t s = gemm_stream_chunks(k);
   return s <= 64 ? (int)s : 0;
 }
 
-// One launch for up to 16 activation rows; nsplit > 1: k in nsplit chunks
-// (NSTEP = 2 when k is a multiple of 4096), the chunks' fp32 sums in part,
-// added by the reduction pass.
+// One launch for up to 16 activation rows; nsplit > 1: k in nsplit chunks,
+// the chunks' fp32 sums in part, added by the reduction pass.
 template <int XM>
 hipError_t launch_mx_stream(int m, int64_t n, int k, const void* a, const uint8_t* as, const uint8_t* b,
                             const uint8_t* bs, void* c, int c_dtype, uint8_t* qcodes, uint8_t* qscales,
                             int nsplit, float* part, hipStream_t stream) {
-  const bool nstep2 = nsplit > 1 ? k % 4096 == 0 : k == 4096;
+  const bool nstep2 = k % 4096 == 0 || (k > 2048 && k <= 4096 && k % 256 == 0);   // chunks of 4096
   // one workgroup per CU-share of rows; with a split or past 16384 rows, as
   // many rows (at most 64) as fill whole rounds of co-resident workgroups
   // (two per CU with NSTEP = 1, one with NSTEP = 2)

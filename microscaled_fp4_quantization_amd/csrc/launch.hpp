@@ -42,6 +42,8 @@ size_t gemm_workspace_bytes(int fmt, int64_t m, int64_t n, int64_t k);
 // rounded up to a multiple of 4), and the pass that adds the nsplit slices
 // in order, applies at * bt (NVFP4; at == nullptr: 1) and stores C.
 int64_t gemm_split_stride(int64_t m, int64_t n);
+// chunks of k for the decode stream kernels (0: a k they do not take)
+int64_t gemm_stream_chunks(int64_t k);
 hipError_t launch_split_reduce(const float* part, int nsplit, int64_t m, int64_t n, const float* at,
                                const float* bt, void* c, int c_dtype, hipStream_t stream);
 

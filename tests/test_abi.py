@@ -72,6 +72,10 @@ def test_workspace_sizes():
     assert L.fp4_gemm_workspace_size(MX, 16, 16384, 6144) == 3 * 16 * 16384 * 4
     assert L.fp4_gemm_workspace_size(MX, 32, 4096, 14336) == 7 * 16 * 4096 * 4   # groups of 16 rows
     assert L.fp4_gemm_workspace_size(MX, 33, 4096, 14336) == 0   # the large kernel, one row of tiles
+    assert L.fp4_gemm_workspace_size(MX, 8, 4096, 5120) == 3 * 8 * 4096 * 4     # a short last chunk
+    assert L.fp4_gemm_workspace_size(MX, 24, 4096, 13824) == 7 * 16 * 4096 * 4  # groups of 16 rows
+    assert L.fp4_gemm_workspace_size(MX, 24, 4096, 5120) == 0    # the generic kernel
+    assert L.fp4_gemm_workspace_size(MX, 8, 4096, 3072) == 0     # one chunk
 
 
 def _q(fn, fmt=NV, x=FAKE, dt=fp4.BF16, rows=4, k=64, codes=FAKE, scales=FAKE,
@@ -180,6 +184,7 @@ def test_gemm_w4a16_rejects_bad_arguments():
     assert ws(NV, 8, 64, 5120) == 3 * 8 * 64 * 4                  # the last chunk half empty
     assert ws(NV, 8, 64, 4160) == 0                               # k % 128 != 0: the fallback kernel
     assert ws(MX, 8, 64, 8192) == 2 * 8 * 64 * 4 and ws(MX, 20, 64, 14336) == 7 * 16 * 64 * 4
+    assert ws(MX, 8, 64, 5120) == 3 * 8 * 64 * 4 and ws(MX, 8, 64, 4160) == 0
     assert g(k=8192) == E                                # workspace missing
     assert g(k=8192, ws=FAKE, wsb=2 * 8 * 64 * 4 - 1) == E
     assert g(k=8192, ws=FAKE_ODD, wsb=2 * 8 * 64 * 4) == E

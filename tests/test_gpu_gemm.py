@@ -130,6 +130,10 @@ def test_mxfp4_many_tiles(m, n, k, out_dtype):
     (8, 4096, 14336, "bf16"),      # a down projection: k split in 7 chunks of 2048
     (16, 20000, 2048, "f32"),      # past 16384 weight rows: whole rounds of workgroups
     (3, 777, 12288, "bf16"),       # 3 chunks of 4096
+    (8, 5120, 13824, "f32"),       # 7 chunks, the last three quarters full
+    (16, 3000, 5120, "bf16"),      # 3 chunks, the last half empty
+    (3, 1000, 3072, "f32"),        # one chunk of 4096, 12 of 16 slices
+    (12, 777, 2176, "bf16"),       # 2 chunks, the second with one slice
 ])
 def test_mxfp4_decode_stream(m, n, k, out_dtype):
     # the MXFP4 decode kernel on the block-scaled FP4 matrix instruction
@@ -159,6 +163,8 @@ def test_mxfp4_decode_stream(m, n, k, out_dtype):
     ("nvfp4", 33, 3000, 3072, "f32"),     # one short chunk per group
     ("mxfp4", 17, 777, 4096, "f32"),
     ("mxfp4", 32, 5000, 8192, "bf16"),    # two groups, each with k split in 2 chunks
+    ("mxfp4", 24, 3000, 9216, "f32"),     # two groups, 5 chunks of 2048, the last half full
+    ("mxfp4", 24, 3000, 5120, "f32"),     # a short last chunk of a k up to 8192: the generic kernel
     ("mxfp4", 33, 14336, 4096, "f32"),    # 33..255 rows: the large kernel, one row of tiles at row 0
     ("mxfp4", 48, 5000, 8192, "bf16"),
     ("mxfp4", 128, 28672, 2048, "bf16"),  # the same, every tile half-width
@@ -368,6 +374,8 @@ def test_rotated_full_size():
     ("mxfp4", 3, 16384, 4096, torch.bfloat16),
     ("mxfp4", 5, 64, 1024, torch.bfloat16),      # k outside the one-launch path: two calls
     ("mxfp4", 8, 4096, 14336, torch.bfloat16),   # one launch over 7 chunks of k + the reduction
+    ("mxfp4", 8, 5120, 13824, torch.bfloat16),   # the last chunk three quarters full (its codes too)
+    ("mxfp4", 12, 1000, 3072, torch.bfloat16),   # one chunk, 12 of 16 slices
 ])
 def test_quantize_gemm(fmt, m, n, k, xdt):
     g = torch.Generator().manual_seed(4)

@@ -83,6 +83,8 @@ def test_shapes(m, n, k):
     (20, 1000, 4096),        # launches of 16 and 4 rows
     (8, 4096, 14336),        # k split in 7 chunks of 2048
     (20, 17000, 8192),       # 2 chunks of 4096 past 16384 weight rows, two launches
+    (8, 5120, 13824),        # 7 chunks, the last three quarters full
+    (12, 2000, 3072),        # one chunk of 4096, 12 of 16 slices
 ])
 def test_mxfp4_stream(m, n, k):
     # W4A16 with MXFP4 weights on the decode stream kernel (bf16 products of
