@@ -444,9 +444,10 @@ __global__ __launch_bounds__(64 * kStrWaves) void gemm_nv_stream(
   // split k (part != nullptr; codes in or W4A16): workgroup row blockIdx.y
   // takes the 2048 NSTEP values from kc0 on, and its fp32 sums go to part
   const int kc0 = (int)blockIdx.y * (kStrWaves * 128 * NSTEP);
-  // k not a whole number of chunks (codes in, W4A16): a slice that starts
-  // past k loads the last slice again, in bounds, and adds nothing
-  const bool kdead = kc0 + wave * (128 * NSTEP) >= k;
+  // k not a whole number of chunks (codes in, W4A16; the one-launch
+  // quantize takes whole chunks only): a slice that starts past k loads the
+  // last slice again, in bounds, and adds nothing
+  const bool kdead = !GMAX && kc0 + wave * (128 * NSTEP) >= k;
   const int ks0 = kdead ? k - 128 * NSTEP : kc0 + wave * (128 * NSTEP);   // first value of this wave's slice
   const int64_t kbytes = k / 2, kblocks = k / 16;
 
