@@ -27,15 +27,14 @@ hipError_t launch_gemm_large(int fmt, int64_t m, int64_t n, int64_t k,
 // workgroup rows; the slices' fp32 sums go to the workspace.
 // A small batch past 16 rows on the decode kernels, in groups of 16
 // activation rows, W streamed once per group:
-// - NVFP4 with one chunk of k (2048..4096 values) below 96 rows.  The generic kernel took
-//   105-207 us for 17..100 rows of a 14336x4096 weight, the decode kernel
-//   10 us per 16 rows.
+// - NVFP4 with one chunk of k (2048..4096 values) below 96 rows.  The
+//   generic kernel took 105-207 us for 17..100 rows of a 14336x4096 weight,
+//   the decode kernel 10 us per 16 rows.
 // - NVFP4 with a longer k (2 to 64 chunks of the split-k decode kernel) up
-//   to 64 rows.  A group costs about what 16 rows
-//   alone do (13.6 us for a 4096x14336 weight, 38 us for 8192x28672, 9.5
-//   us for 4096x8192), the large kernel with one row of tiles a flat 84,
-//   146 and 55 us: four groups tie or win on all three, more lose on the
-//   largest.
+//   to 64 rows.  A group costs about what 16 rows alone do (13.6 us for a
+//   4096x14336 weight, 38 us for 8192x28672, 9.5 us for 4096x8192), the
+//   large kernel with one row of tiles a flat 84, 146 and 55 us: four
+//   groups tie or win on all three, more lose on the largest.
 // - MXFP4 up to 32 rows (k as below); from 33 the large kernel (one row of
 //   tiles) is as fast as two groups.
 constexpr int64_t kNvLongGroupsBelow = 65;
